@@ -1,0 +1,262 @@
+"""CPU oracle for the sparse Mixture-of-Experts MLP block (Qwen3-MoE / Qwen3-VL-MoE).
+
+TEST INFRASTRUCTURE ONLY. This module is imported by the tests, by the package's smoke check and
+by the CPU-baseline leg of the benchmark. The product path never imports, calls or falls back to it.
+It shares no code with the HIP path: plain NumPy, float64 unless a page fixes the precision.
+
+Page names used in citations:
+  [MoE-ch27]  "27. Mixture of experts" (inference.shantanugoel.com/27-moe)
+  [VL-MoE-src] the Qwen3-VL-MoE source walk-through (agent.csdn.net article on qwen3_vl_moe)
+  [VL-post]   "Qwen3-VL + MoE: train to deploy" (gopikrishnatummala.com)
+  [Keras]     "Qwen3-VL-MoE" Keras port docs (imvision12.github.io/ZeroModels/qwen3_vl_moe)
+  [30B-cfg]   Qwen3-VL-30B-A3B MoE architecture explainer (adg.csdn.net)
+
+Every function is pinned by tests in tests/test_oracle.py against the pages' worked examples,
+closed forms, special cases and brute force, except where its docstring says "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------------------------
+# Router: [MoE-ch27] section "The router" (steps 1-3 and the TopKRouter description);
+#         [VL-MoE-src] routing section of Qwen3VLMoeTextSparseMoeBlock.forward.
+# --------------------------------------------------------------------------------------------
+
+def router_logits(x, w_router):
+    """logits[n, e] = sum_d x[n, d] * W_r[e, d]: one linear layer, no bias ([MoE-ch27] "The router").
+
+    Computed in float64 from the stored values, so for bf16 or fp32 inputs it is exact up to
+    float64 summation rounding."""
+    return np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+
+
+def softmax(logits, dtype=np.float32):
+    """Softmax over all experts, max-subtracted. The page fixes FP32 for this step ([MoE-ch27],
+    "The router", step 1, and the parity note after the example), so the default takes the
+    float64 logits to float32 and does exp, sum and divide in float32. ``dtype=np.float64``
+    gives the same definition at higher precision (used to cross-check)."""
+    lg = np.asarray(logits).astype(dtype)
+    m = lg.max(axis=-1, keepdims=True)
+    ex = np.exp(lg - m)
+    return ex / ex.sum(axis=-1, keepdims=True)
+
+
+def select_top_k(probs, k):
+    """The k largest probabilities per token, in descending order; equal probabilities go to the
+    lower expert index ([MoE-ch27] "The router" step 2; ties broken by index per the parity note).
+
+    A stable sort of -p keeps equal keys in index order, which is exactly that rule."""
+    order = np.argsort(-probs, axis=-1, kind="stable")
+    experts = order[..., :k]
+    return experts.astype(np.int64), np.take_along_axis(probs, experts, axis=-1)
+
+
+def route(x, w_router, k, norm_topk_prob=True, prob_dtype=np.float32):
+    """x[N,D] -> (logits[N,E] f64, probs[N,E], weights[N,k], experts[N,k]).
+
+    Steps of [MoE-ch27] "The router": linear scores, FP32 softmax over all E, top-k, then divide the
+    kept weights by their sum when norm_topk_prob is set (step 3; also [VL-MoE-src], the
+    renormalisation step, which always applies it; [Keras] lists it as a flag)."""
+    logits = router_logits(x, w_router)
+    probs = softmax(logits, prob_dtype)
+    experts, weights = select_top_k(probs, k)
+    if norm_topk_prob:
+        weights = weights / weights.sum(axis=-1, keepdims=True)
+    return logits, probs, weights, experts
+
+
+def k_gap(probs, k):
+    """Per token, p_(k) - p_(k+1) of the sorted probabilities (inf when k == E). Used to find
+    tokens whose selection is decided by rounding (a near tie across the top-k boundary)."""
+    srt = -np.sort(-np.asarray(probs, np.float64), axis=-1)
+    if k >= srt.shape[-1]:
+        return np.full(srt.shape[:-1], np.inf)
+    return srt[..., k - 1] - srt[..., k]
+
+
+# --------------------------------------------------------------------------------------------
+# Experts: [MoE-ch27] section "Dispatch" (Experts: stacked gate_up_proj [E, 2I, D] with gate rows
+# first, down_proj [E, D, I]; expert(e, x) = down(silu(gate) * up)); [VL-MoE-src] expert section.
+# --------------------------------------------------------------------------------------------
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def swiglu(v, gate_up, down):
+    """One SwiGLU expert on rows v[m, D]: gate = first I rows of gate_up, up = last I rows,
+    out = (silu(v G^T) * (v U^T)) Dn^T, all in float64 ([MoE-ch27] "Dispatch", Experts.expert)."""
+    v = np.asarray(v, np.float64)
+    gu = np.asarray(gate_up, np.float64)
+    dn = np.asarray(down, np.float64)
+    inter = dn.shape[1]
+    g = v @ gu[:inter].T
+    u = v @ gu[inter:].T
+    return (silu(g) * u) @ dn.T
+
+
+# --------------------------------------------------------------------------------------------
+# Dispatch: [MoE-ch27] section "Dispatch: getting tokens to their experts", grouped form steps 1-4.
+# --------------------------------------------------------------------------------------------
+
+def permute(experts, n_experts):
+    """Sort the N*k assignments a = n*k + j by expert, stably ([MoE-ch27] "Dispatch", grouped step 1).
+
+    Returns counts[E] (bincount), offsets[E+1] (exclusive prefix sum; offsets[e] is where expert e's
+    rows start), order[A] (assignment id at each sorted position), token_of[A] = order // k
+    (step 2: which token row each sorted position reads) and slot_pos[A], the inverse of order
+    (sorted position of assignment a)."""
+    experts = np.asarray(experts)
+    k = experts.shape[-1]
+    flat = experts.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=n_experts)
+    offsets = np.zeros(n_experts + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    slot_pos = np.empty_like(order)
+    slot_pos[order] = np.arange(flat.size)
+    return counts, offsets, order, order // k, slot_pos
+
+
+def grouped_expert_ffn(x_rows, offsets, gate_up, down):
+    """Run group g's SwiGLU expert on its contiguous slice rows[offsets[g]:offsets[g+1]]
+    ([MoE-ch27] "Dispatch", grouped step 3). Empty groups are skipped. Returns out_perm[rows, D]."""
+    x_rows = np.asarray(x_rows, np.float64)
+    out = np.zeros((x_rows.shape[0], np.asarray(down).shape[-2]), np.float64)
+    for g in range(len(offsets) - 1):
+        a, b = int(offsets[g]), int(offsets[g + 1])
+        if b > a:
+            out[a:b] = swiglu(x_rows[a:b], gate_up[g], down[g])
+    return out
+
+
+def combine(out_perm, weights, slot_pos, shared_out=None, shared_scale=None):
+    """Unpermute: y[n] = sum_j w[n, j] * out_perm[slot_pos[n*k + j]] (+ shared_scale[n] * shared_out[n]).
+
+    This is [MoE-ch27] "Dispatch" grouped step 4 (multiply by the routing weight, then add each
+    token's k contributions back into its row), written as a gather over the token's own slots
+    instead of index_add_; the sum is the same."""
+    w = np.asarray(weights, np.float64)
+    n, k = w.shape
+    rows = np.asarray(out_perm, np.float64)[np.asarray(slot_pos).reshape(n, k)]   # [N, k, D]
+    y = np.einsum("nk,nkd->nd", w, rows)
+    if shared_out is not None:
+        s = np.ones(n) if shared_scale is None else np.asarray(shared_scale, np.float64)
+        y = y + s[:, None] * np.asarray(shared_out, np.float64)
+    return y
+
+
+def shared_expert(x, shared_gate_up, shared_down, w_shared_gate=None):
+    """(scale[N], out[N,D]): the always-on shared SwiGLU expert and its gate sigmoid(w_s . x)
+    ([MoE-ch27] "The shared expert", its equation and SparseMoeBlock). Without w_s the scale is 1
+    (an ungated shared expert, the DeepSeekMoE form named in [VL-post])."""
+    x = np.asarray(x, np.float64)
+    out = swiglu(x, shared_gate_up, shared_down)
+    if w_shared_gate is None:
+        return np.ones(x.shape[0]), out
+    return sigmoid(x @ np.asarray(w_shared_gate, np.float64)), out
+
+
+# --------------------------------------------------------------------------------------------
+# The whole block, in three written forms that must agree.
+# --------------------------------------------------------------------------------------------
+
+def forward_grouped(x, w_router, gate_up, down, k, norm_topk_prob=True,
+                    shared_gate_up=None, shared_down=None, w_shared_gate=None, routing=None):
+    """The block as [MoE-ch27] SparseMoeBlock.forward with grouped dispatch: route, sort by expert,
+    run each expert on its slice, weight, unpermute, then add the gated shared expert.
+
+    ``routing=(weights, experts)`` replaces the router's choice (used to force the oracle's choice
+    on the GPU path where a near tie makes the selection a matter of rounding).
+    Returns (y[N,D] float64, dict of intermediates)."""
+    x = np.asarray(x, np.float64)
+    E = np.asarray(w_router).shape[0]
+    if routing is None:
+        logits, probs, weights, experts = route(x, w_router, k, norm_topk_prob)
+    else:
+        weights, experts = routing
+        logits = probs = None
+    counts, offsets, order, token_of, slot_pos = permute(experts, E)
+    out_perm = grouped_expert_ffn(x[token_of], offsets, gate_up, down)
+    y = combine(out_perm, weights, slot_pos)
+    scale = None
+    if shared_gate_up is not None:
+        scale, s = shared_expert(x, shared_gate_up, shared_down, w_shared_gate)
+        y = y + scale[:, None] * s
+    return y, dict(logits=logits, probs=probs, weights=weights, experts=experts, counts=counts,
+                   offsets=offsets, token_of=token_of, slot_pos=slot_pos, shared_scale=scale)
+
+
+def forward_loop(x, w_router, gate_up, down, k, norm_topk_prob=True,
+                 shared_gate_up=None, shared_down=None, w_shared_gate=None):
+    """Loop dispatch ([MoE-ch27] "Dispatch", forward_loop; [VL-MoE-src] training branch): for each
+    expert that received tokens, gather them, run it, scatter-add the weighted result."""
+    x = np.asarray(x, np.float64)
+    _, _, weights, experts = route(x, w_router, k, norm_topk_prob)
+    y = np.zeros_like(x)
+    for e in np.unique(experts):
+        token, slot = np.nonzero(experts == e)
+        contrib = swiglu(x[token], gate_up[e], down[e]) * np.asarray(weights, np.float64)[token, slot, None]
+        np.add.at(y, token, contrib)
+    if shared_gate_up is not None:
+        scale, s = shared_expert(x, shared_gate_up, shared_down, w_shared_gate)
+        y = y + scale[:, None] * s
+    return y
+
+
+def forward_dense_masked(x, w_router, gate_up, down, k, norm_topk_prob=True,
+                         shared_gate_up=None, shared_down=None, w_shared_gate=None):
+    """Dense evaluation ([VL-MoE-src] inference branch): every expert on every token, multiplied by a
+    dense [N, E] routing matrix that is zero outside each token's top-k (the scatter_ step), summed
+    over experts. E/k times the necessary work: tiny inputs only."""
+    x = np.asarray(x, np.float64)
+    E = np.asarray(w_router).shape[0]
+    _, _, weights, experts = route(x, w_router, k, norm_topk_prob)
+    dense = np.zeros((x.shape[0], E), np.float64)
+    np.put_along_axis(dense, experts, np.asarray(weights, np.float64), axis=1)
+    all_out = np.stack([swiglu(x, gate_up[e], down[e]) for e in range(E)])   # [E, N, D]
+    y = np.einsum("ne,end->nd", dense, all_out)
+    if shared_gate_up is not None:
+        scale, s = shared_expert(x, shared_gate_up, shared_down, w_shared_gate)
+        y = y + scale[:, None] * s
+    return y
+
+
+# --------------------------------------------------------------------------------------------
+# Accounting used by the benchmark.
+# --------------------------------------------------------------------------------------------
+
+def moe_parameter_split(hidden, layers, experts, top_k, intermediate, shared_intermediate=0):
+    """(stored, active-per-token) expert parameters of the MLP part ([MoE-ch27] closing section,
+    moe_parameter_split): per expert 3*h*I; each layer also holds the router's E*h and a shared
+    expert's 3*h*I_s."""
+    per_expert = 3 * hidden * intermediate
+    shared = 3 * hidden * shared_intermediate
+    router = experts * hidden
+    return (layers * (experts * per_expert + shared + router),
+            layers * (top_k * per_expert + shared + router))
+
+
+def expected_touched_experts(n_experts, top_k, batch):
+    """E * (1 - (1 - k/E)^B): distinct experts a batch of B tokens touches when each picks k of E
+    roughly uniformly ([MoE-ch27] "The economics of MoE inference")."""
+    return n_experts * (1.0 - (1.0 - top_k / n_experts) ** batch)
+
+
+def switch_aux_loss(probs, experts, n_experts):
+    """Switch-Transformer balance statistic E * sum_e f_e * P_e, f_e = fraction of the N*k assignments
+    routed to e, P_e = mean router probability of e ([VL-post] "An auxiliary balance loss", reading
+    its N as the number of experts; [MoE-ch27] "Dispatch", closing paragraph). The caller applies
+    the coefficient alpha."""
+    probs = np.asarray(probs, np.float64)
+    counts = np.bincount(np.asarray(experts).reshape(-1), minlength=n_experts)
+    f = counts / counts.sum()
+    P = probs.mean(axis=0)
+    return float(n_experts * np.sum(f * P)), f, P

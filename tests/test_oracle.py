@@ -1,0 +1,309 @@
+"""Pins for the CPU oracle: the pages' worked examples, closed forms, special cases and brute force.
+
+None of these re-types the oracle's own formula: each check comes from a printed value, a
+textbook identity, an independent library routine or a pure-Python loop.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _token_for_probs(p, perm):
+    """Token x and router W_r (a permutation matrix, not symmetric) whose logits are ln p.
+    logits[e] = x[perm[e]] = ln p[e]; a transposed W_r would read x[perm^-1[e]] instead."""
+    E = len(p)
+    w = np.zeros((E, E))
+    w[np.arange(E), perm] = 1.0
+    x = np.zeros(E)
+    x[perm] = np.log(p)
+    return x[None, :], w
+
+
+PERM4 = np.array([2, 0, 3, 1])   # perm^-1 = [1, 3, 0, 2] != perm, so W_r^T differs from W_r
+
+
+def test_worked_router_example_renormalised():
+    g = load_golden("router_worked_example.json")
+    x, w = _token_for_probs(np.array(g["probs"]), PERM4)
+    _, probs, weights, experts = O.route(x, w, g["top_k"], norm_topk_prob=True)
+    np.testing.assert_allclose(probs[0], g["probs"], atol=1e-7)
+    assert experts[0].tolist() == g["experts"]
+    np.testing.assert_allclose(weights[0], g["weights_renormalised"], atol=1e-7)
+
+
+def test_worked_router_example_kept_without_renorm():
+    g = load_golden("router_worked_example.json")
+    x, w = _token_for_probs(np.array(g["probs"]), PERM4)
+    _, _, weights, experts = O.route(x, w, g["top_k"], norm_topk_prob=False)
+    assert experts[0].tolist() == g["experts"]
+    np.testing.assert_allclose(weights[0], g["weights_kept"], atol=1e-7)
+
+
+def test_renorm_example_second_page():
+    g = load_golden("renorm_example.json")
+    kept = g["kept"]
+    rest = (1.0 - sum(kept)) / 8.0          # 0.0875 < 0.1: the kept pair is the top-2
+    p = np.array(kept + [rest] * 8)
+    perm = np.roll(np.arange(10), 3)
+    x, w = _token_for_probs(p, perm)
+    _, _, weights, experts = O.route(x, w, 2, norm_topk_prob=True)
+    # descending order: expert 1 (0.2) then expert 0 (0.1)
+    assert experts[0].tolist() == [1, 0]
+    np.testing.assert_allclose(weights[0][::-1], g["renormalised_exact"], atol=1e-7)
+    cut = [math.floor(v * 100) / 100 for v in weights[0][::-1]]
+    assert cut == g["renormalised_as_printed"]
+
+
+def test_tie_goes_to_lower_index_worked_probs():
+    # probs [0.1, 0.5, 0.3, 0.1] with k = 3: experts 0 and 3 tie for the third slot.
+    x, w = _token_for_probs(np.array([0.1, 0.5, 0.3, 0.1]), PERM4)
+    _, probs, _, experts = O.route(x, w, 3, norm_topk_prob=False)
+    assert probs[0][0] == probs[0][3]       # an exact tie in fp32
+    assert experts[0].tolist() == [1, 2, 0]
+
+
+def test_tie_rule_duplicated_router_rows_brute_force():
+    rng = np.random.default_rng(3)
+    E, D, N, k = 9, 16, 200, 4
+    w = rng.standard_normal((E, D))
+    w[5] = w[1]
+    w[7] = w[1]
+    w[8] = w[2]                             # bitwise-equal logits for these pairs
+    x = rng.standard_normal((N, D))
+    _, probs, _, experts = O.route(x, w, k, norm_topk_prob=False)
+    n_ties = 0
+    for n in range(N):
+        p = [float(v) for v in probs[n]]
+        ref = sorted(range(E), key=lambda e: (-p[e], e))[:k]      # Python's sort, index tie-break
+        assert experts[n].tolist() == ref
+        n_ties += (1 in ref and 5 in ref)
+    assert n_ties > 0                       # the tie case really occurred
+
+
+def test_renorm_invariant_and_flag_off():
+    rng = np.random.default_rng(4)
+    E, D, N, k = 13, 24, 300, 5
+    w = rng.standard_normal((E, D)) * 0.3
+    x = rng.standard_normal((N, D))
+    _, probs, wts, ex = O.route(x, w, k, norm_topk_prob=True)
+    assert np.all(np.abs(wts.astype(np.float64).sum(1) - 1.0) <= k * 2.0 ** -24)
+    _, probs2, wts2, ex2 = O.route(x, w, k, norm_topk_prob=False)
+    assert np.array_equal(ex, ex2)
+    assert np.array_equal(wts2, np.take_along_axis(probs2, ex2, 1))
+    assert np.all(wts2.astype(np.float64).sum(1) <= 1.0 + 1e-6)
+    assert np.all(np.diff(wts2, axis=1) <= 0)        # descending slot order
+
+
+def test_softmax_matches_scipy_and_fp64():
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((50, 31)) * 3
+    ref = scipy.special.softmax(lg, axis=1)
+    np.testing.assert_allclose(O.softmax(lg, np.float64), ref, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(O.softmax(lg), ref, atol=1e-7)
+
+
+def test_fp32_and_fp64_router_agree_away_from_ties():
+    rng = np.random.default_rng(6)
+    E, D, N, k = 16, 32, 400, 4
+    w = rng.standard_normal((E, D)) * 0.2
+    x = rng.standard_normal((N, D))
+    _, p64, w64, e64 = O.route(x, w, k, True, prob_dtype=np.float64)
+    _, p32, w32, e32 = O.route(x, w, k, True)
+    far = O.k_gap(p64, k) > 1e-5
+    assert far.mean() > 0.95
+    assert np.array_equal(e64[far], e32[far])
+    np.testing.assert_allclose(w32[far], w64[far], atol=1e-6)
+
+
+def _brute_swiglu(v, gu, dn):
+    """Pure-Python SwiGLU for one row: silu(g) * u then the down projection, math.exp only."""
+    I = dn.shape[1]
+    D = len(v)
+    h = []
+    for i in range(I):
+        g = sum(float(gu[i, d]) * float(v[d]) for d in range(D))
+        u = sum(float(gu[I + i, d]) * float(v[d]) for d in range(D))
+        h.append(g / (1.0 + math.exp(-g)) * u)
+    return [sum(float(dn[o, i]) * h[i] for i in range(I)) for o in range(dn.shape[0])]
+
+
+def test_swiglu_brute_force():
+    rng = np.random.default_rng(7)
+    D, I, m = 6, 5, 3
+    gu = rng.standard_normal((2 * I, D))
+    dn = rng.standard_normal((D, I))
+    v = rng.standard_normal((m, D))
+    got = O.swiglu(v, gu, dn)
+    for r in range(m):
+        np.testing.assert_allclose(got[r], _brute_swiglu(v[r], gu, dn), rtol=1e-12, atol=1e-12)
+
+
+def _tiny_layer(seed, N=11, D=8, E=5, k=2, I=6, Is=0):
+    rng = np.random.default_rng(seed)
+    p = dict(x=rng.standard_normal((N, D)), w_router=rng.standard_normal((E, D)) * 0.5,
+             gate_up=rng.standard_normal((E, 2 * I, D)) * 0.3, down=rng.standard_normal((E, D, I)) * 0.3)
+    if Is:
+        p.update(shared_gate_up=rng.standard_normal((2 * Is, D)) * 0.3,
+                 shared_down=rng.standard_normal((D, Is)) * 0.3,
+                 w_shared_gate=rng.standard_normal(D) * 0.3)
+    return p
+
+
+def _brute_layer(p, k, norm):
+    """Pure-Python loops: per token, route with an index tie-break, then sum the chosen experts."""
+    _, probs, _, _ = O.route(p["x"], p["w_router"], k, norm)   # probabilities only (pinned above)
+    N, D = p["x"].shape
+    E = p["w_router"].shape[0]
+    y = np.zeros((N, D))
+    for n in range(N):
+        pr = [float(v) for v in probs[n]]
+        sel = sorted(range(E), key=lambda e: (-pr[e], e))[:k]
+        ws = [np.float32(pr[e]) for e in sel]           # the page keeps FP32 probabilities
+        if norm:
+            s = np.float32(0)
+            for v in ws:
+                s = np.float32(s + v)
+            ws = [np.float32(v / s) for v in ws]
+        ws = [float(v) for v in ws]
+        for e, wv in zip(sel, ws):
+            y[n] += wv * np.array(_brute_swiglu(p["x"][n], p["gate_up"][e], p["down"][e]))
+        if "shared_gate_up" in p:
+            z = sum(float(a) * float(b) for a, b in zip(p["x"][n], p["w_shared_gate"]))
+            y[n] += (1.0 / (1.0 + math.exp(-z))) * np.array(
+                _brute_swiglu(p["x"][n], p["shared_gate_up"], p["shared_down"]))
+    return y
+
+
+@pytest.mark.parametrize("norm", [True, False])
+@pytest.mark.parametrize("Is", [0, 7])
+def test_three_forms_and_brute_force_agree(norm, Is):
+    p = _tiny_layer(11 + Is, Is=Is, k=3)
+    kw = {} if not Is else dict(shared_gate_up=p["shared_gate_up"], shared_down=p["shared_down"],
+                                w_shared_gate=p["w_shared_gate"])
+    args = (p["x"], p["w_router"], p["gate_up"], p["down"], 3, norm)
+    yg, _ = O.forward_grouped(*args, **kw)
+    yl = O.forward_loop(*args, **kw)
+    yd = O.forward_dense_masked(*args, **kw)
+    np.testing.assert_allclose(yl, yg, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(yd, yg, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(_brute_layer(p, 3, norm), yg, rtol=0, atol=1e-7 * np.abs(yg).max())
+
+
+def test_k_equals_one_is_the_single_expert():
+    p = _tiny_layer(21, k=1)
+    y, st = O.forward_grouped(p["x"], p["w_router"], p["gate_up"], p["down"], 1, True)
+    assert np.all(st["weights"] == 1.0)
+    for n in range(p["x"].shape[0]):
+        e = int(st["experts"][n, 0])
+        ref = _brute_swiglu(p["x"][n], p["gate_up"][e], p["down"][e])
+        np.testing.assert_allclose(y[n], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_k_equals_e_is_the_dense_softmax_mixture():
+    p = _tiny_layer(22, E=4, k=4)
+    y, _ = O.forward_grouped(p["x"], p["w_router"], p["gate_up"], p["down"], 4, True)
+    pr = scipy.special.softmax(p["x"] @ p["w_router"].T, axis=1)          # textbook softmax
+    outs = [np.array([_brute_swiglu(p["x"][n], p["gate_up"][e], p["down"][e]) for n in range(len(p["x"]))])
+            for e in range(4)]
+    ref = sum(pr[:, e:e + 1] * outs[e] for e in range(4))
+    np.testing.assert_allclose(y, ref, rtol=0, atol=2e-6 * np.abs(ref).max())
+
+
+def test_permute_against_python_stable_sort():
+    rng = np.random.default_rng(8)
+    N, k, E = 57, 3, 11
+    experts = np.stack([rng.choice(E, size=k, replace=False) for _ in range(N)])
+    counts, offsets, order, token_of, slot_pos = O.permute(experts, E)
+    flat = experts.reshape(-1).tolist()
+    ref = sorted(range(N * k), key=lambda a: flat[a])        # Python's sort is stable
+    assert order.tolist() == ref
+    assert token_of.tolist() == [a // k for a in ref]
+    assert counts.tolist() == [flat.count(e) for e in range(E)]
+    assert offsets[0] == 0 and offsets[-1] == N * k and np.all(np.diff(offsets) >= 0)
+    assert np.array_equal(order[slot_pos], np.arange(N * k))
+    for e in range(E):
+        seg = order[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)                      # assignment ids ascend inside an expert
+        assert all(flat[a] == e for a in seg)
+
+
+def test_combine_gather_equals_page_index_add_form():
+    rng = np.random.default_rng(9)
+    N, k, E, D = 13, 3, 6, 5
+    experts = np.stack([rng.choice(E, size=k, replace=False) for _ in range(N)])
+    weights = rng.random((N, k))
+    out_perm = rng.standard_normal((N * k, D))
+    _, _, order, token_of, slot_pos = O.permute(experts, E)
+    y = O.combine(out_perm, weights, slot_pos)
+    ref = np.zeros((N, D))
+    wflat = weights.reshape(-1)
+    for p_ in range(N * k):                                  # index_add_ of the weighted rows
+        ref[token_of[p_]] += out_perm[p_] * wflat[order[p_]]
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-13)
+
+
+def test_shared_expert_gate_special_cases():
+    rng = np.random.default_rng(10)
+    D, Is, N = 7, 4, 5
+    sgu = rng.standard_normal((2 * Is, D))
+    sdn = rng.standard_normal((D, Is))
+    x = rng.standard_normal((N, D))
+    scale, out = O.shared_expert(x, sgu, sdn, np.zeros(D))
+    assert np.all(scale == 0.5)                              # sigmoid(0)
+    for n in range(N):
+        np.testing.assert_allclose(out[n], _brute_swiglu(x[n], sgu, sdn), rtol=1e-12, atol=1e-12)
+    s1, _ = O.shared_expert(x, sgu, sdn, None)
+    assert np.all(s1 == 1.0)
+
+
+def test_parameter_split_reproduces_printed_numbers():
+    g = load_golden("parameter_split.json")
+    stored, active = O.moe_parameter_split(g["hidden"], g["layers"], g["experts"], g["top_k"],
+                                           g["intermediate"], g["shared_intermediate"])
+    assert round(stored / 1e9, 1) == g["expert_params_stored_B"]
+    assert round(active / 1e9, 2) == g["expert_params_active_B"]
+    assert round(active / stored, 3) == g["active_fraction"]
+
+
+def test_touched_experts_formula_monte_carlo():
+    rng = np.random.default_rng(12)
+    E, k, B = 128, 8, 64
+    seen = [len(np.unique(np.concatenate([rng.choice(E, k, replace=False) for _ in range(B)])))
+            for _ in range(200)]
+    assert abs(np.mean(seen) - O.expected_touched_experts(E, k, B)) < 1.0
+    # the page's reading at batch 32: almost every expert, about B*k/E = 2 tokens each
+    assert O.expected_touched_experts(E, k, 32) > 0.85 * E
+
+
+def test_switch_aux_loss_closed_forms():
+    E = 8
+    # perfectly uniform: f_e = P_e = 1/E  ->  E * E * (1/E^2) = 1
+    probs = np.full((E, E), 1.0 / E)
+    experts = np.arange(E)[:, None]
+    loss, f, P = O.switch_aux_loss(probs, experts, E)
+    assert abs(loss - 1.0) < 1e-12
+    # collapsed: every token to expert 0 with probability 1  ->  E
+    probs = np.zeros((16, E))
+    probs[:, 0] = 1.0
+    loss, _, _ = O.switch_aux_loss(probs, np.zeros((16, 1), int), E)
+    assert abs(loss - E) < 1e-12
+
+
+def test_k_gap():
+    p = np.array([[0.1, 0.5, 0.3, 0.1]])
+    assert O.k_gap(p, 2)[0] == pytest.approx(0.2)
+    assert O.k_gap(p, 3)[0] == 0.0
+    assert O.k_gap(p, 4)[0] == np.inf
