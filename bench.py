@@ -1,0 +1,192 @@
+"""Benchmark of the MI355X MoE block: one step = one full pass of the block (route -> permute ->
+grouped gate_up+SwiGLU -> grouped down -> [shared expert] -> combine) over one batch of seeded
+synthetic tokens already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill] [--no-cpu-baseline]
+
+Prints ONE JSON line. `value` is whole-layer tokens/s on the headline workload (the 16,384-token
+Qwen3-VL-30B-A3B prefill layer). `roofline` reports the grouped gate_up GEMM (the dominant kernel),
+timed with events on its launch stream inside the timed steps. `decode` adds the 64-token decode
+layer (weight-read bound). `cpu_baseline` times the CPU oracle on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "MoE-layer tokens/s; % bf16 MFMA peak (prefill), % HBM GB/s (decode)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(shape, touched):
+    """FLOPs and bytes the method itself must do (not the dense all-expert work it avoids)."""
+    N, D, E, k, I, Is = shape.n_tokens, shape.hidden, shape.n_experts, shape.top_k, shape.inter, shape.shared_inter
+    b = 2 if shape.dtype == "bf16" else 4
+    flops = 2 * N * D * E + 6 * D * I * N * k + (6 * D * Is * N + 2 * N * D if Is else 0)
+    bytes_ = touched * 3 * D * I * b + E * D * b + (3 * D * Is * b + D * b if Is else 0) + 2 * N * D * b + N * k * 8
+    gate_up_flops = 4 * D * I * N * k
+    gate_up_bytes = touched * 2 * I * D * b + N * k * D * b + N * k * I * b
+    return dict(flops=flops, bytes=bytes_, gate_up_flops=gate_up_flops, gate_up_bytes=gate_up_bytes)
+
+
+def run_workload(name, steps, warmup, out_dtype):
+    import torch
+    from mixture_experts_layer_10_amd import binding as B
+    from mixture_experts_layer_10_amd import inputs as I
+    from mixture_experts_layer_10_amd.chain import Chain
+
+    shape = I.WORKLOADS[name]
+    t0 = time.perf_counter()
+    data = I.make_inputs(shape)
+    dev = B.to_device(data.store)
+    log(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s")
+    cfg = B.config_for(shape, out_dtype)
+    chain = Chain(cfg, dev)
+    y_ref = B.forward(cfg, dev)
+    for _ in range(warmup):
+        chain.step()
+    torch.cuda.synchronize()
+    assert torch.equal(chain.y.view(torch.int16 if chain.y.dtype == torch.bfloat16 else torch.int32),
+                       y_ref.view(torch.int16 if y_ref.dtype == torch.bfloat16 else torch.int32)), \
+        "chain and moe_forward disagree"
+    counts = chain.counts.cpu().numpy()
+    touched = int((counts > 0).sum())
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    all0, all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    all0.record()
+    for i in range(steps):
+        chain.step(ev[i])
+    all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = all0.elapsed_time(all1)
+    gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = wall * 1e3 / steps
+    alg = algorithmic(shape, touched)
+    log(f"[bench] {name}: {ms_per_step:.3f} ms/step (gpu {gpu_ms / steps:.3f}), gate_up {gate_up_ms:.3f} ms, "
+        f"touched {touched}/{shape.n_experts}")
+    return dict(shape=shape, data=data, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
+                gate_up_ms=gate_up_ms, touched=touched, counts=counts, alg=alg,
+                tokens_per_s=shape.n_tokens / (ms_per_step / 1e3))
+
+
+def cpu_baseline(data, target_s=15.0):
+    """The CPU oracle (grouped form, fp64) on a seeded token sample of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    s = data.shape
+    w_router = data.values("w_router")
+    gate_up, down = data.values("gate_up"), data.values("down")     # converted outside the timed region
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        toks = np.sort(rng.choice(s.n_tokens, size=n, replace=False))
+        x = data.token_rows(toks)
+        t0 = time.perf_counter()
+        O.forward_grouped(x, w_router, gate_up, down, s.top_k, s.norm_topk_prob)
+        return time.perf_counter() - t0
+
+    n = min(64, s.n_tokens)
+    dt = run(n)
+    n2 = int(min(s.n_tokens, max(n, n * target_s / max(dt, 1e-3))))
+    dt2 = run(n2)
+    log(f"[bench] cpu oracle: {n2} tokens in {dt2:.1f}s with {threads} threads")
+    return dict(value=n2 / dt2, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{n2} of {s.n_tokens} tokens of the {s.name} workload (seeded sample), grouped fp64 oracle")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--out-dtype", default="f32")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    main_run = run_workload(args.workload, args.steps, args.warmup, args.out_dtype)
+    shape, alg = main_run["shape"], main_run["alg"]
+    gemm_s = main_run["gate_up_ms"] / 1e3
+    prefill_like = alg["gate_up_flops"] / alg["gate_up_bytes"] > 500
+    if prefill_like:
+        achieved = alg["gate_up_flops"] / gemm_s / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None)
+    else:
+        achieved = alg["gate_up_bytes"] / gemm_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
+    roof["kernel"] = "gemm_bf16_kernel (grouped gate_up + SwiGLU)"
+    roof["per_launch"] = dict(flops=alg["gate_up_flops"], bytes=alg["gate_up_bytes"], avg_ms=round(main_run["gate_up_ms"], 4))
+    layer_s = main_run["ms_per_step"] / 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(main_run["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_run["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded; random-init weights N(0, 0.02^2))",
+        "config": {"workload": shape.name, "n_tokens": shape.n_tokens, "hidden": shape.hidden,
+                   "n_experts": shape.n_experts, "top_k": shape.top_k, "inter": shape.inter,
+                   "shared_inter": shape.shared_inter, "norm_topk_prob": shape.norm_topk_prob,
+                   "zipf_s": shape.zipf_s, "out_dtype": args.out_dtype, "seed": shape.seed,
+                   "parallelism": "none (1 GPU)"},
+        "layer": {"tflops": round(alg["flops"] / layer_s / 1e12, 2),
+                  "mfma_frac": round(alg["flops"] / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "alg_gbs": round(alg["bytes"] / layer_s / 1e9, 1),
+                  "hbm_frac": round(alg["bytes"] / layer_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "experts_touched": main_run["touched"], "max_rows_per_expert": int(main_run["counts"].max()),
+                  "min_rows_per_expert": int(main_run["counts"].min())},
+        "roofline": roof,
+    }
+    if not args.no_decode and args.workload != "decode":
+        dec = run_workload("decode", max(args.steps, 50), args.warmup, args.out_dtype)
+        ds = dec["ms_per_step"] / 1e3
+        out["decode"] = {"workload": "decode", "tokens_per_s": round(dec["tokens_per_s"], 1),
+                         "ms_per_step": round(dec["ms_per_step"], 4),
+                         "alg_gbs": round(dec["alg"]["bytes"] / ds / 1e9, 1),
+                         "hbm_frac": round(dec["alg"]["bytes"] / ds / 1e9 / PEAK_HBM_GBS, 4),
+                         "experts_touched": dec["touched"],
+                         "gate_up_ms": round(dec["gate_up_ms"], 4),
+                         "gate_up_hbm_frac": round(dec["alg"]["gate_up_bytes"] / (dec["gate_up_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(main_run["data"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

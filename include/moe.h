@@ -1,0 +1,156 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) sparse Mixture-of-Experts MLP block.
+ *
+ * The block is the Qwen3-MoE / Qwen3-VL-MoE expert layer:
+ *   y = sum over the token's top-k experts of w_i * expert_i(x)  [+ sigmoid(w_s . x) * shared(x)]
+ * ("27. Mixture of experts", sections "The router", "The shared expert" and "Dispatch";
+ *  "Qwen3-VL + MoE: train to deploy", section "What a mixture-of-experts layer is", its equation).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned by the caller.
+ *    The library never allocates or frees device memory and keeps no state between calls.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ *    Outputs are valid once that stream has completed. There is no host synchronisation.
+ *  - Validation runs on the host before anything is enqueued. A call that returns an error has
+ *    enqueued nothing, except MOE_ERR_HIP, which reports a failed launch (hipGetLastError).
+ *    moe_last_error() then gives a message naming the offending argument.
+ *  - n_tokens == 0 is a successful no-op (after the configuration itself is validated).
+ *  - Inputs are assumed finite; what NaN or Inf routing selects is unspecified.
+ *  - Calls on one stream are ordered; concurrent calls on different streams must not share
+ *    output or workspace buffers.
+ *
+ * Layouts (the stacked-expert layout of "27. Mixture of experts", section "Dispatch", class Experts,
+ * whose linear layers read weights as [out, in], so every GEMM operand is contiguous along K):
+ *   x           [N, D]
+ *   w_router    [E, D]             logits = x W_r^T, no bias
+ *   gate_up     [E, 2I, D]         rows [0, I) gate, rows [I, 2I) up
+ *   down        [E, D, I]
+ *   shared_gate_up [2I_s, D], shared_down [D, I_s], w_shared_gate [D]
+ * dtype (moe_config.dtype) applies to x and every weight; routing outputs are always fp32
+ * weights and int32 expert ids; intermediate expert outputs are fp32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null required pointer, negative or zero size, k > E, ...      */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but not implemented: dtype, alignment, E > 512, ...       */
+  MOE_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than moe_workspace_bytes()   */
+  MOE_ERR_HIP = -4          /* a kernel launch failed                                           */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Shape and options of one MoE layer. Refuses, never defaults: every field must be set
+ * (the config-ingestion lesson of "27. Mixture of experts", section "Qwen3-MoE", Note). */
+typedef struct {
+  int64_t n_tokens;       /* N  >= 0: tokens, flattened over batch and sequence               */
+  int64_t hidden;         /* D  >= 1: model width (bf16: multiple of 8; fp32: multiple of 4)  */
+  int64_t n_experts;      /* E  in [1, 512]                                                   */
+  int64_t top_k;          /* k  in [1, E]                                                     */
+  int64_t inter;          /* I  >= 1: expert inner width (same alignment as D)                */
+  int64_t shared_inter;   /* I_s >= 0: shared expert inner width, 0 = no shared expert        */
+  int32_t norm_topk_prob; /* 1: divide kept weights by their sum; 0: keep the probabilities   */
+  int32_t dtype;          /* moe_dtype of x and all weights                                   */
+  int32_t out_dtype;      /* moe_dtype of y                                                   */
+  int32_t reserved;       /* must be 0                                                        */
+} moe_config;
+
+/* Human-readable name of a status code. Never NULL. */
+const char* moe_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Bytes of device workspace moe_forward needs for this configuration (also enough for
+ * moe_permute). Host only; no GPU needed. Returns MOE_ERR_INVALID_ARG/UNSUPPORTED for a bad
+ * configuration, else writes *bytes. */
+int moe_workspace_bytes(const moe_config* cfg, size_t* bytes);
+
+/* Router: logits = x W_r^T (fp32 accumulation, logits never rounded), p = softmax over all E in
+ * fp32, the k largest p in descending order with equal p going to the lower expert index, then
+ * w = p_sel / sum(p_sel) when norm_topk_prob ("27. Mixture of experts", section "The router",
+ * steps 1-3, TopKRouter and the parity note).
+ *   x [N, D], w_router [E, D]                      (dtype)
+ *   w_shared_gate [D] or NULL                      (dtype) shared-expert gate vector w_s
+ *   logits [N, E] fp32 or NULL                     optional copy of the router logits
+ *   weights [N, k] fp32, experts [N, k] int32      required outputs
+ *   shared_scale [N] fp32 or NULL                  sigmoid(w_s . x); required iff w_shared_gate */
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const void* w_shared_gate,
+              float* logits, float* weights, int32_t* experts, float* shared_scale, void* stream);
+
+/* Grouping by expert: the N*k assignments a = n*k + j are sorted by expert id, stably (ties keep
+ * assignment order), with no atomics on ranks, so the result is deterministic ("27. Mixture of
+ * experts", section "Dispatch", grouped dispatch steps 1-2; stretch exercise 2 for the row-offset
+ * prefix sum).
+ *   experts [N, k] int32 in [0, E)                 (ids outside that range: undefined result)
+ *   counts [E], offsets [E+1] int32                rows of expert e are [offsets[e], offsets[e+1])
+ *   token_of [N*k] int32                           token each sorted row came from
+ *   slot_pos [N*k] int32                           sorted row of assignment a (inverse permutation)
+ *   x [N, D] and x_perm [N*k, D] (dtype)           optional pair: x_perm[p] = x[token_of[p]]
+ *   ws, ws_bytes                                   workspace, at least moe_workspace_bytes() */
+int moe_permute(const moe_config* cfg, const int32_t* experts, const void* x, int32_t* counts,
+                int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU experts ("27. Mixture of experts", section "Dispatch", Experts.expert and grouped
+ * step 3: one launch runs every group's matmuls on its contiguous rows). For group g and each
+ * row p in [offsets[g], offsets[g+1]):
+ *   h[p, i]   = silu(sum_d X[p, d] G[g, i, d]) * (sum_d X[p, d] G[g, I + i, d])  (moe_expert_gate_up)
+ *   out[p, :] = sum_i h[p, i] Dn[g, :, i]                                        (moe_expert_down)
+ * where X[p] = x[row_index[p]] if row_index is non-NULL, else x[p] (x holds max_rows rows).
+ * cfg gives D (hidden) and dtype; n_tokens, n_experts, top_k and inter of cfg are not used here.
+ *   n_groups G >= 1, inter I >= 1 (the width of these experts: cfg.inter or cfg.shared_inter)
+ *   max_rows: host-known upper bound of offsets[G] (e.g. N*k); sizes the launch and buffers
+ *   offsets [G+1] int32 on device, offsets[0] == 0 and non-decreasing, or NULL for one group of
+ *     max_rows rows
+ *   gate_up [G, 2I, D], down [G, D, I] (dtype)
+ *   h [max_rows, I] (dtype; bf16 when dtype is bf16, the matrix-core input), out [max_rows, D] fp32
+ * Accumulation is fp32; with bf16 the SwiGLU product is rounded to bf16 once (the second GEMM's
+ * input). Rows at or past offsets[G] are left untouched. */
+int moe_expert_gate_up(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows,
+                       const void* x, const int32_t* row_index, const int32_t* offsets,
+                       const void* gate_up, void* h, void* stream);
+int moe_expert_down(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows,
+                    const int32_t* offsets, const void* h, const void* down, float* out, void* stream);
+/* Both of the above in order. */
+int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows,
+                   const void* x, const int32_t* row_index, const int32_t* offsets,
+                   const void* gate_up, const void* down, void* h, float* out, void* stream);
+
+/* Weighted unpermute ("27. Mixture of experts", section "Dispatch", grouped step 4, and the
+ * shared-expert equation): y[n] = sum_{j<k} w[n,j] * out_perm[slot_pos[n*k+j]]
+ *                                  (+ shared_scale[n] * shared_out[n]),
+ * summed in fp32 in slot order j = 0..k-1, then the shared term, rounded once to out_dtype.
+ * A gather per token (no atomics): deterministic.
+ *   out_perm [N*k, D] fp32, weights [N, k] fp32, slot_pos [N*k] int32
+ *   shared_out [N, D] fp32 or NULL; shared_scale [N] fp32 or NULL (NULL with shared_out: scale 1)
+ *   y [N, D] (out_dtype) */
+int moe_combine(const moe_config* cfg, const float* out_perm, const float* weights,
+                const int32_t* slot_pos, const float* shared_out, const float* shared_scale, void* y,
+                void* stream);
+
+/* The whole block: moe_route -> moe_permute -> moe_expert_ffn over the routed groups (rows gathered
+ * straight from x) -> [shared expert as one more group over all N rows] -> moe_combine.
+ *   shared_gate_up, shared_down: required iff cfg.shared_inter > 0; w_shared_gate may be NULL
+ *     (ungated shared expert, scale 1)
+ *   y [N, D] (out_dtype); weights_out [N, k] fp32 / experts_out [N, k] int32: optional copies
+ *   ws, ws_bytes: workspace of at least moe_workspace_bytes(cfg) bytes, 256-byte aligned */
+int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up,
+                const void* down, const void* shared_gate_up, const void* shared_down,
+                const void* w_shared_gate, void* y, float* weights_out, int32_t* experts_out,
+                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,419 @@
+// Grouped expert GEMMs ("27. Mixture of experts", section "Dispatch": Experts.expert run on each
+// expert's contiguous rows, which "a grouped GEMM kernel does as one launch"; stretch exercise 2:
+// one program per (expert, output tile), driven by the row-offset prefix sum).
+//
+//   gate_up: h[p, i]   = silu(X[p] . G[g, i]) * (X[p] . G[g, I + i])   SwiGLU fused in the epilogue
+//   down:    out[p, n] = h[p] . Dn[g, n]                               fp32 output
+//
+// Both operands are contiguous along K (weights stored [out, in]), so A and B tiles are loaded the
+// same way: 16-byte vectors, 8 lanes per 128-byte row segment. Tiles are staged in LDS with an XOR
+// swizzle of the 16-byte chunks (chunk c of row r sits at c ^ (r & 7)), so the matrix-core operand
+// reads (32 rows at one k offset) hit distinct banks. bf16 uses 32x32x16 matrix-core steps with
+// fp32 accumulators; fp32 uses an LDS-tiled FMA kernel.
+//
+// Scheduling: persistent workgroups. Each builds, in LDS, the prefix sum over groups of
+// ceil(rows_g / BM) * n_tiles from the device-side offsets (no host round trip), then walks the
+// tile list. Tile t -> (group by binary search, m-tile, n-tile), n fastest, so neighbouring tiles
+// share their A rows and their expert's weights. Workgroup w runs on XCD w % 8; the list is cut into
+// runs of (grid / 8) consecutive tiles per XCD, so tiles that share data share an L2.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------------
+// Tile list shared by both kernels.
+// ---------------------------------------------------------------------------------------------
+template <int NT>
+__device__ void build_tile_prefix(const int32_t* offsets, int G, int64_t max_rows, int BM, int n_tiles,
+                                  int* s_pref, int* s_tmp) {
+  // s_pref[g] = sum_{g' < g} ceil(rows_g' / BM) * n_tiles, for g = 0..G. G <= 2 * NT.
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto tiles_of = [&](int g) -> int {
+    if (g >= G) return 0;
+    const int64_t rows = offsets ? static_cast<int64_t>(offsets[g + 1] - offsets[g]) : max_rows;
+    return static_cast<int>((rows + BM - 1) / BM) * n_tiles;
+  };
+  const int v0 = tiles_of(2 * tid), v1 = tiles_of(2 * tid + 1);
+  const int own = v0 + v1;
+  int inc = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_tmp[w];
+  const int excl = before + inc - own;
+  if (2 * tid < G) s_pref[2 * tid] = excl;
+  if (2 * tid + 1 < G) s_pref[2 * tid + 1] = excl + v0;
+  // the total: groups at or past G contribute nothing, so the last thread's inclusive sum is it
+  // (written separately because G may equal 2 * NT, one past the last slot the loop covers)
+  if (tid == NT - 1) s_pref[G] = before + inc;
+  __syncthreads();
+}
+
+__device__ __forceinline__ int find_group(const int* s_pref, int G, int t) {
+  int lo = 0, hi = G;  // invariant: s_pref[lo] <= t < s_pref[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int tile_of_round(int r, int w, int P) {
+  if ((P & 7) == 0) {
+    const int per = P >> 3;
+    return (r * 8 + (w & 7)) * per + (w >> 3);
+  }
+  return r * P + w;
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 matrix-core kernel.
+//   WM x WN waves; each wave owns TM x TN blocks of 32x32.
+//   BM = WM*TM*32 rows of A per tile, BNB = WN*TN*32 rows of B (weight rows) per tile.
+//   SwiGLU: TN == 2, block 0 of a wave reads gate rows, block 1 the matching up rows; the tile's
+//   B rows are [gate i0 .. i0+BNB/2) then [up I+i0 .. I+i0+BNB/2), giving BNB/2 h columns.
+// ---------------------------------------------------------------------------------------------
+constexpr int kBK = 64;            // k per LDS stage (8 chunks of 16 bytes per row)
+
+template <int WM, int TM, int WN, int TN, bool kSwiGLU>
+struct BfCfg {
+  static constexpr int BM = WM * TM * 32;
+  static constexpr int BNB = WN * TN * 32;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int A_LD = BM * 8 / NT;     // 16-byte chunks of A each thread loads per stage
+  static constexpr int B_LD = BNB * 8 / NT;
+  static constexpr int OUT_COLS = kSwiGLU ? BNB / 2 : BNB;
+  static_assert(!kSwiGLU || TN == 2, "SwiGLU pairs one gate block with one up block");
+  static_assert(A_LD * NT == BM * 8 && B_LD * NT == BNB * 8, "tile must split evenly over threads");
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+
+template <int WM, int TM, int WN, int TN, bool kSwiGLU>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
+  using C = BfCfg<WM, TM, WN, TN, kSwiGLU>;
+  constexpr int BM = C::BM, BNB = C::BNB, NT = C::NT;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BNB * kBK];
+  __shared__ int s_pref[1025];
+  __shared__ int s_tmp[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int G = a.G;
+  // K and the output width
+  const int K = kSwiGLU ? a.D : a.I;
+  const int NOUT = kSwiGLU ? a.I : a.D;
+  const int n_tiles = (NOUT + C::OUT_COLS - 1) / C::OUT_COLS;
+
+  build_tile_prefix<NT>(a.offsets, G, a.max_rows, BM, n_tiles, s_pref, s_tmp);
+  const int total = s_pref[G];
+  const int P = gridDim.x;
+
+  const uint16_t* X = static_cast<const uint16_t*>(a.x);
+  const uint16_t* W = static_cast<const uint16_t*>(a.w);
+  const int ksteps = (K + kBK - 1) / kBK;
+
+  for (int r = 0;; ++r) {
+    const int t = tile_of_round(r, blockIdx.x, P);
+    if (r * P >= total) break;
+    if (t >= total) continue;
+    const int g = find_group(s_pref, G, t);
+    const int local = t - s_pref[g];
+    const int mt = local / n_tiles, nt = local - mt * n_tiles;
+    const int64_t row0 = a.offsets ? a.offsets[g] : 0;
+    const int64_t rows = a.offsets ? static_cast<int64_t>(a.offsets[g + 1]) - row0 : a.max_rows;
+    if (rows <= 0) continue;           // cannot happen with a consistent prefix; never index row -1
+    const int m0 = mt * BM;
+    const int c0 = nt * C::OUT_COLS;   // first output column of the tile
+
+    // Source rows for this thread's A and B chunks (fixed over k).
+    const uint16_t* srcA[C::A_LD];
+    int chA[C::A_LD];
+#pragma unroll
+    for (int j = 0; j < C::A_LD; ++j) {
+      const int idx = tid + j * NT, rr = idx >> 3;
+      chA[j] = idx & 7;
+      const int64_t lr = min<int64_t>(m0 + rr, rows - 1);   // rows past the group: any valid row
+      const int64_t p = row0 + lr;
+      const int64_t src = a.row_index ? a.row_index[p] : p;
+      srcA[j] = X + src * K + chA[j] * 8;
+    }
+    const uint16_t* srcB[C::B_LD];
+    int chB[C::B_LD];
+    const uint16_t* Wg = W + static_cast<int64_t>(g) * (kSwiGLU ? 2LL * a.I * a.D : static_cast<int64_t>(a.D) * a.I);
+#pragma unroll
+    for (int j = 0; j < C::B_LD; ++j) {
+      const int idx = tid + j * NT, rr = idx >> 3;
+      chB[j] = idx & 7;
+      int wrow;
+      if (kSwiGLU) {
+        const int half = BNB / 2;
+        const int ci = min(c0 + (rr % half), NOUT - 1);
+        wrow = rr < half ? ci : a.I + ci;
+      } else {
+        wrow = min(c0 + rr, NOUT - 1);
+      }
+      srcB[j] = Wg + static_cast<int64_t>(wrow) * K + chB[j] * 8;
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+    u32x4 ra[C::A_LD], rb[C::B_LD];
+    auto gload = [&](int ks) {
+      const int kb = ks * kBK;
+#pragma unroll
+      for (int j = 0; j < C::A_LD; ++j)
+        ra[j] = (kb + chA[j] * 8 < K) ? *reinterpret_cast<const u32x4*>(srcA[j] + kb) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < C::B_LD; ++j)
+        rb[j] = (kb + chB[j] * 8 < K) ? *reinterpret_cast<const u32x4*>(srcB[j] + kb) : u32x4{0, 0, 0, 0};
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < C::A_LD; ++j) {
+        const int rr = (tid + j * NT) >> 3;
+        *reinterpret_cast<u32x4*>(&sA[buf][swz(rr, chA[j])]) = ra[j];
+      }
+#pragma unroll
+      for (int j = 0; j < C::B_LD; ++j) {
+        const int rr = (tid + j * NT) >> 3;
+        *reinterpret_cast<u32x4*>(&sB[buf][swz(rr, chB[j])]) = rb[j];
+      }
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const int buf = ks & 1;
+      if (ks + 1 < ksteps) gload(ks + 1);
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int ch = kk * 2 + (lane >> 5);
+        u32x4 fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = (wm * TM + i) * 32 + (lane & 31);
+          fa[i] = *reinterpret_cast<const u32x4*>(&sA[buf][swz(row, ch)]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = kSwiGLU ? (j * (BNB / 2) + wn * 32 + (lane & 31)) : ((wn * TN + j) * 32 + (lane & 31));
+          fb[j] = *reinterpret_cast<const u32x4*>(&sB[buf][swz(row, ch)]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+      }
+      if (ks + 1 < ksteps) sstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // Epilogue.
+    if constexpr (kSwiGLU) {
+      uint16_t* H = static_cast<uint16_t*>(a.out);
+      const int col = c0 + wn * 32 + (lane & 31);
+      if (col < NOUT) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int rr = m0 + (wm * TM + i) * 32 + acc_row(e, lane);
+            if (rr < rows) {
+              const float gt = acc[i][0][e], up = acc[i][1][e];
+              H[(row0 + rr) * NOUT + col] = f32_to_bf16(silu(gt) * up);
+            }
+          }
+      }
+    } else {
+      float* O = static_cast<float*>(a.out);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = c0 + (wn * TN + j) * 32 + (lane & 31);
+        if (col < NOUT) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int rr = m0 + (wm * TM + i) * 32 + acc_row(e, lane);
+              if (rr < rows) O[(row0 + rr) * NOUT + col] = acc[i][j][e];
+            }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32 kernel: 64 x 64 tiles, 256 threads, 4 x 4 register blocking, k step 16.
+//   SwiGLU: B tile = 32 gate rows + the 32 matching up rows; each thread keeps 4 rows x 2 h columns
+//   of gate and of up accumulators.
+// ---------------------------------------------------------------------------------------------
+template <bool kSwiGLU>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
+  constexpr int BM = 64, BNB = 64, BK = 16, NT = 256;
+  constexpr int OUT_COLS = kSwiGLU ? 32 : 64;
+  __shared__ float sA[BK][BM + 4];
+  __shared__ float sB[BK][BNB + 4];
+  __shared__ int s_pref[1025];
+  __shared__ int s_tmp[16];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int G = a.G;
+  const int K = kSwiGLU ? a.D : a.I;
+  const int NOUT = kSwiGLU ? a.I : a.D;
+  const int n_tiles = (NOUT + OUT_COLS - 1) / OUT_COLS;
+  build_tile_prefix<NT>(a.offsets, G, a.max_rows, BM, n_tiles, s_pref, s_tmp);
+  const int total = s_pref[G];
+  const int P = gridDim.x;
+  const float* X = static_cast<const float*>(a.x);
+  const float* W = static_cast<const float*>(a.w);
+
+  for (int r = 0;; ++r) {
+    const int t = tile_of_round(r, blockIdx.x, P);
+    if (r * P >= total) break;
+    if (t >= total) continue;
+    const int g = find_group(s_pref, G, t);
+    const int local = t - s_pref[g];
+    const int mt = local / n_tiles, nt = local - mt * n_tiles;
+    const int64_t row0 = a.offsets ? a.offsets[g] : 0;
+    const int64_t rows = a.offsets ? static_cast<int64_t>(a.offsets[g + 1]) - row0 : a.max_rows;
+    if (rows <= 0) continue;
+    const int m0 = mt * BM, c0 = nt * OUT_COLS;
+    const float* Wg = W + static_cast<int64_t>(g) * (kSwiGLU ? 2LL * a.I * a.D : static_cast<int64_t>(a.D) * a.I);
+
+    // loader: thread -> (row = tid / 4, k quad = tid % 4)
+    const int lr = tid >> 2, lq = tid & 3;
+    const int64_t arow = min<int64_t>(m0 + lr, rows - 1);
+    const int64_t ap = row0 + arow;
+    const float* srcA = X + (a.row_index ? static_cast<int64_t>(a.row_index[ap]) : ap) * K + lq * 4;
+    int wrow;
+    if (kSwiGLU) {
+      const int ci = min(c0 + (lr & 31), NOUT - 1);
+      wrow = lr < 32 ? ci : a.I + ci;
+    } else {
+      wrow = min(c0 + lr, NOUT - 1);
+    }
+    const float* srcB = Wg + static_cast<int64_t>(wrow) * K + lq * 4;
+
+    float acc[4][4] = {};
+    for (int kb = 0; kb < K; kb += BK) {
+      const bool ok = kb + lq * 4 < K;
+      const f32x4 va = ok ? *reinterpret_cast<const f32x4*>(srcA + kb) : f32x4{0, 0, 0, 0};
+      const f32x4 vb = ok ? *reinterpret_cast<const f32x4*>(srcB + kb) : f32x4{0, 0, 0, 0};
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sA[lq * 4 + q][lr] = va[q];
+        sB[lq * 4 + q][lr] = vb[q];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < BK; ++kk) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = sA[kk][ty * 4 + i];
+        if (kSwiGLU) {
+          bv[0] = sB[kk][tx * 2];
+          bv[1] = sB[kk][tx * 2 + 1];
+          bv[2] = sB[kk][32 + tx * 2];
+          bv[3] = sB[kk][32 + tx * 2 + 1];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bv[j] = sB[kk][tx * 4 + j];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      }
+    }
+    float* O = static_cast<float*>(a.out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = m0 + ty * 4 + i;
+      if (rr >= rows) continue;
+      if (kSwiGLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = c0 + tx * 2 + j;
+          if (col < NOUT) O[(row0 + rr) * NOUT + col] = silu(acc[i][j]) * acc[i][2 + j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = c0 + tx * 4 + j;
+          if (col < NOUT) O[(row0 + rr) * NOUT + col] = acc[i][j];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Launch: a persistent grid of at most one workgroup per CU (the bf16 kernels use > 80 KB of LDS).
+// ---------------------------------------------------------------------------------------------
+static int64_t tile_upper_bound(const GemmArgs& a, int BM, int n_tiles) {
+  const int64_t m_tiles = a.offsets ? (a.max_rows / BM + std::min<int64_t>(a.G, a.max_rows)) : (a.max_rows + BM - 1) / BM;
+  return m_tiles * n_tiles;
+}
+
+static unsigned persistent_grid(int64_t ub, int per_cu) {
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
+  int64_t p = std::min<int64_t>(ub, cap);
+  if (p >= 8) p &= ~int64_t(7);
+  return static_cast<unsigned>(std::max<int64_t>(p, 1));
+}
+
+template <int WM, int TM, int WN, int TN, bool kSwiGLU>
+static void launch_bf16(const GemmArgs& a, hipStream_t st) {
+  using C = BfCfg<WM, TM, WN, TN, kSwiGLU>;
+  const int NOUT = kSwiGLU ? a.I : a.D;
+  const int n_tiles = (NOUT + C::OUT_COLS - 1) / C::OUT_COLS;
+  constexpr int lds = 2 * (C::BM + C::BNB) * kBK * 2;
+  const unsigned grid = persistent_grid(tile_upper_bound(a, C::BM, n_tiles), lds <= 76 * 1024 ? 2 : 1);
+  gemm_bf16_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, C::NT, 0, st>>>(a);
+}
+
+template <bool kSwiGLU>
+static void launch_f32(const GemmArgs& a, hipStream_t st) {
+  const int NOUT = kSwiGLU ? a.I : a.D;
+  const int out_cols = kSwiGLU ? 32 : 64;
+  const int n_tiles = (NOUT + out_cols - 1) / out_cols;
+  const unsigned grid = persistent_grid(tile_upper_bound(a, 64, n_tiles), 4);
+  gemm_f32_kernel<kSwiGLU><<<grid, 256, 0, st>>>(a);
+}
+
+// Rows per group decide the tile height: few rows per expert (decode) -> 32-row tiles with wide
+// weight tiles; many rows -> 256 x 256 tiles.
+static bool small_rows(const GemmArgs& a) {
+  if (!a.offsets) return a.max_rows <= 64;
+  return a.max_rows <= 64LL * a.G;
+}
+
+void launch_gate_up(const GemmArgs& a, hipStream_t st) {
+  if (!a.bf16) return launch_f32<true>(a, st);
+  if (small_rows(a)) return launch_bf16<1, 1, 4, 2, true>(a, st);
+  return launch_bf16<2, 4, 4, 2, true>(a, st);
+}
+
+void launch_down(const GemmArgs& a, hipStream_t st) {
+  if (!a.bf16) return launch_f32<false>(a, st);
+  if (small_rows(a)) return launch_bf16<1, 1, 4, 2, false>(a, st);
+  return launch_bf16<2, 4, 4, 2, false>(a, st);
+}
+
+}  // namespace moe

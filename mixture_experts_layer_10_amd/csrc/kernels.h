@@ -1,0 +1,71 @@
+// Internal launcher interface between the C ABI (moe_abi.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  const void* x;
+  const void* w_router;
+  const void* w_shared_gate;  // may be null
+  float* logits;              // may be null
+  float* weights;
+  int32_t* experts;
+  float* shared_scale;        // non-null iff w_shared_gate
+  int64_t N;
+  int D, E, k;
+  int norm;
+  bool bf16;
+};
+void launch_route(const RouteArgs& a, hipStream_t st);
+
+// Permutation: assignments are processed in chunks of kPermChunk by one workgroup each.
+constexpr int kPermChunk = 2048;
+struct PermuteArgs {
+  const int32_t* experts;   // [A]
+  int32_t* block_counts;    // [n_chunks * E] workspace
+  int32_t* counts;          // [E]
+  int32_t* offsets;         // [E + 1]
+  int32_t* token_of;        // [A]
+  int32_t* slot_pos;        // [A]
+  int64_t A;
+  int E, k;
+};
+void launch_permute(const PermuteArgs& a, hipStream_t st);
+int64_t permute_chunks(int64_t A);
+
+// x_perm[p] = x[token_of[p]] for p < rows (row_bytes % 16 == 0).
+void launch_gather_rows(const void* x, const int32_t* token_of, void* x_perm, int64_t rows,
+                        int64_t row_bytes, hipStream_t st);
+
+struct GemmArgs {
+  const void* x;          // gate_up: activations; down: h
+  const int32_t* row_index;
+  const int32_t* offsets; // [G+1] or null (one group of max_rows rows)
+  const void* w;          // gate_up [G, 2I, D] or down [G, D, I]
+  void* out;              // gate_up: h [rows, I]; down: out [rows, D] fp32
+  int64_t max_rows;
+  int G;
+  int D, I;
+  bool bf16;
+};
+void launch_gate_up(const GemmArgs& a, hipStream_t st);
+void launch_down(const GemmArgs& a, hipStream_t st);
+
+struct CombineArgs {
+  const float* out_perm;
+  const float* weights;
+  const int32_t* slot_pos;
+  const float* shared_out;    // may be null
+  const float* shared_scale;  // may be null
+  void* y;
+  int64_t N;
+  int D, k;
+  bool out_bf16;
+};
+void launch_combine(const CombineArgs& a, hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,362 @@
+// C ABI of the MoE block: host-side validation, workspace carving and kernel launches.
+// Every check runs before anything is enqueued; see include/moe.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+static int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+static int ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+static int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+constexpr int64_t kMaxExperts = 512;
+
+static size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+static int validate_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens = %lld < 0", (long long)c->n_tokens);
+  if (c->hidden < 1) return fail(MOE_ERR_INVALID_ARG, "hidden = %lld < 1", (long long)c->hidden);
+  if (c->n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts = %lld < 1", (long long)c->n_experts);
+  if (c->top_k < 1) return fail(MOE_ERR_INVALID_ARG, "top_k = %lld < 1", (long long)c->top_k);
+  if (c->top_k > c->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k = %lld > n_experts = %lld", (long long)c->top_k, (long long)c->n_experts);
+  if (c->inter < 1) return fail(MOE_ERR_INVALID_ARG, "inter = %lld < 1", (long long)c->inter);
+  if (c->shared_inter < 0) return fail(MOE_ERR_INVALID_ARG, "shared_inter = %lld < 0", (long long)c->shared_inter);
+  if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1)
+    return fail(MOE_ERR_INVALID_ARG, "norm_topk_prob = %d (must be 0 or 1)", c->norm_topk_prob);
+  if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved = %d (must be 0)", c->reserved);
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
+  if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "out_dtype %d not supported", c->out_dtype);
+  const int64_t align = c->dtype == MOE_BF16 ? 8 : 4;
+  if (c->hidden % align) return fail(MOE_ERR_UNSUPPORTED, "hidden = %lld is not a multiple of %lld", (long long)c->hidden, (long long)align);
+  if (c->inter % align) return fail(MOE_ERR_UNSUPPORTED, "inter = %lld is not a multiple of %lld", (long long)c->inter, (long long)align);
+  if (c->shared_inter % align)
+    return fail(MOE_ERR_UNSUPPORTED, "shared_inter = %lld is not a multiple of %lld", (long long)c->shared_inter, (long long)align);
+  if (c->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts = %lld > %lld", (long long)c->n_experts, (long long)kMaxExperts);
+  if (c->hidden > (1 << 20) || c->inter > (1 << 20) || c->shared_inter > (1 << 20))
+    return fail(MOE_ERR_UNSUPPORTED, "hidden/inter above 2^20");
+  if (c->n_tokens > 0 && c->n_tokens * c->top_k > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k = %lld exceeds int32 row indices", (long long)(c->n_tokens * c->top_k));
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t weights, experts, shared_scale, counts, offsets, block_counts, token_of, slot_pos, h, out, sh_h, sh_out, total;
+};
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+static Layout layout_of(const moe_config* c) {
+  Layout L{};
+  const size_t N = static_cast<size_t>(c->n_tokens), A = N * static_cast<size_t>(c->top_k);
+  const size_t E = static_cast<size_t>(c->n_experts), D = static_cast<size_t>(c->hidden);
+  const size_t I = static_cast<size_t>(c->inter), Is = static_cast<size_t>(c->shared_inter);
+  const size_t eb = elem_bytes(c->dtype);
+  size_t at = 0;
+  auto take = [&](size_t bytes) { const size_t p = at; at += align256(bytes); return p; };
+  L.block_counts = take(static_cast<size_t>(permute_chunks(static_cast<int64_t>(A))) * E * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.weights = take(A * 4);
+  L.experts = take(A * 4);
+  L.token_of = take(A * 4);
+  L.slot_pos = take(A * 4);
+  L.shared_scale = take(Is ? N * 4 : 0);
+  L.h = take(A * I * eb);
+  L.out = take(A * D * 4);
+  L.sh_h = take(Is ? N * Is * eb : 0);
+  L.sh_out = take(Is ? N * D * 4 : 0);
+  L.total = at;
+  return L;
+}
+
+static size_t permute_ws_bytes(const moe_config* c) {
+  const size_t A = static_cast<size_t>(c->n_tokens) * static_cast<size_t>(c->top_k);
+  return static_cast<size_t>(permute_chunks(static_cast<int64_t>(A))) * static_cast<size_t>(c->n_experts) * 4;
+}
+
+#define MOE_TRY(expr)            \
+  do {                           \
+    const int _s = (expr);       \
+    if (_s != MOE_OK) return _s; \
+  } while (0)
+
+static int route_impl(const moe_config* c, const void* x, const void* w_router, const void* w_shared_gate,
+                      float* logits, float* weights, int32_t* experts, float* shared_scale, hipStream_t st) {
+  RouteArgs a{};
+  a.x = x;
+  a.w_router = w_router;
+  a.w_shared_gate = w_shared_gate;
+  a.logits = logits;
+  a.weights = weights;
+  a.experts = experts;
+  a.shared_scale = shared_scale;
+  a.N = c->n_tokens;
+  a.D = static_cast<int>(c->hidden);
+  a.E = static_cast<int>(c->n_experts);
+  a.k = static_cast<int>(c->top_k);
+  a.norm = c->norm_topk_prob;
+  a.bf16 = c->dtype == MOE_BF16;
+  launch_route(a, st);
+  return check_launch("moe_route");
+}
+
+static int permute_impl(const moe_config* c, const int32_t* experts, const void* x, int32_t* counts,
+                        int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, int32_t* block_counts,
+                        hipStream_t st) {
+  PermuteArgs a{};
+  a.experts = experts;
+  a.block_counts = block_counts;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.token_of = token_of;
+  a.slot_pos = slot_pos;
+  a.A = c->n_tokens * c->top_k;
+  a.E = static_cast<int>(c->n_experts);
+  a.k = static_cast<int>(c->top_k);
+  launch_permute(a, st);
+  if (x_perm) launch_gather_rows(x, token_of, x_perm, a.A, c->hidden * static_cast<int64_t>(elem_bytes(c->dtype)), st);
+  return check_launch("moe_permute");
+}
+
+static int ffn_checks(const moe_config* c, int64_t n_groups, int64_t inter, int64_t max_rows, const int32_t* offsets) {
+  MOE_TRY(validate_config(c));
+  if (n_groups < 1) return fail(MOE_ERR_INVALID_ARG, "n_groups = %lld < 1", (long long)n_groups);
+  if (n_groups > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_groups = %lld > %lld", (long long)n_groups, (long long)kMaxExperts);
+  if (inter < 1) return fail(MOE_ERR_INVALID_ARG, "inter = %lld < 1", (long long)inter);
+  const int64_t align = c->dtype == MOE_BF16 ? 8 : 4;
+  if (inter % align) return fail(MOE_ERR_UNSUPPORTED, "inter = %lld is not a multiple of %lld", (long long)inter, (long long)align);
+  if (inter > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "inter above 2^20");
+  if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows = %lld < 0", (long long)max_rows);
+  if (max_rows > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "max_rows above int32");
+  if (!offsets && n_groups != 1) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL with n_groups = %lld", (long long)n_groups);
+  return MOE_OK;
+}
+
+static GemmArgs gemm_args(const moe_config* c, int64_t n_groups, int64_t inter, int64_t max_rows, const void* x,
+                          const int32_t* row_index, const int32_t* offsets, const void* w, void* out) {
+  GemmArgs a{};
+  a.x = x;
+  a.row_index = row_index;
+  a.offsets = offsets;
+  a.w = w;
+  a.out = out;
+  a.max_rows = max_rows;
+  a.G = static_cast<int>(n_groups);
+  a.D = static_cast<int>(c->hidden);
+  a.I = static_cast<int>(inter);
+  a.bf16 = c->dtype == MOE_BF16;
+  return a;
+}
+
+static int combine_impl(const moe_config* c, const float* out_perm, const float* weights, const int32_t* slot_pos,
+                        const float* shared_out, const float* shared_scale, void* y, hipStream_t st) {
+  CombineArgs a{};
+  a.out_perm = out_perm;
+  a.weights = weights;
+  a.slot_pos = slot_pos;
+  a.shared_out = shared_out;
+  a.shared_scale = shared_scale;
+  a.y = y;
+  a.N = c->n_tokens;
+  a.D = static_cast<int>(c->hidden);
+  a.k = static_cast<int>(c->top_k);
+  a.out_bf16 = c->out_dtype == MOE_BF16;
+  launch_combine(a, st);
+  return check_launch("moe_combine");
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
+  MOE_TRY(validate_config(cfg));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout_of(cfg).total;
+  return ok();
+}
+
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const void* w_shared_gate, float* logits,
+              float* weights, int32_t* experts, float* shared_scale, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (cfg->n_tokens == 0) return ok();
+  if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+  if (!w_router) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
+  if (!weights) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (!experts) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
+  if ((w_shared_gate == nullptr) != (shared_scale == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "w_shared_gate and shared_scale must be both set or both NULL");
+  MOE_TRY(route_impl(cfg, x, w_router, w_shared_gate, logits, weights, experts, shared_scale,
+                     static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* experts, const void* x, int32_t* counts, int32_t* offsets,
+                int32_t* token_of, int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (cfg->n_tokens > 0 && !experts) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
+  if (!counts) return fail(MOE_ERR_INVALID_ARG, "counts is NULL");
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if (cfg->n_tokens > 0 && (!token_of || !slot_pos)) return fail(MOE_ERR_INVALID_ARG, "token_of or slot_pos is NULL");
+  if ((x == nullptr) != (x_perm == nullptr)) return fail(MOE_ERR_INVALID_ARG, "x and x_perm must be both set or both NULL");
+  const size_t need = permute_ws_bytes(cfg);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+  // counts and offsets are defined even for N == 0 (all zero), so the scan always runs.
+  MOE_TRY(permute_impl(cfg, experts, x, counts, offsets, token_of, slot_pos, x_perm, static_cast<int32_t*>(ws),
+                       static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int moe_expert_gate_up(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows, const void* x,
+                       const int32_t* row_index, const int32_t* offsets, const void* gate_up, void* h, void* stream) {
+  MOE_TRY(ffn_checks(cfg, n_groups, inter, max_rows, offsets));
+  if (max_rows == 0) return ok();
+  if (!x || !gate_up || !h) return fail(MOE_ERR_INVALID_ARG, "x, gate_up or h is NULL");
+  launch_gate_up(gemm_args(cfg, n_groups, inter, max_rows, x, row_index, offsets, gate_up, h),
+                 static_cast<hipStream_t>(stream));
+  MOE_TRY(check_launch("moe_expert_gate_up"));
+  return ok();
+}
+
+int moe_expert_down(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows, const int32_t* offsets,
+                    const void* h, const void* down, float* out, void* stream) {
+  MOE_TRY(ffn_checks(cfg, n_groups, inter, max_rows, offsets));
+  if (max_rows == 0) return ok();
+  if (!h || !down || !out) return fail(MOE_ERR_INVALID_ARG, "h, down or out is NULL");
+  launch_down(gemm_args(cfg, n_groups, inter, max_rows, h, nullptr, offsets, down, out), static_cast<hipStream_t>(stream));
+  MOE_TRY(check_launch("moe_expert_down"));
+  return ok();
+}
+
+int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows, const void* x,
+                   const int32_t* row_index, const int32_t* offsets, const void* gate_up, const void* down, void* h,
+                   float* out, void* stream) {
+  MOE_TRY(ffn_checks(cfg, n_groups, inter, max_rows, offsets));
+  if (max_rows == 0) return ok();
+  if (!x || !gate_up || !down || !h || !out) return fail(MOE_ERR_INVALID_ARG, "x, gate_up, down, h or out is NULL");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  launch_gate_up(gemm_args(cfg, n_groups, inter, max_rows, x, row_index, offsets, gate_up, h), st);
+  MOE_TRY(check_launch("moe_expert_ffn (gate_up)"));
+  launch_down(gemm_args(cfg, n_groups, inter, max_rows, h, nullptr, offsets, down, out), st);
+  MOE_TRY(check_launch("moe_expert_ffn (down)"));
+  return ok();
+}
+
+int moe_combine(const moe_config* cfg, const float* out_perm, const float* weights, const int32_t* slot_pos,
+                const float* shared_out, const float* shared_scale, void* y, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (cfg->n_tokens == 0) return ok();
+  if (!out_perm || !weights || !slot_pos || !y) return fail(MOE_ERR_INVALID_ARG, "out_perm, weights, slot_pos or y is NULL");
+  if (shared_scale && !shared_out) return fail(MOE_ERR_INVALID_ARG, "shared_scale given without shared_out");
+  MOE_TRY(combine_impl(cfg, out_perm, weights, slot_pos, shared_out, shared_scale, y, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
+                const void* shared_gate_up, const void* shared_down, const void* w_shared_gate, void* y,
+                float* weights_out, int32_t* experts_out, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (cfg->n_tokens == 0) return ok();
+  if (!x || !w_router || !gate_up || !down || !y) return fail(MOE_ERR_INVALID_ARG, "x, w_router, gate_up, down or y is NULL");
+  if (cfg->shared_inter > 0 && (!shared_gate_up || !shared_down))
+    return fail(MOE_ERR_INVALID_ARG, "shared_inter > 0 needs shared_gate_up and shared_down");
+  if (cfg->shared_inter == 0 && (shared_gate_up || shared_down || w_shared_gate))
+    return fail(MOE_ERR_INVALID_ARG, "shared expert tensors given with shared_inter == 0");
+  const Layout L = layout_of(cfg);
+  if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, L.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MOE_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+
+  char* base = static_cast<char*>(ws);
+  float* weights = weights_out ? weights_out : reinterpret_cast<float*>(base + L.weights);
+  int32_t* experts = experts_out ? experts_out : reinterpret_cast<int32_t*>(base + L.experts);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* token_of = reinterpret_cast<int32_t*>(base + L.token_of);
+  int32_t* slot_pos = reinterpret_cast<int32_t*>(base + L.slot_pos);
+  float* shared_scale = (cfg->shared_inter && w_shared_gate) ? reinterpret_cast<float*>(base + L.shared_scale) : nullptr;
+  void* h = base + L.h;
+  float* out = reinterpret_cast<float*>(base + L.out);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t A = cfg->n_tokens * cfg->top_k;
+
+  MOE_TRY(route_impl(cfg, x, w_router, shared_scale ? w_shared_gate : nullptr, nullptr, weights, experts, shared_scale, st));
+  MOE_TRY(permute_impl(cfg, experts, nullptr, counts, offsets, token_of, slot_pos, nullptr,
+                       reinterpret_cast<int32_t*>(base + L.block_counts), st));
+  launch_gate_up(gemm_args(cfg, cfg->n_experts, cfg->inter, A, x, token_of, offsets, gate_up, h), st);
+  MOE_TRY(check_launch("moe_forward (gate_up)"));
+  launch_down(gemm_args(cfg, cfg->n_experts, cfg->inter, A, h, nullptr, offsets, down, out), st);
+  MOE_TRY(check_launch("moe_forward (down)"));
+  float* sh_out = nullptr;
+  if (cfg->shared_inter > 0) {
+    void* sh_h = base + L.sh_h;
+    sh_out = reinterpret_cast<float*>(base + L.sh_out);
+    launch_gate_up(gemm_args(cfg, 1, cfg->shared_inter, cfg->n_tokens, x, nullptr, nullptr, shared_gate_up, sh_h), st);
+    MOE_TRY(check_launch("moe_forward (shared gate_up)"));
+    launch_down(gemm_args(cfg, 1, cfg->shared_inter, cfg->n_tokens, sh_h, nullptr, nullptr, shared_down, sh_out), st);
+    MOE_TRY(check_launch("moe_forward (shared down)"));
+  }
+  MOE_TRY(combine_impl(cfg, out, weights, slot_pos, sh_out, shared_scale, y, st));
+  return ok();
+}
+
+}  // extern "C"

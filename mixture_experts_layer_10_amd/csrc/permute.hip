@@ -1,0 +1,137 @@
+// Grouping of the N*k assignments by expert: histogram -> prefix scan -> stable scatter
+// ("27. Mixture of experts", section "Dispatch", grouped dispatch steps 1-2; stretch exercise 2,
+//  the prefix-sum array of row offsets).
+//
+// Deterministic by construction: ranks come from ordered ballots inside a wave and ordered
+// per-wave counts inside a round, never from atomics (LDS atomics only build counts, whose value
+// does not depend on order).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kPermThreads = 256;
+
+int64_t permute_chunks(int64_t A) { return (A + kPermChunk - 1) / kPermChunk; }
+
+// Pass 1: per-chunk expert histogram.
+__global__ __launch_bounds__(kPermThreads) void perm_count_kernel(PermuteArgs a) {
+  __shared__ int s_cnt[512];
+  const int E = a.E;
+  for (int e = threadIdx.x; e < E; e += kPermThreads) s_cnt[e] = 0;
+  __syncthreads();
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * kPermChunk;
+  const int64_t hi = min<int64_t>(lo + kPermChunk, a.A);
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kPermThreads) atomicAdd(&s_cnt[a.experts[i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kPermThreads) a.block_counts[blockIdx.x * static_cast<int64_t>(E) + e] = s_cnt[e];
+}
+
+// Pass 2 (one workgroup of 512 threads, one expert per thread): counts, offsets, and each chunk's
+// starting row for each expert (written back over block_counts).
+__global__ __launch_bounds__(512) void perm_scan_kernel(PermuteArgs a, int n_chunks) {
+  __shared__ int s_wave[8];
+  const int E = a.E, e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < n_chunks; ++b) {
+      int32_t* p = a.block_counts + static_cast<int64_t>(b) * E + e;
+      const int c = *p;
+      *p = total;
+      total += c;
+    }
+    a.counts[e] = total;
+  }
+  // exclusive scan of total over e: inclusive wave scan, then the wave totals
+  int inc = total;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  const int excl = before + inc - total;
+  if (e < E) {
+    a.offsets[e] = excl;
+    for (int b = 0; b < n_chunks; ++b) a.block_counts[static_cast<int64_t>(b) * E + e] += excl;
+  }
+  if (e == 0) a.offsets[E] = static_cast<int32_t>(a.A);
+}
+
+// Pass 3: stable scatter. Rounds of 256 assignments in order; inside a wave, the rank among equal
+// experts comes from a ballot match; across the 4 waves of a round, from per-wave counts in LDS.
+__global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(PermuteArgs a, int nbits) {
+  __shared__ int s_run[512];
+  __shared__ int s_wcnt[4][512];
+  const int E = a.E, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kPermThreads) {
+    s_run[e] = a.block_counts[blockIdx.x * static_cast<int64_t>(E) + e];
+    s_wcnt[0][e] = s_wcnt[1][e] = s_wcnt[2][e] = s_wcnt[3][e] = 0;
+  }
+  __syncthreads();
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * kPermChunk;
+  const int64_t hi = min<int64_t>(lo + kPermChunk, a.A);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = lo; base < hi; base += kPermThreads) {
+    const int64_t i = base + tid;
+    const bool valid = i < hi;
+    const int e = valid ? a.experts[i] : 0;
+    uint64_t m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t b = __ballot(set);
+      m &= set ? b : ~b;
+    }
+    const int rank = __popcll(m & below);
+    const int cnt = __popcll(m);
+    if (valid && rank == 0) s_wcnt[wave][e] = cnt;
+    __syncthreads();
+    int pos = 0;
+    if (valid) {
+      pos = s_run[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wcnt[w][e];
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&s_run[e], cnt);
+      s_wcnt[wave][e] = 0;
+    }
+    __syncthreads();
+    if (valid) {
+      a.token_of[pos] = static_cast<int32_t>(i / a.k);
+      a.slot_pos[i] = pos;
+    }
+  }
+}
+
+void launch_permute(const PermuteArgs& a, hipStream_t st) {
+  const int n_chunks = static_cast<int>(permute_chunks(a.A));
+  int nbits = 1;
+  while ((1 << nbits) < a.E) ++nbits;
+  if (n_chunks > 0) perm_count_kernel<<<n_chunks, kPermThreads, 0, st>>>(a);
+  perm_scan_kernel<<<1, 512, 0, st>>>(a, n_chunks);
+  if (n_chunks > 0) perm_scatter_kernel<<<n_chunks, kPermThreads, 0, st>>>(a, nbits);
+}
+
+// Row gather: one wave per row, 16-byte vectors.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ x, const int32_t* __restrict__ token_of,
+                                                          u32x4* __restrict__ x_perm, int64_t rows, int64_t vecs) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const u32x4* src = x + static_cast<int64_t>(token_of[row]) * vecs;
+  u32x4* dst = x_perm + row * vecs;
+  for (int64_t v = threadIdx.x & 63; v < vecs; v += 64) dst[v] = src[v];
+}
+
+void launch_gather_rows(const void* x, const int32_t* token_of, void* x_perm, int64_t rows,
+                        int64_t row_bytes, hipStream_t st) {
+  if (rows <= 0) return;
+  const unsigned grid = static_cast<unsigned>((rows + 3) / 4);
+  gather_rows_kernel<<<grid, 256, 0, st>>>(static_cast<const u32x4*>(x), token_of, static_cast<u32x4*>(x_perm),
+                                           rows, row_bytes / 16);
+}
+
+}  // namespace moe

@@ -107,12 +107,29 @@ class MoeInputs:
             return bf16_bits_to_f32(a).astype(np.float64)
         return a.astype(np.float64)
 
+    def expert_view(self, name: str) -> "ExpertView":
+        """Lazy float64 view of a stacked [E, ...] tensor: view[e] converts expert e only."""
+        return ExpertView(self.store[name])
+
     def token_rows(self, idx) -> np.ndarray:
         """Exact float64 values of x for the given token indices only."""
         a = self.store["x"][np.asarray(idx)]
         if a.dtype == np.uint16:
             return bf16_bits_to_f32(a).astype(np.float64)
         return a.astype(np.float64)
+
+
+class ExpertView:
+    def __init__(self, a: np.ndarray):
+        self.a = a
+        self.shape = a.shape
+
+    def __len__(self):
+        return self.a.shape[0]
+
+    def __getitem__(self, e):
+        v = self.a[e]
+        return bf16_bits_to_f32(v).astype(np.float64) if v.dtype == np.uint16 else v.astype(np.float64)
 
 
 TENSOR_ORDER = ["x", "w_router", "gate_up", "down", "shared_gate_up", "shared_down", "w_shared_gate"]

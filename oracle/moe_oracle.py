@@ -129,7 +129,7 @@ def grouped_expert_ffn(x_rows, offsets, gate_up, down):
     """Run group g's SwiGLU expert on its contiguous slice rows[offsets[g]:offsets[g+1]]
     ([MoE-ch27] "Dispatch", grouped step 3). Empty groups are skipped. Returns out_perm[rows, D]."""
     x_rows = np.asarray(x_rows, np.float64)
-    out = np.zeros((x_rows.shape[0], np.asarray(down).shape[-2]), np.float64)
+    out = np.zeros_like(x_rows)                     # expert outputs have the model width D
     for g in range(len(offsets) - 1):
         a, b = int(offsets[g]), int(offsets[g + 1])
         if b > a:
