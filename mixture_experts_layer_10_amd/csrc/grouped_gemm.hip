@@ -95,7 +95,10 @@ struct BfCfg {
   static_assert(A_LD * NT == BM * 8 && B_LD * NT == BNB * 8, "tile must split evenly over threads");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// 128-byte rows (64 bf16). The LDS serves a 16-byte-per-lane read 16 lanes at a time over 64 banks
+// (256 bytes), so 16 consecutive rows at one logical chunk must land in 16 distinct 16-byte slots
+// of a 256-byte window: chunk c of row r sits at c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 template <int WM, int TM, int WN, int TN, bool kSwiGLU>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
@@ -258,6 +261,213 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Streaming bf16 kernel (K % 128 == 0): tiles of 32 k-values (64-byte rows) move straight from
+// global memory into LDS with global_load_lds (no register round trip), four stages deep, so three
+// stages of loads are in flight while one is consumed. Chunk c of row r sits at c ^ ((r >> 2) & 3):
+// 16 consecutive rows at one chunk cover a 256-byte window's 16 slots. One DMA instruction writes
+// 64 lanes x 16 bytes = 16 rows contiguously, so the swizzle is applied to the global side: lane l
+// fetches chunk (l & 3) ^ (((l >> 2) >> 2) & 3) of row l >> 2.
+// 32-row blocks of a tile that lie past the group's last row skip their matrix-core steps.
+// ---------------------------------------------------------------------------------------------
+constexpr int kSK = 32;
+
+// Direct global -> LDS copy of 16 bytes per lane; lane l lands at lds_dst + 16 l. Issued as inline
+// asm so the compiler does not insert waits for it; the kernel orders it explicitly (vmcnt + barrier).
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)lds_dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory");
+#endif
+}
+
+template <int WM, int TM, int WN, int TN, bool kSwiGLU>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
+  constexpr int BM = WM * TM * 32, BNB = WN * TN * 32, NT = WM * WN * 64, NW = WM * WN;
+  constexpr int A_INS = BM / 16 / NW, B_INS = BNB / 16 / NW;   // DMA instructions per wave per stage
+  constexpr int OUT_COLS = kSwiGLU ? BNB / 2 : BNB;
+  constexpr int PER_STAGE = A_INS + B_INS;
+  static_assert(A_INS * 16 * NW == BM && B_INS * 16 * NW == BNB, "tile rows must split into 16-row DMA groups");
+  static_assert(!kSwiGLU || TN % 2 == 0, "SwiGLU pairs gate blocks with up blocks");
+  // one array per stage: the four buffers are distinct objects
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * kSK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * kSK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[BM * kSK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA3[BM * kSK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BNB * kSK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BNB * kSK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BNB * kSK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB3[BNB * kSK];
+  __shared__ int s_pref[1025];
+  __shared__ int s_tmp[16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int G = a.G;
+  const int K = kSwiGLU ? a.D : a.I;
+  const int NOUT = kSwiGLU ? a.I : a.D;
+  const int n_tiles = (NOUT + OUT_COLS - 1) / OUT_COLS;
+  build_tile_prefix<NT>(a.offsets, G, a.max_rows, BM, n_tiles, s_pref, s_tmp);
+  const int total = s_pref[G];
+  const int P = gridDim.x;
+  const uint16_t* X = static_cast<const uint16_t*>(a.x);
+  const uint16_t* W = static_cast<const uint16_t*>(a.w);
+  const int ksteps = K / kSK;                        // a multiple of 4
+  const int lrow = lane >> 2;                         // row within a 16-row DMA group
+  const int lch = (lane & 3) ^ ((lrow >> 2) & 3);     // logical chunk this lane fetches
+
+  // LDS read offsets: fragment rows are 32-aligned + (lane & 31), so row bits 2..3 are lane bits
+  // 2..3 and the chunk of k-step kk is (2 kk + (lane >> 5)) ^ ((lane >> 2) & 3).
+  int koA[2], koB[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int pc = ((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 3;
+    koA[kk] = (wm * TM * 32 + (lane & 31)) * kSK + pc;
+    koB[kk] = ((kSwiGLU ? wn * (TN / 2) : wn * TN) * 32 + (lane & 31)) * kSK + pc;
+  }
+  // s_waitcnt immediates: vmcnt(n) in bits 3:0 and 15:14, expcnt/lgkmcnt fields at "no wait"
+  constexpr int W2 = ((2 * PER_STAGE) & 15) | (((2 * PER_STAGE) >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  constexpr int W1 = (PER_STAGE & 15) | ((PER_STAGE >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  constexpr int W0 = (0x7 << 4) | (0xF << 8);
+
+  for (int r = 0;; ++r) {
+    const int t = tile_of_round(r, blockIdx.x, P);
+    if (r * P >= total) break;
+    if (t >= total) continue;
+    const int g = find_group(s_pref, G, t);
+    const int local = t - s_pref[g];
+    const int64_t row0 = a.offsets ? a.offsets[g] : 0;
+    const int64_t rows = a.offsets ? static_cast<int64_t>(a.offsets[g + 1]) - row0 : a.max_rows;
+    if (rows <= 0) continue;
+    const int mt = local / n_tiles, nt = local - mt * n_tiles;
+    const int m0 = mt * BM;
+    const int c0 = nt * OUT_COLS;
+    // 32-row blocks of this wave that hold real rows (uniform across the wave)
+    const int live = static_cast<int>(min<int64_t>(TM, max<int64_t>(0, (rows - m0 - wm * TM * 32 + 31) / 32)));
+
+    const uint16_t* srcA[A_INS];
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) {
+      const int rr = (wave * A_INS + j) * 16 + lrow;
+      const int64_t lr = min<int64_t>(m0 + rr, rows - 1);   // rows past the group read a valid row
+      const int64_t p = row0 + lr;
+      const int64_t src = a.row_index ? a.row_index[p] : p;
+      srcA[j] = X + src * K + lch * 8;
+    }
+    const uint16_t* Wg = W + static_cast<int64_t>(g) * (kSwiGLU ? 2LL * a.I * a.D : static_cast<int64_t>(a.D) * a.I);
+    const uint16_t* srcB[B_INS];
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) {
+      const int rr = (wave * B_INS + j) * 16 + lrow;
+      int wrow;
+      if (kSwiGLU) {
+        const int half = BNB / 2;
+        const int ci = min(c0 + (rr % half), NOUT - 1);
+        wrow = rr < half ? ci : a.I + ci;
+      } else {
+        wrow = min(c0 + rr, NOUT - 1);
+      }
+      srcB[j] = Wg + static_cast<int64_t>(wrow) * K + lch * 8;
+    }
+    auto issue = [&](int ks, uint16_t* sa, uint16_t* sb) {
+      const int kb = ks * kSK;
+#pragma unroll
+      for (int j = 0; j < A_INS; ++j) dma16(srcA[j] + kb, sa + (wave * A_INS + j) * 512);
+#pragma unroll
+      for (int j = 0; j < B_INS; ++j) dma16(srcB[j] + kb, sb + (wave * B_INS + j) * 512);
+    };
+    // wait for stage s (later stages may stay in flight), then sync the workgroup: after this, stage
+    // s is visible to every wave and every wave has finished reading stage s - 1's buffer
+    auto wait_stage = [&](int s) {
+      const int ahead = min(2, ksteps - 1 - s);
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(W2);
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(W1);
+      else __builtin_amdgcn_s_waitcnt(W0);
+      asm volatile("s_barrier" ::: "memory");
+    };
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&sa[koA[kk] + i * 32 * kSK]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          constexpr int H = TN / 2;
+          const int rowoff = kSwiGLU ? (j < H ? j * 32 : BNB / 2 + (j - H) * 32) : j * 32;
+          fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          if (i < live) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+          }
+      }
+    };
+    __builtin_amdgcn_s_waitcnt(0);       // the previous tile's stores and index loads are done
+    issue(0, sA0, sB0);
+    issue(1, sA1, sB1);
+    issue(2, sA2, sB2);
+    for (int ks = 0; ks < ksteps; ks += 4) {
+      wait_stage(ks);
+      if (ks + 3 < ksteps) issue(ks + 3, sA3, sB3);
+      compute(sA0, sB0);
+      wait_stage(ks + 1);
+      if (ks + 4 < ksteps) issue(ks + 4, sA0, sB0);
+      compute(sA1, sB1);
+      wait_stage(ks + 2);
+      if (ks + 5 < ksteps) issue(ks + 5, sA1, sB1);
+      compute(sA2, sB2);
+      wait_stage(ks + 3);
+      if (ks + 6 < ksteps) issue(ks + 6, sA2, sB2);
+      compute(sA3, sB3);
+    }
+
+    if constexpr (kSwiGLU) {
+      uint16_t* Hh = static_cast<uint16_t*>(a.out);
+      constexpr int H = TN / 2;
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const int col = c0 + (wn * H + j) * 32 + (lane & 31);
+        if (col < NOUT) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int rr = m0 + (wm * TM + i) * 32 + acc_row(e, lane);
+              if (rr < rows) Hh[(row0 + rr) * NOUT + col] = f32_to_bf16(silu(acc[i][j][e]) * acc[i][j + H][e]);
+            }
+        }
+      }
+    } else {
+      float* O = static_cast<float*>(a.out);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = c0 + (wn * TN + j) * 32 + (lane & 31);
+        if (col < NOUT) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int rr = m0 + (wm * TM + i) * 32 + acc_row(e, lane);
+              if (rr < rows) O[(row0 + rr) * NOUT + col] = acc[i][j][e];
+            }
+        }
+      }
+    }
+    __syncthreads();                     // every wave is done with the stage buffers
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // fp32 kernel: 64 x 64 tiles, 256 threads, 4 x 4 register blocking, k step 16.
 //   SwiGLU: B tile = 32 gate rows + the 32 matching up rows; each thread keeps 4 rows x 2 h columns
@@ -388,6 +598,17 @@ static void launch_bf16(const GemmArgs& a, hipStream_t st) {
   gemm_bf16_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, C::NT, 0, st>>>(a);
 }
 
+template <int WM, int TM, int WN, int TN, bool kSwiGLU>
+static void launch_stream(const GemmArgs& a, hipStream_t st) {
+  constexpr int BM = WM * TM * 32, BNB = WN * TN * 32;
+  constexpr int out_cols = kSwiGLU ? BNB / 2 : BNB;
+  const int NOUT = kSwiGLU ? a.I : a.D;
+  const int n_tiles = (NOUT + out_cols - 1) / out_cols;
+  constexpr int lds = 4 * (BM + BNB) * kSK * 2;
+  const unsigned grid = persistent_grid(tile_upper_bound(a, BM, n_tiles), lds <= 76 * 1024 ? 2 : 1);
+  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, WM * WN * 64, 0, st>>>(a);
+}
+
 template <bool kSwiGLU>
 static void launch_f32(const GemmArgs& a, hipStream_t st) {
   const int NOUT = kSwiGLU ? a.I : a.D;
@@ -404,15 +625,21 @@ static bool small_rows(const GemmArgs& a) {
   return a.max_rows <= 64LL * a.G;
 }
 
+// Streaming path when K is a multiple of 128 (four 32-wide stages per loop trip); the
+// register-staged kernel covers the other K.
+static bool streamable(const GemmArgs& a, bool gate_up) { return ((gate_up ? a.D : a.I) % 128) == 0; }
+
 void launch_gate_up(const GemmArgs& a, hipStream_t st) {
   if (!a.bf16) return launch_f32<true>(a, st);
   if (small_rows(a)) return launch_bf16<1, 1, 4, 2, true>(a, st);
+  if (streamable(a, true)) return launch_stream<2, 4, 4, 2, true>(a, st);
   return launch_bf16<2, 4, 4, 2, true>(a, st);
 }
 
 void launch_down(const GemmArgs& a, hipStream_t st) {
   if (!a.bf16) return launch_f32<false>(a, st);
   if (small_rows(a)) return launch_bf16<1, 1, 4, 2, false>(a, st);
+  if (streamable(a, false)) return launch_stream<2, 4, 4, 2, false>(a, st);
   return launch_bf16<2, 4, 4, 2, false>(a, st);
 }
 

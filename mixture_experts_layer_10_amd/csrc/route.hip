@@ -3,104 +3,39 @@
 // ("27. Mixture of experts", section "The router", steps 1-3 and the parity note; section
 //  "The shared expert", its equation.)
 //
-// One workgroup (4 waves) owns 64 tokens and all E <= 512 experts, so the softmax never leaves the
-// workgroup. bf16: the [64 x E] logits come from 32x32x16 matrix-core steps (bf16 products are exact
-// in fp32, accumulation in fp32), written to LDS unrounded. fp32: plain FMA dot products.
-// Selection: each wave walks 16 tokens; a lane holds experts lane, lane+64, ...; k rounds of a
+// One workgroup (4 waves) owns a tile of tokens and all E <= 512 experts, so the softmax never
+// leaves the workgroup.
+//  bf16: 32 tokens per workgroup. x[32 x 64] and W_r[E x 64] k-slices are staged in LDS (16-byte
+//        chunks, XOR swizzle, register prefetch of the next slice); wave w computes expert blocks
+//        w, w+4, ... with 32x32x16 matrix-core steps (bf16 products are exact in fp32, fp32
+//        accumulation). The logits land in LDS unrounded, over the staging buffers.
+//  fp32: 64 tokens per workgroup, plain FMA dot products.
+// Selection: each wave walks its tokens; a lane holds experts lane, lane+64, ...; k rounds of a
 // wave-wide (p, index) arg-max with ties to the lower index.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kRouteTokens = 64;
 constexpr int kRouteThreads = 256;
 
-template <int EB, bool kBf16>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
-  constexpr int kCols = EB * 128;                 // padded expert columns held in LDS
-  constexpr int kPer = kCols / kWave;             // logits per lane during selection
-  __shared__ float s_logit[kRouteTokens * kCols];
-  __shared__ float s_sel_p[4][512];
-  __shared__ int s_sel_e[4][512];
-
+// Softmax, top-k and outputs for token rows [0, n_rows) of a workgroup whose logits sit in
+// s_logit[t * cols + e]. sel_p / sel_e: per-wave scratch of 512 entries each.
+__device__ void route_select(const RouteArgs& a, const float* s_logit, int cols, int64_t n0, int n_rows,
+                             float* sel_p_all, int* sel_e_all) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRouteTokens;
-  const int D = a.D, E = a.E;
-
-  if constexpr (kBf16) {
-    const uint16_t* x = static_cast<const uint16_t*>(a.x);
-    const uint16_t* w = static_cast<const uint16_t*>(a.w_router);
-    f32x16 acc[2][EB];
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int b = 0; b < EB; ++b) acc[r][b] = f32x16{};
-    const int64_t r0 = min<int64_t>(n0 + (lane & 31), a.N - 1);
-    const int64_t r1 = min<int64_t>(n0 + 32 + (lane & 31), a.N - 1);
-    const uint16_t* xa0 = x + r0 * D;
-    const uint16_t* xa1 = x + r1 * D;
-    const uint16_t* wb[EB];
-#pragma unroll
-    for (int b = 0; b < EB; ++b) {
-      int e = (wave + 4 * b) * 32 + (lane & 31);
-      wb[b] = w + static_cast<int64_t>(min(e, E - 1)) * D;   // columns >= E are masked later
-    }
-    const int koff = (lane >> 5) * 8;
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const int kk = k0 + koff;
-      const bool ok = kk < D;                    // D % 8 == 0: a lane's 8 values are all in or out
-      u32x4 a0 = ok ? *reinterpret_cast<const u32x4*>(xa0 + kk) : u32x4{0, 0, 0, 0};
-      u32x4 a1 = ok ? *reinterpret_cast<const u32x4*>(xa1 + kk) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int b = 0; b < EB; ++b) {
-        if ((wave + 4 * b) * 32 < E) {
-          u32x4 bv = ok ? *reinterpret_cast<const u32x4*>(wb[b] + kk) : u32x4{0, 0, 0, 0};
-          acc[0][b] = mfma32(a0, bv, acc[0][b]);
-          acc[1][b] = mfma32(a1, bv, acc[1][b]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int b = 0; b < EB; ++b) {
-        const int col = (wave + 4 * b) * 32 + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s_logit[(r * 32 + acc_row(i, lane)) * kCols + col] = acc[r][b][i];
-      }
-  } else {
-    const float* x = static_cast<const float*>(a.x);
-    const float* w = static_cast<const float*>(a.w_router);
-    for (int idx = tid; idx < kRouteTokens * E; idx += kRouteThreads) {
-      const int t = idx / E, e = idx - t * E;
-      const int64_t n = min<int64_t>(n0 + t, a.N - 1);
-      const f32x4* xr = reinterpret_cast<const f32x4*>(x + n * D);
-      const f32x4* wr = reinterpret_cast<const f32x4*>(w + static_cast<int64_t>(e) * D);
-      float s = 0.f;
-      for (int d = 0; d < D / 4; ++d) {
-        f32x4 u = xr[d], v = wr[d];
-        s = fmaf(u[0], v[0], s);
-        s = fmaf(u[1], v[1], s);
-        s = fmaf(u[2], v[2], s);
-        s = fmaf(u[3], v[3], s);
-      }
-      s_logit[t * kCols + e] = s;
-    }
-  }
-  __syncthreads();
-
-  const int k = a.k;
-  for (int t = wave; t < kRouteTokens; t += 4) {
+  const int E = a.E, D = a.D, k = a.k;
+  float* sel_p = sel_p_all + wave * 512;
+  int* sel_e = sel_e_all + wave * 512;
+  for (int t = wave; t < n_rows; t += 4) {
     const int64_t n = n0 + t;
-    if (n >= a.N) break;
+    constexpr int kPer = 8;                    // E <= 512 = 8 per lane
     float v[kPer];
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int e = lane + kWave * j;
-      v[j] = e < E ? s_logit[t * kCols + e] : -INFINITY;
+      v[j] = e < E ? s_logit[t * cols + e] : -INFINITY;
       m = fmaxf(m, v[j]);
     }
     m = wave_max(m);
@@ -118,7 +53,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       v[j] = e < E ? v[j] / s : -1.f;          // probabilities; -1 marks "not a candidate"
     }
     if (a.logits) {
-      for (int e = lane; e < E; e += kWave) a.logits[n * E + e] = s_logit[t * kCols + e];
+      for (int e = lane; e < E; e += kWave) a.logits[n * E + e] = s_logit[t * cols + e];
     }
     float kept_sum = 0.f;
     for (int r = 0; r < k; ++r) {
@@ -138,19 +73,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       for (int j = 0; j < kPer; ++j)
         if (lane + kWave * j == be) v[j] = -1.f;
       kept_sum += bp;                            // slot order, identical in every lane
-      if (lane == 0) { s_sel_p[wave][r] = bp; s_sel_e[wave][r] = be; }
+      if (lane == 0) { sel_p[r] = bp; sel_e[r] = be; }
     }
-    __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int r = lane; r < k; r += kWave) {
-      const float p = s_sel_p[wave][r];
+      const float p = sel_p[r];
       a.weights[n * k + r] = a.norm ? p / kept_sum : p;
-      a.experts[n * k + r] = s_sel_e[wave][r];
+      a.experts[n * k + r] = sel_e[r];
     }
     if (a.w_shared_gate) {
       float z = 0.f;
-      if constexpr (kBf16) {
+      if (a.bf16) {
         const uint16_t* xr = static_cast<const uint16_t*>(a.x) + n * D;
         const uint16_t* ws = static_cast<const uint16_t*>(a.w_shared_gate);
         for (int d = lane; d < D; d += kWave) z = fmaf(bf16_to_f32(xr[d]), bf16_to_f32(ws[d]), z);
@@ -162,27 +97,157 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       z = wave_sum(z);
       if (lane == 0) a.shared_scale[n] = 1.f / (1.f + expf(-z));
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
-template <int EB>
-static void launch_route_eb(const RouteArgs& a, hipStream_t st) {
-  const unsigned grid = static_cast<unsigned>((a.N + kRouteTokens - 1) / kRouteTokens);
-  if (a.bf16)
-    route_kernel<EB, true><<<grid, kRouteThreads, 0, st>>>(a);
-  else
-    route_kernel<EB, false><<<grid, kRouteThreads, 0, st>>>(a);
+// ---------------------------------------------------------------------------------------------
+// bf16: EP = padded experts / 128; wave w owns 32-expert blocks w + 4 b, b < EP.
+// ---------------------------------------------------------------------------------------------
+constexpr int kRtTok = 32;
+constexpr int kRtBK = 64;
+
+__device__ __forceinline__ int rswz(int row, int chunk) { return row * kRtBK + ((chunk ^ (row & 7)) << 3); }
+
+template <int EP>
+__global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) {
+  constexpr int EPAD = EP * 128;
+  constexpr int XS = kRtTok * kRtBK;             // elements of one x stage
+  constexpr int WS = EPAD * kRtBK;               // elements of one W stage
+  constexpr int STAGE_BYTES = 2 * (XS + WS) * 2;
+  constexpr int LOGIT_BYTES = kRtTok * EPAD * 4;
+  constexpr int SEL_BYTES = 4 * 512 * 8;
+  static_assert(LOGIT_BYTES + SEL_BYTES <= STAGE_BYTES, "logits and selection scratch alias the stages");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGE_BYTES / 2];
+  uint16_t* sX = smem;                           // [2][XS]
+  uint16_t* sW = smem + 2 * XS;                  // [2][WS]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRtTok;
+  const int D = a.D, E = a.E;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* w = static_cast<const uint16_t*>(a.w_router);
+
+  // loaders: x: one chunk per thread (32 rows x 8 chunks); W: EP*4 chunks per thread
+  constexpr int WL = EPAD * 8 / kRouteThreads;
+  const int xr = tid >> 3, xc = tid & 7;
+  const uint16_t* srcX = x + min<int64_t>(n0 + xr, a.N - 1) * D + xc * 8;
+  const uint16_t* srcW[WL];
+  int wrow[WL], wch[WL];
+#pragma unroll
+  for (int j = 0; j < WL; ++j) {
+    const int idx = tid + j * kRouteThreads;
+    wrow[j] = idx >> 3;
+    wch[j] = idx & 7;
+    srcW[j] = w + static_cast<int64_t>(min(wrow[j], E - 1)) * D + wch[j] * 8;
+  }
+  u32x4 rx, rw[WL];
+  auto gload = [&](int kb) {
+    rx = (kb + xc * 8 < D) ? *reinterpret_cast<const u32x4*>(srcX + kb) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < WL; ++j)
+      rw[j] = (kb + wch[j] * 8 < D && wrow[j] < E) ? *reinterpret_cast<const u32x4*>(srcW[j] + kb) : u32x4{0, 0, 0, 0};
+  };
+  auto sstore = [&](int buf) {
+    *reinterpret_cast<u32x4*>(&sX[buf * XS + rswz(xr, xc)]) = rx;
+#pragma unroll
+    for (int j = 0; j < WL; ++j) *reinterpret_cast<u32x4*>(&sW[buf * WS + rswz(wrow[j], wch[j])]) = rw[j];
+  };
+
+  f32x16 acc[EP];
+#pragma unroll
+  for (int b = 0; b < EP; ++b) acc[b] = f32x16{};
+  const int ksteps = (D + kRtBK - 1) / kRtBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < ksteps) gload((ks + 1) * kRtBK);
+#pragma unroll
+    for (int kk = 0; kk < kRtBK / 16; ++kk) {
+      const int ch = kk * 2 + (lane >> 5);
+      const u32x4 fa = *reinterpret_cast<const u32x4*>(&sX[buf * XS + rswz(lane & 31, ch)]);
+#pragma unroll
+      for (int b = 0; b < EP; ++b) {
+        if ((wave + 4 * b) * 32 < E) {
+          const u32x4 fb = *reinterpret_cast<const u32x4*>(&sW[buf * WS + rswz((wave + 4 * b) * 32 + (lane & 31), ch)]);
+          acc[b] = mfma32(fa, fb, acc[b]);
+        }
+      }
+    }
+    if (ks + 1 < ksteps) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  float* s_logit = reinterpret_cast<float*>(smem);                         // [kRtTok][EPAD]
+  float* s_selp = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + LOGIT_BYTES);
+  int* s_sele = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + LOGIT_BYTES + 4 * 512 * 4);
+#pragma unroll
+  for (int b = 0; b < EP; ++b) {
+    const int col = (wave + 4 * b) * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_logit[acc_row(i, lane) * EPAD + col] = acc[b][i];
+  }
+  __syncthreads();
+  const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
+  route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32: FMA dot products, 64 tokens per workgroup.
+// ---------------------------------------------------------------------------------------------
+template <int EP>
+__global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a) {
+  constexpr int kTok = 64;
+  constexpr int EPAD = EP * 128;
+  __shared__ float s_logit[kTok * EPAD];
+  __shared__ float s_selp[4 * 512];
+  __shared__ int s_sele[4 * 512];
+  const int tid = threadIdx.x;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTok;
+  const int D = a.D, E = a.E;
+  const float* x = static_cast<const float*>(a.x);
+  const float* w = static_cast<const float*>(a.w_router);
+  for (int idx = tid; idx < kTok * E; idx += kRouteThreads) {
+    const int t = idx / E, e = idx - t * E;
+    const int64_t n = min<int64_t>(n0 + t, a.N - 1);
+    const f32x4* xv = reinterpret_cast<const f32x4*>(x + n * D);
+    const f32x4* wv = reinterpret_cast<const f32x4*>(w + static_cast<int64_t>(e) * D);
+    float s = 0.f;
+    for (int d = 0; d < D / 4; ++d) {
+      const f32x4 u = xv[d], v = wv[d];
+      s = fmaf(u[0], v[0], s);
+      s = fmaf(u[1], v[1], s);
+      s = fmaf(u[2], v[2], s);
+      s = fmaf(u[3], v[3], s);
+    }
+    s_logit[t * EPAD + e] = s;
+  }
+  __syncthreads();
+  const int n_rows = static_cast<int>(min<int64_t>(kTok, a.N - n0));
+  route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
+}
+
+template <int EP>
+static void launch_route_ep(const RouteArgs& a, hipStream_t st) {
+  if (a.bf16) {
+    const unsigned grid = static_cast<unsigned>((a.N + kRtTok - 1) / kRtTok);
+    route_bf16_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
+  } else {
+    const unsigned grid = static_cast<unsigned>((a.N + 63) / 64);
+    route_f32_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
+  }
 }
 
 void launch_route(const RouteArgs& a, hipStream_t st) {
-  const int blocks32 = (a.E + 31) / 32;
-  const int eb = (blocks32 + 3) / 4;
-  switch (eb) {
-    case 1: launch_route_eb<1>(a, st); break;
-    case 2: launch_route_eb<2>(a, st); break;
-    case 3: launch_route_eb<3>(a, st); break;
-    default: launch_route_eb<4>(a, st); break;
+  switch ((a.E + 127) / 128) {
+    case 1: launch_route_ep<1>(a, st); break;
+    case 2: launch_route_ep<2>(a, st); break;
+    case 3: launch_route_ep<3>(a, st); break;
+    default: launch_route_ep<4>(a, st); break;
   }
 }
 
