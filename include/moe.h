@@ -83,9 +83,14 @@ int moe_workspace_bytes(const moe_config* cfg, size_t* bytes);
  *   w_shared_gate [D] or NULL                      (dtype) shared-expert gate vector w_s
  *   logits [N, E] fp32 or NULL                     optional copy of the router logits
  *   weights [N, k] fp32, experts [N, k] int32      required outputs
- *   shared_scale [N] fp32 or NULL                  sigmoid(w_s . x); required iff w_shared_gate */
+ *   shared_scale [N] fp32 or NULL                  sigmoid(w_s . x); required iff w_shared_gate
+ *   ws, ws_bytes: optional workspace (256-byte aligned, at least moe_workspace_bytes()). With it,
+ *     few-token batches split the D contraction over more workgroups (partial logits summed in a
+ *     fixed order); with ws == NULL the router runs in one pass. The two give the same selection
+ *     rule but may differ in the last bits of the fp32 logits. */
 int moe_route(const moe_config* cfg, const void* x, const void* w_router, const void* w_shared_gate,
-              float* logits, float* weights, int32_t* experts, float* shared_scale, void* stream);
+              float* logits, float* weights, int32_t* experts, float* shared_scale, void* ws, size_t ws_bytes,
+              void* stream);
 
 /* Grouping by expert: the N*k assignments a = n*k + j are sorted by expert id, stably (ties keep
  * assignment order), with no atomics on ranks, so the result is deterministic ("27. Mixture of
@@ -138,7 +143,7 @@ int moe_combine(const moe_config* cfg, const float* out_perm, const float* weigh
                 const int32_t* slot_pos, const float* shared_out, const float* shared_scale, void* y,
                 void* stream);
 
-/* The whole block: moe_route -> moe_permute -> moe_expert_ffn over the routed groups (rows gathered
+/* The whole block: moe_route (with ws) -> moe_permute -> moe_expert_ffn over the routed groups (rows gathered
  * straight from x) -> [shared expert as one more group over all N rows] -> moe_combine.
  *   shared_gate_up, shared_down: required iff cfg.shared_inter > 0; w_shared_gate may be NULL
  *     (ungated shared expert, scale 1)

@@ -74,7 +74,7 @@ def load(path: str = LIB_PATH):
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_workspace_bytes": (ctypes.c_int, [_CFG, ctypes.POINTER(ctypes.c_size_t)]),
-        "moe_route": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_route": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "moe_permute": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "moe_expert_gate_up": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
         "moe_expert_down": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -127,10 +127,17 @@ def moe_workspace_bytes(cfg: MoeConfig) -> int:
     return n.value
 
 
-def moe_route(cfg, x, w_router, w_shared_gate, logits, weights, experts, shared_scale, stream=None):
+def _nbytes(ws, ws_bytes):
+    if ws_bytes is not None:
+        return ws_bytes
+    return 0 if ws is None or isinstance(ws, int) else ws.numel() * ws.element_size()
+
+
+def moe_route(cfg, x, w_router, w_shared_gate, logits, weights, experts, shared_scale, ws=None, ws_bytes=None,
+              stream=None):
     _check("moe_route", load().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(w_shared_gate),
                                          _ptr(logits), _ptr(weights), _ptr(experts), _ptr(shared_scale),
-                                         _stream(stream)))
+                                         _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
 
 
 def moe_permute(cfg, experts, x, counts, offsets, token_of, slot_pos, x_perm, ws, ws_bytes=None, stream=None):

@@ -31,7 +31,7 @@ class Chain:
     def step(self, gate_up_events=None):
         c, d = self.cfg, self.dev
         B.moe_route(c, d["x"], d["w_router"], d.get("w_shared_gate") if self.gated else None, None,
-                    self.weights, self.experts, self.shared_scale)
+                    self.weights, self.experts, self.shared_scale, self.ws)
         B.moe_permute(c, self.experts, None, self.counts, self.offsets, self.token_of, self.slot_pos, None, self.ws)
         if gate_up_events:
             gate_up_events[0].record()

@@ -38,6 +38,13 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 acc) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
 }
 
+// One 16x16x32 bf16 step: acc[16x16] += A[16x32] * B[32x16]; lane l supplies A row / B column
+// (l % 16) with eight k values from k-group (l / 16). Result: element i of lane l holds row
+// 4*(l/16) + i, column l % 16.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
+}
+
 // Accumulator layout of the 32x32 matrix-core result: element i of lane l holds
 // row 8*(i/4) + 4*(l/32) + (i%4), column l % 32.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
@@ -55,5 +62,23 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's 16 bytes land
+// at lds_dst + 16 l, so one instruction fills 1 KB of LDS contiguously; lds_dst must be uniform.
+// Issued as inline asm so the compiler inserts no waits for it: callers order it with an explicit
+// s_waitcnt vmcnt(n) and a barrier. (Loads return in issue order, so the compiler's own vmcnt
+// waits for its loads stay conservative with these in the queue.)
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)lds_dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory");
+#endif
+}
+
+// s_waitcnt immediate for vmcnt(n) alone (bits 3:0 and 15:14; expcnt and lgkmcnt at "no wait").
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 }  // namespace moe

@@ -273,23 +273,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------------------------
 constexpr int kSK = 32;
 
-// Direct global -> LDS copy of 16 bytes per lane; lane l lands at lds_dst + 16 l. Issued as inline
-// asm so the compiler does not insert waits for it; the kernel orders it explicitly (vmcnt + barrier).
-__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const void*)lds_dst));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory");
-#endif
-}
-
 template <int WM, int TM, int WN, int TN, bool kSwiGLU>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32, NT = WM * WN * 64, NW = WM * WN;
-  constexpr int A_INS = BM / 16 / NW, B_INS = BNB / 16 / NW;   // DMA instructions per wave per stage
+  // DMA instructions per wave per stage; with fewer 16-row A groups than waves (BM = 32), waves
+  // repeat a group (identical bytes to the same LDS place), so every wave issues the same count
+  constexpr int A_GROUPS = BM / 16;
+  constexpr int A_INS = (A_GROUPS + NW - 1) / NW, B_INS = BNB / 16 / NW;
   constexpr int OUT_COLS = kSwiGLU ? BNB / 2 : BNB;
   constexpr int PER_STAGE = A_INS + B_INS;
-  static_assert(A_INS * 16 * NW == BM && B_INS * 16 * NW == BNB, "tile rows must split into 16-row DMA groups");
+  static_assert(A_INS * NW == A_GROUPS || A_INS == 1, "A rows must split into 16-row DMA groups");
+  static_assert(B_INS * 16 * NW == BNB, "B rows must split into 16-row DMA groups");
   static_assert(!kSwiGLU || TN % 2 == 0, "SwiGLU pairs gate blocks with up blocks");
   // one array per stage: the four buffers are distinct objects
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * kSK];
@@ -328,10 +322,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     koA[kk] = (wm * TM * 32 + (lane & 31)) * kSK + pc;
     koB[kk] = ((kSwiGLU ? wn * (TN / 2) : wn * TN) * 32 + (lane & 31)) * kSK + pc;
   }
-  // s_waitcnt immediates: vmcnt(n) in bits 3:0 and 15:14, expcnt/lgkmcnt fields at "no wait"
-  constexpr int W2 = ((2 * PER_STAGE) & 15) | (((2 * PER_STAGE) >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-  constexpr int W1 = (PER_STAGE & 15) | ((PER_STAGE >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-  constexpr int W0 = (0x7 << 4) | (0xF << 8);
+  constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
 
   for (int r = 0;; ++r) {
     const int t = tile_of_round(r, blockIdx.x, P);
@@ -351,7 +342,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     const uint16_t* srcA[A_INS];
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) {
-      const int rr = (wave * A_INS + j) * 16 + lrow;
+      const int rr = ((wave * A_INS + j) % A_GROUPS) * 16 + lrow;
       const int64_t lr = min<int64_t>(m0 + rr, rows - 1);   // rows past the group read a valid row
       const int64_t p = row0 + lr;
       const int64_t src = a.row_index ? a.row_index[p] : p;
@@ -375,7 +366,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     auto issue = [&](int ks, uint16_t* sa, uint16_t* sb) {
       const int kb = ks * kSK;
 #pragma unroll
-      for (int j = 0; j < A_INS; ++j) dma16(srcA[j] + kb, sa + (wave * A_INS + j) * 512);
+      for (int j = 0; j < A_INS; ++j) dma16(srcA[j] + kb, sa + ((wave * A_INS + j) % A_GROUPS) * 512);
 #pragma unroll
       for (int j = 0; j < B_INS; ++j) dma16(srcB[j] + kb, sb + (wave * B_INS + j) * 512);
     };
@@ -386,7 +377,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
       if (ahead >= 2) __builtin_amdgcn_s_waitcnt(W2);
       else if (ahead == 1) __builtin_amdgcn_s_waitcnt(W1);
       else __builtin_amdgcn_s_waitcnt(W0);
-      asm volatile("s_barrier" ::: "memory");
+      lds_barrier();
     };
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -466,6 +457,132 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     }
     __syncthreads();                     // every wave is done with the stage buffers
   }
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// Weight-streaming kernel for short groups (decode: a few rows per expert). Every weight byte is
+// used by one wave only, so there is nothing to share through LDS: each wave owns one task =
+// (group, 16 output columns) and streams that block's weight rows with nontemporal 16-byte loads
+// straight into 16x16x32 matrix-core fragments (lane l: row l % 16, 16 bytes of k-group l / 16,
+// i.e. 64 contiguous bytes per row per k-step), with the group's activation rows (tiny, L2-resident)
+// loaded the same way. No barriers; U k-steps of loads are in flight per wave.
+// MB = 16-row blocks per pass; groups with more rows take several passes over the weights.
+// gate_up: a task holds 16 gate rows and the 16 matching up rows (SwiGLU in the epilogue).
+// Requires K % 32 == 0.
+// ---------------------------------------------------------------------------------------------
+template <int MB, bool kSwiGLU>
+__global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
+  constexpr int NB = kSwiGLU ? 2 : 1;       // weight blocks of 16 rows per task
+  constexpr int U = 4;                      // k-steps per load batch (two batches in flight)
+  const int lane = threadIdx.x & 63;
+  const int K = kSwiGLU ? a.D : a.I;
+  const int NOUT = kSwiGLU ? a.I : a.D;
+  const int ncb = (NOUT + 15) / 16;
+  const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (task >= static_cast<int64_t>(a.G) * ncb) return;
+  const int g = static_cast<int>(task / ncb);
+  const int cb = static_cast<int>(task - static_cast<int64_t>(g) * ncb);
+  const int64_t row0 = a.offsets ? a.offsets[g] : 0;
+  const int64_t rows = a.offsets ? static_cast<int64_t>(a.offsets[g + 1]) - row0 : a.max_rows;
+  if (rows <= 0) return;
+  const uint16_t* X = static_cast<const uint16_t*>(a.x);
+  const uint16_t* Wg = static_cast<const uint16_t*>(a.w) +
+                       static_cast<int64_t>(g) * (kSwiGLU ? 2LL * a.I * a.D : static_cast<int64_t>(a.D) * a.I);
+  const int kg = (lane >> 4) * 8;           // this lane's k offset inside a 32-wide step
+  const int col = cb * 16 + (lane & 15);
+  const int ccol = min(col, NOUT - 1);
+  const uint16_t* wrow[NB];
+  wrow[0] = Wg + static_cast<int64_t>(ccol) * K + kg;
+  if (kSwiGLU) wrow[NB - 1] = Wg + static_cast<int64_t>(a.I + ccol) * K + kg;
+  const int ksteps = K / 32;
+
+  for (int64_t m0 = 0; m0 < rows; m0 += 16 * MB) {
+    const uint16_t* xrow[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int64_t lr = min<int64_t>(m0 + b * 16 + (lane & 15), rows - 1);
+      const int64_t p = row0 + lr;
+      const int64_t src = a.row_index ? a.row_index[p] : p;
+      xrow[b] = X + src * K + kg;
+    }
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // register double buffer: the loads of the next U k-steps are issued before the matrix-core
+    // steps of the current ones, so U k-steps of weight loads are always in flight
+    u32x4 fb[2][U][NB], fa[2][U][MB];
+    auto load = [&](int buf, int k0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          fb[buf][u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + (k0 + u) * 32));
+#pragma unroll
+        for (int b = 0; b < MB; ++b) fa[buf][u][b] = *reinterpret_cast<const u32x4*>(xrow[b] + (k0 + u) * 32);
+      }
+    };
+    auto math = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[b][j] = mfma16(fa[buf][u][b], fb[buf][u][j], acc[b][j]);
+    };
+    const int full = ksteps / U;                 // U-step batches
+    int ks = full * U;
+    if (full > 0) {
+      load(0, 0);
+      int q = 0;
+      for (; q + 2 <= full; q += 2) {            // two batches per trip keeps the buffers static
+        if (q + 1 < full) load(1, (q + 1) * U);
+        math(0);
+        if (q + 2 < full) load(0, (q + 2) * U);
+        math(1);
+      }
+      if (q < full) math(0);                     // odd batch count: the last one sits in buffer 0
+    }
+    for (; ks < ksteps; ++ks) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const u32x4 fa = *reinterpret_cast<const u32x4*>(xrow[b] + ks * 32);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[b][j] = mfma16(fa, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + ks * 32)), acc[b][j]);
+      }
+    }
+    if (col < NOUT) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t rr = m0 + b * 16 + 4 * (lane >> 4) + i;
+          if (rr < rows) {
+            if constexpr (kSwiGLU)
+              static_cast<uint16_t*>(a.out)[(row0 + rr) * NOUT + col] = f32_to_bf16(silu(acc[b][0][i]) * acc[b][1][i]);
+            else
+              static_cast<float*>(a.out)[(row0 + rr) * NOUT + col] = acc[b][0][i];
+          }
+        }
+    }
+  }
+}
+
+template <bool kSwiGLU>
+static void launch_wstream(const GemmArgs& a, hipStream_t st) {
+  const int NOUT = kSwiGLU ? a.I : a.D;
+  const int64_t tasks = static_cast<int64_t>(a.G) * ((NOUT + 15) / 16);
+  const unsigned grid = static_cast<unsigned>((tasks + 3) / 4);
+  const int64_t mean_rows = a.offsets ? a.max_rows / std::max(a.G, 1) : a.max_rows;
+  if (mean_rows <= 8)
+    gemm_wstream_kernel<1, kSwiGLU><<<grid, 256, 0, st>>>(a);
+  else if (mean_rows <= 20)
+    gemm_wstream_kernel<2, kSwiGLU><<<grid, 256, 0, st>>>(a);
+  else
+    gemm_wstream_kernel<4, kSwiGLU><<<grid, 256, 0, st>>>(a);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -605,7 +722,12 @@ static void launch_stream(const GemmArgs& a, hipStream_t st) {
   const int NOUT = kSwiGLU ? a.I : a.D;
   const int n_tiles = (NOUT + out_cols - 1) / out_cols;
   constexpr int lds = 4 * (BM + BNB) * kSK * 2;
-  const unsigned grid = persistent_grid(tile_upper_bound(a, BM, n_tiles), lds <= 76 * 1024 ? 2 : 1);
+  // Short-row tiles (few rows per group) are pure weight streams: one workgroup per tile lets the
+  // dispatcher start a new tile wherever one finishes instead of running fixed rounds with a
+  // half-empty last round. Tall tiles keep a persistent grid (one prologue per workgroup).
+  const int64_t ub = tile_upper_bound(a, BM, n_tiles);
+  const unsigned grid = BM <= 32 ? static_cast<unsigned>(std::max<int64_t>(ub, 1))
+                                 : persistent_grid(ub, lds <= 76 * 1024 ? 2 : 1);
   gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, WM * WN * 64, 0, st>>>(a);
 }
 
@@ -631,16 +753,18 @@ static bool streamable(const GemmArgs& a, bool gate_up) { return ((gate_up ? a.D
 
 void launch_gate_up(const GemmArgs& a, hipStream_t st) {
   if (!a.bf16) return launch_f32<true>(a, st);
-  if (small_rows(a)) return launch_bf16<1, 1, 4, 2, true>(a, st);
-  if (streamable(a, true)) return launch_stream<2, 4, 4, 2, true>(a, st);
-  return launch_bf16<2, 4, 4, 2, true>(a, st);
+  const bool stream = streamable(a, true);
+  if (small_rows(a) && a.D % 32 == 0) return launch_wstream<true>(a, st);
+  if (small_rows(a)) return stream ? launch_stream<1, 1, 4, 2, true>(a, st) : launch_bf16<1, 1, 4, 2, true>(a, st);
+  return stream ? launch_stream<2, 4, 4, 2, true>(a, st) : launch_bf16<2, 4, 4, 2, true>(a, st);
 }
 
 void launch_down(const GemmArgs& a, hipStream_t st) {
   if (!a.bf16) return launch_f32<false>(a, st);
-  if (small_rows(a)) return launch_bf16<1, 1, 4, 2, false>(a, st);
-  if (streamable(a, false)) return launch_stream<2, 4, 4, 2, false>(a, st);
-  return launch_bf16<2, 4, 4, 2, false>(a, st);
+  const bool stream = streamable(a, false);
+  if (small_rows(a) && a.I % 32 == 0) return launch_wstream<false>(a, st);
+  if (small_rows(a)) return stream ? launch_stream<1, 1, 4, 2, false>(a, st) : launch_bf16<1, 1, 4, 2, false>(a, st);
+  return stream ? launch_stream<2, 4, 4, 2, false>(a, st) : launch_bf16<2, 4, 4, 2, false>(a, st);
 }
 
 }  // namespace moe

@@ -13,11 +13,15 @@ struct RouteArgs {
   float* weights;
   int32_t* experts;
   float* shared_scale;        // non-null iff w_shared_gate
+  float* partial;             // scratch for a split contraction [slices][N][E], or null
   int64_t N;
   int D, E, k;
   int norm;
   bool bf16;
 };
+constexpr int kMaxRouteSlices = 16;
+int route_slices_for(int64_t N, int D, bool bf16);   // slices used when scratch is given
+int route_slices(const RouteArgs& a);
 void launch_route(const RouteArgs& a, hipStream_t st);
 
 // Permutation: assignments are processed in chunks of kPermChunk by one workgroup each.

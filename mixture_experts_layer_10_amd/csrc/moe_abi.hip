@@ -83,8 +83,15 @@ static int validate_config(const moe_config* c) {
   return MOE_OK;
 }
 
+// Scratch of a split router contraction: slices x N x E fp32 (0 when it runs in one pass).
+static size_t route_partial_bytes(const moe_config* c) {
+  const int slices = route_slices_for(c->n_tokens, static_cast<int>(c->hidden), c->dtype == MOE_BF16);
+  return slices > 1 ? static_cast<size_t>(slices) * static_cast<size_t>(c->n_tokens) * static_cast<size_t>(c->n_experts) * 4 : 0;
+}
+
 struct Layout {
-  size_t weights, experts, shared_scale, counts, offsets, block_counts, token_of, slot_pos, h, out, sh_h, sh_out, total;
+  size_t route_partial, weights, experts, shared_scale, counts, offsets, block_counts, token_of, slot_pos, h, out,
+      sh_h, sh_out, total;
 };
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -97,6 +104,7 @@ static Layout layout_of(const moe_config* c) {
   const size_t eb = elem_bytes(c->dtype);
   size_t at = 0;
   auto take = [&](size_t bytes) { const size_t p = at; at += align256(bytes); return p; };
+  L.route_partial = take(route_partial_bytes(c));
   L.block_counts = take(static_cast<size_t>(permute_chunks(static_cast<int64_t>(A))) * E * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
@@ -125,8 +133,10 @@ static size_t permute_ws_bytes(const moe_config* c) {
   } while (0)
 
 static int route_impl(const moe_config* c, const void* x, const void* w_router, const void* w_shared_gate,
-                      float* logits, float* weights, int32_t* experts, float* shared_scale, hipStream_t st) {
+                      float* logits, float* weights, int32_t* experts, float* shared_scale, float* partial,
+                      hipStream_t st) {
   RouteArgs a{};
+  a.partial = partial;
   a.x = x;
   a.w_router = w_router;
   a.w_shared_gate = w_shared_gate;
@@ -236,7 +246,7 @@ int moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
 }
 
 int moe_route(const moe_config* cfg, const void* x, const void* w_router, const void* w_shared_gate, float* logits,
-              float* weights, int32_t* experts, float* shared_scale, void* stream) {
+              float* weights, int32_t* experts, float* shared_scale, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate_config(cfg));
   if (cfg->n_tokens == 0) return ok();
   if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
@@ -245,7 +255,14 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
   if (!experts) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
   if ((w_shared_gate == nullptr) != (shared_scale == nullptr))
     return fail(MOE_ERR_INVALID_ARG, "w_shared_gate and shared_scale must be both set or both NULL");
-  MOE_TRY(route_impl(cfg, x, w_router, w_shared_gate, logits, weights, experts, shared_scale,
+  float* partial = nullptr;
+  if (ws) {
+    const size_t need = route_partial_bytes(cfg);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+    if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MOE_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+    if (need > 0) partial = static_cast<float*>(ws);
+  }
+  MOE_TRY(route_impl(cfg, x, w_router, w_shared_gate, logits, weights, experts, shared_scale, partial,
                      static_cast<hipStream_t>(stream)));
   return ok();
 }
@@ -339,7 +356,9 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t A = cfg->n_tokens * cfg->top_k;
 
-  MOE_TRY(route_impl(cfg, x, w_router, shared_scale ? w_shared_gate : nullptr, nullptr, weights, experts, shared_scale, st));
+  float* partial = L.route_partial == L.block_counts ? nullptr : reinterpret_cast<float*>(base + L.route_partial);
+  MOE_TRY(route_impl(cfg, x, w_router, shared_scale ? w_shared_gate : nullptr, nullptr, weights, experts, shared_scale,
+                     route_partial_bytes(cfg) ? partial : nullptr, st));
   MOE_TRY(permute_impl(cfg, experts, nullptr, counts, offsets, token_of, slot_pos, nullptr,
                        reinterpret_cast<int32_t*>(base + L.block_counts), st));
   launch_gate_up(gemm_args(cfg, cfg->n_experts, cfg->inter, A, x, token_of, offsets, gate_up, h), st);

@@ -5,10 +5,11 @@
 //
 // One workgroup (4 waves) owns a tile of tokens and all E <= 512 experts, so the softmax never
 // leaves the workgroup.
-//  bf16: 32 tokens per workgroup. x[32 x 64] and W_r[E x 64] k-slices are staged in LDS (16-byte
-//        chunks, XOR swizzle, register prefetch of the next slice); wave w computes expert blocks
-//        w, w+4, ... with 32x32x16 matrix-core steps (bf16 products are exact in fp32, fp32
-//        accumulation). The logits land in LDS unrounded, over the staging buffers.
+//  bf16: 32 tokens per workgroup. k-slices of x and W_r are staged in LDS (16-byte chunks, XOR
+//        swizzle); with D % 128 == 0 they stream straight from global memory into four LDS stages,
+//        otherwise through registers into two. Wave w computes expert blocks w, w+4, ... with
+//        32x32x16 matrix-core steps (bf16 products are exact in fp32, fp32 accumulation). The
+//        logits land in LDS unrounded, over the staging buffers.
 //  fp32: 64 tokens per workgroup, plain FMA dot products.
 // Selection: each wave walks its tokens; a lane holds experts lane, lane+64, ...; k rounds of a
 // wave-wide (p, index) arg-max with ties to the lower index.
@@ -109,7 +110,9 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
 constexpr int kRtTok = 32;
 constexpr int kRtBK = 64;
 
-__device__ __forceinline__ int rswz(int row, int chunk) { return row * kRtBK + ((chunk ^ (row & 7)) << 3); }
+// 128-byte rows; chunk c of row r at c ^ ((r >> 1) & 7) (16 rows at one chunk -> 16 distinct slots
+// of a 256-byte bank window)
+__device__ __forceinline__ int rswz(int row, int chunk) { return row * kRtBK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 template <int EP>
 __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) {
@@ -196,6 +199,160 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
 }
 
+
+// Pipelined variant for D % 128 == 0: 32-wide k-slices go straight from global memory into four LDS
+// stages (three in flight). Rows are 64 bytes; chunk c of row r sits at c ^ ((r >> 2) & 3) so the
+// 16 lanes the LDS serves together hit 16 distinct 16-byte slots. One DMA instruction = 16 rows.
+// Per stage each wave issues 2 EP instructions of W_r rows plus one of x rows (waves 2 and 3 repeat
+// waves 0 and 1's x rows into the same place, so every wave issues the same count).
+constexpr int kRsK = 32;
+
+template <int EP>
+__global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a) {
+  constexpr int EPAD = EP * 128;
+  constexpr int XS = kRtTok * kRsK, WS = EPAD * kRsK;    // elements per stage
+  constexpr int PER_STAGE = 2 * EP + 1;
+  constexpr int LOGIT_BYTES = kRtTok * EPAD * 4;
+  constexpr int SEL_BYTES = 4 * 512 * 8;
+  static_assert(LOGIT_BYTES + SEL_BYTES <= 4 * WS * 2, "logits and selection scratch alias the W stages");
+  __shared__ __attribute__((aligned(1024))) uint16_t sW[4 * WS];   // four W stages, then logits
+  __shared__ __attribute__((aligned(1024))) uint16_t sX[4 * XS];
+  uint16_t *sW0 = sW, *sW1 = sW + WS, *sW2 = sW + 2 * WS, *sW3 = sW + 3 * WS;
+  uint16_t *sX0 = sX, *sX1 = sX + XS, *sX2 = sX + 2 * XS, *sX3 = sX + 3 * XS;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRtTok;
+  const int D = a.D, E = a.E;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* w = static_cast<const uint16_t*>(a.w_router);
+  const int lrow = lane >> 2;
+  const int lch = (lane & 3) ^ ((lrow >> 2) & 3);
+  const int xg = wave & 1;                                  // x DMA group (rows 16 xg .. 16 xg + 15)
+  // k-slice of this workgroup: all of D, or D / gridDim.y when the contraction is split
+  const int kslice = D / static_cast<int>(gridDim.y);
+  const int64_t kbase = static_cast<int64_t>(blockIdx.y) * kslice;
+  const uint16_t* srcX = x + min<int64_t>(n0 + xg * 16 + lrow, a.N - 1) * D + kbase + lch * 8;
+  const uint16_t* srcW[2 * EP];
+#pragma unroll
+  for (int q = 0; q < 2 * EP; ++q) {
+    const int row = (wave + 4 * q) * 16 + lrow;            // W DMA group wave + 4 q
+    srcW[q] = w + static_cast<int64_t>(min(row, E - 1)) * D + kbase + lch * 8;
+  }
+  auto issue = [&](int ks, uint16_t* sx, uint16_t* sw) {
+    const int kb = ks * kRsK;
+    dma16(srcX + kb, sx + xg * 512);
+#pragma unroll
+    for (int q = 0; q < 2 * EP; ++q) dma16(srcW[q] + kb, sw + (wave + 4 * q) * 512);
+  };
+  const int ksteps = kslice / kRsK;
+  constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
+  auto wait_stage = [&](int st) {
+    const int ahead = min(2, ksteps - 1 - st);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(W2);
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(W1);
+    else __builtin_amdgcn_s_waitcnt(W0);
+    lds_barrier();
+  };
+  int ko[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) ko[kk] = (lane & 31) * kRsK + (((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 3);
+  f32x16 acc[EP];
+#pragma unroll
+  for (int b = 0; b < EP; ++b) acc[b] = f32x16{};
+  auto compute = [&](const uint16_t* sx, const uint16_t* sw) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4 fa = *reinterpret_cast<const u32x4*>(&sx[ko[kk]]);
+#pragma unroll
+      for (int b = 0; b < EP; ++b) {
+        if ((wave + 4 * b) * 32 < E) {
+          const u32x4 fb = *reinterpret_cast<const u32x4*>(&sw[(wave + 4 * b) * 32 * kRsK + ko[kk]]);
+          acc[b] = mfma32(fa, fb, acc[b]);
+        }
+      }
+    }
+  };
+  issue(0, sX0, sW0);
+  issue(1, sX1, sW1);
+  issue(2, sX2, sW2);
+  for (int ks = 0; ks < ksteps; ks += 4) {
+    wait_stage(ks);
+    if (ks + 3 < ksteps) issue(ks + 3, sX3, sW3);
+    compute(sX0, sW0);
+    wait_stage(ks + 1);
+    if (ks + 4 < ksteps) issue(ks + 4, sX0, sW0);
+    compute(sX1, sW1);
+    wait_stage(ks + 2);
+    if (ks + 5 < ksteps) issue(ks + 5, sX1, sW1);
+    compute(sX2, sW2);
+    wait_stage(ks + 3);
+    if (ks + 6 < ksteps) issue(ks + 6, sX2, sW2);
+    compute(sX3, sW3);
+  }
+  if (gridDim.y > 1) {
+    // split contraction: this slice's partial logits go to partial[blockIdx.y][n][e]
+    float* part = a.partial + static_cast<int64_t>(blockIdx.y) * a.N * E;
+#pragma unroll
+    for (int b = 0; b < EP; ++b) {
+      const int col = (wave + 4 * b) * 32 + (lane & 31);
+      if (col < E) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t n = n0 + acc_row(i, lane);
+          if (n < a.N) part[n * E + col] = acc[b][i];
+        }
+      }
+    }
+    return;
+  }
+  __syncthreads();                                          // all reads of the stages are done
+  float* s_logit = reinterpret_cast<float*>(sW);
+  float* s_selp = reinterpret_cast<float*>(reinterpret_cast<char*>(sW) + LOGIT_BYTES);
+  int* s_sele = reinterpret_cast<int*>(reinterpret_cast<char*>(sW) + LOGIT_BYTES + 4 * 512 * 4);
+#pragma unroll
+  for (int b = 0; b < EP; ++b) {
+    const int col = (wave + 4 * b) * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_logit[acc_row(i, lane) * EPAD + col] = acc[b][i];
+  }
+  __syncthreads();
+  const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
+  route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
+}
+
+
+// Second pass of a split contraction: logits[n][e] = sum over slices s = 0, 1, ... of
+// partial[s][n][e], added in slice order (deterministic), then the same selection as the fused
+// path. 8 tokens per workgroup; each thread loads all slices of an entry before adding them.
+constexpr int kFinTok = 8;
+
+template <int EP>
+__global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(RouteArgs a, int n_slices) {
+  constexpr int EPAD = EP * 128;
+  __shared__ float s_logit[kFinTok * EPAD];
+  __shared__ float s_selp[4 * 512];
+  __shared__ int s_sele[4 * 512];
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kFinTok;
+  const int E = a.E;
+  const int n_rows = static_cast<int>(min<int64_t>(kFinTok, a.N - n0));
+  const int64_t slice_stride = a.N * E;
+  for (int idx = threadIdx.x; idx < n_rows * E; idx += kRouteThreads) {
+    const int t = idx / E, e = idx - t * E;
+    const float* p = a.partial + (n0 + t) * E + e;
+    float v[kMaxRouteSlices];
+#pragma unroll
+    for (int sl = 0; sl < kMaxRouteSlices; ++sl) v[sl] = sl < n_slices ? p[sl * slice_stride] : 0.f;
+    float sum = v[0];
+#pragma unroll
+    for (int sl = 1; sl < kMaxRouteSlices; ++sl)
+      if (sl < n_slices) sum += v[sl];
+    s_logit[t * EPAD + e] = sum;
+  }
+  __syncthreads();
+  route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
+}
+
 // ---------------------------------------------------------------------------------------------
 // fp32: FMA dot products, 64 tokens per workgroup.
 // ---------------------------------------------------------------------------------------------
@@ -231,11 +388,34 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a) {
   route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
 }
 
+// Slices of the contraction: each workgroup walks D / slices columns in 32-wide stages with three
+// stages in flight, so with few token tiles the walk is latency-bound; splitting D over more
+// workgroups shortens it. Aim for about 1024 workgroups; each slice keeps >= 128 columns (four
+// stages). Needs the partial-logit scratch (slices * N * E fp32).
+int route_slices_for(int64_t N, int D, bool bf16) {
+  if (!bf16 || D % (4 * kRsK) != 0) return 1;
+  const int64_t tiles = (N + kRtTok - 1) / kRtTok;
+  int s = 1;
+  while (s * 2 * tiles <= 1024 && (D % (2 * s * 4 * kRsK)) == 0 && 2 * s <= kMaxRouteSlices) s *= 2;
+  return s;
+}
+
+int route_slices(const RouteArgs& a) { return a.partial ? route_slices_for(a.N, a.D, a.bf16) : 1; }
+
 template <int EP>
 static void launch_route_ep(const RouteArgs& a, hipStream_t st) {
   if (a.bf16) {
     const unsigned grid = static_cast<unsigned>((a.N + kRtTok - 1) / kRtTok);
-    route_bf16_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
+    const int slices = route_slices(a);
+    if (slices > 1) {
+      route_stream_kernel<EP><<<dim3(grid, slices), kRouteThreads, 0, st>>>(a);
+      const unsigned fgrid = static_cast<unsigned>((a.N + kFinTok - 1) / kFinTok);
+      route_finish_kernel<EP><<<fgrid, kRouteThreads, 0, st>>>(a, slices);
+    } else if (a.D % (4 * kRsK) == 0) {
+      route_stream_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
+    } else {
+      route_bf16_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
+    }
   } else {
     const unsigned grid = static_cast<unsigned>((a.N + 63) / 64);
     route_f32_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);

@@ -90,10 +90,10 @@ FAKE = 1 << 20    # never dereferenced: every call below fails validation on the
 def test_route_refuses_before_launch(lib):
     c = B.make_config(64, 128, 8, 2, 64)
     with pytest.raises(B.MoeError) as ei:
-        B.moe_route(c, None, FAKE, None, None, FAKE, FAKE, None, stream=0)
+        B.moe_route(c, None, FAKE, None, None, FAKE, FAKE, None, None, stream=0)
     assert ei.value.status == B.MOE_ERR_INVALID_ARG and "x" in str(ei.value)
     with pytest.raises(B.MoeError) as ei:          # gate without a place for its output
-        B.moe_route(c, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, stream=0)
+        B.moe_route(c, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, stream=0)
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
 
 

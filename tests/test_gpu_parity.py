@@ -53,7 +53,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_route(name, want_logits=True):
+def run_route(name, want_logits=True, with_ws=False):
     d, dev = data_of(name)
     s = d.shape
     cfg = B.config_for(s)
@@ -62,17 +62,19 @@ def run_route(name, want_logits=True):
     e = torch.empty((N, k), dtype=torch.int32, device="cuda")
     lg = torch.empty((N, E), dtype=torch.float32, device="cuda") if want_logits else None
     ss = torch.empty((N,), dtype=torch.float32, device="cuda") if "w_shared_gate" in dev else None
-    B.moe_route(cfg, dev["x"], dev["w_router"], dev.get("w_shared_gate"), lg, w, e, ss)
+    ws = B.alloc_workspace(cfg) if with_ws else None
+    B.moe_route(cfg, dev["x"], dev["w_router"], dev.get("w_shared_gate"), lg, w, e, ss, ws)
     torch.cuda.synchronize()
     return w, e, lg, ss
 
 
+@pytest.mark.parametrize("with_ws", [False, True], ids=["one_pass", "split_k"])
 @pytest.mark.parametrize("name", SMALL + FULL)
-def test_route(name):
-    say(f"[route] {name}")
+def test_route(name, with_ws):
+    say(f"[route] {name} ws={with_ws}")
     d, dev = data_of(name)
     s = d.shape
-    w, e, lg, ss = run_route(name)
+    w, e, lg, ss = run_route(name, with_ws=with_ws)
     logits, probs, w_ref, e_ref = O.route(d.values("x"), d.values("w_router"), s.top_k, s.norm_topk_prob)
     lerr = np.abs(to_np(lg) - logits).max()
     assert lerr <= 5e-5 * max(1.0, np.abs(logits).max()), f"logit error {lerr}"
