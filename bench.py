@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--out-dtype", default="f32")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy a 256 MiB buffer once (a kernel of known traffic for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -144,7 +147,8 @@ def main():
         achieved = alg["gate_up_bytes"] / gemm_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
-    roof["kernel"] = "gemm_bf16_kernel (grouped gate_up + SwiGLU)"
+    roof["kernel"] = "gemm_stream_kernel<2,4,4,2,true> (grouped gate_up + SwiGLU)" if prefill_like else \
+        "gemm_wstream_kernel<1,true> (grouped gate_up + SwiGLU, weight streaming)"
     roof["per_launch"] = dict(flops=alg["gate_up_flops"], bytes=alg["gate_up_bytes"], avg_ms=round(main_run["gate_up_ms"], 4))
     layer_s = main_run["ms_per_step"] / 1e3
     out = {
@@ -183,6 +187,13 @@ def main():
                          "experts_touched": dec["touched"],
                          "gate_up_ms": round(dec["gate_up_ms"], 4),
                          "gate_up_hbm_frac": round(dec["alg"]["gate_up_bytes"] / (dec["gate_up_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if args.copy_calibration:
+        src = torch.ones(64 * 2**20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "written": dst.numel() * 4}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(main_run["data"])
     print(json.dumps(out), flush=True)
