@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (; j + 8 <= k; j += 8) {
       f32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = o[static_cast<int64_t>(s_p[j + u]) * D4 + c];
+      for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&o[static_cast<int64_t>(s_p[j + u]) * D4 + c]);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float w = s_w[j + u];
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
     }
     for (; j < k; ++j) {
-      const f32x4 v = o[static_cast<int64_t>(s_p[j]) * D4 + c];
+      const f32x4 v = __builtin_nontemporal_load(&o[static_cast<int64_t>(s_p[j]) * D4 + c]);
       const float w = s_w[j];
       acc[0] = fmaf(w, v[0], acc[0]);
       acc[1] = fmaf(w, v[1], acc[1]);

@@ -61,6 +61,52 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave-wide reductions with DPP row operations (VALU, no LDS traffic): swap neighbours, swap pairs,
+// mirror within 8, mirror within 16 -> every lane holds its 16-lane row's result; the four row
+// results are then combined from lanes 15, 31, 47, 63 in a fixed order, so the result is the same
+// in every lane and deterministic.
+#define MOE_DPP(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), (ctrl), 0xF, 0xF, false)
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_f(float v, Op op) {
+  v = op(v, __int_as_float(MOE_DPP(__float_as_int(v), kDppXor1)));
+  v = op(v, __int_as_float(MOE_DPP(__float_as_int(v), kDppXor2)));
+  v = op(v, __int_as_float(MOE_DPP(__float_as_int(v), kDppHalfMirror)));
+  v = op(v, __int_as_float(MOE_DPP(__float_as_int(v), kDppMirror)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return op(op(r0, r1), op(r2, r3));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  return wave_reduce_f(v, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  return wave_reduce_f(v, [](float a, float b) { return a + b; });
+}
+
+// Wave-wide arg-max over (p, e) pairs: larger p wins, equal p goes to the lower e.
+__device__ __forceinline__ void argmax_step(float& p, int& e, float op, int oe) {
+  if (op > p || (op == p && oe < e)) { p = op; e = oe; }
+}
+__device__ __forceinline__ void wave_argmax_dpp(float& p, int& e) {
+  argmax_step(p, e, __int_as_float(MOE_DPP(__float_as_int(p), kDppXor1)), MOE_DPP(e, kDppXor1));
+  argmax_step(p, e, __int_as_float(MOE_DPP(__float_as_int(p), kDppXor2)), MOE_DPP(e, kDppXor2));
+  argmax_step(p, e, __int_as_float(MOE_DPP(__float_as_int(p), kDppHalfMirror)), MOE_DPP(e, kDppHalfMirror));
+  argmax_step(p, e, __int_as_float(MOE_DPP(__float_as_int(p), kDppMirror)), MOE_DPP(e, kDppMirror));
+  float bp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 15));
+  int be = __builtin_amdgcn_readlane(e, 15);
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    argmax_step(bp, be, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 16 * r + 15)),
+                __builtin_amdgcn_readlane(e, 16 * r + 15));
+  p = bp;
+  e = be;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's 16 bytes land

@@ -6,9 +6,9 @@
 //   down:    out[p, n] = h[p] . Dn[g, n]                               fp32 output
 //
 // Both operands are contiguous along K (weights stored [out, in]), so A and B tiles are loaded the
-// same way: 16-byte vectors, 8 lanes per 128-byte row segment. Tiles are staged in LDS with an XOR
-// swizzle of the 16-byte chunks (chunk c of row r sits at c ^ (r & 7)), so the matrix-core operand
-// reads (32 rows at one k offset) hit distinct banks. bf16 uses 32x32x16 matrix-core steps with
+// same way: 16-byte vectors. Tiles are staged in LDS with an XOR swizzle of the 16-byte chunks
+// (defined with each kernel), so the matrix-core operand reads (32 rows at one k offset) hit
+// distinct banks. bf16 uses 32x32x16 matrix-core steps with
 // fp32 accumulators; fp32 uses an LDS-tiled FMA kernel.
 //
 // Scheduling: persistent workgroups. Each builds, in LDS, the prefix sum over groups of

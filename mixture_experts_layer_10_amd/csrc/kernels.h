@@ -20,7 +20,7 @@ struct RouteArgs {
   bool bf16;
 };
 constexpr int kMaxRouteSlices = 16;
-int route_slices_for(int64_t N, int D, bool bf16);   // slices used when scratch is given
+int route_slices_for(int64_t N, int D, int E, bool bf16);   // slices used when scratch is given
 int route_slices(const RouteArgs& a);
 void launch_route(const RouteArgs& a, hipStream_t st);
 

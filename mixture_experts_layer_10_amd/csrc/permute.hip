@@ -34,7 +34,19 @@ __global__ __launch_bounds__(512) void perm_scan_kernel(PermuteArgs a, int n_chu
   const int E = a.E, e = threadIdx.x, lane = e & 63, wave = e >> 6;
   int total = 0;
   if (e < E) {
-    for (int b = 0; b < n_chunks; ++b) {
+    // eight chunk counts in flight at a time (each thread walks its own expert's column)
+    int b = 0;
+    for (; b + 8 <= n_chunks; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = a.block_counts[static_cast<int64_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a.block_counts[static_cast<int64_t>(b + u) * E + e] = total;
+        total += c[u];
+      }
+    }
+    for (; b < n_chunks; ++b) {
       int32_t* p = a.block_counts + static_cast<int64_t>(b) * E + e;
       const int c = *p;
       *p = total;
@@ -56,6 +68,7 @@ __global__ __launch_bounds__(512) void perm_scan_kernel(PermuteArgs a, int n_chu
   const int excl = before + inc - total;
   if (e < E) {
     a.offsets[e] = excl;
+#pragma unroll 8
     for (int b = 0; b < n_chunks; ++b) a.block_counts[static_cast<int64_t>(b) * E + e] += excl;
   }
   if (e == 0) a.offsets[E] = static_cast<int32_t>(a.A);
@@ -107,10 +120,82 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(PermuteArgs 
   }
 }
 
+// Small batches (decode): one workgroup of 8 waves does the histogram, the scan and the stable
+// scatter, instead of three launches whose fixed cost would dominate.
+constexpr int kPermSmallMax = 8192;
+
+__global__ __launch_bounds__(512) void perm_small_kernel(PermuteArgs a, int nbits) {
+  __shared__ int s_pos[512];         // counts, then each expert's next sorted position
+  __shared__ int s_wcnt[8][512];
+  __shared__ int s_wave[8];
+  const int E = a.E, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t A = a.A;
+  if (tid < E) s_pos[tid] = 0;
+  for (int w = 0; w < 8; ++w)
+    if (tid < E) s_wcnt[w][tid] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < A; i += 512) atomicAdd(&s_pos[a.experts[i]], 1);
+  __syncthreads();
+  const int total = tid < E ? s_pos[tid] : 0;
+  int inc = total;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  const int excl = before + inc - total;
+  if (tid < E) {
+    a.counts[tid] = total;
+    a.offsets[tid] = excl;
+    s_pos[tid] = excl;
+  }
+  if (tid == 0) a.offsets[E] = static_cast<int32_t>(A);
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = 0; base < A; base += 512) {
+    const int64_t i = base + tid;
+    const bool valid = i < A;
+    const int e = valid ? a.experts[i] : 0;
+    uint64_t m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t b = __ballot(set);
+      m &= set ? b : ~b;
+    }
+    const int rank = __popcll(m & below);
+    const int cnt = __popcll(m);
+    if (valid && rank == 0) s_wcnt[wave][e] = cnt;
+    __syncthreads();
+    int pos = 0;
+    if (valid) {
+      pos = s_pos[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wcnt[w][e];
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&s_pos[e], cnt);
+      s_wcnt[wave][e] = 0;
+    }
+    __syncthreads();
+    if (valid) {
+      a.token_of[pos] = static_cast<int32_t>(i / a.k);
+      a.slot_pos[i] = pos;
+    }
+  }
+}
+
 void launch_permute(const PermuteArgs& a, hipStream_t st) {
   const int n_chunks = static_cast<int>(permute_chunks(a.A));
   int nbits = 1;
   while ((1 << nbits) < a.E) ++nbits;
+  if (a.A <= kPermSmallMax) {
+    perm_small_kernel<<<1, 512, 0, st>>>(a, nbits);
+    return;
+  }
   if (n_chunks > 0) perm_count_kernel<<<n_chunks, kPermThreads, 0, st>>>(a);
   perm_scan_kernel<<<1, 512, 0, st>>>(a, n_chunks);
   if (n_chunks > 0) perm_scatter_kernel<<<n_chunks, kPermThreads, 0, st>>>(a, nbits);

@@ -39,7 +39,7 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
       v[j] = e < E ? s_logit[t * cols + e] : -INFINITY;
       m = fmaxf(m, v[j]);
     }
-    m = wave_max(m);
+    m = wave_max_dpp(m);
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -47,7 +47,7 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
       v[j] = e < E ? expf(v[j] - m) : 0.f;
       s += v[j];
     }
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int e = lane + kWave * j;
@@ -64,12 +64,7 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
       for (int j = 0; j < kPer; ++j) {          // strict '>' keeps the lowest index of a lane
         if (v[j] > bp) { bp = v[j]; be = lane + kWave * j; }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float op = __shfl_xor(bp, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        if (op > bp || (op == bp && oe < be)) { bp = op; be = oe; }
-      }
+      wave_argmax_dpp(bp, be);
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
         if (lane + kWave * j == be) v[j] = -1.f;
@@ -95,7 +90,7 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
         const float* ws = static_cast<const float*>(a.w_shared_gate);
         for (int d = lane; d < D; d += kWave) z = fmaf(xr[d], ws[d], z);
       }
-      z = wave_sum(z);
+      z = wave_sum_dpp(z);
       if (lane == 0) a.shared_scale[n] = 1.f / (1.f + expf(-z));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -324,30 +319,40 @@ __global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a
 
 // Second pass of a split contraction: logits[n][e] = sum over slices s = 0, 1, ... of
 // partial[s][n][e], added in slice order (deterministic), then the same selection as the fused
-// path. 8 tokens per workgroup; each thread loads all slices of an entry before adding them.
-constexpr int kFinTok = 8;
-
-template <int EP>
+// path. TOK tokens per workgroup; every thread issues all its loads (up to MS slices of each of
+// its entries) before adding anything, so a workgroup's loads are in flight together.
+template <int EP, int TOK, int MS>
 __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(RouteArgs a, int n_slices) {
   constexpr int EPAD = EP * 128;
-  __shared__ float s_logit[kFinTok * EPAD];
+  constexpr int PER = (TOK * EPAD + kRouteThreads - 1) / kRouteThreads;
+  __shared__ float s_logit[TOK * EPAD];
   __shared__ float s_selp[4 * 512];
   __shared__ int s_sele[4 * 512];
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kFinTok;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * TOK;
   const int E = a.E;
-  const int n_rows = static_cast<int>(min<int64_t>(kFinTok, a.N - n0));
+  const int n_rows = static_cast<int>(min<int64_t>(TOK, a.N - n0));
   const int64_t slice_stride = a.N * E;
-  for (int idx = threadIdx.x; idx < n_rows * E; idx += kRouteThreads) {
-    const int t = idx / E, e = idx - t * E;
+  float v[PER][MS];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int idx = threadIdx.x + q * kRouteThreads;
+    const int t = idx / EPAD, e = idx - t * EPAD;
+    const bool ok = t < n_rows && e < E;
     const float* p = a.partial + (n0 + t) * E + e;
-    float v[kMaxRouteSlices];
 #pragma unroll
-    for (int sl = 0; sl < kMaxRouteSlices; ++sl) v[sl] = sl < n_slices ? p[sl * slice_stride] : 0.f;
-    float sum = v[0];
+    for (int sl = 0; sl < MS; ++sl) v[q][sl] = (ok && sl < n_slices) ? p[sl * slice_stride] : 0.f;
+  }
 #pragma unroll
-    for (int sl = 1; sl < kMaxRouteSlices; ++sl)
-      if (sl < n_slices) sum += v[sl];
-    s_logit[t * EPAD + e] = sum;
+  for (int q = 0; q < PER; ++q) {
+    const int idx = threadIdx.x + q * kRouteThreads;
+    const int t = idx / EPAD, e = idx - t * EPAD;
+    if (t < TOK) {
+      float sum = v[q][0];
+#pragma unroll
+      for (int sl = 1; sl < MS; ++sl)
+        if (sl < n_slices) sum += v[q][sl];
+      s_logit[t * EPAD + e] = sum;
+    }
   }
   __syncthreads();
   route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
@@ -390,17 +395,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a) {
 
 // Slices of the contraction: each workgroup walks D / slices columns in 32-wide stages with three
 // stages in flight, so with few token tiles the walk is latency-bound; splitting D over more
-// workgroups shortens it. Aim for about 1024 workgroups; each slice keeps >= 128 columns (four
+// workgroups shortens it. Aim for about 2048 workgroups; each slice keeps >= 128 columns (four
 // stages). Needs the partial-logit scratch (slices * N * E fp32).
-int route_slices_for(int64_t N, int D, bool bf16) {
+int route_slices_for(int64_t N, int D, int E, bool bf16) {
   if (!bf16 || D % (4 * kRsK) != 0) return 1;
   const int64_t tiles = (N + kRtTok - 1) / kRtTok;
   int s = 1;
-  while (s * 2 * tiles <= 1024 && (D % (2 * s * 4 * kRsK)) == 0 && 2 * s <= kMaxRouteSlices) s *= 2;
+  const int64_t slice_bytes = N * E * 4;         // partial logits of one slice; keep all <= 32 MiB
+  while (s * 2 * tiles <= 2048 && (D % (2 * s * 4 * kRsK)) == 0 && 2 * s <= kMaxRouteSlices &&
+         2 * s * slice_bytes <= (32ll << 20))
+    s *= 2;
   return s;
 }
 
-int route_slices(const RouteArgs& a) { return a.partial ? route_slices_for(a.N, a.D, a.bf16) : 1; }
+int route_slices(const RouteArgs& a) { return a.partial ? route_slices_for(a.N, a.D, a.E, a.bf16) : 1; }
 
 template <int EP>
 static void launch_route_ep(const RouteArgs& a, hipStream_t st) {
@@ -409,8 +417,12 @@ static void launch_route_ep(const RouteArgs& a, hipStream_t st) {
     const int slices = route_slices(a);
     if (slices > 1) {
       route_stream_kernel<EP><<<dim3(grid, slices), kRouteThreads, 0, st>>>(a);
-      const unsigned fgrid = static_cast<unsigned>((a.N + kFinTok - 1) / kFinTok);
-      route_finish_kernel<EP><<<fgrid, kRouteThreads, 0, st>>>(a, slices);
+      if (slices <= 4 && a.N >= 1024) {       // long batches: few slices, many tokens per workgroup
+        constexpr int TOK = EP <= 2 ? 16 : 4;
+        route_finish_kernel<EP, TOK, 4><<<static_cast<unsigned>((a.N + TOK - 1) / TOK), kRouteThreads, 0, st>>>(a, slices);
+      } else {                                 // short batches: many slices, two tokens per workgroup
+        route_finish_kernel<EP, 2, kMaxRouteSlices><<<static_cast<unsigned>((a.N + 1) / 2), kRouteThreads, 0, st>>>(a, slices);
+      }
     } else if (a.D % (4 * kRsK) == 0) {
       route_stream_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
     } else {
