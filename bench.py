@@ -43,7 +43,11 @@ def algorithmic(shape, touched):
     return dict(flops=flops, bytes=bytes_, gate_up_flops=gate_up_flops, gate_up_bytes=gate_up_bytes)
 
 
-def run_workload(name, steps, warmup, out_dtype):
+def run_workload(name, steps, warmup, out_dtype, inner_events=True):
+    """Times `steps` whole-path steps. With inner_events the gate_up launch of every timed step is
+    bracketed by events on its stream (its duration comes from the timed region itself); without,
+    the timed steps carry no events (a recorded event idles the GPU for a few microseconds, which
+    matters at decode sizes) and the gate_up duration comes from a second run of `steps` steps."""
     import torch
     from mixture_experts_layer_10_amd import binding as B
     from mixture_experts_layer_10_amd import inputs as I
@@ -53,8 +57,14 @@ def run_workload(name, steps, warmup, out_dtype):
     t0 = time.perf_counter()
     data = I.make_inputs(shape)
     dev = B.to_device(data.store)
-    log(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s")
-    cfg = B.config_for(shape, out_dtype)
+    cfg = B.config_for(shape, out_dtype, packed=True)
+    if B.packable(cfg):                 # expert weights packed once, as at model load
+        dev = B.pack_device_weights(cfg, dev)
+        torch.cuda.synchronize()
+    else:
+        cfg = B.config_for(shape, out_dtype)
+    log(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s (weight layout "
+        f"{'packed' if cfg.weight_layout else 'rows'})")
     chain = Chain(cfg, dev)
     y_ref = B.forward(cfg, dev)
     for _ in range(warmup):
@@ -71,17 +81,21 @@ def run_workload(name, steps, warmup, out_dtype):
     t0 = time.perf_counter()
     all0.record()
     for i in range(steps):
-        chain.step(ev[i])
+        chain.step(ev[i] if inner_events else None)
     all1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = all0.elapsed_time(all1)
+    if not inner_events:
+        for i in range(steps):
+            chain.step(ev[i])
+        torch.cuda.synchronize()
     gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     ms_per_step = wall * 1e3 / steps
     alg = algorithmic(shape, touched)
     log(f"[bench] {name}: {ms_per_step:.3f} ms/step (gpu {gpu_ms / steps:.3f}), gate_up {gate_up_ms:.3f} ms, "
         f"touched {touched}/{shape.n_experts}")
-    return dict(shape=shape, data=data, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
+    return dict(shape=shape, data=data, cfg=cfg, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
                 gate_up_ms=gate_up_ms, touched=touched, counts=counts, alg=alg,
                 tokens_per_s=shape.n_tokens / (ms_per_step / 1e3))
 
@@ -147,8 +161,9 @@ def main():
         achieved = alg["gate_up_bytes"] / gemm_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
-    roof["kernel"] = "gemm_stream_kernel<2,4,4,2,true> (grouped gate_up + SwiGLU)" if prefill_like else \
-        "gemm_wstream_kernel<1,true> (grouped gate_up + SwiGLU, weight streaming)"
+    packed = "true" if main_run["cfg"].weight_layout else "false"
+    roof["kernel"] = f"gemm_stream_kernel<2,4,4,2,true,{packed}> (grouped gate_up + SwiGLU)" if prefill_like else \
+        f"gemm_wstream_kernel<1,true,{packed}> (grouped gate_up + SwiGLU, weight streaming)"
     roof["per_launch"] = dict(flops=alg["gate_up_flops"], bytes=alg["gate_up_bytes"], avg_ms=round(main_run["gate_up_ms"], 4))
     layer_s = main_run["ms_per_step"] / 1e3
     out = {
@@ -168,6 +183,7 @@ def main():
                    "n_experts": shape.n_experts, "top_k": shape.top_k, "inter": shape.inter,
                    "shared_inter": shape.shared_inter, "norm_topk_prob": shape.norm_topk_prob,
                    "zipf_s": shape.zipf_s, "out_dtype": args.out_dtype, "seed": shape.seed,
+                   "weight_layout": "packed" if main_run["cfg"].weight_layout else "rows",
                    "parallelism": "none (1 GPU)"},
         "layer": {"tflops": round(alg["flops"] / layer_s / 1e12, 2),
                   "mfma_frac": round(alg["flops"] / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -178,7 +194,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_decode and args.workload != "decode":
-        dec = run_workload("decode", max(args.steps, 50), args.warmup, args.out_dtype)
+        dec = run_workload("decode", max(args.steps, 50), args.warmup, args.out_dtype, inner_events=False)
         ds = dec["ms_per_step"] / 1e3
         out["decode"] = {"workload": "decode", "tokens_per_s": round(dec["tokens_per_s"], 1),
                          "ms_per_step": round(dec["ms_per_step"], 4),

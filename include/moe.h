@@ -28,6 +28,13 @@
  *   shared_gate_up [2I_s, D], shared_down [D, I_s], w_shared_gate [D]
  * dtype (moe_config.dtype) applies to x and every weight; routing outputs are always fp32
  * weights and int32 expert ids; intermediate expert outputs are fp32.
+ *
+ * Packed expert weights (moe_config.weight_layout = MOE_LAYOUT_PACKED): gate_up, down,
+ * shared_gate_up and shared_down may instead hold the output of moe_pack_weights, a one-time
+ * rearrangement (at model load) of each [G, R, K] matrix into 16 x 32 blocks of 1 KB stored in
+ * the order the matrix cores read them, so that every weight load is one contiguous kilobyte.
+ * The values are the same; results are bitwise identical to the row layout. bf16 only, with
+ * hidden, inter and shared_inter multiples of 128.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -49,6 +56,8 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layout;
+
 /* Shape and options of one MoE layer. Refuses, never defaults: every field must be set
  * (the config-ingestion lesson of "27. Mixture of experts", section "Qwen3-MoE", Note). */
 typedef struct {
@@ -61,7 +70,7 @@ typedef struct {
   int32_t norm_topk_prob; /* 1: divide kept weights by their sum; 0: keep the probabilities   */
   int32_t dtype;          /* moe_dtype of x and all weights                                   */
   int32_t out_dtype;      /* moe_dtype of y                                                   */
-  int32_t reserved;       /* must be 0                                                        */
+  int32_t weight_layout;  /* moe_weight_layout of the expert weights (router weights: rows)  */
 } moe_config;
 
 /* Human-readable name of a status code. Never NULL. */
@@ -130,6 +139,15 @@ int moe_expert_down(const moe_config* cfg, int64_t n_groups, int64_t inter, int6
 int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows,
                    const void* x, const int32_t* row_index, const int32_t* offsets,
                    const void* gate_up, const void* down, void* h, float* out, void* stream);
+
+/* Packs a row-major bf16 matrix stack src [G, R, K] (R % 16 == 0, K % 32 == 0) into dst, the
+ * layout of MOE_LAYOUT_PACKED: block (g, rb, kb) of rows rb*16 .. +15 and columns kb*32 .. +31 is
+ * 1 KB at byte offset ((g * R/16 + rb) * K/32 + kb) * 1024, holding at 16-byte slot l the eight
+ * values of row rb*16 + l % 16, columns kb*32 + 8 (l / 16) .. + 7. dst has src's size and must
+ * not overlap it. Use it on gate_up (R = 2I, K = D), down (R = D, K = I) and the shared pair.
+ * cfg gives dtype (must be bf16); its other fields are not used. */
+int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src,
+                     void* dst, void* stream);
 
 /* Weighted unpermute ("27. Mixture of experts", section "Dispatch", grouped step 4, and the
  * shared-expert equation): y[n] = sum_{j<k} w[n,j] * out_perm[slot_pos[n*k+j]]

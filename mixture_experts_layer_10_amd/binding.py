@@ -19,10 +19,12 @@ LIB_PATH = os.path.join(PKG, "_lib", "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED = 0, 1
 
 # Every symbol include/moe.h declares.
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
-            "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward"]
+            "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_pack_weights", "moe_combine",
+            "moe_forward"]
 
 
 class MoeError(RuntimeError):
@@ -35,7 +37,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("n_experts", ctypes.c_int64),
                 ("top_k", ctypes.c_int64), ("inter", ctypes.c_int64), ("shared_inter", ctypes.c_int64),
                 ("norm_topk_prob", ctypes.c_int32), ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32)]
 
     def copy(self, **kw):
         c = MoeConfig()
@@ -45,16 +47,22 @@ class MoeConfig(ctypes.Structure):
 
 
 def make_config(n_tokens, hidden, n_experts, top_k, inter, shared_inter=0, norm_topk_prob=True,
-                dtype="bf16", out_dtype=None) -> MoeConfig:
+                dtype="bf16", out_dtype=None, packed=False) -> MoeConfig:
     dt = {"bf16": MOE_BF16, "f32": MOE_F32}
     return MoeConfig(n_tokens, hidden, n_experts, top_k, inter, shared_inter, int(bool(norm_topk_prob)),
-                     dt[dtype], dt[out_dtype or dtype], 0)
+                     dt[dtype], dt[out_dtype or dtype], MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_ROWS)
 
 
-def config_for(shape, out_dtype=None) -> MoeConfig:
+def config_for(shape, out_dtype=None, packed=False) -> MoeConfig:
     """MoeConfig for an inputs.MoeShape."""
     return make_config(shape.n_tokens, shape.hidden, shape.n_experts, shape.top_k, shape.inter,
-                       shape.shared_inter, shape.norm_topk_prob, shape.dtype, out_dtype)
+                       shape.shared_inter, shape.norm_topk_prob, shape.dtype, out_dtype, packed)
+
+
+def packable(cfg: MoeConfig) -> bool:
+    """Whether the packed weight layout applies (bf16, widths multiples of 128)."""
+    return (cfg.dtype == MOE_BF16 and cfg.hidden % 128 == 0 and cfg.inter % 128 == 0
+            and cfg.shared_inter % 128 == 0)
 
 
 _lib = None
@@ -79,6 +87,7 @@ def load(path: str = LIB_PATH):
         "moe_expert_gate_up": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
         "moe_expert_down": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
         "moe_expert_ffn": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_pack_weights": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P]),
         "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
         "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     }
@@ -165,6 +174,11 @@ def moe_expert_ffn(cfg, n_groups, inter, max_rows, x, row_index, offsets, gate_u
                                                    _ptr(h), _ptr(out), _stream(stream)))
 
 
+def moe_pack_weights(cfg, n_groups, rows, cols, src, dst, stream=None):
+    _check("moe_pack_weights", load().moe_pack_weights(ctypes.byref(cfg), n_groups, rows, cols, _ptr(src), _ptr(dst),
+                                                       _stream(stream)))
+
+
 def moe_combine(cfg, out_perm, weights, slot_pos, shared_out, shared_scale, y, stream=None):
     _check("moe_combine", load().moe_combine(ctypes.byref(cfg), _ptr(out_perm), _ptr(weights), _ptr(slot_pos),
                                              _ptr(shared_out), _ptr(shared_scale), _ptr(y), _stream(stream)))
@@ -199,6 +213,23 @@ def to_device(store: dict, device="cuda"):
 def torch_dtype(code):
     import torch
     return torch.bfloat16 if code == MOE_BF16 else torch.float32
+
+
+def pack_device_weights(cfg: MoeConfig, dev: dict):
+    """A copy of ``dev`` whose expert weights (gate_up, down and the shared pair) are in the packed
+    layout, made by moe_pack_weights (a one-time step, like loading the model)."""
+    import torch
+    D, E, I, Is = cfg.hidden, cfg.n_experts, cfg.inter, cfg.shared_inter
+    out = dict(dev)
+    shapes = {"gate_up": (E, 2 * I, D), "down": (E, D, I)}
+    if Is:
+        shapes.update(shared_gate_up=(1, 2 * Is, D), shared_down=(1, D, Is))
+    for name, (g, r, c) in shapes.items():
+        src = dev[name]
+        dst = torch.empty_like(src)
+        moe_pack_weights(cfg, g, r, c, src, dst)
+        out[name] = dst
+    return out
 
 
 def alloc_workspace(cfg: MoeConfig, device="cuda"):

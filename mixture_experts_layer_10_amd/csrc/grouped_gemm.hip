@@ -273,7 +273,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------------------------
 constexpr int kSK = 32;
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32, NT = WM * WN * 64, NW = WM * WN;
   // DMA instructions per wave per stage; with fewer 16-row A groups than waves (BM = 32), waves
@@ -315,12 +315,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 
   // LDS read offsets: fragment rows are 32-aligned + (lane & 31), so row bits 2..3 are lane bits
   // 2..3 and the chunk of k-step kk is (2 kk + (lane >> 5)) ^ ((lane >> 2) & 3).
+  // Packed B: each 16-row group's 1 KB holds the fragment in lane order (row r16, 8-wide k chunk q
+  // at (r16 + 16 q) * 8), so 16 lanes read 256 contiguous bytes.
   int koA[2], koB[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int pc = ((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 3;
+    const int rb0 = (kSwiGLU ? wn * (TN / 2) : wn * TN) * 32;
     koA[kk] = (wm * TM * 32 + (lane & 31)) * kSK + pc;
-    koB[kk] = ((kSwiGLU ? wn * (TN / 2) : wn * TN) * 32 + (lane & 31)) * kSK + pc;
+    koB[kk] = kPacked ? rb0 * kSK + ((lane >> 4) & 1) * 512 + (lane & 15) * 8 + (2 * kk + (lane >> 5)) * 128
+                      : (rb0 + (lane & 31)) * kSK + pc;
   }
   constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
 
@@ -352,23 +356,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     const uint16_t* srcB[B_INS];
 #pragma unroll
     for (int j = 0; j < B_INS; ++j) {
-      const int rr = (wave * B_INS + j) * 16 + lrow;
-      int wrow;
-      if (kSwiGLU) {
-        const int half = BNB / 2;
-        const int ci = min(c0 + (rr % half), NOUT - 1);
-        wrow = rr < half ? ci : a.I + ci;
+      const int grp = wave * B_INS + j;
+      if constexpr (kPacked) {
+        // the group's 16 weight rows are one row block (c0, I and NOUT are multiples of 16): one
+        // DMA instruction moves its 1 KB fragment of k-block ks contiguously
+        int rb;
+        if (kSwiGLU) {
+          const int half = BNB / 32;                          // 16-row groups per half
+          const int cb = min(c0 / 16 + grp % half, NOUT / 16 - 1);
+          rb = grp < half ? cb : a.I / 16 + cb;
+        } else {
+          rb = min(c0 / 16 + grp, NOUT / 16 - 1);
+        }
+        srcB[j] = Wg + static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8;
       } else {
-        wrow = min(c0 + rr, NOUT - 1);
+        const int rr = grp * 16 + lrow;
+        int wrow;
+        if (kSwiGLU) {
+          const int half = BNB / 2;
+          const int ci = min(c0 + (rr % half), NOUT - 1);
+          wrow = rr < half ? ci : a.I + ci;
+        } else {
+          wrow = min(c0 + rr, NOUT - 1);
+        }
+        srcB[j] = Wg + static_cast<int64_t>(wrow) * K + lch * 8;
       }
-      srcB[j] = Wg + static_cast<int64_t>(wrow) * K + lch * 8;
     }
     auto issue = [&](int ks, uint16_t* sa, uint16_t* sb) {
       const int kb = ks * kSK;
 #pragma unroll
       for (int j = 0; j < A_INS; ++j) dma16(srcA[j] + kb, sa + ((wave * A_INS + j) % A_GROUPS) * 512);
 #pragma unroll
-      for (int j = 0; j < B_INS; ++j) dma16(srcB[j] + kb, sb + (wave * B_INS + j) * 512);
+      for (int j = 0; j < B_INS; ++j) dma16(srcB[j] + (kPacked ? ks * 512 : kb), sb + (wave * B_INS + j) * 512);
     };
     // wait for stage s (later stages may stay in flight), then sync the workgroup: after this, stage
     // s is visible to every wave and every wave has finished reading stage s - 1's buffer
@@ -471,7 +490,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 // gate_up: a task holds 16 gate rows and the 16 matching up rows (SwiGLU in the epilogue).
 // Requires K % 32 == 0.
 // ---------------------------------------------------------------------------------------------
-template <int MB, bool kSwiGLU>
+template <int MB, bool kSwiGLU, bool kPacked>
 __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   constexpr int NB = kSwiGLU ? 2 : 1;       // weight blocks of 16 rows per task
   constexpr int U = 4;                      // k-steps per load batch (two batches in flight)
@@ -493,8 +512,15 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   const int col = cb * 16 + (lane & 15);
   const int ccol = min(col, NOUT - 1);
   const uint16_t* wrow[NB];
-  wrow[0] = Wg + static_cast<int64_t>(ccol) * K + kg;
-  if (kSwiGLU) wrow[NB - 1] = Wg + static_cast<int64_t>(a.I + ccol) * K + kg;
+  // packed: the task's 16 rows are row block cb; k-step ks of it is 1 KB at + ks * 512 in lane order
+  constexpr int WSTEP = kPacked ? 512 : 32;
+  if constexpr (kPacked) {
+    wrow[0] = Wg + static_cast<int64_t>(cb) * (K / 32) * 512 + lane * 8;
+    if (kSwiGLU) wrow[NB - 1] = Wg + static_cast<int64_t>(a.I / 16 + cb) * (K / 32) * 512 + lane * 8;
+  } else {
+    wrow[0] = Wg + static_cast<int64_t>(ccol) * K + kg;
+    if (kSwiGLU) wrow[NB - 1] = Wg + static_cast<int64_t>(a.I + ccol) * K + kg;
+  }
   const int ksteps = K / 32;
 
   for (int64_t m0 = 0; m0 < rows; m0 += 16 * MB) {
@@ -519,7 +545,7 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
       for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          fb[buf][u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + (k0 + u) * 32));
+          fb[buf][u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + (k0 + u) * WSTEP));
 #pragma unroll
         for (int b = 0; b < MB; ++b) fa[buf][u][b] = *reinterpret_cast<const u32x4*>(xrow[b] + (k0 + u) * 32);
       }
@@ -551,7 +577,7 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
         const u32x4 fa = *reinterpret_cast<const u32x4*>(xrow[b] + ks * 32);
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          acc[b][j] = mfma16(fa, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + ks * 32)), acc[b][j]);
+          acc[b][j] = mfma16(fa, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + ks * WSTEP)), acc[b][j]);
       }
     }
     if (col < NOUT) {
@@ -571,18 +597,18 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   }
 }
 
-template <bool kSwiGLU>
+template <bool kSwiGLU, bool kPacked>
 static void launch_wstream(const GemmArgs& a, hipStream_t st) {
   const int NOUT = kSwiGLU ? a.I : a.D;
   const int64_t tasks = static_cast<int64_t>(a.G) * ((NOUT + 15) / 16);
   const unsigned grid = static_cast<unsigned>((tasks + 3) / 4);
   const int64_t mean_rows = a.offsets ? a.max_rows / std::max(a.G, 1) : a.max_rows;
   if (mean_rows <= 8)
-    gemm_wstream_kernel<1, kSwiGLU><<<grid, 256, 0, st>>>(a);
+    gemm_wstream_kernel<1, kSwiGLU, kPacked><<<grid, 256, 0, st>>>(a);
   else if (mean_rows <= 20)
-    gemm_wstream_kernel<2, kSwiGLU><<<grid, 256, 0, st>>>(a);
+    gemm_wstream_kernel<2, kSwiGLU, kPacked><<<grid, 256, 0, st>>>(a);
   else
-    gemm_wstream_kernel<4, kSwiGLU><<<grid, 256, 0, st>>>(a);
+    gemm_wstream_kernel<4, kSwiGLU, kPacked><<<grid, 256, 0, st>>>(a);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -715,7 +741,7 @@ static void launch_bf16(const GemmArgs& a, hipStream_t st) {
   gemm_bf16_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, C::NT, 0, st>>>(a);
 }
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked>
 static void launch_stream(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32;
   constexpr int out_cols = kSwiGLU ? BNB / 2 : BNB;
@@ -728,7 +754,7 @@ static void launch_stream(const GemmArgs& a, hipStream_t st) {
   const int64_t ub = tile_upper_bound(a, BM, n_tiles);
   const unsigned grid = BM <= 32 ? static_cast<unsigned>(std::max<int64_t>(ub, 1))
                                  : persistent_grid(ub, lds <= 76 * 1024 ? 2 : 1);
-  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, WM * WN * 64, 0, st>>>(a);
+  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked><<<grid, WM * WN * 64, 0, st>>>(a);
 }
 
 template <bool kSwiGLU>
@@ -751,20 +777,46 @@ static bool small_rows(const GemmArgs& a) {
 // register-staged kernel covers the other K.
 static bool streamable(const GemmArgs& a, bool gate_up) { return ((gate_up ? a.D : a.I) % 128) == 0; }
 
-void launch_gate_up(const GemmArgs& a, hipStream_t st) {
-  if (!a.bf16) return launch_f32<true>(a, st);
-  const bool stream = streamable(a, true);
-  if (small_rows(a) && a.D % 32 == 0) return launch_wstream<true>(a, st);
-  if (small_rows(a)) return stream ? launch_stream<1, 1, 4, 2, true>(a, st) : launch_bf16<1, 1, 4, 2, true>(a, st);
-  return stream ? launch_stream<2, 4, 4, 2, true>(a, st) : launch_bf16<2, 4, 4, 2, true>(a, st);
+// The packed layout is accepted only with bf16 and K % 128 == 0 (checked at the boundary), so it
+// always has a streaming kernel.
+template <bool kSwiGLU>
+static void launch_gemm(const GemmArgs& a, hipStream_t st) {
+  if (!a.bf16) return launch_f32<kSwiGLU>(a, st);
+  const int K = kSwiGLU ? a.D : a.I;
+  const bool stream = streamable(a, kSwiGLU);
+  if (a.packed) {
+    if (small_rows(a)) return launch_wstream<kSwiGLU, true>(a, st);
+    return launch_stream<2, 4, 4, 2, kSwiGLU, true>(a, st);
+  }
+  if (small_rows(a) && K % 32 == 0) return launch_wstream<kSwiGLU, false>(a, st);
+  if (small_rows(a)) return stream ? launch_stream<1, 1, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<1, 1, 4, 2, kSwiGLU>(a, st);
+  return stream ? launch_stream<2, 4, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<2, 4, 4, 2, kSwiGLU>(a, st);
 }
 
-void launch_down(const GemmArgs& a, hipStream_t st) {
-  if (!a.bf16) return launch_f32<false>(a, st);
-  const bool stream = streamable(a, false);
-  if (small_rows(a) && a.I % 32 == 0) return launch_wstream<false>(a, st);
-  if (small_rows(a)) return stream ? launch_stream<1, 1, 4, 2, false>(a, st) : launch_bf16<1, 1, 4, 2, false>(a, st);
-  return stream ? launch_stream<2, 4, 4, 2, false>(a, st) : launch_bf16<2, 4, 4, 2, false>(a, st);
+void launch_gate_up(const GemmArgs& a, hipStream_t st) { launch_gemm<true>(a, st); }
+void launch_down(const GemmArgs& a, hipStream_t st) { launch_gemm<false>(a, st); }
+
+// ---------------------------------------------------------------------------------------------
+// Packing: one wave per 16 x 32 fragment; lane l copies the 16 bytes of row l % 16, k-chunk l / 16.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n_frags,
+                                                   int R, int K) {
+  const int64_t f = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (f >= n_frags) return;
+  const int lane = threadIdx.x & 63;
+  const int KB = K / 32, RB = R / 16;
+  const int64_t kb = f % KB;
+  const int64_t grb = f / KB;                          // g * RB + rb
+  const int64_t g = grb / RB, rb = grb - g * RB;
+  const int64_t row = g * R + rb * 16 + (lane & 15);
+  dst[f * 64 + lane] = src[(row * K + kb * 32 + (lane >> 4) * 8) / 8];
+}
+
+void launch_pack(const uint16_t* src, uint16_t* dst, int64_t G, int R, int K, hipStream_t st) {
+  const int64_t n_frags = G * (R / 16) * (K / 32);
+  if (n_frags <= 0) return;
+  pack_kernel<<<static_cast<unsigned>((n_frags + 3) / 4), 256, 0, st>>>(reinterpret_cast<const u32x4*>(src),
+                                                                        reinterpret_cast<u32x4*>(dst), n_frags, R, K);
 }
 
 }  // namespace moe

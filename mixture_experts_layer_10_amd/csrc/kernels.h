@@ -47,15 +47,21 @@ struct GemmArgs {
   const void* x;          // gate_up: activations; down: h
   const int32_t* row_index;
   const int32_t* offsets; // [G+1] or null (one group of max_rows rows)
-  const void* w;          // gate_up [G, 2I, D] or down [G, D, I]
+  const void* w;          // gate_up [G, 2I, D] or down [G, D, I] (rows), or their packed form
   void* out;              // gate_up: h [rows, I]; down: out [rows, D] fp32
   int64_t max_rows;
   int G;
   int D, I;
   bool bf16;
+  bool packed;            // w in the packed layout (bf16, K % 128 == 0, rows % 16 == 0)
 };
 void launch_gate_up(const GemmArgs& a, hipStream_t st);
 void launch_down(const GemmArgs& a, hipStream_t st);
+
+// Packed weight layout: a [G, R, K] bf16 matrix (R % 16 == 0, K % 32 == 0) stored as 16 x 32
+// fragments, fragment (g, rb, kb) at element ((g * R/16 + rb) * K/32 + kb) * 512, each 1 KB in
+// matrix-core lane order (lane l: row rb*16 + l % 16, k = kb*32 + 8 (l / 16) .. + 7).
+void launch_pack(const uint16_t* src, uint16_t* dst, int64_t G, int R, int K, hipStream_t st);
 
 struct CombineArgs {
   const float* out_perm;

@@ -66,7 +66,8 @@ static int validate_config(const moe_config* c) {
   if (c->shared_inter < 0) return fail(MOE_ERR_INVALID_ARG, "shared_inter = %lld < 0", (long long)c->shared_inter);
   if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1)
     return fail(MOE_ERR_INVALID_ARG, "norm_topk_prob = %d (must be 0 or 1)", c->norm_topk_prob);
-  if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved = %d (must be 0)", c->reserved);
+  if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d (must be 0 or 1)", c->weight_layout);
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
   if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "out_dtype %d not supported", c->out_dtype);
@@ -75,6 +76,11 @@ static int validate_config(const moe_config* c) {
   if (c->inter % align) return fail(MOE_ERR_UNSUPPORTED, "inter = %lld is not a multiple of %lld", (long long)c->inter, (long long)align);
   if (c->shared_inter % align)
     return fail(MOE_ERR_UNSUPPORTED, "shared_inter = %lld is not a multiple of %lld", (long long)c->shared_inter, (long long)align);
+  if (c->weight_layout == MOE_LAYOUT_PACKED) {
+    if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights need dtype bf16");
+    if (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128)
+      return fail(MOE_ERR_UNSUPPORTED, "packed weights need hidden, inter and shared_inter multiples of 128");
+  }
   if (c->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts = %lld > %lld", (long long)c->n_experts, (long long)kMaxExperts);
   if (c->hidden > (1 << 20) || c->inter > (1 << 20) || c->shared_inter > (1 << 20))
     return fail(MOE_ERR_UNSUPPORTED, "hidden/inter above 2^20");
@@ -181,6 +187,8 @@ static int ffn_checks(const moe_config* c, int64_t n_groups, int64_t inter, int6
   const int64_t align = c->dtype == MOE_BF16 ? 8 : 4;
   if (inter % align) return fail(MOE_ERR_UNSUPPORTED, "inter = %lld is not a multiple of %lld", (long long)inter, (long long)align);
   if (inter > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "inter above 2^20");
+  if (c->weight_layout == MOE_LAYOUT_PACKED && inter % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights need inter = %lld to be a multiple of 128", (long long)inter);
   if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows = %lld < 0", (long long)max_rows);
   if (max_rows > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "max_rows above int32");
   if (!offsets && n_groups != 1) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL with n_groups = %lld", (long long)n_groups);
@@ -200,6 +208,7 @@ static GemmArgs gemm_args(const moe_config* c, int64_t n_groups, int64_t inter, 
   a.D = static_cast<int>(c->hidden);
   a.I = static_cast<int>(inter);
   a.bf16 = c->dtype == MOE_BF16;
+  a.packed = c->weight_layout == MOE_LAYOUT_PACKED;
   return a;
 }
 
@@ -317,6 +326,29 @@ int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64
   MOE_TRY(check_launch("moe_expert_ffn (gate_up)"));
   launch_down(gemm_args(cfg, n_groups, inter, max_rows, h, nullptr, offsets, down, out), st);
   MOE_TRY(check_launch("moe_expert_ffn (down)"));
+  return ok();
+}
+
+int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src, void* dst,
+                     void* stream) {
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packing needs dtype bf16");
+  if (n_groups < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
+  if (rows % 16 || cols % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "packing needs rows %% 16 == 0 and cols %% 32 == 0 (got %lld x %lld)",
+                (long long)rows, (long long)cols);
+  if (rows > (1 << 24) || cols > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "rows/cols above 2^24");
+  const int64_t n = n_groups * rows * cols;
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src or dst is NULL");
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + 2 * n && d0 < s0 + 2 * n) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15)
+    return fail(MOE_ERR_UNSUPPORTED, "src and dst must be 16-byte aligned");
+  launch_pack(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), n_groups, static_cast<int>(rows),
+              static_cast<int>(cols), static_cast<hipStream_t>(stream));
+  MOE_TRY(check_launch("moe_pack_weights"));
   return ok();
 }
 

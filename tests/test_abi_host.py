@@ -28,7 +28,7 @@ def header_functions():
 
 def test_header_symbols_all_exported(lib):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -63,7 +63,8 @@ def test_workspace_bytes_host_only(lib):
     ("inter", 0, B.MOE_ERR_INVALID_ARG),
     ("shared_inter", -8, B.MOE_ERR_INVALID_ARG),
     ("norm_topk_prob", 2, B.MOE_ERR_INVALID_ARG),
-    ("reserved", 1, B.MOE_ERR_INVALID_ARG),
+    ("weight_layout", 2, B.MOE_ERR_INVALID_ARG),
+    ("weight_layout", 1, B.MOE_ERR_UNSUPPORTED),      # packed needs widths that are multiples of 128
     ("dtype", 7, B.MOE_ERR_UNSUPPORTED),
     ("out_dtype", 3, B.MOE_ERR_UNSUPPORTED),
     ("hidden", 36, B.MOE_ERR_UNSUPPORTED),             # bf16 rows must be 16-byte vectors
@@ -76,6 +77,41 @@ def test_config_validation(lib, field, value, status):
         B.moe_workspace_bytes(c)
     assert ei.value.status == status
     assert field.split("_")[0] in B.last_error() or B.last_error()
+
+
+def test_packed_layout_rules(lib):
+    ok = B.make_config(64, 256, 8, 2, 128, shared_inter=384, packed=True)
+    assert B.moe_workspace_bytes(ok) > 0 and B.packable(ok)
+    for bad in (B.make_config(64, 256, 8, 2, 128, dtype="f32", packed=True),
+                B.make_config(64, 256, 8, 2, 128, shared_inter=64, packed=True),
+                B.make_config(64, 200, 8, 2, 128, packed=True)):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_workspace_bytes(bad)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "packed" in str(ei.value)
+    # the standalone expert entry points check the width they are given
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_expert_ffn(ok, 8, 96, 128, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def test_pack_refuses_before_launch(lib):
+    c = B.make_config(64, 256, 8, 2, 128)
+    cases = [
+        (dict(cfg=B.make_config(64, 256, 8, 2, 128, dtype="f32")), B.MOE_ERR_UNSUPPORTED),
+        (dict(rows=24), B.MOE_ERR_UNSUPPORTED),
+        (dict(cols=48), B.MOE_ERR_UNSUPPORTED),
+        (dict(rows=-16), B.MOE_ERR_INVALID_ARG),
+        (dict(src=None), B.MOE_ERR_INVALID_ARG),
+        (dict(dst=FAKE + 1024), B.MOE_ERR_INVALID_ARG),          # overlaps src
+        (dict(dst=FAKE * 4 + 8), B.MOE_ERR_UNSUPPORTED),         # not 16-byte aligned
+    ]
+    for kw, status in cases:
+        a = dict(cfg=c, n_groups=2, rows=32, cols=64, src=FAKE, dst=FAKE * 4)
+        a.update(kw)
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_pack_weights(a["cfg"], a["n_groups"], a["rows"], a["cols"], a["src"], a["dst"], stream=0)
+        assert ei.value.status == status, (kw, str(ei.value))
+    B.moe_pack_weights(c, 0, 32, 64, None, None, stream=0)       # nothing to pack: no-op
 
 
 def test_null_config_and_null_out(lib):

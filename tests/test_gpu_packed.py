@@ -1,0 +1,98 @@
+"""Packed expert weights (moe_pack_weights / MOE_LAYOUT_PACKED) on the GPU.
+
+The packed layout only rearranges the bf16 values, and the kernels read the same values into the
+same matrix-core lanes, so every result must be bitwise identical to the row layout's; the row
+layout itself is held to the oracle by test_gpu_parity.py. The packing is checked bit for bit
+against its definition written as a numpy reshape/transpose.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_experts_layer_10_amd import binding as B
+from mixture_experts_layer_10_amd import inputs as I
+from parity_util import GAP, compare_routing, oracle_layer, rel_err, to_np, y_tolerance
+from test_gpu_parity import data_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+def pack_reference(w):
+    """[G, R, K] -> the documented packed order: block (g, rb, kb), slot l = row l % 16, k-chunk l / 16."""
+    G, R, K = w.shape
+    return np.ascontiguousarray(w.reshape(G, R // 16, 16, K // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5)).reshape(-1)
+
+
+@pytest.mark.parametrize("G,R,K", [(1, 16, 32), (3, 48, 96), (2, 1536, 2048), (5, 2048, 768)])
+def test_pack_weights_bit_exact(G, R, K):
+    say(f"[pack] {G}x{R}x{K}")
+    rng = np.random.default_rng(G * 1000 + R + K)
+    bits = rng.integers(0, 1 << 16, size=(G, R, K), dtype=np.uint16)
+    src = torch.from_numpy(bits.view(np.int16)).cuda()
+    dst = torch.full_like(src, -1)
+    B.moe_pack_weights(B.make_config(1, 128, 1, 1, 128), G, R, K, src, dst)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy().view(np.uint16).reshape(-1), pack_reference(bits))
+
+
+def _ffn(cfg, G, I_, R, x, ridx, off, gu, dn):
+    h = torch.full((R, I_), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((R, cfg.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    B.moe_expert_ffn(cfg, G, I_, R, x, ridx, off, gu, dn, h, out)
+    torch.cuda.synchronize()
+    return h, out
+
+
+@pytest.mark.parametrize("D,I_,rows", [
+    (256, 128, [300, 0, 5, 257, 1, 64, 513]),       # tall groups: 256-row tiles
+    (2048, 768, [3, 0, 1, 7, 2, 5, 4, 6]),          # a few rows per group: weight streaming
+    (384, 256, [17, 40, 0, 9]),
+])
+def test_packed_ffn_equals_rows(D, I_, rows):
+    say(f"[packed ffn] D={D} I={I_} rows={rows}")
+    G = len(rows)
+    offsets = np.zeros(G + 1, np.int64)
+    offsets[1:] = np.cumsum(rows)
+    R = int(offsets[-1])
+    d = I.make_inputs(I.custom_shape("ffn", R, D, G, 1, I_, seed=300 + D))
+    dev = B.to_device(d.store)
+    cfg_rows = B.make_config(R, D, G, 1, I_)
+    cfg_pack = B.make_config(R, D, G, 1, I_, packed=True)
+    pdev = B.pack_device_weights(cfg_pack, dev)
+    off = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    ridx = torch.from_numpy(np.random.default_rng(1).permutation(R).astype(np.int32)).cuda()
+    h0, o0 = _ffn(cfg_rows, G, I_, R, dev["x"], ridx, off, dev["gate_up"], dev["down"])
+    h1, o1 = _ffn(cfg_pack, G, I_, R, dev["x"], ridx, off, pdev["gate_up"], pdev["down"])
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    assert torch.equal(o0.view(torch.int32), o1.view(torch.int32))
+    ref = O.grouped_expert_ffn(d.values("x")[ridx.cpu().numpy()], offsets, d.expert_view("gate_up"),
+                               d.expert_view("down"))
+    assert rel_err(to_np(o1), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "keras", "fanout", "many_empty"])
+def test_packed_forward_equals_rows(name):
+    say(f"[packed forward] {name}")
+    d, dev = data_of(name)
+    s = d.shape
+    cfg_rows = B.config_for(s, "f32")
+    cfg_pack = B.config_for(s, "f32", packed=True)
+    assert B.packable(cfg_pack)
+    pdev = B.pack_device_weights(cfg_pack, dev)
+    N, k = s.n_tokens, s.top_k
+    outs = []
+    for cfg, dv in ((cfg_rows, dev), (cfg_pack, pdev)):
+        w = torch.empty((N, k), dtype=torch.float32, device="cuda")
+        e = torch.empty((N, k), dtype=torch.int32, device="cuda")
+        y = B.forward(cfg, dv, weights=w, experts=e)
+        torch.cuda.synchronize()
+        outs.append((y, w, e))
+    (y0, w0, e0), (y1, w1, e1) = outs
+    assert torch.equal(e0, e1) and torch.equal(w0.view(torch.int32), w1.view(torch.int32))
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    if name == "decode":            # and once more straight against the oracle
+        _, probs, w_ref, e_ref = O.route(d.values("x"), d.values("w_router"), k, s.norm_topk_prob)
+        same, _ = compare_routing(to_np(w1).astype(np.float64), to_np(e1), w_ref, e_ref, probs, k)
+        y_ref, _ = oracle_layer(d)
+        assert rel_err(to_np(y1)[same], y_ref[same]) <= y_tolerance(s.dtype, "f32", y_ref)
