@@ -10,9 +10,13 @@
 //        otherwise through registers into two. Wave w computes expert blocks w, w+4, ... with
 //        32x32x16 matrix-core steps (bf16 products are exact in fp32, fp32 accumulation). The
 //        logits land in LDS unrounded, over the staging buffers.
+//        Long batches (N >= 8192, D % 512 == 0, D <= 2048) keep the whole x tile in LDS instead
+//        and stream the router weights from L2 (x-stationary kernel, eight waves).
 //  fp32: 64 tokens per workgroup, plain FMA dot products.
-// Selection: each wave walks its tokens; a lane holds experts lane, lane+64, ...; k rounds of a
-// wave-wide (p, index) arg-max with ties to the lower index.
+// Selection: E <= 128 and k <= 8: 16 lanes per token, each sorting 8 candidates, then four rounds
+// of pairwise merges of sorted lists. Otherwise each wave walks its tokens; a lane holds experts
+// lane, lane+64, ...; k rounds of a wave-wide (p, index) arg-max. Either way ties go to the lower
+// index.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,16 +25,18 @@ namespace moe {
 constexpr int kRouteThreads = 256;
 
 // Softmax, top-k and outputs for token rows [0, n_rows) of a workgroup whose logits sit in
-// s_logit[t * cols + e]. sel_p / sel_e: per-wave scratch of 512 entries each.
+// s_logit[t * cols + e]. sel_p / sel_e: per-wave scratch of 512 entries each. A lane holds
+// experts lane + 64 j, j < 2 EP (E <= 128 EP).
+template <int EP>
 __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols, int64_t n0, int n_rows,
-                             float* sel_p_all, int* sel_e_all) {
+                             float* sel_p_all, int* sel_e_all, int nw = 4) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, D = a.D, k = a.k;
   float* sel_p = sel_p_all + wave * 512;
   int* sel_e = sel_e_all + wave * 512;
-  for (int t = wave; t < n_rows; t += 4) {
+  for (int t = wave; t < n_rows; t += nw) {
     const int64_t n = n0 + t;
-    constexpr int kPer = 8;                    // E <= 512 = 8 per lane
+    constexpr int kPer = 2 * EP;
     float v[kPer];
     float m = -INFINITY;
 #pragma unroll
@@ -97,6 +103,135 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+}
+
+// Selection with 16 lanes per token (E <= 128, k <= 8): lane j of a token's group holds experts
+// j + 16 i, i < 8, sorts its eight (p, e) pairs, then four xor rounds merge pairs of sorted lists
+// (top 8 of the union: elementwise best of one list against the other reversed, a bitonic sequence,
+// then a 3-stage bitonic merge). Order: larger p first, equal p -> lower expert index, a total
+// order, so every lane of the group ends with the same list. Tokens base + 4 w + g (g = lane / 16)
+// of wave w; nw waves share the tile.
+__device__ __forceinline__ bool sel_better(float pa, int ea, float pb, int eb) {
+  return pa > pb || (pa == pb && ea < eb);
+}
+__device__ __forceinline__ void sel_ce(float& pa, int& ea, float& pb, int& eb) {   // (a, b) -> (better, worse)
+  const bool sw = sel_better(pb, eb, pa, ea);
+  const float tp = sw ? pb : pa, up = sw ? pa : pb;
+  const int te = sw ? eb : ea, ue = sw ? ea : eb;
+  pa = tp; ea = te; pb = up; eb = ue;
+}
+__device__ __forceinline__ void sel_bitonic_merge8(float* p, int* e) {                // bitonic -> sorted
+#pragma unroll
+  for (int d = 4; d >= 1; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & d) == 0) sel_ce(p[i], e[i], p[i + d], e[i + d]);
+}
+
+template <int EP>
+__device__ void route_select16(const RouteArgs& a, const float* s_logit, int cols, int64_t n0, int n_rows, int nw) {
+  static_assert(EP == 1, "16-lane selection covers E <= 128");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15;
+  const int E = a.E, D = a.D, k = a.k;
+  for (int base = 0; base < n_rows; base += 4 * nw) {
+    const int t = base + 4 * wave + (lane >> 4);
+    const bool valid = t < n_rows;
+    float p[8];
+    int e[8];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      e[i] = j + 16 * i;
+      p[i] = (valid && e[i] < E) ? s_logit[t * cols + e[i]] : -INFINITY;
+      m = fmaxf(m, p[i]);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = e[i] < E ? expf(p[i] - m) : 0.f;
+      sum += p[i];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 16);   // commutative pairs: same in every lane
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = e[i] < E ? p[i] / sum : -1.f;  // -1: never selected
+    // sort the lane's eight: bitonic sort (sizes 2, 4, 8)
+#pragma unroll
+    for (int size = 2; size <= 8; size <<= 1)
+#pragma unroll
+      for (int d = size >> 1; d >= 1; d >>= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int l = i ^ d;
+          if (l > i) {
+            if ((i & size) == 0) sel_ce(p[i], e[i], p[l], e[l]);
+            else sel_ce(p[l], e[l], p[i], e[i]);
+          }
+        }
+    // merge with the partner lists
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      float q[8];
+      int f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        q[i] = __shfl_xor(p[i], o, 16);
+        f[i] = __shfl_xor(e[i], o, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (sel_better(q[7 - i], f[7 - i], p[i], e[i])) { p[i] = q[7 - i]; e[i] = f[7 - i]; }
+      sel_bitonic_merge8(p, e);
+    }
+    float kept = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (r < k) kept += p[r];                                       // slot order, same in every lane
+    if (valid) {
+      const int64_t n = n0 + t;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r == j && r < k) {
+          a.weights[n * k + r] = a.norm ? p[r] / kept : p[r];
+          a.experts[n * k + r] = e[r];
+        }
+      if (a.logits) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (j + 16 * i < E) a.logits[n * E + j + 16 * i] = s_logit[t * cols + j + 16 * i];
+      }
+    }
+    if (a.w_shared_gate) {                                         // 16 lanes per token
+      float z = 0.f;
+      if (valid) {
+        const int64_t n = n0 + t;
+        if (a.bf16) {
+          const uint16_t* xr = static_cast<const uint16_t*>(a.x) + n * D;
+          const uint16_t* ws = static_cast<const uint16_t*>(a.w_shared_gate);
+          for (int d = j; d < D; d += 16) z = fmaf(bf16_to_f32(xr[d]), bf16_to_f32(ws[d]), z);
+        } else {
+          const float* xr = static_cast<const float*>(a.x) + n * D;
+          const float* ws = static_cast<const float*>(a.w_shared_gate);
+          for (int d = j; d < D; d += 16) z = fmaf(xr[d], ws[d], z);
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 16);
+      if (valid && j == 0) a.shared_scale[n0 + t] = 1.f / (1.f + expf(-z));
+    }
+  }
+}
+
+// E <= 128 and k <= 8 take the 16-lane selection, other shapes the per-wave one.
+template <int EP>
+__device__ void select_tokens(const RouteArgs& a, const float* s_logit, int cols, int64_t n0, int n_rows,
+                              float* sel_p, int* sel_e, int nw) {
+  if constexpr (EP == 1) {
+    if (a.k <= 8) return route_select16<EP>(a, s_logit, cols, n0, n_rows, nw);
+  }
+  route_select<EP>(a, s_logit, cols, n0, n_rows, sel_p, sel_e, nw);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -191,7 +326,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   }
   __syncthreads();
   const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
-  route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
+  select_tokens<EP>(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele, 4);
 }
 
 
@@ -313,9 +448,117 @@ __global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a
   }
   __syncthreads();
   const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
-  route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
+  select_tokens<EP>(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele, 4);
 }
 
+
+// x-stationary variant for long batches (bf16, D % 512 == 0, D <= 2048): the workgroup's 32
+// token rows (up to 128 KB) move into LDS once, with 1 KB contiguous DMA instructions, and the
+// router weights (shared by every token tile, so L2-resident) stream from global memory straight
+// into matrix-core fragments, U k-steps of loads in flight. No partial logits and no second pass.
+// Eight waves: wave w takes expert blocks (w % 4) + 4 b over half h = w / 4 of the contraction;
+// the halves are added in the order h = 0 + h = 1. LDS: 16-byte chunk c of row r sits at
+// c ^ (r & 15), so the 16 rows one ds_read_b128 serves together hit 16 distinct bank slots.
+constexpr int kXsMaxD = 2048;
+constexpr int kXsThreads = 512;
+
+template <int EP>
+__global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
+  constexpr int EPAD = EP * 128;
+  constexpr int U = EP <= 2 ? 8 : 4;                        // k-steps per load batch
+  constexpr int HI_FLOATS = 4 * EP * 16 * 64;               // upper-half accumulators of waves 4..7
+  static_assert(HI_FLOATS * 4 <= kRtTok * kXsMaxD * 2, "upper-half sums alias the x tile");
+  static_assert(kRtTok * EPAD * 4 + 2 * 8 * 512 * 4 <= kRtTok * kXsMaxD * 2, "logits alias the x tile");
+  __shared__ __attribute__((aligned(1024))) uint16_t sX[kRtTok * kXsMaxD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int eg = wave & 3, kh = wave >> 2;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRtTok;
+  const int D = a.D, E = a.E;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* w = static_cast<const uint16_t*>(a.w_router);
+  // x tile: instruction i covers row i / IPR, 16-byte chunks 64 (i % IPR) .. + 63 of it
+  const int IPR = D / 512;
+  for (int i = wave; i < kRtTok * IPR; i += kXsThreads / 64) {
+    const int r = i / IPR, q = i - r * IPR;
+    const int64_t n = min<int64_t>(n0 + r, a.N - 1);
+    dma16(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
+  }
+  // weight rows of this wave's blocks; lane: row lane % 32, k-group lane / 32; k from kh * D / 2
+  const int ks0 = kh * (D / 32);                            // first 16-wide k-step of this half
+  const uint16_t* wp[EP];
+#pragma unroll
+  for (int b = 0; b < EP; ++b)
+    wp[b] = w + static_cast<int64_t>(min((eg + 4 * b) * 32 + (lane & 31), E - 1)) * D + ks0 * 16 + 8 * (lane >> 5);
+  u32x4 fb[2][U][EP];
+  auto loadw = [&](int buf, int k0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < EP; ++b)
+        if ((eg + 4 * b) * 32 < E) fb[buf][u][b] = *reinterpret_cast<const u32x4*>(wp[b] + (k0 + u) * 16);
+  };
+  f32x16 acc[EP];
+#pragma unroll
+  for (int b = 0; b < EP; ++b) acc[b] = f32x16{};
+  const int arow = (lane & 31) * D;
+  auto math = [&](int buf, int k0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (2 * (ks0 + k0 + u) + (lane >> 5)) ^ (lane & 15);
+      const u32x4 fa = *reinterpret_cast<const u32x4*>(&sX[arow + c * 8]);
+#pragma unroll
+      for (int b = 0; b < EP; ++b)
+        if ((eg + 4 * b) * 32 < E) acc[b] = mfma32(fa, fb[buf][u][b], acc[b]);
+    }
+  };
+  loadw(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);                            // the x tile (and the first weights) landed
+  __syncthreads();
+  const int full = D / 32 / U;                              // batches per half; even: D % 512 == 0, U <= 8
+  for (int q = 0; q < full; q += 2) {
+    if (q + 1 < full) loadw(1, (q + 1) * U);
+    math(0, q * U);
+    if (q + 2 < full) loadw(0, (q + 2) * U);
+    math(1, (q + 1) * U);
+  }
+  __syncthreads();                                          // every wave is done reading the x tile
+  float* hi = reinterpret_cast<float*>(sX);
+  if (kh == 1) {
+#pragma unroll
+    for (int b = 0; b < EP; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) hi[((eg * EP + b) * 16 + i) * 64 + lane] = acc[b][i];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int b = 0; b < EP; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][i] += hi[((eg * EP + b) * 16 + i) * 64 + lane];
+  }
+  __syncthreads();                                          // the upper-half sums are consumed
+  float* s_logit = reinterpret_cast<float*>(sX);            // [kRtTok][EPAD]
+  float* s_selp = s_logit + kRtTok * EPAD;
+  int* s_sele = reinterpret_cast<int*>(s_selp + 8 * 512);
+  if (kh == 0) {
+#pragma unroll
+    for (int b = 0; b < EP; ++b) {
+      const int col = (eg + 4 * b) * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_logit[acc_row(i, lane) * EPAD + col] = acc[b][i];
+    }
+  }
+  __syncthreads();
+  const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
+  select_tokens<EP>(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele, kXsThreads / 64);
+}
+
+// Long bf16 batches with a suitable width take the x-stationary kernel (one workgroup per CU, so
+// it wants at least a round of tiles).
+static bool route_xs_ok(int64_t N, int D, bool bf16) {
+  return bf16 && D % 512 == 0 && D <= kXsMaxD && N >= 8192;
+}
 
 // Second pass of a split contraction: logits[n][e] = sum over slices s = 0, 1, ... of
 // partial[s][n][e], added in slice order (deterministic), then the same selection as the fused
@@ -355,7 +598,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(RouteArgs a
     }
   }
   __syncthreads();
-  route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
+  select_tokens<EP>(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele, 4);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -390,7 +633,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a) {
   }
   __syncthreads();
   const int n_rows = static_cast<int>(min<int64_t>(kTok, a.N - n0));
-  route_select(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele);
+  select_tokens<EP>(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele, 4);
 }
 
 // Slices of the contraction: each workgroup walks D / slices columns in 32-wide stages with three
@@ -398,7 +641,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a) {
 // workgroups shortens it. Aim for about 2048 workgroups; each slice keeps >= 128 columns (four
 // stages). Needs the partial-logit scratch (slices * N * E fp32).
 int route_slices_for(int64_t N, int D, int E, bool bf16) {
-  if (!bf16 || D % (4 * kRsK) != 0) return 1;
+  if (!bf16 || D % (4 * kRsK) != 0 || route_xs_ok(N, D, bf16)) return 1;
   const int64_t tiles = (N + kRtTok - 1) / kRtTok;
   int s = 1;
   const int64_t slice_bytes = N * E * 4;         // partial logits of one slice; keep all <= 32 MiB
@@ -415,7 +658,9 @@ static void launch_route_ep(const RouteArgs& a, hipStream_t st) {
   if (a.bf16) {
     const unsigned grid = static_cast<unsigned>((a.N + kRtTok - 1) / kRtTok);
     const int slices = route_slices(a);
-    if (slices > 1) {
+    if (route_xs_ok(a.N, a.D, a.bf16)) {
+      route_xs_kernel<EP><<<grid, kXsThreads, 0, st>>>(a);
+    } else if (slices > 1) {
       route_stream_kernel<EP><<<dim3(grid, slices), kRouteThreads, 0, st>>>(a);
       if (slices <= 4 && a.N >= 1024) {       // long batches: few slices, many tokens per workgroup
         constexpr int TOK = EP <= 2 ? 16 : 4;

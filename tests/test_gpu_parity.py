@@ -33,6 +33,8 @@ ODD = {
     "no_renorm": I.custom_shape("no_renorm", 66, 96, 12, 3, 48, norm_topk_prob=False, seed=20),
     "tiles": I.custom_shape("tiles", 600, 264, 4, 2, 200, seed=21),       # > 256 rows per expert
     "e512": I.custom_shape("e512", 130, 64, 512, 10, 16, shared_inter=16, seed=22),
+    # long batch (x-stationary router) with a ragged last token tile and two 128-expert blocks
+    "xs_e200": I.custom_shape("xs_e200", 8200, 512, 200, 6, 128, seed=23),
 }
 SMALL = ["tiny"] + list(ODD)
 FULL = ["keras", "decode", "prefill", "fanout"]
