@@ -554,6 +554,70 @@ __global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
   select_tokens<EP>(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele, kXsThreads / 64);
 }
 
+// E <= 128: the same x tile with 16x16x32 matrix-core steps. Wave w owns experts 16 w .. + 15
+// over the whole contraction and both 16-token halves of the tile; its weight loads are 16 rows x
+// 64 bytes, so the lines it reuses over consecutive k-steps (16 x 128 bytes) stay in L1.
+template <int U>
+__global__ __launch_bounds__(kXsThreads) void route_xs16_kernel(RouteArgs a) {
+  constexpr int EPAD = 128;
+  static_assert(kRtTok * EPAD * 4 <= kRtTok * kXsMaxD * 2, "logits alias the x tile");
+  __shared__ __attribute__((aligned(1024))) uint16_t sX[kRtTok * kXsMaxD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRtTok;
+  const int D = a.D, E = a.E;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* w = static_cast<const uint16_t*>(a.w_router);
+  const int IPR = D / 512;
+  for (int i = wave; i < kRtTok * IPR; i += kXsThreads / 64) {
+    const int r = i / IPR, q = i - r * IPR;
+    const int64_t n = min<int64_t>(n0 + r, a.N - 1);
+    dma16(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
+  }
+  const bool active = wave * 16 < E;                        // uniform
+  const uint16_t* wp = w + static_cast<int64_t>(min(wave * 16 + (lane & 15), E - 1)) * D + 8 * (lane >> 4);
+  u32x4 fb[2][U];
+  auto loadw = [&](int buf, int k0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (active) fb[buf][u] = *reinterpret_cast<const u32x4*>(wp + (k0 + u) * 32);
+  };
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const int r0 = lane & 15;                                 // token of this lane in each half
+  auto math = [&](int buf, int k0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (4 * (k0 + u) + (lane >> 4)) ^ r0;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const u32x4 fa = *reinterpret_cast<const u32x4*>(&sX[(tb * 16 + r0) * D + c * 8]);
+        if (active) acc[tb] = mfma16(fa, fb[buf][u], acc[tb]);
+      }
+    }
+  };
+  loadw(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);                            // the x tile (and the first weights) landed
+  __syncthreads();
+  const int full = D / 32 / U;                              // even: D % 512 == 0, U <= 8
+  for (int q = 0; q < full; q += 2) {
+    if (q + 1 < full) loadw(1, (q + 1) * U);
+    math(0, q * U);
+    if (q + 2 < full) loadw(0, (q + 2) * U);
+    math(1, (q + 1) * U);
+  }
+  __syncthreads();                                          // every wave is done reading the x tile
+  float* s_logit = reinterpret_cast<float*>(sX);            // [kRtTok][EPAD]
+  if (active) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_logit[(tb * 16 + 4 * (lane >> 4) + i) * EPAD + wave * 16 + (lane & 15)] = acc[tb][i];
+  }
+  __syncthreads();
+  const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
+  route_select16<1>(a, s_logit, EPAD, n0, n_rows, kXsThreads / 64);
+}
+
 // Long bf16 batches with a suitable width take the x-stationary kernel (one workgroup per CU, so
 // it wants at least a round of tiles).
 static bool route_xs_ok(int64_t N, int D, bool bf16) {
@@ -659,7 +723,10 @@ static void launch_route_ep(const RouteArgs& a, hipStream_t st) {
     const unsigned grid = static_cast<unsigned>((a.N + kRtTok - 1) / kRtTok);
     const int slices = route_slices(a);
     if (route_xs_ok(a.N, a.D, a.bf16)) {
-      route_xs_kernel<EP><<<grid, kXsThreads, 0, st>>>(a);
+      if (EP == 1 && a.k <= 8)
+        route_xs16_kernel<8><<<grid, kXsThreads, 0, st>>>(a);
+      else
+        route_xs_kernel<EP><<<grid, kXsThreads, 0, st>>>(a);
     } else if (slices > 1) {
       route_stream_kernel<EP><<<dim3(grid, slices), kRouteThreads, 0, st>>>(a);
       if (slices <= 4 && a.N >= 1024) {       // long batches: few slices, many tokens per workgroup
