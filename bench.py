@@ -43,6 +43,27 @@ def algorithmic(shape, touched):
     return dict(flops=flops, bytes=bytes_, gate_up_flops=gate_up_flops, gate_up_bytes=gate_up_bytes)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE runs scaled by a copy of known size), or None when there is none or the kernel
+    sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gate_up_prefill_traffic.md")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in ("grouped_gemm.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "mixture_experts_layer_10_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic-record:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec["kernel"] == kernel and rec["sources_sha256"] == h.hexdigest():
+                    return rec["bytes_per_launch"]
+    return None
+
+
 def run_workload(name, steps, warmup, out_dtype, inner_events=True):
     """Times `steps` whole-path steps. With inner_events the gate_up launch of every timed step is
     bracketed by events on its stream (its duration comes from the timed region itself); without,
@@ -162,8 +183,10 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
     packed = "true" if main_run["cfg"].weight_layout else "false"
-    roof["kernel"] = f"gemm_stream_kernel<2,4,4,2,true,{packed}> (grouped gate_up + SwiGLU)" if prefill_like else \
-        f"gemm_wstream_kernel<1,true,{packed}> (grouped gate_up + SwiGLU, weight streaming)"
+    kname = f"gemm_stream_kernel<2,4,4,2,true,{packed}>" if prefill_like else f"gemm_wstream_kernel<1,true,{packed}>"
+    roof["kernel"] = kname + (" (grouped gate_up + SwiGLU)" if prefill_like else " (grouped gate_up + SwiGLU, weight streaming)")
+    if args.workload == "prefill":
+        roof["traffic"] = measured_traffic(kname)
     roof["per_launch"] = dict(flops=alg["gate_up_flops"], bytes=alg["gate_up_bytes"], avg_ms=round(main_run["gate_up_ms"], 4))
     layer_s = main_run["ms_per_step"] / 1e3
     out = {
