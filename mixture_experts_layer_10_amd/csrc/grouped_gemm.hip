@@ -295,6 +295,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sB2[BNB * kSK];
   __shared__ __attribute__((aligned(1024))) uint16_t sB3[BNB * kSK];
   __shared__ int s_pref[1025];
+  __shared__ int s_off[1025];           // group row offsets (no global round trip per tile)
   __shared__ int s_tmp[16];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -304,7 +305,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   const int K = kSwiGLU ? a.D : a.I;
   const int NOUT = kSwiGLU ? a.I : a.D;
   const int n_tiles = (NOUT + OUT_COLS - 1) / OUT_COLS;
-  build_tile_prefix<NT>(a.offsets, G, a.max_rows, BM, n_tiles, s_pref, s_tmp);
+  for (int g = tid; g <= G; g += NT)
+    s_off[g] = a.offsets ? a.offsets[g] : (g == 0 ? 0 : static_cast<int>(a.max_rows));
+  build_tile_prefix<NT>(a.offsets, G, a.max_rows, BM, n_tiles, s_pref, s_tmp);   // ends with a barrier
   const int total = s_pref[G];
   const int P = gridDim.x;
   const uint16_t* X = static_cast<const uint16_t*>(a.x);
@@ -328,32 +331,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   }
   constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
 
-  for (int r = 0;; ++r) {
+  // One tile's fixed data. make_tile reads the group table in LDS and, for gathered rows, the row
+  // indices of its A rows (global loads whose values are first used when its DMA is issued).
+  struct Tile {
+    bool valid;
+    int m0, c0, live;
+    int64_t row0, rows;
+    const uint16_t* srcA[A_INS];
+    const uint16_t* srcB[B_INS];
+  };
+  auto make_tile = [&](int r) {
+    Tile T;
     const int t = tile_of_round(r, blockIdx.x, P);
-    if (r * P >= total) break;
-    if (t >= total) continue;
+    T.valid = r * P < total && t < total;             // t grows with r: past the list, nothing follows
+    if (!T.valid) return T;
     const int g = find_group(s_pref, G, t);
     const int local = t - s_pref[g];
-    const int64_t row0 = a.offsets ? a.offsets[g] : 0;
-    const int64_t rows = a.offsets ? static_cast<int64_t>(a.offsets[g + 1]) - row0 : a.max_rows;
-    if (rows <= 0) continue;
+    T.row0 = s_off[g];
+    T.rows = static_cast<int64_t>(s_off[g + 1]) - T.row0;   // > 0: empty groups own no tiles
     const int mt = local / n_tiles, nt = local - mt * n_tiles;
-    const int m0 = mt * BM;
-    const int c0 = nt * OUT_COLS;
+    T.m0 = mt * BM;
+    T.c0 = nt * OUT_COLS;
     // 32-row blocks of this wave that hold real rows (uniform across the wave)
-    const int live = static_cast<int>(min<int64_t>(TM, max<int64_t>(0, (rows - m0 - wm * TM * 32 + 31) / 32)));
-
-    const uint16_t* srcA[A_INS];
+    T.live = static_cast<int>(min<int64_t>(TM, max<int64_t>(0, (T.rows - T.m0 - wm * TM * 32 + 31) / 32)));
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) {
       const int rr = ((wave * A_INS + j) % A_GROUPS) * 16 + lrow;
-      const int64_t lr = min<int64_t>(m0 + rr, rows - 1);   // rows past the group read a valid row
-      const int64_t p = row0 + lr;
+      const int64_t lr = min<int64_t>(T.m0 + rr, T.rows - 1);   // rows past the group read a valid row
+      const int64_t p = T.row0 + lr;
       const int64_t src = a.row_index ? a.row_index[p] : p;
-      srcA[j] = X + src * K + lch * 8;
+      T.srcA[j] = X + src * K + lch * 8;
     }
     const uint16_t* Wg = W + static_cast<int64_t>(g) * (kSwiGLU ? 2LL * a.I * a.D : static_cast<int64_t>(a.D) * a.I);
-    const uint16_t* srcB[B_INS];
 #pragma unroll
     for (int j = 0; j < B_INS; ++j) {
       const int grp = wave * B_INS + j;
@@ -363,85 +372,108 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         int rb;
         if (kSwiGLU) {
           const int half = BNB / 32;                          // 16-row groups per half
-          const int cb = min(c0 / 16 + grp % half, NOUT / 16 - 1);
+          const int cb = min(T.c0 / 16 + grp % half, NOUT / 16 - 1);
           rb = grp < half ? cb : a.I / 16 + cb;
         } else {
-          rb = min(c0 / 16 + grp, NOUT / 16 - 1);
+          rb = min(T.c0 / 16 + grp, NOUT / 16 - 1);
         }
-        srcB[j] = Wg + static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8;
+        T.srcB[j] = Wg + static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8;
       } else {
         const int rr = grp * 16 + lrow;
         int wrow;
         if (kSwiGLU) {
           const int half = BNB / 2;
-          const int ci = min(c0 + (rr % half), NOUT - 1);
+          const int ci = min(T.c0 + (rr % half), NOUT - 1);
           wrow = rr < half ? ci : a.I + ci;
         } else {
-          wrow = min(c0 + rr, NOUT - 1);
+          wrow = min(T.c0 + rr, NOUT - 1);
         }
-        srcB[j] = Wg + static_cast<int64_t>(wrow) * K + lch * 8;
+        T.srcB[j] = Wg + static_cast<int64_t>(wrow) * K + lch * 8;
       }
     }
-    auto issue = [&](int ks, uint16_t* sa, uint16_t* sb) {
-      const int kb = ks * kSK;
+    return T;
+  };
+  auto issue = [&](const Tile& T, int ks, uint16_t* sa, uint16_t* sb) {
+    const int kb = ks * kSK;
 #pragma unroll
-      for (int j = 0; j < A_INS; ++j) dma16(srcA[j] + kb, sa + ((wave * A_INS + j) % A_GROUPS) * 512);
+    for (int j = 0; j < A_INS; ++j) dma16(T.srcA[j] + kb, sa + ((wave * A_INS + j) % A_GROUPS) * 512);
 #pragma unroll
-      for (int j = 0; j < B_INS; ++j) dma16(srcB[j] + (kPacked ? ks * 512 : kb), sb + (wave * B_INS + j) * 512);
-    };
-    // wait for stage s (later stages may stay in flight), then sync the workgroup: after this, stage
-    // s is visible to every wave and every wave has finished reading stage s - 1's buffer
-    auto wait_stage = [&](int s) {
-      const int ahead = min(2, ksteps - 1 - s);
-      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(W2);
-      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(W1);
-      else __builtin_amdgcn_s_waitcnt(W0);
-      lds_barrier();
-    };
-    f32x16 acc[TM][TN];
+    for (int j = 0; j < B_INS; ++j) dma16(T.srcB[j] + (kPacked ? ks * 512 : kb), sb + (wave * B_INS + j) * 512);
+  };
+  // wait for stage s (later stages may stay in flight), then sync the workgroup: after this, stage
+  // s is visible to every wave and every wave has finished reading stage s - 1's buffer. Loads
+  // retire in order, so "at most n outstanding" implies stage s has landed even with the previous
+  // tile's epilogue stores still counted.
+  auto wait_stage = [&](int s) {
+    const int ahead = min(2, ksteps - 1 - s);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(W2);
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(W1);
+    else __builtin_amdgcn_s_waitcnt(W0);
+    lds_barrier();
+  };
+  f32x16 acc[TM][TN];
+  auto compute = [&](const uint16_t* sa, const uint16_t* sb, int live) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&sa[koA[kk] + i * 32 * kSK]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        constexpr int H = TN / 2;
+        const int rowoff = kSwiGLU ? (j < H ? j * 32 : BNB / 2 + (j - H) * 32) : j * 32;
+        fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        if (i < live) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+        }
+    }
+  };
+
+  // Tiles are software-pipelined: the next tile's first three stages go out as soon as every wave
+  // has passed the last stage's barrier (buffers 0-2 are free then), so their latency overlaps the
+  // last k-slice and the epilogue stores instead of following them.
+  Tile cur = make_tile(0);
+  if (cur.valid) {
+    issue(cur, 0, sA0, sB0);
+    issue(cur, 1, sA1, sB1);
+    issue(cur, 2, sA2, sB2);
+  }
+  for (int r = 0; cur.valid; ++r) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 fa[TM], fb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&sa[koA[kk] + i * 32 * kSK]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          constexpr int H = TN / 2;
-          const int rowoff = kSwiGLU ? (j < H ? j * 32 : BNB / 2 + (j - H) * 32) : j * 32;
-          fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          if (i < live) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
-          }
-      }
-    };
-    __builtin_amdgcn_s_waitcnt(0);       // the previous tile's stores and index loads are done
-    issue(0, sA0, sB0);
-    issue(1, sA1, sB1);
-    issue(2, sA2, sB2);
+    Tile nxt;
+    nxt.valid = false;
     for (int ks = 0; ks < ksteps; ks += 4) {
+      const bool last = ks + 4 >= ksteps;
       wait_stage(ks);
-      if (ks + 3 < ksteps) issue(ks + 3, sA3, sB3);
-      compute(sA0, sB0);
+      if (ks + 3 < ksteps) issue(cur, ks + 3, sA3, sB3);
+      if (last) nxt = make_tile(r + 1);
+      compute(sA0, sB0, cur.live);
       wait_stage(ks + 1);
-      if (ks + 4 < ksteps) issue(ks + 4, sA0, sB0);
-      compute(sA1, sB1);
+      if (ks + 4 < ksteps) issue(cur, ks + 4, sA0, sB0);
+      compute(sA1, sB1, cur.live);
       wait_stage(ks + 2);
-      if (ks + 5 < ksteps) issue(ks + 5, sA1, sB1);
-      compute(sA2, sB2);
-      wait_stage(ks + 3);
-      if (ks + 6 < ksteps) issue(ks + 6, sA2, sB2);
-      compute(sA3, sB3);
+      if (ks + 5 < ksteps) issue(cur, ks + 5, sA1, sB1);
+      compute(sA2, sB2, cur.live);
+      wait_stage(ks + 3);                 // the last stage: everything this wave issued has landed
+      if (ks + 6 < ksteps) issue(cur, ks + 6, sA2, sB2);
+      if (last && nxt.valid) {
+        issue(nxt, 0, sA0, sB0);
+        issue(nxt, 1, sA1, sB1);
+        issue(nxt, 2, sA2, sB2);
+      }
+      compute(sA3, sB3, cur.live);
     }
-
+    // Epilogue. The next tile writes buffer 3 only after its first barrier, which every wave
+    // reaches after finishing these reads of buffer 3.
+    const int64_t row0 = cur.row0, rows = cur.rows;
+    const int m0 = cur.m0, c0 = cur.c0;
     if constexpr (kSwiGLU) {
       uint16_t* Hh = static_cast<uint16_t*>(a.out);
       constexpr int H = TN / 2;
@@ -474,7 +506,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         }
       }
     }
-    __syncthreads();                     // every wave is done with the stage buffers
+    cur = nxt;
   }
 }
 
