@@ -29,12 +29,13 @@
  * dtype (moe_config.dtype) applies to x and every weight; routing outputs are always fp32
  * weights and int32 expert ids; intermediate expert outputs are fp32.
  *
- * Packed expert weights (moe_config.weight_layout = MOE_LAYOUT_PACKED): gate_up, down,
- * shared_gate_up and shared_down may instead hold the output of moe_pack_weights, a one-time
- * rearrangement (at model load) of each [G, R, K] matrix into 16 x 32 blocks of 1 KB stored in
- * the order the matrix cores read them, so that every weight load is one contiguous kilobyte.
- * The values are the same; results are bitwise identical to the row layout. bf16 only, with
- * hidden, inter and shared_inter multiples of 128.
+ * Packed weights (moe_config.weight_layout = MOE_LAYOUT_PACKED): w_router (as a [1, E, D] stack),
+ * gate_up, down, shared_gate_up and shared_down instead hold the output of moe_pack_weights, a
+ * one-time rearrangement (at model load) of each [G, R, K] matrix into 16 x 32 blocks of 1 KB
+ * stored in the order the matrix cores read them, so that every weight load is one contiguous
+ * kilobyte. The values are the same; results are bitwise identical to the row layout. bf16 only,
+ * with hidden, inter and shared_inter multiples of 128 and n_experts a multiple of 16.
+ * w_shared_gate is a vector and keeps its layout.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -144,7 +145,8 @@ int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64
  * layout of MOE_LAYOUT_PACKED: block (g, rb, kb) of rows rb*16 .. +15 and columns kb*32 .. +31 is
  * 1 KB at byte offset ((g * R/16 + rb) * K/32 + kb) * 1024, holding at 16-byte slot l the eight
  * values of row rb*16 + l % 16, columns kb*32 + 8 (l / 16) .. + 7. dst has src's size and must
- * not overlap it. Use it on gate_up (R = 2I, K = D), down (R = D, K = I) and the shared pair.
+ * not overlap it. Use it on w_router (G = 1, R = E, K = D), gate_up (R = 2I, K = D), down (R = D,
+ * K = I) and the shared pair.
  * cfg gives dtype (must be bf16); its other fields are not used. */
 int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src,
                      void* dst, void* stream);

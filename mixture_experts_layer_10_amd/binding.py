@@ -60,9 +60,9 @@ def config_for(shape, out_dtype=None, packed=False) -> MoeConfig:
 
 
 def packable(cfg: MoeConfig) -> bool:
-    """Whether the packed weight layout applies (bf16, widths multiples of 128)."""
+    """Whether the packed weight layout applies (bf16, widths multiples of 128, E multiple of 16)."""
     return (cfg.dtype == MOE_BF16 and cfg.hidden % 128 == 0 and cfg.inter % 128 == 0
-            and cfg.shared_inter % 128 == 0)
+            and cfg.shared_inter % 128 == 0 and cfg.n_experts % 16 == 0)
 
 
 _lib = None
@@ -216,12 +216,12 @@ def torch_dtype(code):
 
 
 def pack_device_weights(cfg: MoeConfig, dev: dict):
-    """A copy of ``dev`` whose expert weights (gate_up, down and the shared pair) are in the packed
-    layout, made by moe_pack_weights (a one-time step, like loading the model)."""
+    """A copy of ``dev`` whose weight matrices (router, gate_up, down and the shared pair) are in the
+    packed layout, made by moe_pack_weights (a one-time step, like loading the model)."""
     import torch
     D, E, I, Is = cfg.hidden, cfg.n_experts, cfg.inter, cfg.shared_inter
     out = dict(dev)
-    shapes = {"gate_up": (E, 2 * I, D), "down": (E, D, I)}
+    shapes = {"w_router": (1, E, D), "gate_up": (E, 2 * I, D), "down": (E, D, I)}
     if Is:
         shapes.update(shared_gate_up=(1, 2 * Is, D), shared_down=(1, D, Is))
     for name, (g, r, c) in shapes.items():

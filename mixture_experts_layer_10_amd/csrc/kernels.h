@@ -18,6 +18,7 @@ struct RouteArgs {
   int D, E, k;
   int norm;
   bool bf16;
+  bool packed;                // w_router in the packed layout ([1, E, D] stack, E % 16 == 0)
 };
 constexpr int kMaxRouteSlices = 16;
 int route_slices_for(int64_t N, int D, int E, bool bf16);   // slices used when scratch is given

@@ -80,6 +80,8 @@ static int validate_config(const moe_config* c) {
     if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights need dtype bf16");
     if (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128)
       return fail(MOE_ERR_UNSUPPORTED, "packed weights need hidden, inter and shared_inter multiples of 128");
+    if (c->n_experts % 16)
+      return fail(MOE_ERR_UNSUPPORTED, "packed weights need n_experts = %lld to be a multiple of 16", (long long)c->n_experts);
   }
   if (c->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts = %lld > %lld", (long long)c->n_experts, (long long)kMaxExperts);
   if (c->hidden > (1 << 20) || c->inter > (1 << 20) || c->shared_inter > (1 << 20))
@@ -157,6 +159,7 @@ static int route_impl(const moe_config* c, const void* x, const void* w_router, 
   a.k = static_cast<int>(c->top_k);
   a.norm = c->norm_topk_prob;
   a.bf16 = c->dtype == MOE_BF16;
+  a.packed = c->weight_layout == MOE_LAYOUT_PACKED;
   launch_route(a, st);
   return check_launch("moe_route");
 }

@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
 // waves 0 and 1's x rows into the same place, so every wave issues the same count).
 constexpr int kRsK = 32;
 
-template <int EP>
+template <int EP, bool kPW>
 __global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a) {
   constexpr int EPAD = EP * 128;
   constexpr int XS = kRtTok * kRsK, WS = EPAD * kRsK;    // elements per stage
@@ -366,14 +366,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a
   const uint16_t* srcW[2 * EP];
 #pragma unroll
   for (int q = 0; q < 2 * EP; ++q) {
-    const int row = (wave + 4 * q) * 16 + lrow;            // W DMA group wave + 4 q
-    srcW[q] = w + static_cast<int64_t>(min(row, E - 1)) * D + kbase + lch * 8;
+    if constexpr (kPW) {                                   // 16-row block wave + 4 q: 1 KB per k-block
+      const int rb = min(wave + 4 * q, E / 16 - 1);
+      srcW[q] = w + (static_cast<int64_t>(rb) * (D / 32) + kbase / 32) * 512 + lane * 8;
+    } else {
+      const int row = (wave + 4 * q) * 16 + lrow;          // W DMA group wave + 4 q
+      srcW[q] = w + static_cast<int64_t>(min(row, E - 1)) * D + kbase + lch * 8;
+    }
   }
   auto issue = [&](int ks, uint16_t* sx, uint16_t* sw) {
     const int kb = ks * kRsK;
     dma16(srcX + kb, sx + xg * 512);
 #pragma unroll
-    for (int q = 0; q < 2 * EP; ++q) dma16(srcW[q] + kb, sw + (wave + 4 * q) * 512);
+    for (int q = 0; q < 2 * EP; ++q) dma16(srcW[q] + (kPW ? ks * 512 : kb), sw + (wave + 4 * q) * 512);
   };
   const int ksteps = kslice / kRsK;
   constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
@@ -384,9 +389,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a
     else __builtin_amdgcn_s_waitcnt(W0);
     lds_barrier();
   };
-  int ko[2];
+  // packed weights: a 16-row group's 1 KB holds (row r16, 8-wide k chunk q) at (r16 + 16 q) * 8
+  int ko[2], kob[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) ko[kk] = (lane & 31) * kRsK + (((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 3);
+  for (int kk = 0; kk < 2; ++kk) {
+    ko[kk] = (lane & 31) * kRsK + (((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 3);
+    kob[kk] = kPW ? ((lane >> 4) & 1) * 512 + (lane & 15) * 8 + (2 * kk + (lane >> 5)) * 128 : ko[kk];
+  }
   f32x16 acc[EP];
 #pragma unroll
   for (int b = 0; b < EP; ++b) acc[b] = f32x16{};
@@ -397,7 +406,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a
 #pragma unroll
       for (int b = 0; b < EP; ++b) {
         if ((wave + 4 * b) * 32 < E) {
-          const u32x4 fb = *reinterpret_cast<const u32x4*>(&sw[(wave + 4 * b) * 32 * kRsK + ko[kk]]);
+          const u32x4 fb = *reinterpret_cast<const u32x4*>(&sw[(wave + 4 * b) * 32 * kRsK + kob[kk]]);
           acc[b] = mfma32(fa, fb, acc[b]);
         }
       }
@@ -462,7 +471,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a
 constexpr int kXsMaxD = 2048;
 constexpr int kXsThreads = 512;
 
-template <int EP>
+template <int EP, bool kPW>
 __global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
   constexpr int EPAD = EP * 128;
   constexpr int U = EP <= 2 ? 8 : 4;                        // k-steps per load batch
@@ -486,17 +495,28 @@ __global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
   }
   // weight rows of this wave's blocks; lane: row lane % 32, k-group lane / 32; k from kh * D / 2
   const int ks0 = kh * (D / 32);                            // first 16-wide k-step of this half
+  // packed weights: row e's 16-wide k-step s sits in block (e / 16, s / 2) at slot
+  // e % 16 + 16 (2 (s % 2) + lane / 32)
   const uint16_t* wp[EP];
 #pragma unroll
-  for (int b = 0; b < EP; ++b)
-    wp[b] = w + static_cast<int64_t>(min((eg + 4 * b) * 32 + (lane & 31), E - 1)) * D + ks0 * 16 + 8 * (lane >> 5);
+  for (int b = 0; b < EP; ++b) {
+    if constexpr (kPW) {
+      const int rb = min((eg + 4 * b) * 2 + ((lane >> 4) & 1), E / 16 - 1);
+      wp[b] = w + static_cast<int64_t>(rb) * (D / 32) * 512 + ((lane & 15) + 16 * (lane >> 5)) * 8;
+    } else {
+      wp[b] = w + static_cast<int64_t>(min((eg + 4 * b) * 32 + (lane & 31), E - 1)) * D + ks0 * 16 + 8 * (lane >> 5);
+    }
+  }
   u32x4 fb[2][U][EP];
   auto loadw = [&](int buf, int k0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      const int s = ks0 + k0 + u;
 #pragma unroll
       for (int b = 0; b < EP; ++b)
-        if ((eg + 4 * b) * 32 < E) fb[buf][u][b] = *reinterpret_cast<const u32x4*>(wp[b] + (k0 + u) * 16);
+        if ((eg + 4 * b) * 32 < E)
+          fb[buf][u][b] = *reinterpret_cast<const u32x4*>(kPW ? wp[b] + (s >> 1) * 512 + (s & 1) * 256 : wp[b] + (k0 + u) * 16);
+    }
   };
   f32x16 acc[EP];
 #pragma unroll
@@ -557,7 +577,7 @@ __global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
 // E <= 128: the same x tile with 16x16x32 matrix-core steps. Wave w owns experts 16 w .. + 15
 // over the whole contraction and both 16-token halves of the tile; its weight loads are 16 rows x
 // 64 bytes, so the lines it reuses over consecutive k-steps (16 x 128 bytes) stay in L1.
-template <int U>
+template <int U, bool kPW>
 __global__ __launch_bounds__(kXsThreads) void route_xs16_kernel(RouteArgs a) {
   constexpr int EPAD = 128;
   static_assert(kRtTok * EPAD * 4 <= kRtTok * kXsMaxD * 2, "logits alias the x tile");
@@ -575,12 +595,14 @@ __global__ __launch_bounds__(kXsThreads) void route_xs16_kernel(RouteArgs a) {
     dma16(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
   }
   const bool active = wave * 16 < E;                        // uniform
-  const uint16_t* wp = w + static_cast<int64_t>(min(wave * 16 + (lane & 15), E - 1)) * D + 8 * (lane >> 4);
+  // packed weights: block (wave, s) is this wave's 16 rows at k-step s, 1 KB in lane order
+  const uint16_t* wp = kPW ? w + static_cast<int64_t>(min(wave, E / 16 - 1)) * (D / 32) * 512 + lane * 8
+                           : w + static_cast<int64_t>(min(wave * 16 + (lane & 15), E - 1)) * D + 8 * (lane >> 4);
   u32x4 fb[2][U];
   auto loadw = [&](int buf, int k0) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (active) fb[buf][u] = *reinterpret_cast<const u32x4*>(wp + (k0 + u) * 32);
+      if (active) fb[buf][u] = *reinterpret_cast<const u32x4*>(wp + (k0 + u) * (kPW ? 512 : 32));
   };
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const int r0 = lane & 15;                                 // token of this lane in each half
@@ -717,29 +739,35 @@ int route_slices_for(int64_t N, int D, int E, bool bf16) {
 
 int route_slices(const RouteArgs& a) { return a.partial ? route_slices_for(a.N, a.D, a.E, a.bf16) : 1; }
 
+template <int EP, bool kPW>
+static void launch_route_bf16(const RouteArgs& a, hipStream_t st) {
+  const unsigned grid = static_cast<unsigned>((a.N + kRtTok - 1) / kRtTok);
+  const int slices = route_slices(a);
+  if (route_xs_ok(a.N, a.D, a.bf16)) {
+    if (EP == 1 && a.k <= 8)
+      route_xs16_kernel<8, kPW><<<grid, kXsThreads, 0, st>>>(a);
+    else
+      route_xs_kernel<EP, kPW><<<grid, kXsThreads, 0, st>>>(a);
+  } else if (slices > 1) {
+    route_stream_kernel<EP, kPW><<<dim3(grid, slices), kRouteThreads, 0, st>>>(a);
+    if (slices <= 4 && a.N >= 1024) {       // long batches: few slices, many tokens per workgroup
+      constexpr int TOK = EP <= 2 ? 16 : 4;
+      route_finish_kernel<EP, TOK, 4><<<static_cast<unsigned>((a.N + TOK - 1) / TOK), kRouteThreads, 0, st>>>(a, slices);
+    } else {                                 // short batches: many slices, two tokens per workgroup
+      route_finish_kernel<EP, 2, kMaxRouteSlices><<<static_cast<unsigned>((a.N + 1) / 2), kRouteThreads, 0, st>>>(a, slices);
+    }
+  } else if (a.D % (4 * kRsK) == 0) {
+    route_stream_kernel<EP, kPW><<<grid, kRouteThreads, 0, st>>>(a);
+  } else if constexpr (!kPW) {              // packed weights always have D % 128 == 0
+    route_bf16_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
+  }
+}
+
 template <int EP>
 static void launch_route_ep(const RouteArgs& a, hipStream_t st) {
   if (a.bf16) {
-    const unsigned grid = static_cast<unsigned>((a.N + kRtTok - 1) / kRtTok);
-    const int slices = route_slices(a);
-    if (route_xs_ok(a.N, a.D, a.bf16)) {
-      if (EP == 1 && a.k <= 8)
-        route_xs16_kernel<8><<<grid, kXsThreads, 0, st>>>(a);
-      else
-        route_xs_kernel<EP><<<grid, kXsThreads, 0, st>>>(a);
-    } else if (slices > 1) {
-      route_stream_kernel<EP><<<dim3(grid, slices), kRouteThreads, 0, st>>>(a);
-      if (slices <= 4 && a.N >= 1024) {       // long batches: few slices, many tokens per workgroup
-        constexpr int TOK = EP <= 2 ? 16 : 4;
-        route_finish_kernel<EP, TOK, 4><<<static_cast<unsigned>((a.N + TOK - 1) / TOK), kRouteThreads, 0, st>>>(a, slices);
-      } else {                                 // short batches: many slices, two tokens per workgroup
-        route_finish_kernel<EP, 2, kMaxRouteSlices><<<static_cast<unsigned>((a.N + 1) / 2), kRouteThreads, 0, st>>>(a, slices);
-      }
-    } else if (a.D % (4 * kRsK) == 0) {
-      route_stream_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
-    } else {
-      route_bf16_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);
-    }
+    if (a.packed) launch_route_bf16<EP, true>(a, st);
+    else launch_route_bf16<EP, false>(a, st);
   } else {
     const unsigned grid = static_cast<unsigned>((a.N + 63) / 64);
     route_f32_kernel<EP><<<grid, kRouteThreads, 0, st>>>(a);

@@ -80,11 +80,12 @@ def test_config_validation(lib, field, value, status):
 
 
 def test_packed_layout_rules(lib):
-    ok = B.make_config(64, 256, 8, 2, 128, shared_inter=384, packed=True)
+    ok = B.make_config(64, 256, 16, 2, 128, shared_inter=384, packed=True)
     assert B.moe_workspace_bytes(ok) > 0 and B.packable(ok)
-    for bad in (B.make_config(64, 256, 8, 2, 128, dtype="f32", packed=True),
-                B.make_config(64, 256, 8, 2, 128, shared_inter=64, packed=True),
-                B.make_config(64, 200, 8, 2, 128, packed=True)):
+    for bad in (B.make_config(64, 256, 16, 2, 128, dtype="f32", packed=True),
+                B.make_config(64, 256, 16, 2, 128, shared_inter=64, packed=True),
+                B.make_config(64, 200, 16, 2, 128, packed=True),
+                B.make_config(64, 256, 8, 2, 128, packed=True)):          # the router needs E % 16 == 0
         with pytest.raises(B.MoeError) as ei:
             B.moe_workspace_bytes(bad)
         assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "packed" in str(ei.value)

@@ -58,8 +58,12 @@ def test_packed_ffn_equals_rows(D, I_, rows):
     d = I.make_inputs(I.custom_shape("ffn", R, D, G, 1, I_, seed=300 + D))
     dev = B.to_device(d.store)
     cfg_rows = B.make_config(R, D, G, 1, I_)
-    cfg_pack = B.make_config(R, D, G, 1, I_, packed=True)
-    pdev = B.pack_device_weights(cfg_pack, dev)
+    # the expert entry points take the group count as an argument; cfg.n_experts only has to be valid
+    cfg_pack = B.make_config(R, D, 16, 1, I_, packed=True)
+    pdev = {}
+    for name, (r_, c_) in {"gate_up": (2 * I_, D), "down": (D, I_)}.items():
+        pdev[name] = torch.empty_like(dev[name])
+        B.moe_pack_weights(cfg_pack, G, r_, c_, dev[name], pdev[name])
     off = torch.from_numpy(offsets.astype(np.int32)).cuda()
     ridx = torch.from_numpy(np.random.default_rng(1).permutation(R).astype(np.int32)).cuda()
     h0, o0 = _ffn(cfg_rows, G, I_, R, dev["x"], ridx, off, dev["gate_up"], dev["down"])
@@ -71,10 +75,57 @@ def test_packed_ffn_equals_rows(D, I_, rows):
     assert rel_err(to_np(o1), ref) <= 2e-2
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "keras", "fanout", "many_empty"])
+PACKED_SHAPES = {
+    "small": I.custom_shape("small_packed", 5, 256, 32, 2, 128, seed=31),
+    "xs_e208": I.custom_shape("xs_e208", 8200, 512, 208, 6, 128, seed=32),     # x-stationary, E > 128
+    "xs_e48": I.custom_shape("xs_e48", 8193, 1024, 48, 4, 256, seed=33),       # x-stationary 16x16, ragged
+}
+
+
+def packed_data(name):
+    if name in PACKED_SHAPES:
+        d = I.make_inputs(PACKED_SHAPES[name])
+        return d, B.to_device(d.store)
+    return data_of(name)
+
+
+@pytest.mark.parametrize("with_ws", [False, True], ids=["one_pass", "ws"])
+@pytest.mark.parametrize("name", ["decode", "keras_like", "prefill", "fanout", "xs_e208", "xs_e48"])
+def test_packed_router_equals_rows(name, with_ws):
+    # every router path (split over D, one pass, x-stationary 16x16 and 32x32) on packed W_r
+    if name == "keras_like":
+        d = I.make_inputs(I.custom_shape("keras_like", 512, 2048, 64, 4, 1408, seed=34))
+        dev = B.to_device(d.store)
+    else:
+        d, dev = packed_data(name)
+    s = d.shape
+    say(f"[packed router] {name} ws={with_ws}")
+    outs = []
+    for packed in (False, True):
+        cfg = B.config_for(s, packed=packed)
+        wr = dev["w_router"]
+        if packed:
+            wr = torch.empty_like(dev["w_router"])
+            B.moe_pack_weights(cfg, 1, s.n_experts, s.hidden, dev["w_router"], wr)
+        N, k, E = s.n_tokens, s.top_k, s.n_experts
+        w = torch.empty((N, k), dtype=torch.float32, device="cuda")
+        e = torch.empty((N, k), dtype=torch.int32, device="cuda")
+        lg = torch.empty((N, E), dtype=torch.float32, device="cuda")
+        ss = torch.empty((N,), dtype=torch.float32, device="cuda") if "w_shared_gate" in dev else None
+        B.moe_route(cfg, dev["x"], wr, dev.get("w_shared_gate"), lg, w, e, ss, B.alloc_workspace(cfg) if with_ws else None)
+        torch.cuda.synchronize()
+        outs.append((lg, w, e))
+    (l0, w0, e0), (l1, w1, e1) = outs
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+    assert torch.equal(e0, e1) and torch.equal(w0.view(torch.int32), w1.view(torch.int32))
+    _, probs, w_ref, e_ref = O.route(d.values("x"), d.values("w_router"), s.top_k, s.norm_topk_prob)
+    compare_routing(to_np(w1).astype(np.float64), to_np(e1), w_ref, e_ref, probs, s.top_k)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "fanout", "small", "xs_e208"])
 def test_packed_forward_equals_rows(name):
     say(f"[packed forward] {name}")
-    d, dev = data_of(name)
+    d, dev = packed_data(name)
     s = d.shape
     cfg_rows = B.config_for(s, "f32")
     cfg_pack = B.config_for(s, "f32", packed=True)
