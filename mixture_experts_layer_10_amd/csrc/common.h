@@ -88,6 +88,23 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return wave_reduce_f(v, [](float a, float b) { return a + b; });
 }
 
+// Exchange with lane ^ m inside each 16-lane row (m = 1, 2, 4, 8), in registers: m = 1, 2 are quad
+// permutes; m = 4, 8 take the row shifted left (lanes with bit m clear, their partner is above) or
+// right (bit set). Only in-row sources are ever selected.
+template <int M>
+__device__ __forceinline__ int xor16(int v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "row-local exchange");
+  if constexpr (M == 1) return MOE_DPP(v, kDppXor1);
+  else if constexpr (M == 2) return MOE_DPP(v, kDppXor2);
+  else {
+    const int up = MOE_DPP(v, 0x100 + M);      // row_shl:M  (lane i <- lane i + M)
+    const int dn = MOE_DPP(v, 0x110 + M);      // row_shr:M  (lane i <- lane i - M)
+    return (__lane_id() & M) ? dn : up;
+  }
+}
+template <int M>
+__device__ __forceinline__ float xor16f(float v) { return __int_as_float(xor16<M>(__float_as_int(v))); }
+
 // Wave-wide arg-max over (p, e) pairs: larger p wins, equal p goes to the lower e.
 __device__ __forceinline__ void argmax_step(float& p, int& e, float op, int oe) {
   if (op > p || (op == p && oe < e)) { p = op; e = oe; }

@@ -28,29 +28,45 @@ __global__ __launch_bounds__(kPermThreads) void perm_count_kernel(PermuteArgs a)
 }
 
 // Pass 2 (one workgroup of 512 threads, one expert per thread): counts, offsets, and each chunk's
-// starting row for each expert (written back over block_counts).
+// starting row for each expert (written back over block_counts). With at most kScanRegs chunks a
+// thread holds its expert's whole column in registers: one round of loads, one round of stores.
+constexpr int kScanRegs = 64;
+
+template <bool kInRegs>
 __global__ __launch_bounds__(512) void perm_scan_kernel(PermuteArgs a, int n_chunks) {
   __shared__ int s_wave[8];
   const int E = a.E, e = threadIdx.x, lane = e & 63, wave = e >> 6;
   int total = 0;
+  int c[kInRegs ? kScanRegs : 1];
   if (e < E) {
-    // eight chunk counts in flight at a time (each thread walks its own expert's column)
-    int b = 0;
-    for (; b + 8 <= n_chunks; b += 8) {
-      int c[8];
+    if constexpr (kInRegs) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = a.block_counts[static_cast<int64_t>(b + u) * E + e];
+      for (int b = 0; b < kScanRegs; ++b) c[b] = b < n_chunks ? a.block_counts[static_cast<int64_t>(b) * E + e] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        a.block_counts[static_cast<int64_t>(b + u) * E + e] = total;
-        total += c[u];
+      for (int b = 0; b < kScanRegs; ++b) {      // exclusive running sum down the column
+        const int v = c[b];
+        c[b] = total;
+        total += v;
       }
-    }
-    for (; b < n_chunks; ++b) {
-      int32_t* p = a.block_counts + static_cast<int64_t>(b) * E + e;
-      const int c = *p;
-      *p = total;
-      total += c;
+    } else {
+      // eight chunk counts in flight at a time (each thread walks its own expert's column)
+      int b = 0;
+      for (; b + 8 <= n_chunks; b += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = a.block_counts[static_cast<int64_t>(b + u) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          a.block_counts[static_cast<int64_t>(b + u) * E + e] = total;
+          total += v[u];
+        }
+      }
+      for (; b < n_chunks; ++b) {
+        int32_t* p = a.block_counts + static_cast<int64_t>(b) * E + e;
+        const int v = *p;
+        *p = total;
+        total += v;
+      }
     }
     a.counts[e] = total;
   }
@@ -68,8 +84,14 @@ __global__ __launch_bounds__(512) void perm_scan_kernel(PermuteArgs a, int n_chu
   const int excl = before + inc - total;
   if (e < E) {
     a.offsets[e] = excl;
+    if constexpr (kInRegs) {
+#pragma unroll
+      for (int b = 0; b < kScanRegs; ++b)
+        if (b < n_chunks) a.block_counts[static_cast<int64_t>(b) * E + e] = c[b] + excl;
+    } else {
 #pragma unroll 8
-    for (int b = 0; b < n_chunks; ++b) a.block_counts[static_cast<int64_t>(b) * E + e] += excl;
+      for (int b = 0; b < n_chunks; ++b) a.block_counts[static_cast<int64_t>(b) * E + e] += excl;
+    }
   }
   if (e == 0) a.offsets[E] = static_cast<int32_t>(a.A);
 }
@@ -197,7 +219,10 @@ void launch_permute(const PermuteArgs& a, hipStream_t st) {
     return;
   }
   if (n_chunks > 0) perm_count_kernel<<<n_chunks, kPermThreads, 0, st>>>(a);
-  perm_scan_kernel<<<1, 512, 0, st>>>(a, n_chunks);
+  if (n_chunks <= kScanRegs)
+    perm_scan_kernel<true><<<1, 512, 0, st>>>(a, n_chunks);
+  else
+    perm_scan_kernel<false><<<1, 512, 0, st>>>(a, n_chunks);
   if (n_chunks > 0) perm_scatter_kernel<<<n_chunks, kPermThreads, 0, st>>>(a, nbits);
 }
 

@@ -17,6 +17,8 @@
 // of pairwise merges of sorted lists. Otherwise each wave walks its tokens; a lane holds experts
 // lane, lane+64, ...; k rounds of a wave-wide (p, index) arg-max. Either way ties go to the lower
 // index.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -145,16 +147,20 @@ __device__ void route_select16(const RouteArgs& a, const float* s_logit, int col
       p[i] = (valid && e[i] < E) ? s_logit[t * cols + e[i]] : -INFINITY;
       m = fmaxf(m, p[i]);
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    m = fmaxf(m, xor16f<1>(m));
+    m = fmaxf(m, xor16f<2>(m));
+    m = fmaxf(m, xor16f<4>(m));
+    m = fmaxf(m, xor16f<8>(m));
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       p[i] = e[i] < E ? expf(p[i] - m) : 0.f;
       sum += p[i];
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 16);   // commutative pairs: same in every lane
+    sum += xor16f<1>(sum);                                          // commutative pairs: same in every lane
+    sum += xor16f<2>(sum);
+    sum += xor16f<4>(sum);
+    sum += xor16f<8>(sum);
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = e[i] < E ? p[i] / sum : -1.f;  // -1: never selected
     // sort the lane's eight: bitonic sort (sizes 2, 4, 8)
@@ -171,20 +177,24 @@ __device__ void route_select16(const RouteArgs& a, const float* s_logit, int col
           }
         }
     // merge with the partner lists
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
+    auto merge = [&](auto mc) {
+      constexpr int M = decltype(mc)::value;
       float q[8];
       int f[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        q[i] = __shfl_xor(p[i], o, 16);
-        f[i] = __shfl_xor(e[i], o, 16);
+        q[i] = xor16f<M>(p[i]);
+        f[i] = xor16<M>(e[i]);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (sel_better(q[7 - i], f[7 - i], p[i], e[i])) { p[i] = q[7 - i]; e[i] = f[7 - i]; }
       sel_bitonic_merge8(p, e);
-    }
+    };
+    merge(std::integral_constant<int, 1>{});
+    merge(std::integral_constant<int, 2>{});
+    merge(std::integral_constant<int, 4>{});
+    merge(std::integral_constant<int, 8>{});
     float kept = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r)
@@ -217,8 +227,10 @@ __device__ void route_select16(const RouteArgs& a, const float* s_logit, int col
           for (int d = j; d < D; d += 16) z = fmaf(xr[d], ws[d], z);
         }
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 16);
+      z += xor16f<1>(z);
+      z += xor16f<2>(z);
+      z += xor16f<4>(z);
+      z += xor16f<8>(z);
       if (valid && j == 0) a.shared_scale[n0 + t] = 1.f / (1.f + expf(-z));
     }
   }
