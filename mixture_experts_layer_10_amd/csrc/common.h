@@ -17,16 +17,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bfloat16 bits, round to nearest, ties to even. NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16 bits, round to nearest, ties to even (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -124,7 +122,9 @@ __device__ __forceinline__ void wave_argmax_dpp(float& p, int& e) {
   e = be;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// z * sigmoid(z) with the hardware exp and reciprocal (each within a couple of ulp of fp32; the
+// result is rounded to bf16 right after, or accumulated in fp32 for fp32 layers).
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's 16 bytes land
 // at lds_dst + 16 l, so one instruction fills 1 KB of LDS contiguously; lds_dst must be uniform.
