@@ -64,6 +64,35 @@ def measured_traffic(kernel):
     return None
 
 
+def time_router_stats(B, chain, cfg, dev, steps):
+    """Router load statistics and balance loss (moe_router_stats) on this workload's logits: the
+    logits come from one moe_route call outside the timing; `steps` timed calls follow."""
+    import torch
+    N, E, k = cfg.n_tokens, cfg.n_experts, cfg.top_k
+    lg = torch.empty((N, E), dtype=torch.float32, device="cuda")
+    w = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    e = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    ss = torch.empty((N,), dtype=torch.float32, device="cuda") if chain.gated else None
+    B.moe_route(cfg, dev["x"], dev["w_router"], dev.get("w_shared_gate") if chain.gated else None, lg, w, e, ss, chain.ws)
+    f = torch.empty(E, dtype=torch.float32, device="cuda")
+    P = torch.empty(E, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    run = lambda: B.moe_router_stats(cfg, lg, chain.counts, f, P, loss, chain.ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # each call is two short kernels, quicker than their host-side submission: a bounded GPU sleep
+    # first lets the host queue every call, so the events time the GPU work back to back
+    torch.cuda._sleep(20_000_000)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    return dict(us=round(us, 2), logits_gbs=round(N * E * 4 / (us * 1e-6) / 1e9, 1), loss=round(float(loss.item()), 6))
+
+
 def run_workload(name, steps, warmup, out_dtype, inner_events=True):
     """Times `steps` whole-path steps. With inner_events the gate_up launch of every timed step is
     bracketed by events on its stream (its duration comes from the timed region itself); without,
@@ -113,10 +142,11 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True):
         torch.cuda.synchronize()
     gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     ms_per_step = wall * 1e3 / steps
+    stats = time_router_stats(B, chain, cfg, dev, steps)
     alg = algorithmic(shape, touched)
     log(f"[bench] {name}: {ms_per_step:.3f} ms/step (gpu {gpu_ms / steps:.3f}), gate_up {gate_up_ms:.3f} ms, "
         f"touched {touched}/{shape.n_experts}")
-    return dict(shape=shape, data=data, cfg=cfg, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
+    return dict(shape=shape, data=data, cfg=cfg, stats=stats, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
                 gate_up_ms=gate_up_ms, touched=touched, counts=counts, alg=alg,
                 tokens_per_s=shape.n_tokens / (ms_per_step / 1e3))
 
@@ -215,6 +245,7 @@ def main():
                   "experts_touched": main_run["touched"], "max_rows_per_expert": int(main_run["counts"].max()),
                   "min_rows_per_expert": int(main_run["counts"].min())},
         "roofline": roof,
+        "router_stats": main_run["stats"],
     }
     if not args.no_decode and args.workload != "decode":
         dec = run_workload("decode", max(args.steps, 50), args.warmup, args.out_dtype, inner_events=False)

@@ -81,7 +81,7 @@ const char* moe_status_string(int status);
 const char* moe_last_error(void);
 
 /* Bytes of device workspace moe_forward needs for this configuration (also enough for
- * moe_permute). Host only; no GPU needed. Returns MOE_ERR_INVALID_ARG/UNSUPPORTED for a bad
+ * moe_permute and moe_router_stats). Host only; no GPU needed. Returns MOE_ERR_INVALID_ARG/UNSUPPORTED for a bad
  * configuration, else writes *bytes. */
 int moe_workspace_bytes(const moe_config* cfg, size_t* bytes);
 
@@ -150,6 +150,20 @@ int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64
  * cfg gives dtype (must be bf16); its other fields are not used. */
 int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src,
                      void* dst, void* stream);
+
+/* Router load statistics and the Switch-style balance loss ("Qwen3-VL + MoE: train to deploy",
+ * section "An auxiliary balance loss", its N read as the number of experts):
+ *   f[e] = counts[e] / (N k)                        fraction of the assignments routed to e
+ *   P[e] = (1/N) sum_n softmax(logits[n])[e]         mean router probability (fp32 softmax)
+ *   loss = E * sum_e f[e] P[e]                        1 for perfectly even routing; the caller
+ *                                                     applies its coefficient
+ *   logits [N, E] fp32 (moe_route's optional output), counts [E] int32 (moe_permute's)
+ *   f [E], P [E], loss [1] fp32 on device
+ *   ws, ws_bytes: workspace of at least moe_workspace_bytes(cfg) bytes
+ * Per-block partial sums in token order, then fixed-order fp64 sums: deterministic.
+ * N = 0 writes zeros. */
+int moe_router_stats(const moe_config* cfg, const float* logits, const int32_t* counts, float* f, float* P,
+                     float* loss, void* ws, size_t ws_bytes, void* stream);
 
 /* Weighted unpermute ("27. Mixture of experts", section "Dispatch", grouped step 4, and the
  * shared-expert equation): y[n] = sum_{j<k} w[n,j] * out_perm[slot_pos[n*k+j]]

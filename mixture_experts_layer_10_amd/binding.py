@@ -23,8 +23,8 @@ MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED = 0, 1
 
 # Every symbol include/moe.h declares.
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
-            "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_pack_weights", "moe_combine",
-            "moe_forward"]
+            "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_pack_weights", "moe_router_stats",
+            "moe_combine", "moe_forward"]
 
 
 class MoeError(RuntimeError):
@@ -88,6 +88,7 @@ def load(path: str = LIB_PATH):
         "moe_expert_down": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
         "moe_expert_ffn": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_pack_weights": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P]),
+        "moe_router_stats": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
         "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     }
@@ -177,6 +178,11 @@ def moe_expert_ffn(cfg, n_groups, inter, max_rows, x, row_index, offsets, gate_u
 def moe_pack_weights(cfg, n_groups, rows, cols, src, dst, stream=None):
     _check("moe_pack_weights", load().moe_pack_weights(ctypes.byref(cfg), n_groups, rows, cols, _ptr(src), _ptr(dst),
                                                        _stream(stream)))
+
+
+def moe_router_stats(cfg, logits, counts, f, P, loss, ws, ws_bytes=None, stream=None):
+    _check("moe_router_stats", load().moe_router_stats(ctypes.byref(cfg), _ptr(logits), _ptr(counts), _ptr(f), _ptr(P),
+                                                       _ptr(loss), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
 
 
 def moe_combine(cfg, out_perm, weights, slot_pos, shared_out, shared_scale, y, stream=None):

@@ -77,6 +77,11 @@ struct CombineArgs {
 };
 void launch_combine(const CombineArgs& a, hipStream_t st);
 
+// Router load statistics (f, P, balance loss); partial: stats_blocks(N) x E fp32 scratch.
+int64_t stats_blocks(int64_t N);
+void launch_stats(const float* logits, const int32_t* counts, float* f, float* P, float* loss, float* partial,
+                  int64_t N, int E, int k, hipStream_t st);
+
 int device_cu_count();
 
 }  // namespace moe

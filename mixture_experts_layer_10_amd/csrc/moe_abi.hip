@@ -130,6 +130,10 @@ static Layout layout_of(const moe_config* c) {
   return L;
 }
 
+static size_t stats_ws_bytes(const moe_config* c) {
+  return static_cast<size_t>(stats_blocks(c->n_tokens)) * static_cast<size_t>(c->n_experts) * 4;
+}
+
 static size_t permute_ws_bytes(const moe_config* c) {
   const size_t A = static_cast<size_t>(c->n_tokens) * static_cast<size_t>(c->top_k);
   return static_cast<size_t>(permute_chunks(static_cast<int64_t>(A))) * static_cast<size_t>(c->n_experts) * 4;
@@ -254,7 +258,7 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 int moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
   MOE_TRY(validate_config(cfg));
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = layout_of(cfg).total;
+  *bytes = std::max(layout_of(cfg).total, stats_ws_bytes(cfg));
   return ok();
 }
 
@@ -352,6 +356,21 @@ int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int6
   launch_pack(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), n_groups, static_cast<int>(rows),
               static_cast<int>(cols), static_cast<hipStream_t>(stream));
   MOE_TRY(check_launch("moe_pack_weights"));
+  return ok();
+}
+
+int moe_router_stats(const moe_config* cfg, const float* logits, const int32_t* counts, float* f, float* P,
+                     float* loss, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (!f || !P || !loss) return fail(MOE_ERR_INVALID_ARG, "f, P or loss is NULL");
+  const int64_t N = cfg->n_tokens;
+  if (N > 0 && (!logits || !counts)) return fail(MOE_ERR_INVALID_ARG, "logits or counts is NULL");
+  const size_t need = stats_ws_bytes(cfg);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0, need);
+  launch_stats(logits, counts, f, P, loss, static_cast<float*>(ws), N, static_cast<int>(cfg->n_experts),
+               static_cast<int>(cfg->top_k), static_cast<hipStream_t>(stream));
+  MOE_TRY(check_launch("moe_router_stats"));
   return ok();
 }
 

@@ -28,7 +28,7 @@ def header_functions():
 
 def test_header_symbols_all_exported(lib):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -113,6 +113,20 @@ def test_pack_refuses_before_launch(lib):
             B.moe_pack_weights(a["cfg"], a["n_groups"], a["rows"], a["cols"], a["src"], a["dst"], stream=0)
         assert ei.value.status == status, (kw, str(ei.value))
     B.moe_pack_weights(c, 0, 32, 64, None, None, stream=0)       # nothing to pack: no-op
+
+
+def test_router_stats_refuses_before_launch(lib):
+    c = B.make_config(300, 128, 8, 2, 64)
+    with pytest.raises(B.MoeError) as ei:                       # no place for the outputs
+        B.moe_router_stats(c, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoeError) as ei:                       # tokens but no logits
+        B.moe_router_stats(c, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoeError) as ei:                       # 2 blocks x 8 experts x 4 B needed
+        B.moe_router_stats(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, stream=0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
+    assert B.moe_workspace_bytes(c) >= 2 * 8 * 4
 
 
 def test_null_config_and_null_out(lib):
