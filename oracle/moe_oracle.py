@@ -260,3 +260,67 @@ def switch_aux_loss(probs, experts, n_experts):
     f = counts / counts.sum()
     P = probs.mean(axis=0)
     return float(n_experts * np.sum(f * P)), f, P
+
+
+# --------------------------------------------------------------------------------------------
+# Routing variants: [VL-post] "Capacity limits" and "Balancing without a loss"; [MoE-ch27] "The
+# router", the note on other routers (a sigmoid score per expert with a learned bias).
+# --------------------------------------------------------------------------------------------
+
+def route_sigmoid_bias(x, w_router, k, bias=None, norm_topk_prob=True):
+    """Sigmoid-score router. scores = sigmoid(logits) in float32; the k experts with the largest
+    scores + bias are picked (descending, equal keys to the lower index); the bias only picks and
+    never enters the weights ([VL-post] "Balancing without a loss"), so the weights are the picked
+    scores, divided by their sum when norm_topk_prob (the same flag as the softmax router).
+    Returns (logits f64, scores f32, keys f32, weights, experts)."""
+    logits = router_logits(x, w_router)
+    lg = logits.astype(np.float32)
+    one = np.float32(1.0)
+    scores = (one / (one + np.exp(-lg))).astype(np.float32)
+    b = np.zeros(scores.shape[-1], np.float32) if bias is None else np.asarray(bias, np.float32)
+    keys = (scores + b).astype(np.float32)
+    experts = np.argsort(-keys, axis=-1, kind="stable")[..., :k].astype(np.int64)
+    weights = np.take_along_axis(scores, experts, axis=-1)
+    if norm_topk_prob:
+        weights = weights / weights.sum(axis=-1, keepdims=True)
+    return logits, scores, keys, weights, experts
+
+
+def capacity_keep(experts, n_experts, capacity):
+    """Capacity limit ([VL-post] "Capacity limits"): every expert has `capacity` slots per batch;
+    the assignments a = n*k + j claim them in assignment order and those that overflow are dropped
+    (their token passes through the block unchanged: the dropped pair contributes nothing).
+    Returns keep[N, k] (bool). A plain loop over the assignments."""
+    experts = np.asarray(experts)
+    flat = experts.reshape(-1)
+    keep = np.zeros(flat.size, bool)
+    used = np.zeros(n_experts, np.int64)
+    for a, e in enumerate(flat):
+        if used[e] < capacity:
+            keep[a] = True
+            used[e] += 1
+    return keep.reshape(experts.shape)
+
+
+def forward_capacity(x, weights, experts, gate_up, down, keep):
+    """y[n] = sum_j keep[n,j] * w[n,j] * expert_{e[n,j]}(x[n]) for a given routing and keep mask
+    ([MoE-ch27] "The router" equation with [VL-post] "Capacity limits"), expert by expert."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(weights, np.float64)
+    experts = np.asarray(experts)
+    y = np.zeros((x.shape[0], np.asarray(down[0]).shape[0]))
+    for e in range(len(gate_up)):
+        n_idx, j_idx = np.nonzero((experts == e) & keep)
+        if n_idx.size:          # a token picks an expert at most once, so n_idx has no repeats
+            y[n_idx] += w[n_idx, j_idx, None] * swiglu(x[n_idx], gate_up[e], down[e])
+    return y
+
+
+def bias_update(bias, counts, n_tokens, top_k, gamma):
+    """One step of the selection-bias nudge ([VL-post] "Balancing without a loss": overloaded
+    experts get their bias lowered slightly, idle ones raised): b_e - gamma * sign(c_e - N k / E),
+    in float32; an expert exactly at the mean load keeps its bias."""
+    counts = np.asarray(counts, np.float64)
+    mean = n_tokens * top_k / counts.size
+    step = np.float32(gamma) * np.sign(counts - mean).astype(np.float32)
+    return (np.asarray(bias, np.float32) - step).astype(np.float32)

@@ -12,6 +12,7 @@ import pytest
 import scipy.special
 
 import oracle as O
+from mixture_experts_layer_10_amd import inputs as I
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -307,3 +308,77 @@ def test_k_gap():
     assert O.k_gap(p, 2)[0] == pytest.approx(0.2)
     assert O.k_gap(p, 3)[0] == 0.0
     assert O.k_gap(p, 4)[0] == np.inf
+
+
+# ---- routing variants ([VL-post] "Capacity limits", "Balancing without a loss";
+#      [MoE-ch27] "The router", the note on sigmoid routers) ----
+
+def test_sigmoid_zero_bias_picks_what_softmax_picks():
+    # both scores are increasing functions of the logit, so without a bias the picks agree
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((200, 32))
+    w = rng.standard_normal((24, 32)) * 0.3
+    _, probs, _, e_soft = O.route(x, w, 5)
+    _, _, keys, _, e_sig = O.route_sigmoid_bias(x, w, 5)
+    clear = (O.k_gap(probs, 5) > 1e-5) & (O.k_gap(keys, 5) > 1e-5)
+    assert clear.sum() > 150
+    assert np.array_equal(e_soft[clear], e_sig[clear])
+
+
+def test_sigmoid_bias_picks_but_does_not_weigh():
+    # logits 0, 1, 2, 3 (x = I, W_r = logits as a column): scores sigmoid(l)
+    x = np.eye(1)
+    w = np.array([[0.0], [1.0], [2.0], [3.0]])
+    _, scores, _, wts, e = O.route_sigmoid_bias(x, w, 2, norm_topk_prob=False)
+    assert list(e[0]) == [3, 2]
+    _, _, _, wts, e = O.route_sigmoid_bias(x, w, 2, bias=[5.0, 0, 0, 0], norm_topk_prob=False)
+    assert list(e[0]) == [0, 3]                               # the bias pulled expert 0 in
+    assert wts[0, 0] == np.float32(0.5)                       # sigmoid(0), no bias in the weight
+    assert abs(wts[0, 1] - 1.0 / (1.0 + np.exp(-3.0))) < 1e-7
+    # equal keys go to the lower index
+    _, _, _, _, e = O.route_sigmoid_bias(np.eye(1), np.zeros((4, 1)), 2, bias=[0, 1, 1, 0])
+    assert list(e[0]) == [1, 2]
+
+
+def test_sigmoid_k_equals_e_renormalised():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((5, 8))
+    w = rng.standard_normal((6, 8))
+    _, scores, _, wts, e = O.route_sigmoid_bias(x, w, 6, bias=rng.standard_normal(6))
+    full = np.take_along_axis(scores, e, axis=-1).astype(np.float64)
+    assert np.allclose(wts, full / full.sum(-1, keepdims=True), rtol=1e-6)
+    assert np.allclose(wts.sum(-1), 1.0, atol=6 * 2.0 ** -24)
+
+
+def test_capacity_keep_by_hand():
+    experts = np.array([[0, 1], [0, 2], [0, 1], [3, 0]])
+    keep = O.capacity_keep(experts, 4, 2)
+    # expert 0 is claimed by assignments 0, 2, 4, 7: the first two keep their slot
+    assert keep.tolist() == [[True, True], [True, True], [False, True], [True, False]]
+    assert O.capacity_keep(experts, 4, 0).sum() == 0
+    assert O.capacity_keep(experts, 4, 4).all()
+
+
+def test_forward_capacity_limits():
+    d = I.make_inputs(I.WORKLOADS["tiny"])
+    s = d.shape
+    x = d.values("x")
+    gu, dn = d.values("gate_up"), d.values("down")
+    _, _, w, e = O.route(x, d.values("w_router"), s.top_k, s.norm_topk_prob)
+    y_full, _ = O.forward_grouped(x, d.values("w_router"), gu, dn, s.top_k, s.norm_topk_prob)
+    roomy = O.capacity_keep(e, s.n_experts, s.n_tokens * s.top_k)
+    assert np.allclose(O.forward_capacity(x, w, e, gu, dn, roomy), y_full, rtol=1e-12, atol=1e-12)
+    assert not O.forward_capacity(x, w, e, gu, dn, O.capacity_keep(e, s.n_experts, 0)).any()
+    # dropping one pair removes exactly that expert's weighted output from its token
+    keep = roomy.copy()
+    keep[3, 1] = False
+    diff = y_full - O.forward_capacity(x, w, e, gu, dn, keep)
+    only = O.swiglu(x[3:4], gu[e[3, 1]], dn[e[3, 1]])[0] * w[3, 1]
+    assert np.allclose(diff[3], only, rtol=1e-10, atol=1e-12)
+    assert np.allclose(np.delete(diff, 3, axis=0), 0.0, atol=1e-12)
+
+
+def test_bias_update_sign_rule():
+    b = O.bias_update([0.5, 0.5, 0.5, 0.5], [10, 2, 4, 0], n_tokens=8, top_k=2, gamma=0.25)
+    assert b.tolist() == [0.25, 0.75, 0.5, 0.75]              # mean load 16 / 4 = 4
+
