@@ -77,20 +77,45 @@ def time_router_stats(B, chain, cfg, dev, steps):
     f = torch.empty(E, dtype=torch.float32, device="cuda")
     P = torch.empty(E, dtype=torch.float32, device="cuda")
     loss = torch.empty(1, dtype=torch.float32, device="cuda")
-    run = lambda: B.moe_router_stats(cfg, lg, chain.counts, f, P, loss, chain.ws)
+    us = gpu_time_us(lambda: B.moe_router_stats(cfg, lg, chain.counts, f, P, loss, chain.ws), steps)
+    return dict(us=round(us, 2), logits_gbs=round(N * E * 4 / (us * 1e-6) / 1e9, 1), loss=round(float(loss.item()), 6))
+
+
+def gpu_time_us(run, steps):
+    """GPU time per call of `run` (short kernels): a bounded GPU sleep first lets the host queue
+    every call, so the events time the GPU work back to back."""
+    import torch
     run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # each call is two short kernels, quicker than their host-side submission: a bounded GPU sleep
-    # first lets the host queue every call, so the events time the GPU work back to back
     torch.cuda._sleep(20_000_000)
     e0.record()
     for _ in range(steps):
         run()
     e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
-    return dict(us=round(us, 2), logits_gbs=round(N * E * 4 / (us * 1e-6) / 1e9, 1), loss=round(float(loss.item()), 6))
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def time_variants(B, chain, cfg, dev, steps):
+    """Routing variants on this workload: the sigmoid-score router with a selection bias, and the
+    capacity-limited permute at 1.25 x the mean load per expert (with the share it drops)."""
+    import torch
+    N, E, k = cfg.n_tokens, cfg.n_experts, cfg.top_k
+    bias = torch.from_numpy(np.random.default_rng(7).normal(0.0, 0.05, E).astype(np.float32)).cuda()
+    w = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    e = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    sig_us = gpu_time_us(lambda: B.moe_route_sigmoid(cfg, dev["x"], dev["w_router"], bias, None, w, e, chain.ws), steps)
+    cap = max(1, int(1.25 * N * k / E))
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    token_of = torch.empty(N * k, dtype=torch.int32, device="cuda")
+    slot_pos = torch.empty(N * k, dtype=torch.int32, device="cuda")
+    run = lambda: B.moe_permute_capped(cfg, cap, chain.experts, None, counts, offsets, token_of, slot_pos, None, chain.ws)
+    cap_us = gpu_time_us(run, steps)
+    kept = int(offsets[E].item())
+    return dict(sigmoid_route_us=round(sig_us, 2), capped_permute_us=round(cap_us, 2), capacity=cap,
+                dropped_share=round(1.0 - kept / (N * k), 4))
 
 
 def run_workload(name, steps, warmup, out_dtype, inner_events=True):
@@ -143,10 +168,11 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True):
     gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     ms_per_step = wall * 1e3 / steps
     stats = time_router_stats(B, chain, cfg, dev, steps)
+    variants = time_variants(B, chain, cfg, dev, steps)
     alg = algorithmic(shape, touched)
     log(f"[bench] {name}: {ms_per_step:.3f} ms/step (gpu {gpu_ms / steps:.3f}), gate_up {gate_up_ms:.3f} ms, "
         f"touched {touched}/{shape.n_experts}")
-    return dict(shape=shape, data=data, cfg=cfg, stats=stats, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
+    return dict(shape=shape, data=data, cfg=cfg, stats=stats, variants=variants, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
                 gate_up_ms=gate_up_ms, touched=touched, counts=counts, alg=alg,
                 tokens_per_s=shape.n_tokens / (ms_per_step / 1e3))
 
@@ -246,6 +272,7 @@ def main():
                   "min_rows_per_expert": int(main_run["counts"].min())},
         "roofline": roof,
         "router_stats": main_run["stats"],
+        "routing_variants": main_run["variants"],
     }
     if not args.no_decode and args.workload != "decode":
         dec = run_workload("decode", max(args.steps, 50), args.warmup, args.out_dtype, inner_events=False)

@@ -102,6 +102,20 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
               float* logits, float* weights, int32_t* experts, float* shared_scale, void* ws, size_t ws_bytes,
               void* stream);
 
+/* Sigmoid-score router ("27. Mixture of experts", section "The router", the note on other routers;
+ * "Qwen3-VL + MoE: train to deploy", section "Balancing without a loss"): logits as moe_route
+ * (fp32, never rounded), s = sigmoid(logits) in fp32, the k experts with the largest s + bias
+ * (descending, equal keys to the lower index); the bias only picks, so
+ * weights = s of the picked experts, divided by their sum when norm_topk_prob.
+ *   bias [E] fp32 on device, or NULL (zeros); other arguments as moe_route (no shared gate). */
+int moe_route_sigmoid(const moe_config* cfg, const void* x, const void* w_router, const float* bias, float* logits,
+                      float* weights, int32_t* experts, void* ws, size_t ws_bytes, void* stream);
+
+/* Selection-bias nudge after a step ("Qwen3-VL + MoE: train to deploy", section "Balancing without
+ * a loss"): bias[e] -= gamma * sign(counts[e] - N k / E), in place, gamma >= 0. counts [E] int32
+ * (e.g. moe_permute's), bias [E] fp32, both on device. */
+int moe_router_bias_update(const moe_config* cfg, const int32_t* counts, float* bias, float gamma, void* stream);
+
 /* Grouping by expert: the N*k assignments a = n*k + j are sorted by expert id, stably (ties keep
  * assignment order), with no atomics on ranks, so the result is deterministic ("27. Mixture of
  * experts", section "Dispatch", grouped dispatch steps 1-2; stretch exercise 2 for the row-offset
@@ -115,6 +129,15 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
 int moe_permute(const moe_config* cfg, const int32_t* experts, const void* x, int32_t* counts,
                 int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* moe_permute with a capacity limit ("Qwen3-VL + MoE: train to deploy", section "Capacity limits"):
+ * each expert keeps its first `capacity` (>= 0) assignments in assignment order a = n*k + j; the
+ * rest are dropped (their token passes through unchanged). counts/offsets cover the kept rows
+ * (offsets[E] = rows kept), token_of and x_perm hold the kept rows only, and slot_pos[a] = -1 for
+ * a dropped assignment, which moe_combine then skips. */
+int moe_permute_capped(const moe_config* cfg, int64_t capacity, const int32_t* experts, const void* x,
+                       int32_t* counts, int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* Grouped SwiGLU experts ("27. Mixture of experts", section "Dispatch", Experts.expert and grouped
  * step 3: one launch runs every group's matmuls on its contiguous rows). For group g and each
@@ -170,7 +193,7 @@ int moe_router_stats(const moe_config* cfg, const float* logits, const int32_t* 
  *                                  (+ shared_scale[n] * shared_out[n]),
  * summed in fp32 in slot order j = 0..k-1, then the shared term, rounded once to out_dtype.
  * A gather per token (no atomics): deterministic.
- *   out_perm [N*k, D] fp32, weights [N, k] fp32, slot_pos [N*k] int32
+ *   out_perm [N*k, D] fp32, weights [N, k] fp32, slot_pos [N*k] int32 (-1: a dropped pair, skipped)
  *   shared_out [N, D] fp32 or NULL; shared_scale [N] fp32 or NULL (NULL with shared_out: scale 1)
  *   y [N, D] (out_dtype) */
 int moe_combine(const moe_config* cfg, const float* out_perm, const float* weights,

@@ -24,7 +24,7 @@ MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED = 0, 1
 # Every symbol include/moe.h declares.
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_pack_weights", "moe_router_stats",
-            "moe_combine", "moe_forward"]
+            "moe_combine", "moe_forward", "moe_route_sigmoid", "moe_router_bias_update", "moe_permute_capped"]
 
 
 class MoeError(RuntimeError):
@@ -89,6 +89,9 @@ def load(path: str = LIB_PATH):
         "moe_expert_ffn": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_pack_weights": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P]),
         "moe_router_stats": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "moe_route_sigmoid": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "moe_router_bias_update": (ctypes.c_int, [_CFG, _P, _P, ctypes.c_float, _P]),
+        "moe_permute_capped": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
         "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     }
@@ -178,6 +181,25 @@ def moe_expert_ffn(cfg, n_groups, inter, max_rows, x, row_index, offsets, gate_u
 def moe_pack_weights(cfg, n_groups, rows, cols, src, dst, stream=None):
     _check("moe_pack_weights", load().moe_pack_weights(ctypes.byref(cfg), n_groups, rows, cols, _ptr(src), _ptr(dst),
                                                        _stream(stream)))
+
+
+def moe_route_sigmoid(cfg, x, w_router, bias, logits, weights, experts, ws=None, ws_bytes=None, stream=None):
+    _check("moe_route_sigmoid", load().moe_route_sigmoid(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias),
+                                                         _ptr(logits), _ptr(weights), _ptr(experts), _ptr(ws),
+                                                         _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_router_bias_update(cfg, counts, bias, gamma, stream=None):
+    _check("moe_router_bias_update", load().moe_router_bias_update(ctypes.byref(cfg), _ptr(counts), _ptr(bias),
+                                                                   float(gamma), _stream(stream)))
+
+
+def moe_permute_capped(cfg, capacity, experts, x, counts, offsets, token_of, slot_pos, x_perm, ws, ws_bytes=None,
+                       stream=None):
+    _check("moe_permute_capped", load().moe_permute_capped(ctypes.byref(cfg), int(capacity), _ptr(experts), _ptr(x),
+                                                           _ptr(counts), _ptr(offsets), _ptr(token_of), _ptr(slot_pos),
+                                                           _ptr(x_perm), _ptr(ws), _nbytes(ws, ws_bytes),
+                                                           _stream(stream)))
 
 
 def moe_router_stats(cfg, logits, counts, f, P, loss, ws, ws_bytes=None, stream=None):

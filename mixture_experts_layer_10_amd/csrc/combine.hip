@@ -8,7 +8,8 @@
 namespace moe {
 
 // One workgroup per token: its k weights and slot rows go to LDS once, then each thread sums 4
-// consecutive columns over the k rows, eight rows' loads in flight at a time.
+// consecutive columns over the k rows, eight rows' loads in flight at a time. A pair dropped by a
+// capacity limit (slot_pos -1) contributes nothing: its row is not read and adds zero.
 template <bool kOutBf16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   __shared__ float s_w[512];
@@ -16,8 +17,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t n = blockIdx.x;
   const int D4 = a.D / 4, k = a.k, tid = threadIdx.x;
   for (int j = tid; j < k; j += 256) {
-    s_w[j] = a.weights[n * k + j];
-    s_p[j] = a.slot_pos[n * k + j];
+    const int p = a.slot_pos[n * k + j];
+    s_w[j] = p >= 0 ? a.weights[n * k + j] : 0.f;
+    s_p[j] = p;
   }
   __syncthreads();
   const f32x4* o = reinterpret_cast<const f32x4*>(a.out_perm);
@@ -28,7 +30,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (; j + 8 <= k; j += 8) {
       f32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&o[static_cast<int64_t>(s_p[j + u]) * D4 + c]);
+      for (int u = 0; u < 8; ++u)
+        v[u] = s_p[j + u] >= 0 ? __builtin_nontemporal_load(&o[static_cast<int64_t>(s_p[j + u]) * D4 + c]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float w = s_w[j + u];
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
     }
     for (; j < k; ++j) {
-      const f32x4 v = __builtin_nontemporal_load(&o[static_cast<int64_t>(s_p[j]) * D4 + c]);
+      const f32x4 v = s_p[j] >= 0 ? __builtin_nontemporal_load(&o[static_cast<int64_t>(s_p[j]) * D4 + c]) : f32x4{0.f, 0.f, 0.f, 0.f};
       const float w = s_w[j];
       acc[0] = fmaf(w, v[0], acc[0]);
       acc[1] = fmaf(w, v[1], acc[1]);

@@ -19,6 +19,8 @@ struct RouteArgs {
   int norm;
   bool bf16;
   bool packed;                // w_router in the packed layout ([1, E, D] stack, E % 16 == 0)
+  bool sigmoid;               // scores sigmoid(logit) picked by score + bias (else fp32 softmax)
+  const float* bias;          // [E] selection bias for sigmoid scores, or null (zeros)
 };
 constexpr int kMaxRouteSlices = 16;
 int route_slices_for(int64_t N, int D, int E, bool bf16);   // slices used when scratch is given
@@ -33,15 +35,16 @@ struct PermuteArgs {
   int32_t* counts;          // [E]
   int32_t* offsets;         // [E + 1]
   int32_t* token_of;        // [A]
-  int32_t* slot_pos;        // [A]
+  int32_t* slot_pos;        // [A]; -1 for an assignment dropped by the capacity limit
   int64_t A;
   int E, k;
+  int64_t capacity;         // rows kept per expert (>= A: no limit)
 };
 void launch_permute(const PermuteArgs& a, hipStream_t st);
 int64_t permute_chunks(int64_t A);
 
-// x_perm[p] = x[token_of[p]] for p < rows (row_bytes % 16 == 0).
-void launch_gather_rows(const void* x, const int32_t* token_of, void* x_perm, int64_t rows,
+// x_perm[p] = x[token_of[p]] for p < min(rows, *n_valid) (row_bytes % 16 == 0; n_valid on device).
+void launch_gather_rows(const void* x, const int32_t* token_of, const int32_t* n_valid, void* x_perm, int64_t rows,
                         int64_t row_bytes, hipStream_t st);
 
 struct GemmArgs {
@@ -81,6 +84,9 @@ void launch_combine(const CombineArgs& a, hipStream_t st);
 int64_t stats_blocks(int64_t N);
 void launch_stats(const float* logits, const int32_t* counts, float* f, float* P, float* loss, float* partial,
                   int64_t N, int E, int k, hipStream_t st);
+
+// Selection-bias nudge: bias[e] -= gamma * sign(counts[e] - A / E).
+void launch_bias_update(const int32_t* counts, float* bias, float gamma, int64_t A, int E, hipStream_t st);
 
 int device_cu_count();
 

@@ -147,8 +147,10 @@ static size_t permute_ws_bytes(const moe_config* c) {
 
 static int route_impl(const moe_config* c, const void* x, const void* w_router, const void* w_shared_gate,
                       float* logits, float* weights, int32_t* experts, float* shared_scale, float* partial,
-                      hipStream_t st) {
+                      hipStream_t st, bool sigmoid = false, const float* bias = nullptr) {
   RouteArgs a{};
+  a.sigmoid = sigmoid;
+  a.bias = bias;
   a.partial = partial;
   a.x = x;
   a.w_router = w_router;
@@ -170,8 +172,9 @@ static int route_impl(const moe_config* c, const void* x, const void* w_router, 
 
 static int permute_impl(const moe_config* c, const int32_t* experts, const void* x, int32_t* counts,
                         int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, int32_t* block_counts,
-                        hipStream_t st) {
+                        hipStream_t st, int64_t capacity = INT64_MAX) {
   PermuteArgs a{};
+  a.capacity = capacity;
   a.experts = experts;
   a.block_counts = block_counts;
   a.counts = counts;
@@ -182,7 +185,8 @@ static int permute_impl(const moe_config* c, const int32_t* experts, const void*
   a.E = static_cast<int>(c->n_experts);
   a.k = static_cast<int>(c->top_k);
   launch_permute(a, st);
-  if (x_perm) launch_gather_rows(x, token_of, x_perm, a.A, c->hidden * static_cast<int64_t>(elem_bytes(c->dtype)), st);
+  if (x_perm)
+    launch_gather_rows(x, token_of, offsets + a.E, x_perm, a.A, c->hidden * static_cast<int64_t>(elem_bytes(c->dtype)), st);
   return check_launch("moe_permute");
 }
 
@@ -262,8 +266,9 @@ int moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
   return ok();
 }
 
-int moe_route(const moe_config* cfg, const void* x, const void* w_router, const void* w_shared_gate, float* logits,
-              float* weights, int32_t* experts, float* shared_scale, void* ws, size_t ws_bytes, void* stream) {
+static int route_entry(const moe_config* cfg, const void* x, const void* w_router, const void* w_shared_gate,
+                       float* logits, float* weights, int32_t* experts, float* shared_scale, void* ws, size_t ws_bytes,
+                       void* stream, bool sigmoid, const float* bias) {
   MOE_TRY(validate_config(cfg));
   if (cfg->n_tokens == 0) return ok();
   if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
@@ -280,25 +285,49 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
     if (need > 0) partial = static_cast<float*>(ws);
   }
   MOE_TRY(route_impl(cfg, x, w_router, w_shared_gate, logits, weights, experts, shared_scale, partial,
-                     static_cast<hipStream_t>(stream)));
+                     static_cast<hipStream_t>(stream), sigmoid, bias));
   return ok();
 }
 
-int moe_permute(const moe_config* cfg, const int32_t* experts, const void* x, int32_t* counts, int32_t* offsets,
-                int32_t* token_of, int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const void* w_shared_gate, float* logits,
+              float* weights, int32_t* experts, float* shared_scale, void* ws, size_t ws_bytes, void* stream) {
+  return route_entry(cfg, x, w_router, w_shared_gate, logits, weights, experts, shared_scale, ws, ws_bytes, stream,
+                     false, nullptr);
+}
+
+int moe_route_sigmoid(const moe_config* cfg, const void* x, const void* w_router, const float* bias, float* logits,
+                      float* weights, int32_t* experts, void* ws, size_t ws_bytes, void* stream) {
+  return route_entry(cfg, x, w_router, nullptr, logits, weights, experts, nullptr, ws, ws_bytes, stream, true, bias);
+}
+
+static int permute_entry(const moe_config* cfg, const int32_t* experts, const void* x, int32_t* counts,
+                         int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes,
+                         void* stream, int64_t capacity) {
   MOE_TRY(validate_config(cfg));
   if (cfg->n_tokens > 0 && !experts) return fail(MOE_ERR_INVALID_ARG, "experts is NULL");
   if (!counts) return fail(MOE_ERR_INVALID_ARG, "counts is NULL");
   if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
   if (cfg->n_tokens > 0 && (!token_of || !slot_pos)) return fail(MOE_ERR_INVALID_ARG, "token_of or slot_pos is NULL");
   if ((x == nullptr) != (x_perm == nullptr)) return fail(MOE_ERR_INVALID_ARG, "x and x_perm must be both set or both NULL");
+  if (capacity < 0) return fail(MOE_ERR_INVALID_ARG, "capacity = %lld < 0", (long long)capacity);
   const size_t need = permute_ws_bytes(cfg);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
   // counts and offsets are defined even for N == 0 (all zero), so the scan always runs.
   MOE_TRY(permute_impl(cfg, experts, x, counts, offsets, token_of, slot_pos, x_perm, static_cast<int32_t*>(ws),
-                       static_cast<hipStream_t>(stream)));
+                       static_cast<hipStream_t>(stream), capacity));
   return ok();
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* experts, const void* x, int32_t* counts, int32_t* offsets,
+                int32_t* token_of, int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  return permute_entry(cfg, experts, x, counts, offsets, token_of, slot_pos, x_perm, ws, ws_bytes, stream, INT64_MAX);
+}
+
+int moe_permute_capped(const moe_config* cfg, int64_t capacity, const int32_t* experts, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return permute_entry(cfg, experts, x, counts, offsets, token_of, slot_pos, x_perm, ws, ws_bytes, stream, capacity);
 }
 
 int moe_expert_gate_up(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows, const void* x,
@@ -371,6 +400,16 @@ int moe_router_stats(const moe_config* cfg, const float* logits, const int32_t* 
   launch_stats(logits, counts, f, P, loss, static_cast<float*>(ws), N, static_cast<int>(cfg->n_experts),
                static_cast<int>(cfg->top_k), static_cast<hipStream_t>(stream));
   MOE_TRY(check_launch("moe_router_stats"));
+  return ok();
+}
+
+int moe_router_bias_update(const moe_config* cfg, const int32_t* counts, float* bias, float gamma, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (!counts || !bias) return fail(MOE_ERR_INVALID_ARG, "counts or bias is NULL");
+  if (!(gamma >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "gamma must be >= 0");
+  launch_bias_update(counts, bias, gamma, cfg->n_tokens * cfg->top_k, static_cast<int>(cfg->n_experts),
+                     static_cast<hipStream_t>(stream));
+  MOE_TRY(check_launch("moe_router_bias_update"));
   return ok();
 }
 

@@ -5,6 +5,10 @@
 // Deterministic by construction: ranks come from ordered ballots inside a wave and ordered
 // per-wave counts inside a round, never from atomics (LDS atomics only build counts, whose value
 // does not depend on order).
+// Capacity limit ("Qwen3-VL + MoE: train to deploy", section "Capacity limits"): an expert keeps
+// its first `capacity` assignments in assignment order. Counts and offsets cover the kept rows;
+// since positions are handed out in assignment order, an assignment is kept exactly when its
+// position falls before its expert's end offset, and a dropped one gets slot_pos -1.
 #include "common.h"
 #include "kernels.h"
 
@@ -68,6 +72,7 @@ __global__ __launch_bounds__(512) void perm_scan_kernel(PermuteArgs a, int n_chu
         total += v;
       }
     }
+    total = static_cast<int>(min<int64_t>(total, a.capacity));   // kept rows (chunk bases unchanged)
     a.counts[e] = total;
   }
   // exclusive scan of total over e: inclusive wave scan, then the wave totals
@@ -93,17 +98,19 @@ __global__ __launch_bounds__(512) void perm_scan_kernel(PermuteArgs a, int n_chu
       for (int b = 0; b < n_chunks; ++b) a.block_counts[static_cast<int64_t>(b) * E + e] += excl;
     }
   }
-  if (e == 0) a.offsets[E] = static_cast<int32_t>(a.A);
+  if (e == E - 1) a.offsets[E] = excl + total;
 }
 
 // Pass 3: stable scatter. Rounds of 256 assignments in order; inside a wave, the rank among equal
 // experts comes from a ballot match; across the 4 waves of a round, from per-wave counts in LDS.
 __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(PermuteArgs a, int nbits) {
   __shared__ int s_run[512];
+  __shared__ int s_end[512];
   __shared__ int s_wcnt[4][512];
   const int E = a.E, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += kPermThreads) {
     s_run[e] = a.block_counts[blockIdx.x * static_cast<int64_t>(E) + e];
+    s_end[e] = a.offsets[e + 1];
     s_wcnt[0][e] = s_wcnt[1][e] = s_wcnt[2][e] = s_wcnt[3][e] = 0;
   }
   __syncthreads();
@@ -136,8 +143,9 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(PermuteArgs 
     }
     __syncthreads();
     if (valid) {
-      a.token_of[pos] = static_cast<int32_t>(i / a.k);
-      a.slot_pos[i] = pos;
+      const bool kept = pos < s_end[e];
+      if (kept) a.token_of[pos] = static_cast<int32_t>(i / a.k);
+      a.slot_pos[i] = kept ? pos : -1;
     }
   }
 }
@@ -148,6 +156,7 @@ constexpr int kPermSmallMax = 8192;
 
 __global__ __launch_bounds__(512) void perm_small_kernel(PermuteArgs a, int nbits) {
   __shared__ int s_pos[512];         // counts, then each expert's next sorted position
+  __shared__ int s_end[512];         // end of each expert's kept rows
   __shared__ int s_wcnt[8][512];
   __shared__ int s_wave[8];
   const int E = a.E, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(512) void perm_small_kernel(PermuteArgs a, int nbit
   __syncthreads();
   for (int64_t i = tid; i < A; i += 512) atomicAdd(&s_pos[a.experts[i]], 1);
   __syncthreads();
-  const int total = tid < E ? s_pos[tid] : 0;
+  const int total = tid < E ? static_cast<int>(min<int64_t>(s_pos[tid], a.capacity)) : 0;   // kept rows
   int inc = total;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -174,8 +183,9 @@ __global__ __launch_bounds__(512) void perm_small_kernel(PermuteArgs a, int nbit
     a.counts[tid] = total;
     a.offsets[tid] = excl;
     s_pos[tid] = excl;
+    s_end[tid] = excl + total;
   }
-  if (tid == 0) a.offsets[E] = static_cast<int32_t>(A);
+  if (tid == E - 1) a.offsets[E] = excl + total;
   __syncthreads();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t base = 0; base < A; base += 512) {
@@ -204,8 +214,9 @@ __global__ __launch_bounds__(512) void perm_small_kernel(PermuteArgs a, int nbit
     }
     __syncthreads();
     if (valid) {
-      a.token_of[pos] = static_cast<int32_t>(i / a.k);
-      a.slot_pos[i] = pos;
+      const bool kept = pos < s_end[e];
+      if (kept) a.token_of[pos] = static_cast<int32_t>(i / a.k);
+      a.slot_pos[i] = kept ? pos : -1;
     }
   }
 }
@@ -228,19 +239,20 @@ void launch_permute(const PermuteArgs& a, hipStream_t st) {
 
 // Row gather: one wave per row, 16-byte vectors.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ x, const int32_t* __restrict__ token_of,
-                                                          u32x4* __restrict__ x_perm, int64_t rows, int64_t vecs) {
+                                                          const int32_t* __restrict__ n_valid, u32x4* __restrict__ x_perm,
+                                                          int64_t rows, int64_t vecs) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  if (row >= rows || row >= *n_valid) return;          // rows past the kept total hold no token
   const u32x4* src = x + static_cast<int64_t>(token_of[row]) * vecs;
   u32x4* dst = x_perm + row * vecs;
   for (int64_t v = threadIdx.x & 63; v < vecs; v += 64) dst[v] = src[v];
 }
 
-void launch_gather_rows(const void* x, const int32_t* token_of, void* x_perm, int64_t rows,
+void launch_gather_rows(const void* x, const int32_t* token_of, const int32_t* n_valid, void* x_perm, int64_t rows,
                         int64_t row_bytes, hipStream_t st) {
   if (rows <= 0) return;
   const unsigned grid = static_cast<unsigned>((rows + 3) / 4);
-  gather_rows_kernel<<<grid, 256, 0, st>>>(static_cast<const u32x4*>(x), token_of, static_cast<u32x4*>(x_perm),
+  gather_rows_kernel<<<grid, 256, 0, st>>>(static_cast<const u32x4*>(x), token_of, n_valid, static_cast<u32x4*>(x_perm),
                                            rows, row_bytes / 16);
 }
 

@@ -47,26 +47,34 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
       v[j] = e < E ? s_logit[t * cols + e] : -INFINITY;
       m = fmaxf(m, v[j]);
     }
-    m = wave_max_dpp(m);
-    float s = 0.f;
+    if (a.sigmoid) {                             // selection keys: sigmoid(logit) + bias
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + kWave * j;
-      v[j] = e < E ? expf(v[j] - m) : 0.f;
-      s += v[j];
-    }
-    s = wave_sum_dpp(s);
+      for (int j = 0; j < kPer; ++j) {
+        const int e = lane + kWave * j;
+        v[j] = e < E ? 1.f / (1.f + expf(-v[j])) + (a.bias ? a.bias[e] : 0.f) : -INFINITY;
+      }
+    } else {
+      m = wave_max_dpp(m);
+      float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + kWave * j;
-      v[j] = e < E ? v[j] / s : -1.f;          // probabilities; -1 marks "not a candidate"
+      for (int j = 0; j < kPer; ++j) {
+        const int e = lane + kWave * j;
+        v[j] = e < E ? expf(v[j] - m) : 0.f;
+        s += v[j];
+      }
+      s = wave_sum_dpp(s);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int e = lane + kWave * j;
+        v[j] = e < E ? v[j] / s : -INFINITY;    // probabilities; -inf marks "not a candidate"
+      }
     }
     if (a.logits) {
       for (int e = lane; e < E; e += kWave) a.logits[n * E + e] = s_logit[t * cols + e];
     }
     float kept_sum = 0.f;
     for (int r = 0; r < k; ++r) {
-      float bp = -2.f;
+      float bp = -INFINITY;
       int be = 0x7fffffff;
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {          // strict '>' keeps the lowest index of a lane
@@ -75,9 +83,11 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
       wave_argmax_dpp(bp, be);
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (lane + kWave * j == be) v[j] = -1.f;
-      kept_sum += bp;                            // slot order, identical in every lane
-      if (lane == 0) { sel_p[r] = bp; sel_e[r] = be; }
+        if (lane + kWave * j == be) v[j] = -INFINITY;
+      // the weight: the probability, or the unbiased sigmoid score of the picked expert
+      const float w = a.sigmoid ? 1.f / (1.f + expf(-s_logit[t * cols + be])) : bp;
+      kept_sum += w;                             // slot order, identical in every lane
+      if (lane == 0) { sel_p[r] = w; sel_e[r] = be; }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -147,22 +157,28 @@ __device__ void route_select16(const RouteArgs& a, const float* s_logit, int col
       p[i] = (valid && e[i] < E) ? s_logit[t * cols + e[i]] : -INFINITY;
       m = fmaxf(m, p[i]);
     }
-    m = fmaxf(m, xor16f<1>(m));
-    m = fmaxf(m, xor16f<2>(m));
-    m = fmaxf(m, xor16f<4>(m));
-    m = fmaxf(m, xor16f<8>(m));
-    float sum = 0.f;
+    if (a.sigmoid) {                                               // keys: sigmoid(logit) + bias
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = e[i] < E ? expf(p[i] - m) : 0.f;
-      sum += p[i];
+      for (int i = 0; i < 8; ++i)
+        p[i] = (valid && e[i] < E) ? 1.f / (1.f + expf(-p[i])) + (a.bias ? a.bias[e[i]] : 0.f) : -INFINITY;
+    } else {
+      m = fmaxf(m, xor16f<1>(m));
+      m = fmaxf(m, xor16f<2>(m));
+      m = fmaxf(m, xor16f<4>(m));
+      m = fmaxf(m, xor16f<8>(m));
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = e[i] < E ? expf(p[i] - m) : 0.f;
+        sum += p[i];
+      }
+      sum += xor16f<1>(sum);                                        // commutative pairs: same in every lane
+      sum += xor16f<2>(sum);
+      sum += xor16f<4>(sum);
+      sum += xor16f<8>(sum);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = e[i] < E ? p[i] / sum : -INFINITY;  // -inf: never selected
     }
-    sum += xor16f<1>(sum);                                          // commutative pairs: same in every lane
-    sum += xor16f<2>(sum);
-    sum += xor16f<4>(sum);
-    sum += xor16f<8>(sum);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = e[i] < E ? p[i] / sum : -1.f;  // -1: never selected
     // sort the lane's eight: bitonic sort (sizes 2, 4, 8)
 #pragma unroll
     for (int size = 2; size <= 8; size <<= 1)
@@ -195,6 +211,11 @@ __device__ void route_select16(const RouteArgs& a, const float* s_logit, int col
     merge(std::integral_constant<int, 2>{});
     merge(std::integral_constant<int, 4>{});
     merge(std::integral_constant<int, 8>{});
+    if (a.sigmoid) {                              // weights: the picked experts' unbiased scores
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r < k && valid) p[r] = 1.f / (1.f + expf(-s_logit[t * cols + e[r]]));
+    }
     float kept = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r)

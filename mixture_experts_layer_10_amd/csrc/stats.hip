@@ -94,4 +94,20 @@ void launch_stats(const float* logits, const int32_t* counts, float* f, float* P
   stats_loss_kernel<<<1, 64, 0, st>>>(f, P, loss, E);
 }
 
+// Selection-bias nudge ("Qwen3-VL + MoE: train to deploy", section "Balancing without a loss":
+// overloaded experts get their bias lowered slightly, idle ones raised): one thread per expert,
+// bias[e] -= gamma * sign(counts[e] - A / E), comparing counts[e] * E with A exactly in integers.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts, float* __restrict__ bias,
+                                                          float gamma, int64_t A, int E) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t load = static_cast<int64_t>(counts[e]) * E;
+  const float sgn = load > A ? 1.f : (load < A ? -1.f : 0.f);
+  bias[e] = bias[e] - gamma * sgn;
+}
+
+void launch_bias_update(const int32_t* counts, float* bias, float gamma, int64_t A, int E, hipStream_t st) {
+  bias_update_kernel<<<static_cast<unsigned>((E + 255) / 256), 256, 0, st>>>(counts, bias, gamma, A, E);
+}
+
 }  // namespace moe

@@ -28,7 +28,7 @@ def header_functions():
 
 def test_header_symbols_all_exported(lib):
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert getattr(lib, n) is not None

@@ -1,0 +1,147 @@
+"""Routing variants on the GPU against the oracle ("Qwen3-VL + MoE: train to deploy", sections
+"Capacity limits" and "Balancing without a loss"; "27. Mixture of experts", section "The router",
+the note on sigmoid routers): moe_route_sigmoid, moe_permute_capped (+ moe_combine skipping
+dropped pairs) and moe_router_bias_update."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_experts_layer_10_amd import binding as B
+from mixture_experts_layer_10_amd import inputs as I
+from parity_util import GAP, W_TOL, rel_err, to_np, y_tolerance
+from test_gpu_parity import data_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("with_ws", [False, True], ids=["one_pass", "ws"])
+@pytest.mark.parametrize("name", ["odd", "e512", "k1", "keras", "decode", "prefill", "fanout", "xs_e200"])
+def test_sigmoid_route(name, with_ws):
+    say(f"[sigmoid route] {name} ws={with_ws}")
+    d, dev = data_of(name)
+    s = d.shape
+    cfg = B.config_for(s)
+    N, k, E = s.n_tokens, s.top_k, s.n_experts
+    bias = np.random.default_rng(7).normal(0.0, 0.05, E).astype(np.float32)
+    w = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    e = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    lg = torch.empty((N, E), dtype=torch.float32, device="cuda")
+    B.moe_route_sigmoid(cfg, dev["x"], dev["w_router"], torch.from_numpy(bias).cuda(), lg, w, e,
+                        B.alloc_workspace(cfg) if with_ws else None)
+    torch.cuda.synchronize()
+    _, _, keys, w_ref, e_ref = O.route_sigmoid_bias(d.values("x"), d.values("w_router"), k, bias, s.norm_topk_prob)
+    near = compare_keyed_routing(to_np(w).astype(np.float64), to_np(e), w_ref, e_ref, keys, k)
+    say(f"  tokens {N}, near ties {near}")
+
+
+def compare_keyed_routing(w_gpu, e_gpu, w_ref, e_ref, keys, k):
+    """The acceptance rules of the softmax router, for selection keys that are not the weights
+    (score + bias): experts bit-exact except where the k-th/(k+1)-th key gap is < 1e-6; adjacent
+    slots whose keys differ by < 1e-6 may come in either order, and then their weights follow
+    their experts, so weights are compared expert by expert (within 1e-5)."""
+    ok = O.k_gap(keys, k) >= GAP
+    srt = -np.sort(-np.asarray(keys, np.float64), axis=-1)[:, :k]
+    close = np.abs(np.diff(srt, axis=1)) < GAP
+    for n in np.nonzero(ok)[0]:
+        for j in range(k):
+            if e_gpu[n, j] != e_ref[n, j]:
+                swap_ok = (j + 1 < k and close[n, j] and e_gpu[n, j] == e_ref[n, j + 1]) or \
+                          (j > 0 and close[n, j - 1] and e_gpu[n, j] == e_ref[n, j - 1])
+                assert swap_ok, f"token {n} slot {j}: expert {e_gpu[n, j]} vs {e_ref[n, j]}"
+        ref = dict(zip(e_ref[n].tolist(), w_ref[n].tolist()))
+        for j in range(k):
+            assert abs(w_gpu[n, j] - ref[int(e_gpu[n, j])]) <= W_TOL, (n, j, w_gpu[n, j], ref[int(e_gpu[n, j])])
+    return int((~ok).sum())
+
+
+def oracle_capped_permute(experts, E, capacity):
+    keep = O.capacity_keep(experts, E, capacity)
+    flat = np.asarray(experts).reshape(-1)
+    k = np.asarray(experts).shape[-1]
+    kept = np.nonzero(keep.reshape(-1))[0]
+    order = kept[np.argsort(flat[kept], kind="stable")]
+    counts = np.bincount(flat[kept], minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    slot_pos = np.full(flat.size, -1, np.int64)
+    slot_pos[order] = np.arange(order.size)
+    return counts, offsets, order // k, slot_pos
+
+
+@pytest.mark.parametrize("N,k,E,cap", [(37, 3, 7, 2), (37, 3, 7, 0), (37, 3, 7, 1000), (1, 1, 1, 1),
+                                       (5000, 8, 128, 30), (5000, 8, 128, 400), (2049, 10, 512, 3),
+                                       (1000, 8, 64, 125)])
+def test_permute_capped_bit_exact(N, k, E, cap):
+    say(f"[capped permute] N={N} k={k} E={E} C={cap}")
+    rng = np.random.default_rng(N + k + E + cap)
+    p = rng.dirichlet(np.full(E, 0.3))                      # skewed loads, so capacities bite
+    experts = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(N)]).astype(np.int32)
+    D = 64
+    x = torch.from_numpy(rng.standard_normal((N, D)).astype(np.float32)).to(torch.bfloat16).cuda()
+    cfg = B.make_config(N, D, E, k, 64)
+    A = N * k
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    token_of = torch.full((A,), -7, dtype=torch.int32, device="cuda")
+    slot_pos = torch.full((A,), -7, dtype=torch.int32, device="cuda")
+    x_perm = torch.zeros((A, D), dtype=torch.bfloat16, device="cuda")
+    B.moe_permute_capped(cfg, cap, torch.from_numpy(experts).cuda(), x, counts, offsets, token_of, slot_pos, x_perm,
+                         B.alloc_workspace(cfg))
+    torch.cuda.synchronize()
+    c_ref, o_ref, t_ref, s_ref = oracle_capped_permute(experts, E, cap)
+    assert np.array_equal(to_np(counts), c_ref)
+    assert np.array_equal(to_np(offsets), o_ref)
+    kept = int(o_ref[-1])
+    assert np.array_equal(to_np(token_of)[:kept], t_ref)
+    assert np.array_equal(to_np(slot_pos), s_ref)
+    assert torch.equal(x_perm[:kept].view(torch.int16), x[torch.from_numpy(t_ref).cuda()].view(torch.int16))
+
+
+@pytest.mark.parametrize("name,frac", [("odd", 0.5), ("keras", 0.6), ("decode", 0.8), ("odd_f32", 0.7)])
+def test_capped_layer(name, frac):
+    say(f"[capped layer] {name} capacity {frac} x mean load")
+    d, dev = data_of(name)
+    s = d.shape
+    cfg = B.config_for(s, "f32")
+    N, k, E, D, Iw = s.n_tokens, s.top_k, s.n_experts, s.hidden, s.inter
+    A = N * k
+    capacity = max(1, int(frac * A / E))
+    w = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    e = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    ws = B.alloc_workspace(cfg)
+    B.moe_route(cfg, dev["x"], dev["w_router"], None, None, w, e, None, ws)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    token_of = torch.empty(A, dtype=torch.int32, device="cuda")
+    slot_pos = torch.empty(A, dtype=torch.int32, device="cuda")
+    B.moe_permute_capped(cfg, capacity, e, None, counts, offsets, token_of, slot_pos, None, ws)
+    h = torch.empty((A, Iw), dtype=B.torch_dtype(cfg.dtype), device="cuda")
+    out = torch.full((A, D), float("nan"), dtype=torch.float32, device="cuda")   # rows past the kept total stay NaN
+    B.moe_expert_ffn(cfg, E, Iw, A, dev["x"], token_of, offsets, dev["gate_up"], dev["down"], h, out)
+    y = torch.empty((N, D), dtype=torch.float32, device="cuda")
+    B.moe_combine(cfg, out, w, slot_pos, None, None, y)
+    torch.cuda.synchronize()
+    we, ee = to_np(w).astype(np.float64), to_np(e)
+    keep = O.capacity_keep(ee, E, capacity)
+    assert (~keep).any(), "the capacity should drop something"
+    y_ref = O.forward_capacity(d.values("x"), we, ee, d.expert_view("gate_up"), d.expert_view("down"), keep)
+    got = to_np(y)
+    assert np.isfinite(got).all()
+    err = rel_err(got, y_ref)
+    tol = y_tolerance(s.dtype, "f32", y_ref)
+    say(f"  dropped {int((~keep).sum())} of {A}, max|dy|/rms = {err:.3e} (tol {tol:.3e})")
+    assert err <= tol
+
+
+def test_router_bias_update_exact():
+    say("[bias update]")
+    rng = np.random.default_rng(9)
+    for N, k, E in ((64, 8, 128), (5, 2, 10), (1000, 2, 3)):
+        counts = rng.integers(0, 2 * N * k // E + 2, E).astype(np.int32)
+        counts[0] = N * k // E if (N * k) % E == 0 else counts[0]          # one expert exactly at the mean
+        bias = rng.normal(0, 0.1, E).astype(np.float32)
+        cfg = B.make_config(N, 64, E, k, 64)
+        b = torch.from_numpy(bias.copy()).cuda()
+        B.moe_router_bias_update(cfg, torch.from_numpy(counts).cuda(), b, 0.001)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(b), O.bias_update(bias, counts, N, k, 0.001))
