@@ -332,38 +332,31 @@ def bias_update(bias, counts, n_tokens, top_k, gamma):
 # 30B model, decode bound by the weight bytes each step reads); [MoE-ch27] "Dispatch" (experts are
 # most of the bytes, 4-bit experts) and stretch exercise 3 (only the experts quantised to 4 bits,
 # the router kept in bf16). The pages name the bit widths but not the quantiser, so the plainest
-# one is read: symmetric absmax with one float32 scale per (row, 128 input columns).
+# one is read: symmetric absmax with one float32 scale per output row (per channel), the scheme of
+# weight-only int8 in the Keras port's framework.
 # --------------------------------------------------------------------------------------------
 
-QUANT_GROUP = 128
-
-
 def quantize_weights(w, bits):
-    """Quantise a [G, R, K] stack (K % 128 == 0) to signed `bits`-bit codes (bits 8 or 4).
+    """Quantise a [G, R, K] stack (R output rows, K inputs) to signed `bits`-bit codes (8 or 4).
 
-    For each row r and column group q of 128 (the input dimension K):
-      m     = max |w| over the group                 (float32, exact for bf16 values)
+    For each row r:
+      m     = max |w[r, :]|                          (float32, exact for bf16 values)
       scale = m / Q                                  (float32 division, Q = 2**(bits-1) - 1)
       code  = clamp(rint(w / scale), -Q, Q)          (float32 quotient, ties to even; 0 if scale 0)
     so code * scale reconstructs w to within scale / 2. Returns (codes int8 [G, R, K],
-    scales float32 [G, R, K/128])."""
+    scales float32 [G, R])."""
     Q = np.float32(2 ** (bits - 1) - 1)
     w32 = np.asarray(w, np.float32)
-    G, R, K = w32.shape
-    grp = w32.reshape(G, R, K // QUANT_GROUP, QUANT_GROUP)
-    m = np.abs(grp).max(axis=-1)
+    m = np.abs(w32).max(axis=-1)
     scales = (m / Q).astype(np.float32)
     nz = scales > 0
     div = np.where(nz, scales, np.float32(1.0))[..., None]
-    codes = np.clip(np.rint((grp / div).astype(np.float32)), -Q, Q)
+    codes = np.clip(np.rint((w32 / div).astype(np.float32)), -Q, Q)
     codes = np.where(nz[..., None], codes, np.float32(0.0))
-    return codes.astype(np.int8).reshape(G, R, K), scales
+    return codes.astype(np.int8), scales
 
 
 def dequantize_weights(codes, scales):
-    """The weights the quantised layer computes with: w'[g, r, c] = code[g, r, c] * scale[g, r, c // 128],
-    in float64 (exact: a small integer times a float32)."""
-    codes = np.asarray(codes)
-    G, R, K = codes.shape
-    s = np.asarray(scales, np.float64)
-    return (codes.astype(np.float64).reshape(G, R, K // QUANT_GROUP, QUANT_GROUP) * s[..., None]).reshape(G, R, K)
+    """The weights the quantised layer computes with: w'[g, r, c] = code[g, r, c] * scale[g, r], in
+    float64 (exact: a small integer times a float32)."""
+    return np.asarray(codes).astype(np.float64) * np.asarray(scales, np.float64)[..., None]
