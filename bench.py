@@ -7,7 +7,8 @@ synthetic tokens already resident in HBM.
 Prints ONE JSON line. `value` is whole-layer tokens/s on the headline workload (the 16,384-token
 Qwen3-VL-30B-A3B prefill layer). `roofline` reports the grouped gate_up GEMM (the dominant kernel),
 timed with events on its launch stream inside the timed steps. `decode` adds the 64-token decode
-layer (weight-read bound). `cpu_baseline` times the CPU oracle on a bounded token sample.
+layer (weight-read bound). `quantized_experts` repeats both with int8 and int4 expert weights
+(one scale per weight row). `cpu_baseline` times the CPU oracle on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -32,14 +33,18 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic(shape, touched):
-    """FLOPs and bytes the method itself must do (not the dense all-expert work it avoids)."""
+def algorithmic(shape, touched, wbits=None):
+    """FLOPs and bytes the method itself must do (not the dense all-expert work it avoids).
+    wbits: bits per expert weight when the experts are quantised (one fp32 scale per weight row)."""
     N, D, E, k, I, Is = shape.n_tokens, shape.hidden, shape.n_experts, shape.top_k, shape.inter, shape.shared_inter
     b = 2 if shape.dtype == "bf16" else 4
+    wb = b if wbits is None else wbits / 8              # bytes per expert weight
+    rows = lambda n_out_rows: 0 if wbits is None else n_out_rows * 4      # scale bytes
     flops = 2 * N * D * E + 6 * D * I * N * k + (6 * D * Is * N + 2 * N * D if Is else 0)
-    bytes_ = touched * 3 * D * I * b + E * D * b + (3 * D * Is * b + D * b if Is else 0) + 2 * N * D * b + N * k * 8
+    bytes_ = (touched * (3 * D * I * wb + rows(2 * I + D)) + E * D * b
+              + (3 * D * Is * wb + rows(2 * Is + D) + D * b if Is else 0) + 2 * N * D * b + N * k * 8)
     gate_up_flops = 4 * D * I * N * k
-    gate_up_bytes = touched * 2 * I * D * b + N * k * D * b + N * k * I * b
+    gate_up_bytes = touched * (2 * I * D * wb + rows(2 * I)) + N * k * D * b + N * k * I * b
     return dict(flops=flops, bytes=bytes_, gate_up_flops=gate_up_flops, gate_up_bytes=gate_up_bytes)
 
 
@@ -118,11 +123,15 @@ def time_variants(B, chain, cfg, dev, steps):
                 dropped_share=round(1.0 - kept / (N * k), 4))
 
 
-def run_workload(name, steps, warmup, out_dtype, inner_events=True):
+LAYOUT_NAMES = {0: "rows", 1: "packed", 2: "int8", 3: "int4"}
+
+
+def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, data=None, extras=True):
     """Times `steps` whole-path steps. With inner_events the gate_up launch of every timed step is
     bracketed by events on its stream (its duration comes from the timed region itself); without,
     the timed steps carry no events (a recorded event idles the GPU for a few microseconds, which
-    matters at decode sizes) and the gate_up duration comes from a second run of `steps` steps."""
+    matters at decode sizes) and the gate_up duration comes from a second run of `steps` steps.
+    layout: 1 packed bf16 experts (rows if the shape cannot be packed), 2 / 3 int8 / int4 experts."""
     import torch
     from mixture_experts_layer_10_amd import binding as B
     from mixture_experts_layer_10_amd import inputs as I
@@ -130,16 +139,20 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True):
 
     shape = I.WORKLOADS[name]
     t0 = time.perf_counter()
-    data = I.make_inputs(shape)
+    if data is None:
+        data = I.make_inputs(shape)
     dev = B.to_device(data.store)
-    cfg = B.config_for(shape, out_dtype, packed=True)
-    if B.packable(cfg):                 # expert weights packed once, as at model load
+    cfg = B.config_for(shape, out_dtype, layout=layout)
+    if layout >= 2:                     # experts quantised once, as at model load
+        dev = B.quantize_device_weights(cfg, dev)
+        torch.cuda.synchronize()
+    elif B.packable(cfg):               # expert weights packed once, as at model load
         dev = B.pack_device_weights(cfg, dev)
         torch.cuda.synchronize()
     else:
         cfg = B.config_for(shape, out_dtype)
     log(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s (weight layout "
-        f"{'packed' if cfg.weight_layout else 'rows'})")
+        f"{LAYOUT_NAMES[cfg.weight_layout]})")
     chain = Chain(cfg, dev)
     y_ref = B.forward(cfg, dev)
     for _ in range(warmup):
@@ -167,14 +180,47 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True):
         torch.cuda.synchronize()
     gate_up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     ms_per_step = wall * 1e3 / steps
-    stats = time_router_stats(B, chain, cfg, dev, steps)
-    variants = time_variants(B, chain, cfg, dev, steps)
-    alg = algorithmic(shape, touched)
+    stats = time_router_stats(B, chain, cfg, dev, steps) if extras else None
+    variants = time_variants(B, chain, cfg, dev, steps) if extras else None
+    alg = algorithmic(shape, touched, {2: 8, 3: 4}.get(cfg.weight_layout))
     log(f"[bench] {name}: {ms_per_step:.3f} ms/step (gpu {gpu_ms / steps:.3f}), gate_up {gate_up_ms:.3f} ms, "
         f"touched {touched}/{shape.n_experts}")
     return dict(shape=shape, data=data, cfg=cfg, stats=stats, variants=variants, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
+                y=y_ref.float().cpu().numpy(),
                 gate_up_ms=gate_up_ms, touched=touched, counts=counts, alg=alg,
                 tokens_per_s=shape.n_tokens / (ms_per_step / 1e3))
+
+
+def quantized_runs(args, runs):
+    """Weight-only quantised experts (int8 and int4, one fp32 scale per weight row; router and
+    activations bf16) on the same inputs as the bf16 runs: step time, HBM fraction of the quantised
+    algorithmic bytes, stored expert bytes, and the layer output's deviation from the bf16 layer."""
+    out = {}
+    for bits, layout in ((8, 2), (4, 3)):
+        res = {}
+        for wl, base in runs.items():
+            decode = wl == "decode"
+            q = run_workload(wl, max(args.steps, 50) if decode else args.steps, args.warmup, args.out_dtype,
+                             inner_events=not decode, layout=layout, data=base["data"], extras=False)
+            st = q["ms_per_step"] / 1e3
+            sh = q["shape"]
+            d = q["y"].astype(np.float64) - base["y"]
+            ref_rms = float(np.sqrt(np.mean(base["y"].astype(np.float64) ** 2)))
+            r = {"ms_per_step": round(q["ms_per_step"], 4), "tokens_per_s": round(q["tokens_per_s"], 1),
+                 "alg_gbs": round(q["alg"]["bytes"] / st / 1e9, 1),
+                 "hbm_frac": round(q["alg"]["bytes"] / st / 1e9 / PEAK_HBM_GBS, 4),
+                 "gate_up_ms": round(q["gate_up_ms"], 4),
+                 "expert_weight_bytes": int(sh.n_experts * (3 * sh.hidden * sh.inter * bits // 8
+                                                            + (2 * sh.inter + sh.hidden) * 4)),
+                 "y_rms_rel_vs_bf16": round(float(np.sqrt(np.mean(d * d))) / ref_rms, 5),
+                 "y_maxabs_rel_vs_bf16": round(float(np.abs(d).max()) / ref_rms, 5)}
+            if decode:
+                r["gate_up_hbm_frac"] = round(q["alg"]["gate_up_bytes"] / (q["gate_up_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
+            else:
+                r["gate_up_tflops"] = round(q["alg"]["gate_up_flops"] / (q["gate_up_ms"] / 1e3) / 1e12, 1)
+            res[wl] = r
+        out[f"int{bits}"] = res
+    return out
 
 
 def cpu_baseline(data, target_s=15.0):
@@ -215,6 +261,7 @@ def main():
     ap.add_argument("--out-dtype", default="f32")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quant", action="store_true", help="skip the int8 / int4 expert runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy a 256 MiB buffer once (a kernel of known traffic for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -284,6 +331,8 @@ def main():
                          "experts_touched": dec["touched"],
                          "gate_up_ms": round(dec["gate_up_ms"], 4),
                          "gate_up_hbm_frac": round(dec["alg"]["gate_up_bytes"] / (dec["gate_up_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if not args.no_quant and args.workload == "prefill":
+            out["quantized_experts"] = quantized_runs(args, {"decode": dec, "prefill": main_run})
     if args.copy_calibration:
         src = torch.ones(64 * 2**20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(PKG, "_lib", "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
-MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED, MOE_LAYOUT_Q8, MOE_LAYOUT_Q4 = 0, 1, 2, 3
 
 # Every symbol include/moe.h declares.
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_pack_weights", "moe_router_stats",
-            "moe_combine", "moe_forward", "moe_route_sigmoid", "moe_router_bias_update", "moe_permute_capped"]
+            "moe_combine", "moe_forward", "moe_route_sigmoid", "moe_router_bias_update", "moe_permute_capped",
+            "moe_quantized_bytes", "moe_quantize_weights"]
 
 
 class MoeError(RuntimeError):
@@ -47,16 +48,19 @@ class MoeConfig(ctypes.Structure):
 
 
 def make_config(n_tokens, hidden, n_experts, top_k, inter, shared_inter=0, norm_topk_prob=True,
-                dtype="bf16", out_dtype=None, packed=False) -> MoeConfig:
+                dtype="bf16", out_dtype=None, packed=False, layout=None) -> MoeConfig:
+    """layout: a MOE_LAYOUT_* value; default rows, or packed when ``packed``."""
     dt = {"bf16": MOE_BF16, "f32": MOE_F32}
+    if layout is None:
+        layout = MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_ROWS
     return MoeConfig(n_tokens, hidden, n_experts, top_k, inter, shared_inter, int(bool(norm_topk_prob)),
-                     dt[dtype], dt[out_dtype or dtype], MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_ROWS)
+                     dt[dtype], dt[out_dtype or dtype], layout)
 
 
-def config_for(shape, out_dtype=None, packed=False) -> MoeConfig:
+def config_for(shape, out_dtype=None, packed=False, layout=None) -> MoeConfig:
     """MoeConfig for an inputs.MoeShape."""
     return make_config(shape.n_tokens, shape.hidden, shape.n_experts, shape.top_k, shape.inter,
-                       shape.shared_inter, shape.norm_topk_prob, shape.dtype, out_dtype, packed)
+                       shape.shared_inter, shape.norm_topk_prob, shape.dtype, out_dtype, packed, layout)
 
 
 def packable(cfg: MoeConfig) -> bool:
@@ -93,6 +97,8 @@ def load(path: str = LIB_PATH):
         "moe_router_bias_update": (ctypes.c_int, [_CFG, _P, _P, ctypes.c_float, _P]),
         "moe_permute_capped": (ctypes.c_int, [_CFG, _I64, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_quantized_bytes": (ctypes.c_int, [_CFG, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_quantize_weights": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P]),
         "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     }
     for name, (res, args) in sig.items():
@@ -183,6 +189,17 @@ def moe_pack_weights(cfg, n_groups, rows, cols, src, dst, stream=None):
                                                        _stream(stream)))
 
 
+def moe_quantized_bytes(cfg, n_groups, rows, cols) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_quantized_bytes", load().moe_quantized_bytes(ctypes.byref(cfg), n_groups, rows, cols, ctypes.byref(n)))
+    return n.value
+
+
+def moe_quantize_weights(cfg, n_groups, rows, cols, src, dst, stream=None):
+    _check("moe_quantize_weights", load().moe_quantize_weights(ctypes.byref(cfg), n_groups, rows, cols, _ptr(src),
+                                                               _ptr(dst), _stream(stream)))
+
+
 def moe_route_sigmoid(cfg, x, w_router, bias, logits, weights, experts, ws=None, ws_bytes=None, stream=None):
     _check("moe_route_sigmoid", load().moe_route_sigmoid(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias),
                                                          _ptr(logits), _ptr(weights), _ptr(experts), _ptr(ws),
@@ -257,6 +274,26 @@ def pack_device_weights(cfg: MoeConfig, dev: dict):
         dst = torch.empty_like(src)
         moe_pack_weights(cfg, g, r, c, src, dst)
         out[name] = dst
+    return out
+
+
+def quantize_device_weights(cfg: MoeConfig, dev: dict):
+    """A copy of ``dev`` (row layout) for a quantised ``cfg``: the router packed (bf16) by
+    moe_pack_weights, gate_up, down and the shared pair quantised by moe_quantize_weights into uint8
+    buffers of moe_quantized_bytes() bytes (a one-time step, like loading the model)."""
+    import torch
+    D, E, I, Is = cfg.hidden, cfg.n_experts, cfg.inter, cfg.shared_inter
+    out = dict(dev)
+    dst = torch.empty_like(dev["w_router"])
+    moe_pack_weights(cfg, 1, E, D, dev["w_router"], dst)
+    out["w_router"] = dst
+    shapes = {"gate_up": (E, 2 * I, D), "down": (E, D, I)}
+    if Is:
+        shapes.update(shared_gate_up=(1, 2 * Is, D), shared_down=(1, D, Is))
+    for name, (g, r, c) in shapes.items():
+        q = torch.empty(moe_quantized_bytes(cfg, g, r, c), dtype=torch.uint8, device=dev[name].device)
+        moe_quantize_weights(cfg, g, r, c, dev[name], q)
+        out[name] = q
     return out
 
 

@@ -9,6 +9,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -137,6 +138,32 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
       (__attribute__((address_space(3))) const void*)lds_dst));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory");
 #endif
+}
+
+// The same for 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes land at lds_dst + 4 l, so
+// one instruction fills 256 bytes of LDS contiguously.
+__device__ __forceinline__ void dma4(const void* src, const void* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)lds_dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base) : "memory");
+#endif
+}
+
+// Weight-only quantised codes -> eight bf16 matrix-core inputs, exactly (|code| <= 127 fits bf16's
+// 8-bit significand); the row's scale is applied to the fp32 sum afterwards.
+// int8: eight signed bytes, code i in byte i; int4: eight signed nibbles, code i in bits 4i..4i+3.
+__device__ __forceinline__ u32x4 codes8_to_bf16(u32x2 c) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(static_cast<int32_t>(c[i >> 2] << (24 - 8 * (i & 3))) >> 24);
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+__device__ __forceinline__ u32x4 codes4_to_bf16(uint32_t c) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(static_cast<int32_t>(c << (28 - 4 * i)) >> 28);
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 
 // s_waitcnt immediate for vmcnt(n) alone (bits 3:0 and 15:14; expcnt and lgkmcnt at "no wait").

@@ -270,10 +270,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
 // 64 lanes x 16 bytes = 16 rows contiguously, so the swizzle is applied to the global side: lane l
 // fetches chunk (l & 3) ^ (((l >> 2) >> 2) & 3) of row l >> 2.
 // 32-row blocks of a tile that lie past the group's last row skip their matrix-core steps.
+// Quantised weights (kQ = 8 or 4): each stage's weight blocks (64 kQ bytes of codes per 16 x 32)
+// move with 4-byte-per-lane DMA; fragments are converted to bf16 exactly as they are read, and each
+// output column is multiplied by its weight row's scale in the epilogue.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSK = 32;
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32, NT = WM * WN * 64, NW = WM * WN;
   // DMA instructions per wave per stage; with fewer 16-row A groups than waves (BM = 32), waves
@@ -281,7 +284,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int A_GROUPS = BM / 16;
   constexpr int A_INS = (A_GROUPS + NW - 1) / NW, B_INS = BNB / 16 / NW;
   constexpr int OUT_COLS = kSwiGLU ? BNB / 2 : BNB;
-  constexpr int PER_STAGE = A_INS + B_INS;
+  constexpr int QB = kQ ? 64 * kQ : 1024;                 // bytes of one 16 x 32 weight block
+  constexpr int B_DMA = kQ == 8 ? 2 * B_INS : B_INS;       // weight DMA instructions per wave per stage
+  constexpr int PER_STAGE = A_INS + B_DMA;
+  static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
   static_assert(A_INS * NW == A_GROUPS || A_INS == 1, "A rows must split into 16-row DMA groups");
   static_assert(B_INS * 16 * NW == BNB, "B rows must split into 16-row DMA groups");
   static_assert(!kSwiGLU || TN % 2 == 0, "SwiGLU pairs gate blocks with up blocks");
@@ -290,10 +296,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * kSK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA2[BM * kSK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA3[BM * kSK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BNB * kSK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BNB * kSK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BNB * kSK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB3[BNB * kSK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BNB * kSK * (kQ ? kQ : 16) / 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BNB * kSK * (kQ ? kQ : 16) / 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BNB * kSK * (kQ ? kQ : 16) / 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB3[BNB * kSK * (kQ ? kQ : 16) / 16];
   __shared__ int s_pref[1025];
   __shared__ int s_off[1025];           // group row offsets (no global round trip per tile)
   __shared__ int s_tmp[16];
@@ -320,15 +326,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   // 2..3 and the chunk of k-step kk is (2 kk + (lane >> 5)) ^ ((lane >> 2) & 3).
   // Packed B: each 16-row group's 1 KB holds the fragment in lane order (row r16, 8-wide k chunk q
   // at (r16 + 16 q) * 8), so 16 lanes read 256 contiguous bytes.
+  // Quantised B: the same block and slot in bytes (QB per block, kQ bytes per slot).
+  const int rb0 = (kSwiGLU ? wn * (TN / 2) : wn * TN) * 32;
   int koA[2], koB[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int pc = ((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 3;
-    const int rb0 = (kSwiGLU ? wn * (TN / 2) : wn * TN) * 32;
     koA[kk] = (wm * TM * 32 + (lane & 31)) * kSK + pc;
-    koB[kk] = kPacked ? rb0 * kSK + ((lane >> 4) & 1) * 512 + (lane & 15) * 8 + (2 * kk + (lane >> 5)) * 128
-                      : (rb0 + (lane & 31)) * kSK + pc;
+    if constexpr (kQ != 0)
+      koB[kk] = (rb0 / 16 + ((lane >> 4) & 1)) * QB + ((lane & 15) + 16 * (2 * kk + (lane >> 5))) * kQ;
+    else
+      koB[kk] = kPacked ? rb0 * kSK + ((lane >> 4) & 1) * 512 + (lane & 15) * 8 + (2 * kk + (lane >> 5)) * 128
+                        : (rb0 + (lane & 31)) * kSK + pc;
   }
+  const int R = kSwiGLU ? 2 * a.I : a.D;              // weight rows per group
   constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
 
   // One tile's fixed data. make_tile reads the group table in LDS and, for gathered rows, the row
@@ -339,6 +350,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     int64_t row0, rows;
     const uint16_t* srcA[A_INS];
     const uint16_t* srcB[B_INS];
+    const char* srcQ[B_INS];          // quantised: this lane's 4 code bytes of k-block 0
+    float sc[TN];                     // quantised: scale of each of this lane's output columns
   };
   auto make_tile = [&](int r) {
     Tile T;
@@ -363,6 +376,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
       T.srcA[j] = X + src * K + lch * 8;
     }
     const uint16_t* Wg = W + static_cast<int64_t>(g) * (kSwiGLU ? 2LL * a.I * a.D : static_cast<int64_t>(a.D) * a.I);
+    if constexpr (kQ != 0) {
+      // the weight row of this lane's column in block j (columns past the output width read a
+      // valid row; their outputs are never stored)
+      const float* S = reinterpret_cast<const float*>(static_cast<const char*>(a.w) + quant_code_bytes(G, R, K, kQ)) +
+                       static_cast<int64_t>(g) * R;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        constexpr int H = TN / 2;
+        if (kSwiGLU) {
+          const int col = min(T.c0 + (wn * H + (j < H ? j : j - H)) * 32 + (lane & 31), NOUT - 1);
+          T.sc[j] = S[j < H ? col : a.I + col];
+        } else {
+          T.sc[j] = S[min(T.c0 + (wn * TN + j) * 32 + (lane & 31), NOUT - 1)];
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < B_INS; ++j) {
       const int grp = wave * B_INS + j;
@@ -377,7 +406,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         } else {
           rb = min(T.c0 / 16 + grp, NOUT / 16 - 1);
         }
-        T.srcB[j] = Wg + static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8;
+        if constexpr (kQ != 0)
+          T.srcQ[j] = static_cast<const char*>(a.w) + quant_code_bytes(g, R, K, kQ) +
+                      static_cast<int64_t>(rb) * (K / kSK) * QB + lane * 4;
+        else
+          T.srcB[j] = Wg + static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8;
       } else {
         const int rr = grp * 16 + lrow;
         int wrow;
@@ -398,8 +431,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) dma16(T.srcA[j] + kb, sa + ((wave * A_INS + j) % A_GROUPS) * 512);
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j) dma16(T.srcB[j] + (kPacked ? ks * 512 : kb), sb + (wave * B_INS + j) * 512);
+    for (int j = 0; j < B_INS; ++j) {
+      if constexpr (kQ != 0) {
+        const char* src = T.srcQ[j] + static_cast<int64_t>(ks) * QB;
+        char* dst = reinterpret_cast<char*>(sb) + (wave * B_INS + j) * QB;
+        dma4(src, dst);
+        if constexpr (kQ == 8) dma4(src + 256, dst + 256);
+      } else {
+        dma16(T.srcB[j] + (kPacked ? ks * 512 : kb), sb + (wave * B_INS + j) * 512);
+      }
+    }
   };
+
   // wait for stage s (later stages may stay in flight), then sync the workgroup: after this, stage
   // s is visible to every wave and every wave has finished reading stage s - 1's buffer. Loads
   // retire in order, so "at most n outstanding" implies stage s has landed even with the previous
@@ -422,7 +465,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
       for (int j = 0; j < TN; ++j) {
         constexpr int H = TN / 2;
         const int rowoff = kSwiGLU ? (j < H ? j * 32 : BNB / 2 + (j - H) * 32) : j * 32;
-        fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
+        if constexpr (kQ == 8)
+          fb[j] = codes8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
+        else if constexpr (kQ == 4)
+          fb[j] = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
+        else
+          fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -474,6 +522,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     // reaches after finishing these reads of buffer 3.
     const int64_t row0 = cur.row0, rows = cur.rows;
     const int m0 = cur.m0, c0 = cur.c0;
+    if constexpr (kQ != 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] *= cur.sc[j];
+    }
     if constexpr (kSwiGLU) {
       uint16_t* Hh = static_cast<uint16_t*>(a.out);
       constexpr int H = TN / 2;
@@ -521,37 +575,77 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 // MB = 16-row blocks per pass; groups with more rows take several passes over the weights.
 // gate_up: a task holds 16 gate rows and the 16 matching up rows (SwiGLU in the epilogue).
 // Requires K % 32 == 0.
+// Quantised weights (kQ = 8 or 4 bits, packed block order): the integer codes go to the matrix
+// cores exactly as bf16, and the lane's output column is multiplied by its row's scale in the
+// epilogue (one scale per weight row, so it factors out of the dot product).
 // ---------------------------------------------------------------------------------------------
-template <int MB, bool kSwiGLU, bool kPacked>
+template <int kQ> struct WRaw { typedef u32x4 T; };          // bf16: 8 values = 16 bytes per lane
+template <> struct WRaw<8> { typedef u32x2 T; };              // int8: 8 codes = 8 bytes
+template <> struct WRaw<4> { typedef uint32_t T; };           // int4: 8 codes = 4 bytes
+
+template <int kQ>
+__device__ __forceinline__ u32x4 to_bf16_frag(typename WRaw<kQ>::T v) {
+  if constexpr (kQ == 8) return codes8_to_bf16(v);
+  else if constexpr (kQ == 4) return codes4_to_bf16(v);
+  else return v;
+}
+
+// Column blocks of 16 per task: quantised codes are smaller than bf16, so a task takes two column
+// blocks to keep more weight bytes in flight per wave, and each activation fragment then feeds twice
+// as many matrix-core steps (one block for MB = 4, whose accumulators would not fit the registers
+// otherwise). Measured on the 64-token decode layer: two blocks beat one (int8 and int4) and four
+// (int4, whose registers then allow one wave per SIMD only).
+template <int kQ, int MB> constexpr int wstream_cols() { return kQ && MB < 4 ? 2 : 1; }
+
+template <int MB, bool kSwiGLU, bool kPacked, int kQ>
 __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
-  constexpr int NB = kSwiGLU ? 2 : 1;       // weight blocks of 16 rows per task
-  constexpr int U = 4;                      // k-steps per load batch (two batches in flight)
+  static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
+  typedef typename WRaw<kQ>::T Raw;
+  constexpr int CB = wstream_cols<kQ, MB>(); // column blocks per task
+  constexpr int NS = kSwiGLU ? 2 : 1;        // weight blocks per column block (gate, up)
+  constexpr int NB = CB * NS;                // weight blocks of 16 rows per task; block j: column
+                                             // block j / NS, part j % NS
+  constexpr int U = 4;                       // k-steps per load batch (two batches in flight)
   const int lane = threadIdx.x & 63;
   const int K = kSwiGLU ? a.D : a.I;
   const int NOUT = kSwiGLU ? a.I : a.D;
+  const int R = kSwiGLU ? 2 * a.I : a.D;     // weight rows per group
   const int ncb = (NOUT + 15) / 16;
+  const int ntc = (ncb + CB - 1) / CB;       // tasks per group
   const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (task >= static_cast<int64_t>(a.G) * ncb) return;
-  const int g = static_cast<int>(task / ncb);
-  const int cb = static_cast<int>(task - static_cast<int64_t>(g) * ncb);
+  if (task >= static_cast<int64_t>(a.G) * ntc) return;
+  const int g = static_cast<int>(task / ntc);
+  const int cb0 = static_cast<int>(task - static_cast<int64_t>(g) * ntc) * CB;
   const int64_t row0 = a.offsets ? a.offsets[g] : 0;
   const int64_t rows = a.offsets ? static_cast<int64_t>(a.offsets[g + 1]) - row0 : a.max_rows;
   if (rows <= 0) return;
   const uint16_t* X = static_cast<const uint16_t*>(a.x);
-  const uint16_t* Wg = static_cast<const uint16_t*>(a.w) +
-                       static_cast<int64_t>(g) * (kSwiGLU ? 2LL * a.I * a.D : static_cast<int64_t>(a.D) * a.I);
-  const int kg = (lane >> 4) * 8;           // this lane's k offset inside a 32-wide step
-  const int col = cb * 16 + (lane & 15);
-  const int ccol = min(col, NOUT - 1);
-  const uint16_t* wrow[NB];
-  // packed: the task's 16 rows are row block cb; k-step ks of it is 1 KB at + ks * 512 in lane order
-  constexpr int WSTEP = kPacked ? 512 : 32;
-  if constexpr (kPacked) {
-    wrow[0] = Wg + static_cast<int64_t>(cb) * (K / 32) * 512 + lane * 8;
-    if (kSwiGLU) wrow[NB - 1] = Wg + static_cast<int64_t>(a.I / 16 + cb) * (K / 32) * 512 + lane * 8;
-  } else {
-    wrow[0] = Wg + static_cast<int64_t>(ccol) * K + kg;
-    if (kSwiGLU) wrow[NB - 1] = Wg + static_cast<int64_t>(a.I + ccol) * K + kg;
+  const int kg = (lane >> 4) * 8;            // this lane's k offset inside a 32-wide step
+  int col[CB];                               // this lane's output column in each column block
+#pragma unroll
+  for (int c = 0; c < CB; ++c) col[c] = (cb0 + c) * 16 + (lane & 15);
+  // wrow[j]: this lane's weight bytes of k-step 0 of block j; k-step ks is WSTEP bytes further.
+  // packed: a column block's 16 rows are one row block; k-step ks of it is one block in lane order.
+  const char* wrow[NB];
+  constexpr int WSTEP = kQ ? 64 * kQ : (kPacked ? 1024 : 64);
+  const char* Wg = static_cast<const char*>(a.w) +
+                   (kQ ? quant_code_bytes(g, R, K, kQ) : static_cast<int64_t>(g) * R * K * 2);
+  float scl[NB];                             // quantised: the scale of each block's row for this lane
+  const float* S = nullptr;
+  if constexpr (kQ != 0)
+    S = reinterpret_cast<const float*>(static_cast<const char*>(a.w) + quant_code_bytes(a.G, R, K, kQ)) +
+        static_cast<int64_t>(g) * R;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int cb = min(cb0 + j / NS, ncb - 1);
+    const int up = (j % NS) * a.I;           // SwiGLU: the up rows follow the I gate rows
+    if constexpr (kPacked) {
+      constexpr int SLOT = kQ ? kQ : 16;     // bytes per lane slot
+      wrow[j] = Wg + static_cast<int64_t>(up / 16 + cb) * (K / 32) * WSTEP + lane * SLOT;
+    } else {
+      wrow[j] = Wg + (static_cast<int64_t>(up + min(cb * 16 + (lane & 15), NOUT - 1)) * K + kg) * 2;
+    }
+    if constexpr (kQ != 0) scl[j] = S[up + min(cb * 16 + (lane & 15), NOUT - 1)];
   }
   const int ksteps = K / 32;
 
@@ -571,13 +665,14 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
       for (int j = 0; j < NB; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // register double buffer: the loads of the next U k-steps are issued before the matrix-core
     // steps of the current ones, so U k-steps of weight loads are always in flight
-    u32x4 fb[2][U][NB], fa[2][U][MB];
+    Raw fb[2][U][NB];
+    u32x4 fa[2][U][MB];
     auto load = [&](int buf, int k0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          fb[buf][u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + (k0 + u) * WSTEP));
+          fb[buf][u][j] = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(wrow[j] + static_cast<int64_t>(k0 + u) * WSTEP));
 #pragma unroll
         for (int b = 0; b < MB; ++b) fa[buf][u][b] = *reinterpret_cast<const u32x4*>(xrow[b] + (k0 + u) * 32);
       }
@@ -586,9 +681,11 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int b = 0; b < MB; ++b)
+        for (int j = 0; j < NB; ++j) {
+          const u32x4 w = to_bf16_frag<kQ>(fb[buf][u][j]);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[b][j] = mfma16(fa[buf][u][b], fb[buf][u][j], acc[b][j]);
+          for (int b = 0; b < MB; ++b) acc[b][j] = mfma16(fa[buf][u][b], w, acc[b][j]);
+        }
     };
     const int full = ksteps / U;                 // U-step batches
     int ks = full * U;
@@ -605,14 +702,22 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
     }
     for (; ks < ksteps; ++ks) {
 #pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        const u32x4 fa = *reinterpret_cast<const u32x4*>(xrow[b] + ks * 32);
+      for (int j = 0; j < NB; ++j) {
+        const u32x4 w = to_bf16_frag<kQ>(__builtin_nontemporal_load(reinterpret_cast<const Raw*>(wrow[j] + static_cast<int64_t>(ks) * WSTEP)));
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[b][j] = mfma16(fa, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + ks * WSTEP)), acc[b][j]);
+        for (int b = 0; b < MB; ++b)
+          acc[b][j] = mfma16(*reinterpret_cast<const u32x4*>(xrow[b] + ks * 32), w, acc[b][j]);
       }
     }
-    if (col < NOUT) {
+    if constexpr (kQ != 0) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[b][j] *= scl[j];
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      if (col[c] >= NOUT) continue;
 #pragma unroll
       for (int b = 0; b < MB; ++b)
 #pragma unroll
@@ -620,27 +725,28 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
           const int64_t rr = m0 + b * 16 + 4 * (lane >> 4) + i;
           if (rr < rows) {
             if constexpr (kSwiGLU)
-              static_cast<uint16_t*>(a.out)[(row0 + rr) * NOUT + col] = f32_to_bf16(silu(acc[b][0][i]) * acc[b][1][i]);
+              static_cast<uint16_t*>(a.out)[(row0 + rr) * NOUT + col[c]] =
+                  f32_to_bf16(silu(acc[b][c * NS][i]) * acc[b][c * NS + 1][i]);
             else
-              static_cast<float*>(a.out)[(row0 + rr) * NOUT + col] = acc[b][0][i];
+              static_cast<float*>(a.out)[(row0 + rr) * NOUT + col[c]] = acc[b][c][i];
           }
         }
     }
   }
 }
 
-template <bool kSwiGLU, bool kPacked>
+template <bool kSwiGLU, bool kPacked, int kQ = 0>
 static void launch_wstream(const GemmArgs& a, hipStream_t st) {
   const int NOUT = kSwiGLU ? a.I : a.D;
-  const int64_t tasks = static_cast<int64_t>(a.G) * ((NOUT + 15) / 16);
-  const unsigned grid = static_cast<unsigned>((tasks + 3) / 4);
+  const int64_t ncb = (NOUT + 15) / 16;
+  auto grid = [&](int cb) { return static_cast<unsigned>((a.G * ((ncb + cb - 1) / cb) + 3) / 4); };
   const int64_t mean_rows = a.offsets ? a.max_rows / std::max(a.G, 1) : a.max_rows;
   if (mean_rows <= 8)
-    gemm_wstream_kernel<1, kSwiGLU, kPacked><<<grid, 256, 0, st>>>(a);
+    gemm_wstream_kernel<1, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 1>()), 256, 0, st>>>(a);
   else if (mean_rows <= 20)
-    gemm_wstream_kernel<2, kSwiGLU, kPacked><<<grid, 256, 0, st>>>(a);
+    gemm_wstream_kernel<2, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 2>()), 256, 0, st>>>(a);
   else
-    gemm_wstream_kernel<4, kSwiGLU, kPacked><<<grid, 256, 0, st>>>(a);
+    gemm_wstream_kernel<4, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 4>()), 256, 0, st>>>(a);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -773,20 +879,20 @@ static void launch_bf16(const GemmArgs& a, hipStream_t st) {
   gemm_bf16_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, C::NT, 0, st>>>(a);
 }
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0>
 static void launch_stream(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32;
   constexpr int out_cols = kSwiGLU ? BNB / 2 : BNB;
   const int NOUT = kSwiGLU ? a.I : a.D;
   const int n_tiles = (NOUT + out_cols - 1) / out_cols;
-  constexpr int lds = 4 * (BM + BNB) * kSK * 2;
+  constexpr int lds = 4 * (BM * 2 + BNB * (kQ ? kQ : 16) / 8) * kSK;
   // Short-row tiles (few rows per group) are pure weight streams: one workgroup per tile lets the
   // dispatcher start a new tile wherever one finishes instead of running fixed rounds with a
   // half-empty last round. Tall tiles keep a persistent grid (one prologue per workgroup).
   const int64_t ub = tile_upper_bound(a, BM, n_tiles);
   const unsigned grid = BM <= 32 ? static_cast<unsigned>(std::max<int64_t>(ub, 1))
                                  : persistent_grid(ub, lds <= 76 * 1024 ? 2 : 1);
-  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked><<<grid, WM * WN * 64, 0, st>>>(a);
+  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked, kQ><<<grid, WM * WN * 64, 0, st>>>(a);
 }
 
 template <bool kSwiGLU>
@@ -816,6 +922,14 @@ static void launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (!a.bf16) return launch_f32<kSwiGLU>(a, st);
   const int K = kSwiGLU ? a.D : a.I;
   const bool stream = streamable(a, kSwiGLU);
+  if (a.qbits == 8) {
+    if (small_rows(a)) return launch_wstream<kSwiGLU, true, 8>(a, st);
+    return launch_stream<2, 4, 4, 2, kSwiGLU, true, 8>(a, st);
+  }
+  if (a.qbits == 4) {
+    if (small_rows(a)) return launch_wstream<kSwiGLU, true, 4>(a, st);
+    return launch_stream<2, 4, 4, 2, kSwiGLU, true, 4>(a, st);
+  }
   if (a.packed) {
     if (small_rows(a)) return launch_wstream<kSwiGLU, true>(a, st);
     return launch_stream<2, 4, 4, 2, kSwiGLU, true>(a, st);

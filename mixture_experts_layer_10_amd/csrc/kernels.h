@@ -58,6 +58,7 @@ struct GemmArgs {
   int D, I;
   bool bf16;
   bool packed;            // w in the packed layout (bf16, K % 128 == 0, rows % 16 == 0)
+  int qbits;              // 0: bf16 weights; 8 or 4: w is a quantised stack (codes, then scales)
 };
 void launch_gate_up(const GemmArgs& a, hipStream_t st);
 void launch_down(const GemmArgs& a, hipStream_t st);
@@ -66,6 +67,13 @@ void launch_down(const GemmArgs& a, hipStream_t st);
 // fragments, fragment (g, rb, kb) at element ((g * R/16 + rb) * K/32 + kb) * 512, each 1 KB in
 // matrix-core lane order (lane l: row rb*16 + l % 16, k = kb*32 + 8 (l / 16) .. + 7).
 void launch_pack(const uint16_t* src, uint16_t* dst, int64_t G, int R, int K, hipStream_t st);
+
+// Quantised stack of a [G, R, K] bf16 matrix (R % 16 == 0, K % 32 == 0) with b = 8 or 4 bits:
+// codes in the packed block order, block (g, rb, kb) of 64 b bytes at ((g * R/16 + rb) * K/32 + kb)
+// * 64 b, slot l (b bytes) = row rb*16 + l % 16, columns kb*32 + 8 (l / 16) .. + 7; then one fp32
+// scale per row, [G, R], from byte G R K b / 8 on.
+__host__ __device__ inline int64_t quant_code_bytes(int64_t G, int64_t R, int64_t K, int bits) { return G * R * K * bits / 8; }
+void launch_quantize(const uint16_t* src, uint8_t* dst, int64_t G, int R, int K, int bits, hipStream_t st);
 
 struct CombineArgs {
   const float* out_perm;

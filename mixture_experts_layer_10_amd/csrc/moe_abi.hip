@@ -54,6 +54,17 @@ constexpr int64_t kMaxExperts = 512;
 
 static size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
+// Bits per expert-weight code of a quantised layout, 0 for bf16 / fp32 weights.
+static int quant_bits(const moe_config* c) {
+  return c->weight_layout == MOE_LAYOUT_Q8 ? 8 : c->weight_layout == MOE_LAYOUT_Q4 ? 4 : 0;
+}
+
+// Weight loads are 16 bytes wide (bf16 rows, packed blocks, quantised codes and scales).
+static int check_weight_align(const void* p, const char* name) {
+  if (reinterpret_cast<uintptr_t>(p) & 15) return fail(MOE_ERR_UNSUPPORTED, "%s at %p is not 16-byte aligned", name, p);
+  return MOE_OK;
+}
+
 static int validate_config(const moe_config* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
   if (c->n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens = %lld < 0", (long long)c->n_tokens);
@@ -66,8 +77,8 @@ static int validate_config(const moe_config* c) {
   if (c->shared_inter < 0) return fail(MOE_ERR_INVALID_ARG, "shared_inter = %lld < 0", (long long)c->shared_inter);
   if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1)
     return fail(MOE_ERR_INVALID_ARG, "norm_topk_prob = %d (must be 0 or 1)", c->norm_topk_prob);
-  if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_PACKED)
-    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d (must be 0 or 1)", c->weight_layout);
+  if (c->weight_layout < MOE_LAYOUT_ROWS || c->weight_layout > MOE_LAYOUT_Q4)
+    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d (must be 0, 1, 2 or 3)", c->weight_layout);
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
   if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "out_dtype %d not supported", c->out_dtype);
@@ -76,7 +87,7 @@ static int validate_config(const moe_config* c) {
   if (c->inter % align) return fail(MOE_ERR_UNSUPPORTED, "inter = %lld is not a multiple of %lld", (long long)c->inter, (long long)align);
   if (c->shared_inter % align)
     return fail(MOE_ERR_UNSUPPORTED, "shared_inter = %lld is not a multiple of %lld", (long long)c->shared_inter, (long long)align);
-  if (c->weight_layout == MOE_LAYOUT_PACKED) {
+  if (c->weight_layout != MOE_LAYOUT_ROWS) {
     if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights need dtype bf16");
     if (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128)
       return fail(MOE_ERR_UNSUPPORTED, "packed weights need hidden, inter and shared_inter multiples of 128");
@@ -165,7 +176,7 @@ static int route_impl(const moe_config* c, const void* x, const void* w_router, 
   a.k = static_cast<int>(c->top_k);
   a.norm = c->norm_topk_prob;
   a.bf16 = c->dtype == MOE_BF16;
-  a.packed = c->weight_layout == MOE_LAYOUT_PACKED;
+  a.packed = c->weight_layout != MOE_LAYOUT_ROWS;     // quantised layouts keep a packed bf16 router
   launch_route(a, st);
   return check_launch("moe_route");
 }
@@ -198,7 +209,7 @@ static int ffn_checks(const moe_config* c, int64_t n_groups, int64_t inter, int6
   const int64_t align = c->dtype == MOE_BF16 ? 8 : 4;
   if (inter % align) return fail(MOE_ERR_UNSUPPORTED, "inter = %lld is not a multiple of %lld", (long long)inter, (long long)align);
   if (inter > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "inter above 2^20");
-  if (c->weight_layout == MOE_LAYOUT_PACKED && inter % 128)
+  if (c->weight_layout != MOE_LAYOUT_ROWS && inter % 128)
     return fail(MOE_ERR_UNSUPPORTED, "packed weights need inter = %lld to be a multiple of 128", (long long)inter);
   if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows = %lld < 0", (long long)max_rows);
   if (max_rows > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "max_rows above int32");
@@ -219,7 +230,8 @@ static GemmArgs gemm_args(const moe_config* c, int64_t n_groups, int64_t inter, 
   a.D = static_cast<int>(c->hidden);
   a.I = static_cast<int>(inter);
   a.bf16 = c->dtype == MOE_BF16;
-  a.packed = c->weight_layout == MOE_LAYOUT_PACKED;
+  a.packed = c->weight_layout != MOE_LAYOUT_ROWS;
+  a.qbits = quant_bits(c);
   return a;
 }
 
@@ -335,6 +347,7 @@ int moe_expert_gate_up(const moe_config* cfg, int64_t n_groups, int64_t inter, i
   MOE_TRY(ffn_checks(cfg, n_groups, inter, max_rows, offsets));
   if (max_rows == 0) return ok();
   if (!x || !gate_up || !h) return fail(MOE_ERR_INVALID_ARG, "x, gate_up or h is NULL");
+  MOE_TRY(check_weight_align(gate_up, "gate_up"));
   launch_gate_up(gemm_args(cfg, n_groups, inter, max_rows, x, row_index, offsets, gate_up, h),
                  static_cast<hipStream_t>(stream));
   MOE_TRY(check_launch("moe_expert_gate_up"));
@@ -346,6 +359,7 @@ int moe_expert_down(const moe_config* cfg, int64_t n_groups, int64_t inter, int6
   MOE_TRY(ffn_checks(cfg, n_groups, inter, max_rows, offsets));
   if (max_rows == 0) return ok();
   if (!h || !down || !out) return fail(MOE_ERR_INVALID_ARG, "h, down or out is NULL");
+  MOE_TRY(check_weight_align(down, "down"));
   launch_down(gemm_args(cfg, n_groups, inter, max_rows, h, nullptr, offsets, down, out), static_cast<hipStream_t>(stream));
   MOE_TRY(check_launch("moe_expert_down"));
   return ok();
@@ -357,6 +371,8 @@ int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64
   MOE_TRY(ffn_checks(cfg, n_groups, inter, max_rows, offsets));
   if (max_rows == 0) return ok();
   if (!x || !gate_up || !down || !h || !out) return fail(MOE_ERR_INVALID_ARG, "x, gate_up, down, h or out is NULL");
+  MOE_TRY(check_weight_align(gate_up, "gate_up"));
+  MOE_TRY(check_weight_align(down, "down"));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   launch_gate_up(gemm_args(cfg, n_groups, inter, max_rows, x, row_index, offsets, gate_up, h), st);
   MOE_TRY(check_launch("moe_expert_ffn (gate_up)"));
@@ -385,6 +401,45 @@ int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int6
   launch_pack(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), n_groups, static_cast<int>(rows),
               static_cast<int>(cols), static_cast<hipStream_t>(stream));
   MOE_TRY(check_launch("moe_pack_weights"));
+  return ok();
+}
+
+static int quant_shape_checks(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols) {
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (quant_bits(cfg) == 0)
+    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d is not a quantised layout (2 or 3)", cfg->weight_layout);
+  if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "quantisation needs dtype bf16");
+  if (n_groups < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
+  if (rows % 16 || cols % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "quantisation needs rows %% 16 == 0 and cols %% 32 == 0 (got %lld x %lld)",
+                (long long)rows, (long long)cols);
+  if (rows > (1 << 24) || cols > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "rows/cols above 2^24");
+  return MOE_OK;
+}
+
+int moe_quantized_bytes(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, size_t* bytes) {
+  MOE_TRY(quant_shape_checks(cfg, n_groups, rows, cols));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = static_cast<size_t>(quant_code_bytes(n_groups, rows, cols, quant_bits(cfg)) + n_groups * rows * 4);
+  return ok();
+}
+
+int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src, void* dst,
+                         void* stream) {
+  MOE_TRY(quant_shape_checks(cfg, n_groups, rows, cols));
+  const int64_t n = n_groups * rows * cols;
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src or dst is NULL");
+  const int bits = quant_bits(cfg);
+  const int64_t out_bytes = quant_code_bytes(n_groups, rows, cols, bits) + n_groups * rows * 4;
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + out_bytes && d0 < s0 + 2 * n) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15)
+    return fail(MOE_ERR_UNSUPPORTED, "src and dst must be 16-byte aligned");
+  launch_quantize(static_cast<const uint16_t*>(src), static_cast<uint8_t*>(dst), n_groups, static_cast<int>(rows),
+                  static_cast<int>(cols), bits, static_cast<hipStream_t>(stream));
+  MOE_TRY(check_launch("moe_quantize_weights"));
   return ok();
 }
 
@@ -429,6 +484,10 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
   MOE_TRY(validate_config(cfg));
   if (cfg->n_tokens == 0) return ok();
   if (!x || !w_router || !gate_up || !down || !y) return fail(MOE_ERR_INVALID_ARG, "x, w_router, gate_up, down or y is NULL");
+  MOE_TRY(check_weight_align(gate_up, "gate_up"));
+  MOE_TRY(check_weight_align(down, "down"));
+  if (shared_gate_up) MOE_TRY(check_weight_align(shared_gate_up, "shared_gate_up"));
+  if (shared_down) MOE_TRY(check_weight_align(shared_down, "shared_down"));
   if (cfg->shared_inter > 0 && (!shared_gate_up || !shared_down))
     return fail(MOE_ERR_INVALID_ARG, "shared_inter > 0 needs shared_gate_up and shared_down");
   if (cfg->shared_inter == 0 && (shared_gate_up || shared_down || w_shared_gate))

@@ -28,7 +28,7 @@ def header_functions():
 
 def test_header_symbols_all_exported(lib):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -63,7 +63,9 @@ def test_workspace_bytes_host_only(lib):
     ("inter", 0, B.MOE_ERR_INVALID_ARG),
     ("shared_inter", -8, B.MOE_ERR_INVALID_ARG),
     ("norm_topk_prob", 2, B.MOE_ERR_INVALID_ARG),
-    ("weight_layout", 2, B.MOE_ERR_INVALID_ARG),
+    ("weight_layout", 4, B.MOE_ERR_INVALID_ARG),
+    ("weight_layout", -1, B.MOE_ERR_INVALID_ARG),
+    ("weight_layout", 2, B.MOE_ERR_UNSUPPORTED),      # quantised: the packed shape rules
     ("weight_layout", 1, B.MOE_ERR_UNSUPPORTED),      # packed needs widths that are multiples of 128
     ("dtype", 7, B.MOE_ERR_UNSUPPORTED),
     ("out_dtype", 3, B.MOE_ERR_UNSUPPORTED),
@@ -113,6 +115,51 @@ def test_pack_refuses_before_launch(lib):
             B.moe_pack_weights(a["cfg"], a["n_groups"], a["rows"], a["cols"], a["src"], a["dst"], stream=0)
         assert ei.value.status == status, (kw, str(ei.value))
     B.moe_pack_weights(c, 0, 32, 64, None, None, stream=0)       # nothing to pack: no-op
+
+
+@pytest.mark.parametrize("layout,bits", [(B.MOE_LAYOUT_Q8, 8), (B.MOE_LAYOUT_Q4, 4)])
+def test_quantized_bytes_and_layout_rules(lib, layout, bits):
+    c = B.make_config(64, 256, 16, 2, 128, shared_inter=384, layout=layout)
+    assert B.moe_workspace_bytes(c) > 0
+    G, R, K = 16, 256, 2048
+    assert B.moe_quantized_bytes(c, G, R, K) == G * R * K * bits // 8 + G * R * 4
+    # the quantised layouts follow the packed shape rules
+    for bad in (B.make_config(64, 256, 16, 2, 128, dtype="f32", layout=layout),
+                B.make_config(64, 256, 16, 2, 96, layout=layout),
+                B.make_config(64, 256, 8, 2, 128, layout=layout)):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_workspace_bytes(bad)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_workspace_bytes(c.copy(weight_layout=4))
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+
+
+def test_quantize_refuses_before_launch(lib):
+    q8 = B.make_config(64, 256, 16, 2, 128, layout=B.MOE_LAYOUT_Q8)
+    cases = [
+        (dict(cfg=B.make_config(64, 256, 16, 2, 128, packed=True)), B.MOE_ERR_INVALID_ARG),   # not quantised
+        (dict(cols=48), B.MOE_ERR_UNSUPPORTED),                  # columns come in blocks of 32
+        (dict(rows=24), B.MOE_ERR_UNSUPPORTED),
+        (dict(rows=-16), B.MOE_ERR_INVALID_ARG),
+        (dict(src=None), B.MOE_ERR_INVALID_ARG),
+        (dict(dst=FAKE + 1024), B.MOE_ERR_INVALID_ARG),          # overlaps src
+        (dict(dst=FAKE * 4 + 8), B.MOE_ERR_UNSUPPORTED),         # not 16-byte aligned
+    ]
+    for kw, status in cases:
+        a = dict(cfg=q8, n_groups=2, rows=32, cols=256, src=FAKE, dst=FAKE * 4)
+        a.update(kw)
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_quantize_weights(a["cfg"], a["n_groups"], a["rows"], a["cols"], a["src"], a["dst"], stream=0)
+        assert ei.value.status == status, (kw, str(ei.value))
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_quantized_bytes(q8, 2, 32, 200)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+    B.moe_quantize_weights(q8, 0, 32, 256, None, None, stream=0)  # nothing to quantise: no-op
+    # expert weights must be 16-byte aligned (every weight load is 16 bytes wide)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_expert_gate_up(q8, 2, 128, 64, FAKE, None, FAKE, FAKE + 4, FAKE, stream=0)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "aligned" in str(ei.value)
 
 
 def test_router_stats_refuses_before_launch(lib):

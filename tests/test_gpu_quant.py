@@ -1,0 +1,174 @@
+"""Weight-only quantised experts (MOE_LAYOUT_Q8 / MOE_LAYOUT_Q4) on the GPU, against the oracle.
+
+* moe_quantize_weights: codes and scales bit for bit against the oracle's quantiser (both sides
+  decide the integer codes with the same float32 divisions), laid out by the documented order
+  written here as a numpy reshape/transpose.
+* moe_expert_ffn and moe_forward on quantised stacks: against the oracle evaluated on the exactly
+  dequantised weights (code * scale in float64), to the bf16 bar (2e-2 of the output RMS).
+* The router stays bf16 (packed), so the expert ids and weights are those of the packed bf16 layer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_experts_layer_10_amd import binding as B
+from mixture_experts_layer_10_amd import inputs as I
+from parity_util import compare_routing, rel_err, to_np, y_tolerance
+from test_gpu_packed import PACKED_SHAPES
+from test_gpu_parity import data_of, say
+
+pytestmark = pytest.mark.gpu
+
+LAYOUT = {8: B.MOE_LAYOUT_Q8, 4: B.MOE_LAYOUT_Q4}
+
+
+def quant_reference_bytes(codes, scales, bits):
+    """Documented byte image of a quantised stack: codes in block order (block (g, rb, kb), slot
+    l = row l % 16, column chunk l / 16, 8 codes per slot; int4 two per byte, low nibble first),
+    then the fp32 scales as [G, R]."""
+    G, R, K = codes.shape
+    slots = codes.reshape(G, R // 16, 16, K // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1, 8)
+    if bits == 8:
+        code_bytes = slots.astype(np.int8).view(np.uint8).reshape(-1)
+    else:
+        nib = (slots.astype(np.int16) & 0xF).astype(np.uint8)
+        code_bytes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).reshape(-1)
+    sc = np.ascontiguousarray(np.asarray(scales, np.float32))
+    return np.concatenate([code_bytes, sc.view(np.uint8).reshape(-1)])
+
+
+def bf16_bits(a):
+    return I.round_to_bf16_bits(np.asarray(a, np.float32))
+
+
+class Dequant:
+    """Lazy float64 view of a quantised-then-dequantised [G, R, K] stack, one group at a time
+    (the quantiser works per row, so a group alone gives the same codes)."""
+
+    def __init__(self, view, bits):
+        self.view, self.bits = view, bits
+
+    def __len__(self):
+        return len(self.view)
+
+    def __getitem__(self, g):
+        c, s = O.quantize_weights(np.asarray(self.view[g], np.float32)[None], self.bits)
+        return O.dequantize_weights(c, s)[0]
+
+
+def quant_stack(cfg, w_dev, G, R, K):
+    q = torch.empty(B.moe_quantized_bytes(cfg, G, R, K), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_weights(cfg, G, R, K, w_dev, q)
+    return q
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("G,R,K", [(1, 16, 32), (3, 48, 96), (2, 1536, 2048), (5, 2048, 768)])
+def test_quantize_weights_bit_exact(bits, G, R, K):
+    say(f"[quantize] int{bits} {G}x{R}x{K}")
+    rng = np.random.default_rng(G * 100 + R + K + bits)
+    w = rng.normal(0.0, 0.02, size=(G, R, K)).astype(np.float32)
+    w[0, 0, :] = 0.0                                      # an all-zero row
+    w[-1, -1, :] *= 1e-30                                 # a row of tiny (still normal) values
+    bits16 = bf16_bits(w)
+    src = torch.from_numpy(bits16.view(np.int16)).cuda().view(torch.bfloat16)
+    cfg = B.make_config(1, 128, 16, 1, 128, layout=LAYOUT[bits])
+    got = quant_stack(cfg, src, G, R, K)
+    torch.cuda.synchronize()
+    codes, scales = O.quantize_weights(I.bf16_bits_to_f32(bits16), bits)
+    ref = quant_reference_bytes(codes, scales, bits)
+    gb = got.cpu().numpy()
+    assert gb.size == ref.size
+    n_codes = G * R * K * bits // 8
+    bad = np.nonzero(gb[:n_codes] != ref[:n_codes])[0]
+    assert bad.size == 0, f"{bad.size} code bytes differ, first at {bad[:5]}"
+    assert np.array_equal(gb[n_codes:], ref[n_codes:])
+
+
+def _ffn(cfg, G, I_, R, x, ridx, off, gu, dn):
+    h = torch.full((R, I_), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((R, cfg.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    B.moe_expert_ffn(cfg, G, I_, R, x, ridx, off, gu, dn, h, out)
+    torch.cuda.synchronize()
+    return h, out
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("D,I_,rows", [
+    (256, 128, [300, 0, 5, 257, 1, 64, 513]),       # tall groups: 256-row tiles, LDS streaming
+    (384, 256, [700, 3, 260]),                      # down output 384 wide: a half-empty column tile
+    (2048, 768, [3, 0, 1, 7, 2, 5, 4, 6]),          # a few rows per group: weight streaming
+    (384, 256, [17, 40, 0, 9]),
+])
+def test_quant_ffn_vs_oracle(bits, D, I_, rows):
+    say(f"[quant ffn] int{bits} D={D} I={I_} rows={rows}")
+    G = len(rows)
+    offsets = np.zeros(G + 1, np.int64)
+    offsets[1:] = np.cumsum(rows)
+    R = int(offsets[-1])
+    d = I.make_inputs(I.custom_shape("qffn", R, D, G, 1, I_, seed=400 + D + bits))
+    dev = B.to_device(d.store)
+    cfg = B.make_config(R, D, 16, 1, I_, layout=LAYOUT[bits])
+    gu = quant_stack(cfg, dev["gate_up"], G, 2 * I_, D)
+    dn = quant_stack(cfg, dev["down"], G, D, I_)
+    off = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    perm = np.random.default_rng(2).permutation(R)
+    ridx = torch.from_numpy(perm.astype(np.int32)).cuda()
+    h, out = _ffn(cfg, G, I_, R, dev["x"], ridx, off, gu, dn)
+    ref = O.grouped_expert_ffn(d.values("x")[perm], offsets, Dequant(d.expert_view("gate_up"), bits),
+                               Dequant(d.expert_view("down"), bits))
+    got = to_np(out)
+    assert np.isfinite(got).all()
+    err = rel_err(got, ref)
+    say(f"  max|d out|/rms = {err:.3e}")
+    assert err <= 2e-2
+
+
+def quant_oracle_layer(d, bits, tokens):
+    s = d.shape
+    kw = {}
+    if s.shared_inter:
+        one = lambda name: Dequant([d.values(name)], bits)[0]
+        kw = dict(shared_gate_up=one("shared_gate_up"), shared_down=one("shared_down"),
+                  w_shared_gate=d.values("w_shared_gate"))
+    return O.forward_grouped(d.token_rows(tokens), d.values("w_router"), Dequant(d.expert_view("gate_up"), bits),
+                             Dequant(d.expert_view("down"), bits), s.top_k, s.norm_topk_prob, **kw)
+
+
+def quant_data(name):
+    if name in PACKED_SHAPES:
+        d = I.make_inputs(PACKED_SHAPES[name])
+        return d, B.to_device(d.store)
+    return data_of(name)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("name,n_sample", [("small", 64), ("decode", 64), ("prefill", 96), ("fanout", 96)])
+def test_quant_forward_vs_oracle(bits, name, n_sample):
+    say(f"[quant forward] int{bits} {name}")
+    d, dev = quant_data(name)
+    s = d.shape
+    N, k = s.n_tokens, s.top_k
+    cfg = B.config_for(s, "f32", layout=LAYOUT[bits])
+    qdev = B.quantize_device_weights(cfg, dev)
+    w = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    e = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    y = B.forward(cfg, qdev, weights=w, experts=e)
+    # the router is the packed bf16 router: same ids and weights bit for bit
+    cfg_p = B.config_for(s, "f32", packed=True)
+    w_p = torch.empty_like(w)
+    e_p = torch.empty_like(e)
+    B.forward(cfg_p, B.pack_device_weights(cfg_p, dev), weights=w_p, experts=e_p)
+    torch.cuda.synchronize()
+    assert torch.equal(e, e_p) and torch.equal(w.view(torch.int32), w_p.view(torch.int32))
+    got = to_np(y)
+    assert np.isfinite(got).all()
+    toks = np.sort(np.random.default_rng(3).choice(N, size=min(n_sample, N), replace=False))
+    y_ref, inter = quant_oracle_layer(d, bits, toks)
+    same, _ = compare_routing(to_np(w)[toks].astype(np.float64), to_np(e)[toks], inter["weights"],
+                              inter["experts"], inter["probs"], k)
+    err = rel_err(got[toks][same], y_ref[same])
+    tol = y_tolerance(s.dtype, "f32", y_ref)
+    say(f"  tokens {same.sum()}/{len(toks)}: max|dy|/rms = {err:.3e} (tol {tol:.3e})")
+    assert err <= tol
