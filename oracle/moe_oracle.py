@@ -360,3 +360,91 @@ def dequantize_weights(codes, scales):
     """The weights the quantised layer computes with: w'[g, r, c] = code[g, r, c] * scale[g, r], in
     float64 (exact: a small integer times a float32)."""
     return np.asarray(codes).astype(np.float64) * np.asarray(scales, np.float64)[..., None]
+
+
+# --------------------------------------------------------------------------------------------
+# Backward pass of the block ([VL-post] "What a mixture-of-experts layer is": the router and the
+# experts are trained end to end through the gated sum). Gradients of L = sum(dy * y) with respect
+# to x, W_r, the expert weights and the shared expert, by the chain rule through the forward
+# definition; the top-k choice is piecewise constant, so unselected probabilities get no gradient.
+# Probabilities are float64 here (the derivative of the exact softmax).
+# --------------------------------------------------------------------------------------------
+
+def swiglu_backward(v, gate_up, down, dout):
+    """For out = (silu(v G^T) * (v U^T)) Dn^T on rows v[m, D] and an output gradient dout[m, D]:
+    returns (dv, dgate_up [2I, D], ddown [D, I], out). silu'(a) = s (1 + a (1 - s)), s = sigmoid(a)."""
+    v = np.asarray(v, np.float64)
+    gu = np.asarray(gate_up, np.float64)
+    dn = np.asarray(down, np.float64)
+    inter = dn.shape[1]
+    a = v @ gu[:inter].T
+    b = v @ gu[inter:].T
+    s = sigmoid(a)
+    h = a * s * b
+    dout = np.asarray(dout, np.float64)
+    ddown = dout.T @ h
+    dh = dout @ dn
+    da = dh * b * (s * (1.0 + a * (1.0 - s)))
+    db = dh * a * s
+    dgate_up = np.concatenate([da.T @ v, db.T @ v], axis=0)
+    dv = da @ gu[:inter] + db @ gu[inter:]
+    return dv, dgate_up, ddown, h @ dn.T
+
+
+def backward(x, w_router, gate_up, down, k, dy, norm_topk_prob=True,
+             shared_gate_up=None, shared_down=None, w_shared_gate=None):
+    """Gradients of L = sum(dy * y) for the block y = sum_j w_j expert_{e_j}(x) [+ g(x) shared(x)].
+
+    Router: logits = x W_r^T, p = softmax (float64), the top-k by p; w = p_sel / S with S = sum of
+    p_sel when norm_topk_prob, so dL/dp_sel_k = (dw_k - sum_j dw_j w_j) / S (else dw_k), with
+    dw_j = dy . expert_{e_j}(x); then dlogits = p * (dp - sum_e dp_e p_e).
+    Experts: for each expert, the rows routed to it with output gradient w_j dy (swiglu_backward).
+    Shared expert: g = sigmoid(w_s . x) (1 if no w_s): ds = g dy, dg = dy . shared(x).
+    Returns dict(dx, dw_router, dgate_up, ddown [, dshared_gate_up, dshared_down, dw_shared_gate],
+    weights, experts, dweights)."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    wr = np.asarray(w_router, np.float64)
+    logits, probs, weights, experts = route(x, wr, k, norm_topk_prob, prob_dtype=np.float64)
+    N, D = x.shape
+    E = wr.shape[0]
+    dx = np.zeros_like(x)
+    dgu = np.zeros((E,) + np.asarray(gate_up[0]).shape)
+    ddn = np.zeros((E,) + np.asarray(down[0]).shape)
+    dw = np.zeros(weights.shape)
+    for e in range(E):
+        n_idx, j_idx = np.nonzero(experts == e)
+        if n_idx.size == 0:
+            continue
+        # a token picks an expert at most once, so n_idx has no repeats
+        w_e = weights[n_idx, j_idx][:, None]
+        dv, dgu[e], ddn[e], out = swiglu_backward(x[n_idx], gate_up[e], down[e], w_e * dy[n_idx])
+        dw[n_idx, j_idx] = np.sum(dy[n_idx] * out, axis=1)
+        dx[n_idx] += dv
+    psel = np.take_along_axis(probs, experts, axis=-1)
+    if norm_topk_prob:
+        S = psel.sum(axis=-1, keepdims=True)
+        dpsel = (dw - np.sum(dw * weights, axis=-1, keepdims=True)) / S
+    else:
+        dpsel = dw
+    dp = np.zeros_like(probs)
+    np.put_along_axis(dp, experts, dpsel, axis=-1)
+    dlogits = probs * (dp - np.sum(dp * probs, axis=-1, keepdims=True))
+    out = dict(dw_router=dlogits.T @ x, dgate_up=dgu, ddown=ddn, weights=weights, experts=experts,
+               dweights=dw, dlogits=dlogits)
+    dx += dlogits @ wr
+    if shared_gate_up is not None:
+        if w_shared_gate is not None:
+            ws_ = np.asarray(w_shared_gate, np.float64)
+            g = sigmoid(x @ ws_)
+        else:
+            g = np.ones(N)
+        dv, out["dshared_gate_up"], out["dshared_down"], s = swiglu_backward(x, shared_gate_up, shared_down,
+                                                                             g[:, None] * dy)
+        dx += dv
+        if w_shared_gate is not None:
+            dz = np.sum(dy * s, axis=1) * g * (1.0 - g)
+            out["dw_shared_gate"] = dz @ x
+            dx += dz[:, None] * ws_[None, :]
+    out["dx"] = dx
+    return out

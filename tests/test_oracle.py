@@ -466,3 +466,92 @@ def test_quantized_layer_is_the_layer_on_dequantised_weights():
     assert np.array_equal(gq, gu.astype(np.float64)) and np.array_equal(dq, dn.astype(np.float64))
     y, _ = O.forward_grouped(x, wr, gq, dq, k)
     assert np.allclose(y, O.forward_loop(x, wr, gq, dq, k), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# Backward pass (backward / swiglu_backward): central finite differences of L = sum(dy * y)
+# ----------------------------------------------------------------------------------------------
+
+def _fd_problem(seed, N=5, D=12, E=6, k=2, I_=7, shared=False):
+    """Tiny fp64 problem whose top-k choice has a wide margin (finite differences never flip it)."""
+    rng = np.random.default_rng(seed)
+    while True:
+        x = rng.normal(size=(N, D))
+        wr = rng.normal(0, 0.6, size=(E, D))
+        _, probs, _, _ = O.route(x, wr, k, True, prob_dtype=np.float64)
+        srt = -np.sort(-probs, axis=1)
+        if np.all(srt[:, k - 1] - srt[:, k] > 1e-3) if k < E else True:
+            break
+    p = dict(x=x, w_router=wr, gate_up=rng.normal(0, 0.3, size=(E, 2 * I_, D)),
+             down=rng.normal(0, 0.3, size=(E, D, I_)), dy=rng.normal(size=(N, D)))
+    if shared:
+        p.update(shared_gate_up=rng.normal(0, 0.3, size=(2 * 5, D)), shared_down=rng.normal(0, 0.3, size=(D, 5)),
+                 w_shared_gate=rng.normal(0, 0.3, size=D))
+    return p
+
+
+def _loss(p, k, norm, **over):
+    q = dict(p, **over)
+    kw = {}
+    if "shared_gate_up" in q:
+        kw = dict(shared_gate_up=q["shared_gate_up"], shared_down=q["shared_down"], w_shared_gate=q["w_shared_gate"])
+    _, _, w, e = O.route(q["x"], q["w_router"], k, norm, prob_dtype=np.float64)
+    y, _ = O.forward_grouped(q["x"], q["w_router"], q["gate_up"], q["down"], k, norm, routing=(w, e), **kw)
+    return float(np.sum(q["dy"] * y))
+
+
+def _fd_check(p, k, norm, grads, names, eps=1e-5):
+    for name, key in names:
+        base = p[name]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            num[idx] = (_loss(p, k, norm, **{name: plus}) - _loss(p, k, norm, **{name: minus})) / (2 * eps)
+        scale = max(np.abs(num).max(), 1e-3)
+        assert np.abs(grads[key] - num).max() <= 1e-7 * scale, (name, np.abs(grads[key] - num).max(), scale)
+
+
+@pytest.mark.parametrize("norm", [True, False])
+def test_backward_matches_finite_differences(norm):
+    p = _fd_problem(11 + norm)
+    k = 2
+    g = O.backward(p["x"], p["w_router"], p["gate_up"], p["down"], k, p["dy"], norm)
+    _fd_check(p, k, norm, g, [("x", "dx"), ("w_router", "dw_router"), ("gate_up", "dgate_up"), ("down", "ddown")])
+
+
+def test_backward_with_gated_shared_expert_matches_finite_differences():
+    p = _fd_problem(13, N=4, D=8, E=5, k=2, I_=4, shared=True)
+    k = 2
+    g = O.backward(p["x"], p["w_router"], p["gate_up"], p["down"], k, p["dy"], True, p["shared_gate_up"],
+                   p["shared_down"], p["w_shared_gate"])
+    _fd_check(p, k, True, g, [("x", "dx"), ("w_router", "dw_router"), ("shared_gate_up", "dshared_gate_up"),
+                              ("shared_down", "dshared_down"), ("w_shared_gate", "dw_shared_gate")])
+
+
+def test_backward_k1_renormalised_router_gets_no_gradient():
+    """k = 1 with renormalisation: the weight is p / p = 1 whatever the logits, so the router
+    weights get exactly zero gradient and dx is the selected expert's input gradient alone."""
+    p = _fd_problem(17, k=1)
+    g = O.backward(p["x"], p["w_router"], p["gate_up"], p["down"], 1, p["dy"], True)
+    assert np.all(g["dw_router"] == 0.0) and np.all(g["dlogits"] == 0.0)
+    e = g["experts"][:, 0]
+    for n in range(p["x"].shape[0]):
+        dv, _, _, _ = O.swiglu_backward(p["x"][n:n + 1], p["gate_up"][e[n]], p["down"][e[n]], p["dy"][n:n + 1])
+        assert np.allclose(g["dx"][n], dv[0], rtol=0, atol=1e-13)
+
+
+def test_swiglu_backward_single_row_by_hand():
+    """One input, one hidden unit, one output: out = silu(g v) (u v) d, so
+    d out / d v = d (silu'(g v) g (u v) + silu(g v) u), checked with the closed form of silu'."""
+    v, g_, u_, d_ = 0.7, -1.3, 0.4, 2.1
+    a = g_ * v
+    s = 1.0 / (1.0 + math.exp(-a))
+    dsilu = s * (1.0 + a * (1.0 - s))
+    dv, dgu, ddn, out = O.swiglu_backward(np.array([[v]]), np.array([[g_], [u_]]), np.array([[d_]]), np.array([[1.0]]))
+    assert math.isclose(out[0, 0], a * s * u_ * v * d_, rel_tol=1e-14)
+    assert math.isclose(dv[0, 0], d_ * (dsilu * g_ * u_ * v + a * s * u_), rel_tol=1e-13)
+    assert math.isclose(ddn[0, 0], a * s * u_ * v, rel_tol=1e-14)
+    assert math.isclose(dgu[0, 0], d_ * u_ * v * dsilu * v, rel_tol=1e-13)
+    assert math.isclose(dgu[1, 0], d_ * a * s * v, rel_tol=1e-13)
