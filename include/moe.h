@@ -203,6 +203,31 @@ int moe_quantized_bytes(const moe_config* cfg, int64_t n_groups, int64_t rows, i
 int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src,
                          void* dst, void* stream);
 
+/* Backward pass of the block ("Qwen3-VL + MoE: train to deploy", section "What a mixture-of-experts
+ * layer is": the router and the experts are trained end to end through the gated sum). Given the
+ * output gradient dy, writes the gradients of L = sum(dy * y) with respect to x and every weight:
+ *   router   w = p_sel / S (S = sum of p_sel) when norm_topk_prob, else p_sel; the top-k choice is
+ *            piecewise constant, so unselected probabilities get no gradient:
+ *            dw[n, j] = dy[n] . expert_{e_j}(x[n]),
+ *            dp_sel = (dw - sum_j dw_j w_j) / S (or dw), dlogits = p (dp - sum_e dp_e p_e),
+ *            dW_r = dlogits^T x, dx += dlogits W_r
+ *   experts  with a = x G_e^T, b = x U_e^T, h = silu(a) b and the row's gradient w dy:
+ *            dh = w dy Dn_e, da = dh b silu'(a), db = dh silu(a),
+ *            dDn_e = sum (w dy)^T h, dG_e = sum da^T x, dU_e = sum db^T x, dx += da G_e + db U_e
+ * The forward's routing, grouping and pre-activations are recomputed from x (nothing is kept from a
+ * moe_forward call). Matrix-core inputs are bf16 (h, w dy, da, db and dlogits rounded once),
+ * accumulation fp32; the sums over an expert's rows run in row order, deterministic.
+ *   cfg: dtype bf16, weight_layout MOE_LAYOUT_ROWS, shared_inter 0 (else MOE_ERR_UNSUPPORTED)
+ *   x [N, D], w_router [E, D], gate_up [E, 2I, D], down [E, D, I], dy [N, D]   (bf16, row-major)
+ *   dx [N, D], dw_router [E, D], dgate_up [E, 2I, D], ddown [E, D, I]       (fp32, overwritten;
+ *     an expert that received no token gets zeros)
+ *   ws, ws_bytes: at least moe_backward_workspace_bytes() bytes, 256-byte aligned
+ * All tensors 16-byte aligned. */
+int moe_backward_workspace_bytes(const moe_config* cfg, size_t* bytes);
+int moe_backward(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
+                 const void* dy, float* dx, float* dw_router, float* dgate_up, float* ddown, void* ws,
+                 size_t ws_bytes, void* stream);
+
 /* Router load statistics and the Switch-style balance loss ("Qwen3-VL + MoE: train to deploy",
  * section "An auxiliary balance loss", its N read as the number of experts):
  *   f[e] = counts[e] / (N k)                        fraction of the assignments routed to e

@@ -25,7 +25,7 @@ MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED, MOE_LAYOUT_Q8, MOE_LAYOUT_Q4 = 0, 1, 2, 3
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_pack_weights", "moe_router_stats",
             "moe_combine", "moe_forward", "moe_route_sigmoid", "moe_router_bias_update", "moe_permute_capped",
-            "moe_quantized_bytes", "moe_quantize_weights"]
+            "moe_quantized_bytes", "moe_quantize_weights", "moe_backward_workspace_bytes", "moe_backward"]
 
 
 class MoeError(RuntimeError):
@@ -99,6 +99,8 @@ def load(path: str = LIB_PATH):
         "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
         "moe_quantized_bytes": (ctypes.c_int, [_CFG, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_quantize_weights": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P]),
+        "moe_backward_workspace_bytes": (ctypes.c_int, [_CFG, ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     }
     for name, (res, args) in sig.items():
@@ -198,6 +200,32 @@ def moe_quantized_bytes(cfg, n_groups, rows, cols) -> int:
 def moe_quantize_weights(cfg, n_groups, rows, cols, src, dst, stream=None):
     _check("moe_quantize_weights", load().moe_quantize_weights(ctypes.byref(cfg), n_groups, rows, cols, _ptr(src),
                                                                _ptr(dst), _stream(stream)))
+
+
+def moe_backward_workspace_bytes(cfg) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_bytes", load().moe_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def moe_backward(cfg, x, w_router, gate_up, down, dy, dx, dw_router, dgate_up, ddown, ws, ws_bytes=None, stream=None):
+    _check("moe_backward", load().moe_backward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(gate_up), _ptr(down),
+                                               _ptr(dy), _ptr(dx), _ptr(dw_router), _ptr(dgate_up), _ptr(ddown),
+                                               _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def backward(cfg: MoeConfig, dev: dict, dy, ws=None, stream=None):
+    """Run moe_backward on the tensors of ``dev``; returns dict(dx, dw_router, dgate_up, ddown) (fp32)."""
+    import torch
+    x = dev["x"]
+    out = {"dx": torch.empty(x.shape, dtype=torch.float32, device=x.device)}
+    for name, key in (("dw_router", "w_router"), ("dgate_up", "gate_up"), ("ddown", "down")):
+        out[name] = torch.empty(dev[key].shape, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(moe_backward_workspace_bytes(cfg), 256), dtype=torch.uint8, device=x.device)
+    moe_backward(cfg, x, dev["w_router"], dev["gate_up"], dev["down"], dy, out["dx"], out["dw_router"], out["dgate_up"],
+                 out["ddown"], ws, stream=stream)
+    return out
 
 
 def moe_route_sigmoid(cfg, x, w_router, bias, logits, weights, experts, ws=None, ws_bytes=None, stream=None):

@@ -1,0 +1,369 @@
+// Backward pass of the MoE block ("Qwen3-VL + MoE: train to deploy", section "What a mixture-of-
+// experts layer is": router and experts trained through the gated sum). For L = sum(dy * y):
+//   experts   z = [a | b] = X_p GU_e^T, h = silu(a) b, dhu = dy[token] Dn_e, dh = w dhu,
+//             da = dh b silu'(a), db = dh silu(a), dw = dhu . h (= dy . expert output),
+//             dx_rows = [da | db] GU_e, dDn_e = sum_p (w dy)^T h, dGU_e = sum_p [da | db]^T X_p
+//   router    dp_sel = (dw - sum_j dw_j w_j) / S (renormalised) or dw, dlogit = p (dp - sum p dp),
+//             dW_r = dlogit^T x, dx += dlogit W_r
+// The contractions over D, I or E run on the grouped GEMM kernels in their [out, in] form on
+// transposed weight copies; the weight gradients, whose contraction runs over each expert's rows,
+// use gemm_wgrad_kernel on transposed activation copies whose per-expert row ranges are padded to
+// multiples of 64 with zeros. This file holds those transposes and the elementwise steps.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kTT = 64;          // transpose tile
+
+// out[g][c][r] = in[g][r][c] for r < R, 0 for R <= r < Rp (bf16). One 64 x 64 tile per workgroup;
+// rows of 16-byte chunks both ways, staged through LDS with a one-element pad per row.
+__global__ __launch_bounds__(256) void transpose_mat_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                            int R, int C, int Rp) {
+  __shared__ uint16_t s[kTT][kTT + 2];
+  const int64_t g = blockIdx.z;
+  const int r0 = blockIdx.y * kTT, c0 = blockIdx.x * kTT, tid = threadIdx.x;
+  const uint16_t* src = in + g * R * static_cast<int64_t>(C);
+  for (int t = tid; t < kTT * (kTT / 8); t += 256) {
+    const int rr = t >> 3, ch = (t & 7) * 8;
+    const int r = r0 + rr, c = c0 + ch;
+    u32x4 v = {0, 0, 0, 0};
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * C + c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[rr][ch + i] = static_cast<uint16_t>(v[i >> 1] >> (16 * (i & 1)));
+  }
+  __syncthreads();
+  uint16_t* dst = out + g * C * static_cast<int64_t>(Rp);
+  for (int t = tid; t < kTT * (kTT / 8); t += 256) {
+    const int cc = t >> 3, ch = (t & 7) * 8;
+    const int c = c0 + cc, r = r0 + ch;
+    if (c >= C || r >= Rp) continue;
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = static_cast<uint32_t>(s[ch + 2 * i][cc]) | (static_cast<uint32_t>(s[ch + 2 * i + 1][cc]) << 16);
+    *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(c) * Rp + r) = v;
+  }
+}
+
+void launch_transpose_mat(const uint16_t* in, uint16_t* out, int64_t G, int R, int C, int Rp, hipStream_t st) {
+  if (G <= 0 || R <= 0 || C <= 0) return;
+  dim3 grid((C + kTT - 1) / kTT, (Rp + kTT - 1) / kTT, static_cast<unsigned>(G));
+  transpose_mat_kernel<<<grid, 256, 0, st>>>(in, out, R, C, Rp);
+}
+
+// Per-expert row ranges padded to multiples of 64: poff[g] = sum_{g' < g} roundup(counts[g'], 64).
+__global__ __launch_bounds__(512) void pad_offsets_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ poff, int G) {
+  __shared__ int s_wave[8];
+  const int g = threadIdx.x, lane = g & 63, wave = g >> 6;
+  const int v = g < G ? (counts[g] + 63) / 64 * 64 : 0;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  if (g < G) poff[g] = before + inc - v;
+  if (g == G - 1) poff[G] = before + inc;
+}
+
+void launch_pad_offsets(const int32_t* counts, int32_t* poff, int G, hipStream_t st) {
+  pad_offsets_kernel<<<1, 512, 0, st>>>(counts, poff, G);
+}
+
+// out[m][q] for the padded row space q in [0, qtot): row q of group g (poff[g] <= q < poff[g+1]) is
+// sorted row p = off[g] + q - poff[g] if that lies inside the group, else zero. The source row is
+// token_of[p] when gathering, the value is scaled by scale[p] when given (rounded to bf16 once).
+// With off == nullptr there is one group of n1 rows padded to qtot.
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const uint16_t* __restrict__ src, int M,
+                                                             const int32_t* __restrict__ gather,
+                                                             const float* __restrict__ scale,
+                                                             const int32_t* __restrict__ off,
+                                                             const int32_t* __restrict__ poff, int G, int n1,
+                                                             int64_t qmax, uint16_t* __restrict__ out, int64_t ld) {
+  __shared__ uint16_t s[kTT][kTT + 2];
+  __shared__ int s_src[kTT];
+  __shared__ float s_scl[kTT];
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * kTT;
+  const int m0 = blockIdx.y * kTT, tid = threadIdx.x;
+  const int64_t qtot = off ? poff[G] : qmax;
+  if (q0 >= qtot) return;
+  if (tid < kTT) {
+    const int64_t q = q0 + tid;
+    int64_t p = -1;
+    if (q < qtot) {
+      if (off) {
+        int lo = 0, hi = G;                           // poff[lo] <= q < poff[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (poff[mid] <= q) lo = mid; else hi = mid;
+        }
+        const int64_t r = q - poff[lo];
+        if (r < off[lo + 1] - off[lo]) p = off[lo] + r;
+      } else if (q < n1) {
+        p = q;
+      }
+    }
+    s_src[tid] = p < 0 ? -1 : (gather ? gather[p] : static_cast<int>(p));
+    s_scl[tid] = p < 0 ? 0.f : (scale ? scale[p] : 1.f);
+  }
+  __syncthreads();
+  for (int t = tid; t < kTT * (kTT / 8); t += 256) {
+    const int qq = t >> 3, ch = (t & 7) * 8;
+    const int m = m0 + ch;
+    const int srow = s_src[qq];
+    u32x4 v = {0, 0, 0, 0};
+    if (srow >= 0 && m < M) v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(srow) * M + m);
+    if (scale) {
+      const float sc = s_scl[qq];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_to_f32(static_cast<uint16_t>(v[i] & 0xffff)) * sc;
+        const float hi = bf16_to_f32(static_cast<uint16_t>(v[i] >> 16)) * sc;
+        v[i] = pack_bf16x2(lo, hi);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[qq][ch + i] = static_cast<uint16_t>(v[i >> 1] >> (16 * (i & 1)));
+  }
+  __syncthreads();
+  for (int t = tid; t < kTT * (kTT / 8); t += 256) {
+    const int mm = t >> 3, ch = (t & 7) * 8;
+    const int m = m0 + mm;
+    const int64_t q = q0 + ch;
+    if (m >= M || q >= qtot) continue;
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = static_cast<uint32_t>(s[ch + 2 * i][mm]) | (static_cast<uint32_t>(s[ch + 2 * i + 1][mm]) << 16);
+    *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(m) * ld + q) = v;
+  }
+}
+
+void launch_transpose_rows(const uint16_t* src, int M, const int32_t* gather, const float* scale, const int32_t* off,
+                           const int32_t* poff, int G, int n1, int64_t qmax, uint16_t* out, int64_t ld, hipStream_t st) {
+  if (qmax <= 0 || M <= 0) return;
+  dim3 grid(static_cast<unsigned>((qmax + kTT - 1) / kTT), (M + kTT - 1) / kTT);
+  transpose_rows_kernel<<<grid, 256, 0, st>>>(src, M, gather, scale, off, poff, G, n1, qmax, out, ld);
+}
+
+// w_perm[slot_pos[a]] = weights[a], assign_of[slot_pos[a]] = a; ones[a] = 1.
+__global__ __launch_bounds__(256) void scatter_assign_kernel(const int32_t* __restrict__ slot_pos, const float* __restrict__ weights,
+                                                             float* __restrict__ w_perm, int32_t* __restrict__ assign_of,
+                                                             float* __restrict__ ones, int64_t A) {
+  const int64_t a = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (a >= A) return;
+  const int p = slot_pos[a];
+  w_perm[p] = weights[a];
+  assign_of[p] = static_cast<int32_t>(a);
+  ones[a] = 1.f;
+}
+
+void launch_scatter_assign(const int32_t* slot_pos, const float* weights, float* w_perm, int32_t* assign_of, float* ones,
+                           int64_t A, hipStream_t st) {
+  if (A <= 0) return;
+  scatter_assign_kernel<<<static_cast<unsigned>((A + 255) / 256), 256, 0, st>>>(slot_pos, weights, w_perm, assign_of, ones, A);
+}
+
+// One wave per sorted row p: from z = [a | b] (fp32) and dhu = dy[token] Dn_e (fp32):
+//   h = bf16(silu(a) b)                 (the forward's rounding)
+//   dw[assign_of[p]] = sum_i dhu_i h_i  (= dy . expert output)
+//   dh = w dhu, da = dh b silu'(a), db = dh silu(a) -> dab = bf16([da | db])
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ z, const float* __restrict__ dhu,
+                                                         const float* __restrict__ w_perm, const int32_t* __restrict__ assign_of,
+                                                         const int32_t* __restrict__ n_rows, int64_t A, int I,
+                                                         uint16_t* __restrict__ h, uint16_t* __restrict__ dab,
+                                                         float* __restrict__ dw) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (p >= A || p >= *n_rows) return;
+  const int lane = threadIdx.x & 63;
+  const float w = w_perm[p];
+  const float* zp = z + p * 2 * I;
+  const float* dp = dhu + p * I;
+  float dot = 0.f;
+  for (int i = lane * 4; i < I; i += 256) {
+    const f32x4 av = *reinterpret_cast<const f32x4*>(zp + i);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(zp + I + i);
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(dp + i);
+    float hh[4], da[4], db[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float a = av[t], b = bv[t];
+      const float s = 1.0f / (1.0f + __expf(-a));
+      hh[t] = bf16_to_f32(f32_to_bf16(a * s * b));
+      dot = fmaf(gv[t], hh[t], dot);
+      const float dh = w * gv[t];
+      da[t] = dh * b * (s * (1.0f + a * (1.0f - s)));
+      db[t] = dh * a * s;
+    }
+    uint2 hv, dav, dbv;
+    hv.x = pack_bf16x2(hh[0], hh[1]);
+    hv.y = pack_bf16x2(hh[2], hh[3]);
+    dav.x = pack_bf16x2(da[0], da[1]);
+    dav.y = pack_bf16x2(da[2], da[3]);
+    dbv.x = pack_bf16x2(db[0], db[1]);
+    dbv.y = pack_bf16x2(db[2], db[3]);
+    *reinterpret_cast<uint2*>(h + p * I + i) = hv;
+    *reinterpret_cast<uint2*>(dab + p * 2 * I + i) = dav;
+    *reinterpret_cast<uint2*>(dab + p * 2 * I + I + i) = dbv;
+  }
+  dot = wave_sum(dot);
+  if (lane == 0) dw[assign_of[p]] = dot;
+}
+
+void launch_swiglu_bwd(const float* z, const float* dhu, const float* w_perm, const int32_t* assign_of, const int32_t* n_rows,
+                       int64_t A, int I, uint16_t* h, uint16_t* dab, float* dw, hipStream_t st) {
+  if (A <= 0) return;
+  swiglu_bwd_kernel<<<static_cast<unsigned>((A + 3) / 4), 256, 0, st>>>(z, dhu, w_perm, assign_of, n_rows, A, I, h, dab, dw);
+}
+
+// One wave per token: p = softmax(logits) in fp32, the gradient of the kept (renormalised) weights
+// back to the logits; dlogit [N, Ep] bf16, zero in the padding columns E <= e < Ep.
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ logits, const float* __restrict__ weights,
+                                                         const int32_t* __restrict__ experts, const float* __restrict__ dw,
+                                                         int64_t N, int E, int Ep, int k, int norm,
+                                                         uint16_t* __restrict__ dlogit) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int lane = threadIdx.x & 63;
+  const float* lg = logits + n * E;
+  float mx = -INFINITY;
+  for (int e = lane; e < E; e += 64) mx = fmaxf(mx, lg[e]);
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int e = lane; e < E; e += 64) sum += __expf(lg[e] - mx);
+  sum = wave_sum(sum);
+  const float inv = 1.0f / sum;
+  // selected weights' gradients, in slot order (every lane computes the same k-term sums)
+  float S = 0.f, dww = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = n * k + j;
+    S += __expf(lg[experts[a]] - mx) * inv;
+    dww += dw[a] * weights[a];
+  }
+  for (int e = lane; e < Ep; e += 64) {
+    float g = 0.f;
+    if (e < E) {
+      float dp = 0.f, t = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int64_t a = n * k + j;
+        const float dps = norm ? (dw[a] - dww) / S : dw[a];
+        const float pj = __expf(lg[experts[a]] - mx) * inv;
+        t += dps * pj;
+        if (experts[a] == e) dp = dps;
+      }
+      const float pe = __expf(lg[e] - mx) * inv;
+      g = pe * (dp - t);
+    }
+    dlogit[n * Ep + e] = f32_to_bf16(g);
+  }
+}
+
+void launch_router_bwd(const float* logits, const float* weights, const int32_t* experts, const float* dw, int64_t N, int E,
+                       int Ep, int k, int norm, uint16_t* dlogit, hipStream_t st) {
+  if (N <= 0) return;
+  router_bwd_kernel<<<static_cast<unsigned>((N + 3) / 4), 256, 0, st>>>(logits, weights, experts, dw, N, E, Ep, k, norm, dlogit);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Weight-gradient GEMM: out[g][m][n] = sum_q A[m][q] B[n][q] over q in [poff[g], poff[g+1]) (or
+// [0, qtot) for one group), A [M][ld], B [Nn][ld] bf16 with zeros in the padding, out fp32.
+// 128 x 128 tiles, four waves of 64 x 64 (2 x 2 blocks of 32 x 32), k step 64 through two LDS
+// buffers (register staged), the XOR swizzle of the forward kernels. One workgroup per tile.
+// ---------------------------------------------------------------------------------------------
+constexpr int kWB = 128, kWK = 64;
+
+__device__ __forceinline__ int wswz(int row, int chunk) { return row * kWK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+__global__ __launch_bounds__(256) void gemm_wgrad_kernel(const uint16_t* __restrict__ Am, const uint16_t* __restrict__ Bm,
+                                                         int64_t ld, const int32_t* __restrict__ poff, int64_t qtot,
+                                                         int M, int Nn, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kWB * kWK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kWB * kWK];
+  const int g = blockIdx.z;
+  const int m0 = blockIdx.y * kWB, n0 = blockIdx.x * kWB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t q0 = poff ? poff[g] : 0;
+  const int64_t q1 = poff ? poff[g + 1] : qtot;
+  const int ksteps = static_cast<int>((q1 - q0) / kWK);
+  // four 16-byte chunks of A and of B per thread and stage: row (tid + 256 j) / 8, chunk tid % 8
+  const uint16_t* srcA[4];
+  const uint16_t* srcB[4];
+  const int ch = tid & 7;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rr = (tid + 256 * j) >> 3;
+    srcA[j] = Am + static_cast<int64_t>(min(m0 + rr, M - 1)) * ld + q0 + ch * 8;
+    srcB[j] = Bm + static_cast<int64_t>(min(n0 + rr, Nn - 1)) * ld + q0 + ch * 8;
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int ks) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = *reinterpret_cast<const u32x4*>(srcA[j] + static_cast<int64_t>(ks) * kWK);
+      rb[j] = *reinterpret_cast<const u32x4*>(srcB[j] + static_cast<int64_t>(ks) * kWK);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = (tid + 256 * j) >> 3;
+      *reinterpret_cast<u32x4*>(&sA[buf][wswz(rr, ch)]) = ra[j];
+      *reinterpret_cast<u32x4*>(&sB[buf][wswz(rr, ch)]) = rb[j];
+    }
+  };
+  if (ksteps > 0) {
+    gload(0);
+    sstore(0);
+    __syncthreads();
+  }
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < ksteps) gload(ks + 1);
+#pragma unroll
+    for (int kk = 0; kk < kWK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      u32x4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&sA[buf][wswz(wm * 64 + i * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const u32x4*>(&sB[buf][wswz(wn * 64 + j * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+    }
+    if (ks + 1 < ksteps) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  float* og = out + static_cast<int64_t>(g) * M * Nn;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    if (n >= Nn) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * 64 + i * 32 + acc_row(e, lane);
+        if (m < M) og[static_cast<int64_t>(m) * Nn + n] = acc[i][j][e];
+      }
+  }
+}
+
+void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32_t* poff, int64_t qtot, int G, int M, int Nn,
+                  float* out, hipStream_t st) {
+  if (G <= 0 || M <= 0 || Nn <= 0) return;
+  dim3 grid((Nn + kWB - 1) / kWB, (M + kWB - 1) / kWB, static_cast<unsigned>(G));
+  gemm_wgrad_kernel<<<grid, 256, 0, st>>>(A, Bm, ld, poff, qtot, M, Nn, out);
+}
+
+}  // namespace moe

@@ -252,6 +252,81 @@ static int combine_impl(const moe_config* c, const float* out_perm, const float*
   return check_launch("moe_combine");
 }
 
+// Backward workspace: routing and permutation state, the recomputed pre-activations, the
+// gradients' intermediates, transposed weight copies and the padded transposed activations.
+struct BwdLayout {
+  size_t route_partial, logits, weights, experts, counts, offsets, block_counts, token_of, slot_pos, w_perm, assign_of,
+      ones, dw, poff, z, dhu, h, dab, dx_rows, dlogit, dxr, dnT, guT, wrT, doT, xgT, hT, dabT, dlogitT, xT, total;
+  int64_t Ep, Qs, Ns;
+};
+
+static BwdLayout bwd_layout_of(const moe_config* c) {
+  BwdLayout L{};
+  const int64_t N = c->n_tokens, A = N * c->top_k, E = c->n_experts, D = c->hidden, I = c->inter;
+  L.Ep = (E + 7) / 8 * 8;
+  L.Qs = (A + 64 * E + 7) / 8 * 8;
+  L.Ns = (N + 63) / 64 * 64;
+  size_t at = 0;
+  auto take = [&](int64_t bytes) { const size_t p = at; at += align256(static_cast<size_t>(bytes)); return p; };
+  L.route_partial = take(static_cast<int64_t>(route_partial_bytes(c)));
+  L.logits = take(N * E * 4);
+  L.weights = take(A * 4);
+  L.experts = take(A * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.block_counts = take(permute_chunks(A) * E * 4);
+  L.token_of = take(A * 4);
+  L.slot_pos = take(A * 4);
+  L.w_perm = take(A * 4);
+  L.assign_of = take(A * 4);
+  L.ones = take(A * 4);
+  L.dw = take(A * 4);
+  L.poff = take((E + 1) * 4);
+  L.z = take(A * 2 * I * 4);
+  L.dhu = take(A * I * 4);
+  L.h = take(A * I * 2);
+  L.dab = take(A * 2 * I * 2);
+  L.dx_rows = take(A * D * 4);
+  L.dlogit = take(N * L.Ep * 2);
+  L.dxr = take(N * D * 4);
+  L.dnT = take(E * I * D * 2);
+  L.guT = take(E * D * 2 * I * 2);
+  L.wrT = take(D * L.Ep * 2);
+  L.doT = take(D * L.Qs * 2);
+  L.xgT = take(D * L.Qs * 2);
+  L.hT = take(I * L.Qs * 2);
+  L.dabT = take(2 * I * L.Qs * 2);
+  L.dlogitT = take(L.Ep * L.Ns * 2);
+  L.xT = take(D * L.Ns * 2);
+  L.total = at;
+  return L;
+}
+
+static int backward_checks(const moe_config* c) {
+  MOE_TRY(validate_config(c));
+  if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs dtype bf16");
+  if (c->weight_layout != MOE_LAYOUT_ROWS) return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs row-layout weights");
+  if (c->shared_inter != 0) return fail(MOE_ERR_UNSUPPORTED, "the backward pass has no shared expert");
+  return MOE_OK;
+}
+
+// The [out, in] grouped GEMM (fp32 output) on arbitrary operands: out[p] = X[row p] W_g^T, K = k_in.
+static GemmArgs nt_args(const void* x, const int32_t* row_index, const int32_t* offsets, int G, int64_t max_rows,
+                        const void* w, int n_out, int k_in, void* out) {
+  GemmArgs a{};
+  a.x = x;
+  a.row_index = row_index;
+  a.offsets = offsets;
+  a.w = w;
+  a.out = out;
+  a.max_rows = max_rows;
+  a.G = G;
+  a.D = n_out;      // the down form: NOUT = D, K = I
+  a.I = k_in;
+  a.bf16 = true;
+  return a;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -440,6 +515,79 @@ int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, 
   launch_quantize(static_cast<const uint16_t*>(src), static_cast<uint8_t*>(dst), n_groups, static_cast<int>(rows),
                   static_cast<int>(cols), bits, static_cast<hipStream_t>(stream));
   MOE_TRY(check_launch("moe_quantize_weights"));
+  return ok();
+}
+
+int moe_backward_workspace_bytes(const moe_config* cfg, size_t* bytes) {
+  MOE_TRY(backward_checks(cfg));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = bwd_layout_of(cfg).total;
+  return ok();
+}
+
+int moe_backward(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
+                 const void* dy, float* dx, float* dw_router, float* dgate_up, float* ddown, void* ws, size_t ws_bytes,
+                 void* stream) {
+  MOE_TRY(backward_checks(cfg));
+  if (cfg->n_tokens == 0) return ok();
+  if (!x || !w_router || !gate_up || !down || !dy) return fail(MOE_ERR_INVALID_ARG, "x, w_router, gate_up, down or dy is NULL");
+  if (!dx || !dw_router || !dgate_up || !ddown) return fail(MOE_ERR_INVALID_ARG, "dx, dw_router, dgate_up or ddown is NULL");
+  for (const void* p : {x, w_router, gate_up, down, dy})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return fail(MOE_ERR_UNSUPPORTED, "inputs must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(dx) | reinterpret_cast<uintptr_t>(dw_router) | reinterpret_cast<uintptr_t>(dgate_up) |
+       reinterpret_cast<uintptr_t>(ddown)) & 15)
+    return fail(MOE_ERR_UNSUPPORTED, "gradient outputs must be 16-byte aligned");
+  const BwdLayout L = bwd_layout_of(cfg);
+  if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, L.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MOE_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+
+  char* base = static_cast<char*>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+  auto H16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t N = cfg->n_tokens, A = N * cfg->top_k;
+  const int E = static_cast<int>(cfg->n_experts), D = static_cast<int>(cfg->hidden), I = static_cast<int>(cfg->inter);
+  const int Ep = static_cast<int>(L.Ep);
+  int32_t* offsets = I32(L.offsets);
+  int32_t* token_of = I32(L.token_of);
+
+  // forward pieces: routing (with logits), grouping, pre-activations z = [a | b]
+  MOE_TRY(route_impl(cfg, x, w_router, nullptr, F(L.logits), F(L.weights), I32(L.experts), nullptr,
+                     route_partial_bytes(cfg) ? F(L.route_partial) : nullptr, st));
+  MOE_TRY(permute_impl(cfg, I32(L.experts), nullptr, I32(L.counts), offsets, token_of, I32(L.slot_pos), nullptr,
+                       I32(L.block_counts), st));
+  launch_scatter_assign(I32(L.slot_pos), F(L.weights), F(L.w_perm), I32(L.assign_of), F(L.ones), A, st);
+  launch_pad_offsets(I32(L.counts), I32(L.poff), E, st);
+  launch_transpose_mat(static_cast<const uint16_t*>(down), H16(L.dnT), E, D, I, D, st);       // [E, I, D]
+  launch_transpose_mat(static_cast<const uint16_t*>(gate_up), H16(L.guT), E, 2 * I, D, 2 * I, st);  // [E, D, 2I]
+  launch_transpose_mat(static_cast<const uint16_t*>(w_router), H16(L.wrT), 1, E, D, Ep, st);  // [D, Ep]
+  MOE_TRY(check_launch("moe_backward (setup)"));
+  launch_down(nt_args(x, token_of, offsets, E, A, gate_up, 2 * I, D, F(L.z)), st);
+  launch_down(nt_args(dy, token_of, offsets, E, A, H16(L.dnT), I, D, F(L.dhu)), st);
+  MOE_TRY(check_launch("moe_backward (recompute)"));
+  // expert and router gradients of the activations
+  launch_swiglu_bwd(F(L.z), F(L.dhu), F(L.w_perm), I32(L.assign_of), offsets + E, A, I, H16(L.h), H16(L.dab), F(L.dw), st);
+  launch_router_bwd(F(L.logits), F(L.weights), I32(L.experts), F(L.dw), N, E, Ep, static_cast<int>(cfg->top_k),
+                    cfg->norm_topk_prob, H16(L.dlogit), st);
+  launch_down(nt_args(H16(L.dab), nullptr, offsets, E, A, H16(L.guT), D, 2 * I, F(L.dx_rows)), st);
+  launch_down(nt_args(H16(L.dlogit), nullptr, nullptr, 1, N, H16(L.wrT), D, Ep, F(L.dxr)), st);
+  moe_config c32 = *cfg;
+  c32.out_dtype = MOE_F32;
+  MOE_TRY(combine_impl(&c32, F(L.dx_rows), F(L.ones), I32(L.slot_pos), F(L.dxr), nullptr, dx, st));
+  // weight gradients over each expert's rows (padded transposes), then over the tokens for W_r
+  const int32_t* poff = I32(L.poff);
+  launch_transpose_rows(static_cast<const uint16_t*>(dy), D, token_of, F(L.w_perm), offsets, poff, E, 0, L.Qs, H16(L.doT), L.Qs, st);
+  launch_transpose_rows(static_cast<const uint16_t*>(x), D, token_of, nullptr, offsets, poff, E, 0, L.Qs, H16(L.xgT), L.Qs, st);
+  launch_transpose_rows(H16(L.h), I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, H16(L.hT), L.Qs, st);
+  launch_transpose_rows(H16(L.dab), 2 * I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, H16(L.dabT), L.Qs, st);
+  launch_transpose_rows(H16(L.dlogit), Ep, nullptr, nullptr, nullptr, nullptr, 1, static_cast<int>(N), L.Ns, H16(L.dlogitT), L.Ns, st);
+  launch_transpose_rows(static_cast<const uint16_t*>(x), D, nullptr, nullptr, nullptr, nullptr, 1, static_cast<int>(N), L.Ns, H16(L.xT), L.Ns, st);
+  MOE_TRY(check_launch("moe_backward (transposes)"));
+  launch_wgrad(H16(L.doT), H16(L.hT), L.Qs, poff, 0, E, D, I, ddown, st);
+  launch_wgrad(H16(L.dabT), H16(L.xgT), L.Qs, poff, 0, E, 2 * I, D, dgate_up, st);
+  launch_wgrad(H16(L.dlogitT), H16(L.xT), L.Ns, nullptr, L.Ns, 1, E, D, dw_router, st);
+  MOE_TRY(check_launch("moe_backward (weight gradients)"));
   return ok();
 }
 

@@ -28,7 +28,7 @@ def header_functions():
 
 def test_header_symbols_all_exported(lib):
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -160,6 +160,26 @@ def test_quantize_refuses_before_launch(lib):
     with pytest.raises(B.MoeError) as ei:
         B.moe_expert_gate_up(q8, 2, 128, 64, FAKE, None, FAKE, FAKE + 4, FAKE, stream=0)
     assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "aligned" in str(ei.value)
+
+
+def test_backward_rules_and_workspace(lib):
+    c = B.make_config(64, 256, 12, 2, 128)
+    n = B.moe_backward_workspace_bytes(c)
+    assert n > 64 * 2 * 2 * 128 * 4                               # at least the recomputed pre-activations
+    for bad, what in ((c.copy(dtype=B.MOE_F32, out_dtype=B.MOE_F32), "bf16"),
+                      (B.make_config(64, 256, 16, 2, 128, packed=True), "row-layout"),
+                      (c.copy(shared_inter=128), "shared")):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_backward_workspace_bytes(bad)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED and what in str(ei.value)
+    args = [FAKE] * 5 + [FAKE * 2] * 4
+    with pytest.raises(B.MoeError) as ei:                          # no workspace
+        B.moe_backward(c, *args, None, 0, stream=0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_backward(c, *args[:4], None, *args[5:], FAKE * 4, n, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    B.moe_backward(c.copy(n_tokens=0), *args, None, 0, stream=0)  # no tokens: no-op
 
 
 def test_router_stats_refuses_before_launch(lib):

@@ -1,0 +1,92 @@
+"""Backward pass (moe_backward) on the GPU against the oracle's chain-rule gradients (fp64,
+pinned by finite differences in test_oracle.py), on the same seeded bf16 inputs and a seeded
+output gradient dy ~ N(0, 1) rounded to bf16.
+
+Bar (derived from the arithmetic; the pages state none for gradients): the matrix-core inputs
+h, w dy, da, db and dlogits are rounded to bf16 once (relative error <= 2^-9 each, two rounded
+operands per product) and accumulated in fp32, so each gradient G must satisfy
+    ||G - G_ref|| / ||G_ref|| <= 1e-2   (Frobenius, about 4 * 2^-9)
+    max|G - G_ref| <= 2e-2 * max|G_ref|.
+The forward's max-abs / RMS measure does not suit weight gradients: an entry is a sum over the few
+rows routed to one expert of products of heavy-tailed factors, so max|G| / RMS(G) reaches 20-30 and
+one bf16 rounding shows as several percent of the RMS (a CPU emulation of these roundings gives the
+same figures as the GPU). Shapes are chosen without near ties in the top-k (the selection, hence
+the gradient, is then unique).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_experts_layer_10_amd import binding as B
+from mixture_experts_layer_10_amd import inputs as I
+from parity_util import GAP, rel_err
+from test_gpu_parity import data_of, say
+
+pytestmark = pytest.mark.gpu
+
+NORM_TOL, MAX_TOL = 1e-2, 2e-2
+
+SHAPES = {
+    "small": I.custom_shape("bwd_small", 40, 256, 16, 2, 128, seed=51),
+    "ragged_e12": I.custom_shape("bwd_e12", 37, 384, 12, 3, 256, seed=52),          # E padded to 16 for W_r^T
+    "keras_like": I.custom_shape("bwd_keras", 512, 2048, 60, 4, 1408, seed=53),      # E = 60, wide experts
+    "tall": I.custom_shape("bwd_tall", 3000, 512, 8, 2, 256, seed=54),               # long per-expert sums
+    "norm_off": I.custom_shape("bwd_nonorm", 64, 256, 16, 4, 128, norm_topk_prob=False, seed=55),
+}
+
+
+def bf16_dev(a):
+    return torch.from_numpy(I.round_to_bf16_bits(np.asarray(a, np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def run_and_compare(d, dev):
+    s = d.shape
+    dy_np = I.bf16_bits_to_f32(I.round_to_bf16_bits(
+        np.random.default_rng(s.seed + 7).standard_normal((s.n_tokens, s.hidden), dtype=np.float32))).astype(np.float64)
+    cfg = B.config_for(s)
+    g = B.backward(cfg, dev, bf16_dev(dy_np))
+    torch.cuda.synchronize()
+    ref = O.backward(d.values("x"), d.values("w_router"), d.expert_view("gate_up"), d.expert_view("down"),
+                     s.top_k, dy_np, s.norm_topk_prob)
+    _, probs, _, _ = O.route(d.values("x"), d.values("w_router"), s.top_k, s.norm_topk_prob)
+    assert (O.k_gap(probs, s.top_k) >= GAP).all(), "shape has near ties: pick another seed"
+    for name, key in (("dx", "dx"), ("dw_router", "dw_router"), ("dgate_up", "dgate_up"), ("ddown", "ddown")):
+        got = g[name].cpu().numpy().astype(np.float64)
+        want = np.asarray(ref[key], np.float64).reshape(got.shape)
+        assert np.isfinite(got).all(), name
+        diff = got - want
+        norm_err = float(np.sqrt(np.sum(diff * diff) / np.sum(want * want)))
+        max_err = float(np.abs(diff).max() / np.abs(want).max())
+        say(f"  {name}: normwise {norm_err:.3e}, max/max {max_err:.3e}, max/rms {rel_err(got, want):.3e}")
+        assert norm_err <= NORM_TOL and max_err <= MAX_TOL, name
+    # experts that received no token get exactly zero gradients
+    idle = np.setdiff1d(np.arange(s.n_experts), np.unique(ref["experts"]))
+    if idle.size:
+        assert not g["dgate_up"][idle].any() and not g["ddown"][idle].any()
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_backward_vs_oracle(name):
+    say(f"[backward] {name}")
+    d = I.make_inputs(SHAPES[name])
+    run_and_compare(d, B.to_device(d.store))
+
+
+@pytest.mark.parametrize("name", ["decode"])
+def test_backward_full_size(name):
+    say(f"[backward] {name} (full size)")
+    d, dev = data_of(name)
+    run_and_compare(d, dev)
+
+
+def test_backward_deterministic():
+    d = I.make_inputs(SHAPES["tall"])
+    dev = B.to_device(d.store)
+    cfg = B.config_for(d.shape)
+    dy = bf16_dev(np.random.default_rng(3).standard_normal((d.shape.n_tokens, d.shape.hidden)))
+    a = B.backward(cfg, dev, dy)
+    b = B.backward(cfg, dev, dy)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), k
