@@ -8,7 +8,8 @@ Prints ONE JSON line. `value` is whole-layer tokens/s on the headline workload (
 Qwen3-VL-30B-A3B prefill layer). `roofline` reports the grouped gate_up GEMM (the dominant kernel),
 timed with events on its launch stream inside the timed steps. `decode` adds the 64-token decode
 layer (weight-read bound). `quantized_experts` repeats both with int8 and int4 expert weights
-(one scale per weight row). `cpu_baseline` times the CPU oracle on a bounded token sample.
+(one scale per weight row). `backward` times moe_backward on both workloads. `cpu_baseline` times
+the CPU oracle on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -223,6 +224,37 @@ def quantized_runs(args, runs):
     return out
 
 
+def time_backward(base, steps, warmup):
+    """moe_backward (gradients of x, W_r, gate_up and down for a seeded dy) on the same inputs as the
+    forward run, row-layout weights: ms per call and TFLOP/s of the gradient contractions
+    (12 D I per assignment + 4 N D E for the router; the recomputed pre-activations, 4 D I per
+    assignment, are counted apart)."""
+    import torch
+    from mixture_experts_layer_10_amd import binding as B
+    sh, data = base["shape"], base["data"]
+    cfg = B.config_for(sh)
+    dev = B.to_device(data.store)
+    dy = torch.randn((sh.n_tokens, sh.hidden), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).cuda()
+    ws = torch.empty(B.moe_backward_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    outs = None
+    for _ in range(max(warmup, 1)):
+        outs = B.backward(cfg, dev, dy, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        B.moe_backward(cfg, dev["x"], dev["w_router"], dev["gate_up"], dev["down"], dy, outs["dx"], outs["dw_router"],
+                       outs["dgate_up"], outs["ddown"], ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    A = sh.n_tokens * sh.top_k
+    flops = 12 * sh.hidden * sh.inter * A + 4 * sh.n_tokens * sh.hidden * sh.n_experts
+    return {"ms": round(ms, 4), "grad_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "recompute_tflops_extra": round(4 * sh.hidden * sh.inter * A / (ms * 1e-3) / 1e12, 1),
+            "workspace_bytes": int(ws.numel()), "weight_layout": "rows"}
+
+
 def cpu_baseline(data, target_s=15.0):
     """The CPU oracle (grouped form, fp64) on a seeded token sample of the same workload."""
     import oracle as O
@@ -262,6 +294,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant", action="store_true", help="skip the int8 / int4 expert runs")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy a 256 MiB buffer once (a kernel of known traffic for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -333,6 +366,10 @@ def main():
                          "gate_up_hbm_frac": round(dec["alg"]["gate_up_bytes"] / (dec["gate_up_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
         if not args.no_quant and args.workload == "prefill":
             out["quantized_experts"] = quantized_runs(args, {"decode": dec, "prefill": main_run})
+        if not args.no_backward and args.workload == "prefill":
+            out["backward"] = {"prefill": time_backward(main_run, args.steps, args.warmup),
+                               "decode": time_backward(dec, max(args.steps, 50), args.warmup)}
+            log(f"[bench] backward: {out['backward']}")
     if args.copy_calibration:
         src = torch.ones(64 * 2**20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

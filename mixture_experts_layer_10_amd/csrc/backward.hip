@@ -366,4 +366,29 @@ void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32
   gemm_wgrad_kernel<<<grid, 256, 0, st>>>(A, Bm, ld, poff, qtot, M, Nn, out);
 }
 
+// Split reduction for a single long group (the router's sum over all tokens): slice s covers
+// [poff[s], poff[s+1]) of the padded range, poff[s] = min(s * chunk, total); the partial results
+// [S][M][Nn] are then added in slice order (deterministic).
+__global__ void slice_offsets_kernel(int32_t* __restrict__ poff, int S, int64_t chunk, int64_t total) {
+  const int s = threadIdx.x;
+  if (s <= S) poff[s] = static_cast<int32_t>(min<int64_t>(s * chunk, total));
+}
+
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part, int S, int64_t n, float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int s = 0; s < S; ++s) acc += part[s * n + i];
+  out[i] = acc;
+}
+
+void launch_wgrad_split(const uint16_t* A, const uint16_t* Bm, int64_t ld, int64_t qtot, int M, int Nn, int S,
+                        int32_t* poff, float* part, float* out, hipStream_t st) {
+  const int64_t chunk = ((qtot + S - 1) / S + kWK - 1) / kWK * kWK;
+  slice_offsets_kernel<<<1, 64, 0, st>>>(poff, S, chunk, qtot);
+  launch_wgrad(A, Bm, ld, poff, 0, S, M, Nn, part, st);
+  const int64_t n = static_cast<int64_t>(M) * Nn;
+  sum_slices_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(part, S, n, out);
+}
+
 }  // namespace moe

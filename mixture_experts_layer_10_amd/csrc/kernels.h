@@ -109,6 +109,9 @@ void launch_router_bwd(const float* logits, const float* weights, const int32_t*
                        int Ep, int k, int norm, uint16_t* dlogit, hipStream_t st);
 void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32_t* poff, int64_t qtot, int G, int M, int Nn,
                   float* out, hipStream_t st);
+constexpr int kWgradSlices = 16;     // split of a single long reduction (poff: kWgradSlices + 1 entries)
+void launch_wgrad_split(const uint16_t* A, const uint16_t* Bm, int64_t ld, int64_t qtot, int M, int Nn, int S,
+                        int32_t* poff, float* part, float* out, hipStream_t st);
 
 int device_cu_count();
 

@@ -256,7 +256,8 @@ static int combine_impl(const moe_config* c, const float* out_perm, const float*
 // gradients' intermediates, transposed weight copies and the padded transposed activations.
 struct BwdLayout {
   size_t route_partial, logits, weights, experts, counts, offsets, block_counts, token_of, slot_pos, w_perm, assign_of,
-      ones, dw, poff, z, dhu, h, dab, dx_rows, dlogit, dxr, dnT, guT, wrT, doT, xgT, hT, dabT, dlogitT, xT, total;
+      ones, dw, poff, z, dhu, h, dab, dx_rows, dlogit, dxr, dnT, guT, wrT, doT, xgT, hT, dabT, dlogitT, xT, spoff,
+      wr_part, total;
   int64_t Ep, Qs, Ns;
 };
 
@@ -298,6 +299,8 @@ static BwdLayout bwd_layout_of(const moe_config* c) {
   L.dabT = take(2 * I * L.Qs * 2);
   L.dlogitT = take(L.Ep * L.Ns * 2);
   L.xT = take(D * L.Ns * 2);
+  L.spoff = take((kWgradSlices + 1) * 4);
+  L.wr_part = take(static_cast<int64_t>(kWgradSlices) * E * D * 4);
   L.total = at;
   return L;
 }
@@ -586,7 +589,7 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   MOE_TRY(check_launch("moe_backward (transposes)"));
   launch_wgrad(H16(L.doT), H16(L.hT), L.Qs, poff, 0, E, D, I, ddown, st);
   launch_wgrad(H16(L.dabT), H16(L.xgT), L.Qs, poff, 0, E, 2 * I, D, dgate_up, st);
-  launch_wgrad(H16(L.dlogitT), H16(L.xT), L.Ns, nullptr, L.Ns, 1, E, D, dw_router, st);
+  launch_wgrad_split(H16(L.dlogitT), H16(L.xT), L.Ns, L.Ns, E, D, kWgradSlices, I32(L.spoff), F(L.wr_part), dw_router, st);
   MOE_TRY(check_launch("moe_backward (weight gradients)"));
   return ok();
 }

@@ -10,8 +10,8 @@ operands per product) and accumulated in fp32, so each gradient G must satisfy
 The forward's max-abs / RMS measure does not suit weight gradients: an entry is a sum over the few
 rows routed to one expert of products of heavy-tailed factors, so max|G| / RMS(G) reaches 20-30 and
 one bf16 rounding shows as several percent of the RMS (a CPU emulation of these roundings gives the
-same figures as the GPU). Shapes are chosen without near ties in the top-k (the selection, hence
-the gradient, is then unique).
+same figures as the GPU). Tokens with a near tie in the top-k (possible either way) get a zero
+output gradient, which removes every gradient term they have; the rest have a unique selection.
 """
 import numpy as np
 import pytest
@@ -44,13 +44,17 @@ def run_and_compare(d, dev):
     s = d.shape
     dy_np = I.bf16_bits_to_f32(I.round_to_bf16_bits(
         np.random.default_rng(s.seed + 7).standard_normal((s.n_tokens, s.hidden), dtype=np.float32))).astype(np.float64)
+    # tokens whose k-th / (k+1)-th probabilities are closer than GAP may be routed either way; with
+    # a zero output gradient every gradient term of such a token vanishes, whatever its routing
+    _, probs, _, _ = O.route(d.values("x"), d.values("w_router"), s.top_k, s.norm_topk_prob)
+    near = O.k_gap(probs, s.top_k) < GAP
+    dy_np[near] = 0.0
+    say(f"  near-tie tokens with zero dy: {int(near.sum())}")
     cfg = B.config_for(s)
     g = B.backward(cfg, dev, bf16_dev(dy_np))
     torch.cuda.synchronize()
     ref = O.backward(d.values("x"), d.values("w_router"), d.expert_view("gate_up"), d.expert_view("down"),
                      s.top_k, dy_np, s.norm_topk_prob)
-    _, probs, _, _ = O.route(d.values("x"), d.values("w_router"), s.top_k, s.norm_topk_prob)
-    assert (O.k_gap(probs, s.top_k) >= GAP).all(), "shape has near ties: pick another seed"
     for name, key in (("dx", "dx"), ("dw_router", "dw_router"), ("dgate_up", "dgate_up"), ("ddown", "ddown")):
         got = g[name].cpu().numpy().astype(np.float64)
         want = np.asarray(ref[key], np.float64).reshape(got.shape)
@@ -61,7 +65,8 @@ def run_and_compare(d, dev):
         say(f"  {name}: normwise {norm_err:.3e}, max/max {max_err:.3e}, max/rms {rel_err(got, want):.3e}")
         assert norm_err <= NORM_TOL and max_err <= MAX_TOL, name
     # experts that received no token get exactly zero gradients
-    idle = np.setdiff1d(np.arange(s.n_experts), np.unique(ref["experts"]))
+    idle = np.setdiff1d(np.arange(s.n_experts), np.unique(ref["experts"][~near]))
+    idle = idle[~np.isin(idle, ref["experts"][near])]
     if idle.size:
         assert not g["dgate_up"][idle].any() and not g["ddown"][idle].any()
 
@@ -73,8 +78,9 @@ def test_backward_vs_oracle(name):
     run_and_compare(d, B.to_device(d.store))
 
 
-@pytest.mark.parametrize("name", ["decode"])
+@pytest.mark.parametrize("name", ["decode", "prefill"])
 def test_backward_full_size(name):
+    # prefill: 256-row GEMM tiles and a 16,263-row sum for the hottest expert's weight gradients
     say(f"[backward] {name} (full size)")
     d, dev = data_of(name)
     run_and_compare(d, dev)
