@@ -336,8 +336,42 @@ def bias_update(bias, counts, n_tokens, top_k, gamma):
 # weight-only int8 in the Keras port's framework.
 # --------------------------------------------------------------------------------------------
 
+FP8_MAX = 448.0      # largest finite OCP e4m3 value, 1.75 * 2^8
+
+
+def fp8_e4m3_value(codes):
+    """Values of OCP e4m3 bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+    is subnormal, m * 2^-9; 0x7f / 0xff are NaN): the format of FP8 weights."""
+    b = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = b & 7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.where((b & 0x7F) == 0x7F, np.nan, sign * val)
+
+
+def fp8_e4m3_encode(v):
+    """Nearest OCP e4m3 byte to each float32 value with |v| <= 448, ties to the even mantissa; the
+    sign bit follows the sign of v (so -0 gives 0x80). In each binade [2^e, 2^(e+1)) the step is
+    2^(e-3); below 2^-6 the subnormal step 2^-9 applies."""
+    v = np.asarray(v, np.float32)
+    a = np.abs(v).astype(np.float64)
+    assert np.all(a <= FP8_MAX), "encode expects values clamped to the finite range"
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    step = 2.0 ** (e - 3)
+    r = np.rint(a / step) * step                       # exact: a / step is a scaled float
+    # r may have rounded up into the next binade (its encoding is then that binade's m = 0)
+    er = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    normal = r >= 2.0 ** -6
+    exp_field = np.where(normal, er + 7, 0).astype(np.int64)
+    mant = np.where(normal, r / 2.0 ** er * 8 - 8, r / 2.0 ** -9).astype(np.int64)
+    return ((np.signbit(v).astype(np.int64) << 7) | (exp_field << 3) | mant).astype(np.uint8)
+
+
 def quantize_weights(w, bits):
-    """Quantise a [G, R, K] stack (R output rows, K inputs) to signed `bits`-bit codes (8 or 4).
+    """Quantise a [G, R, K] stack (R output rows, K inputs) to signed `bits`-bit codes (8 or 4), or
+    to OCP e4m3 bytes for bits == "f8" (see quantize_fp8).
 
     For each row r:
       m     = max |w[r, :]|                          (float32, exact for bf16 values)
@@ -345,6 +379,8 @@ def quantize_weights(w, bits):
       code  = clamp(rint(w / scale), -Q, Q)          (float32 quotient, ties to even; 0 if scale 0)
     so code * scale reconstructs w to within scale / 2. Returns (codes int8 [G, R, K],
     scales float32 [G, R])."""
+    if bits == "f8":
+        return quantize_fp8(w)
     Q = np.float32(2 ** (bits - 1) - 1)
     w32 = np.asarray(w, np.float32)
     m = np.abs(w32).max(axis=-1)
@@ -356,10 +392,28 @@ def quantize_weights(w, bits):
     return codes.astype(np.int8), scales
 
 
+def quantize_fp8(w):
+    """FP8 weights ([VL-post] "Why 3B active parameters feel like 30B": an FP8 copy of the model;
+    read as OCP e4m3 with one float32 scale per output row, like the integer codes):
+      m = max |w[r, :]|, scale = m / 448 (float32 division),
+      code = e4m3(clamp(w / scale, -448, 448)) (float32 quotient, nearest, ties to even);
+    an all-zero row has scale 0 and codes 0. Returns (codes uint8 [G, R, K], scales float32 [G, R])."""
+    w32 = np.asarray(w, np.float32)
+    m = np.abs(w32).max(axis=-1)
+    scales = (m / np.float32(FP8_MAX)).astype(np.float32)
+    nz = scales > 0
+    div = np.where(nz, scales, np.float32(1.0))[..., None]
+    q = np.clip((w32 / div).astype(np.float32), np.float32(-FP8_MAX), np.float32(FP8_MAX))
+    codes = fp8_e4m3_encode(q)
+    return np.where(nz[..., None], codes, np.uint8(0)), scales
+
+
 def dequantize_weights(codes, scales):
     """The weights the quantised layer computes with: w'[g, r, c] = code[g, r, c] * scale[g, r], in
-    float64 (exact: a small integer times a float32)."""
-    return np.asarray(codes).astype(np.float64) * np.asarray(scales, np.float64)[..., None]
+    float64 (exact: a small integer, or an e4m3 value for uint8 FP8 codes, times a float32)."""
+    codes = np.asarray(codes)
+    vals = fp8_e4m3_value(codes) if codes.dtype == np.uint8 else codes.astype(np.float64)
+    return vals * np.asarray(scales, np.float64)[..., None]
 
 
 # --------------------------------------------------------------------------------------------

@@ -555,3 +555,47 @@ def test_swiglu_backward_single_row_by_hand():
     assert math.isclose(ddn[0, 0], a * s * u_ * v, rel_tol=1e-14)
     assert math.isclose(dgu[0, 0], d_ * u_ * v * dsilu * v, rel_tol=1e-13)
     assert math.isclose(dgu[1, 0], d_ * a * s * v, rel_tol=1e-13)
+
+
+def test_fp8_e4m3_table_and_encode_by_hand():
+    """OCP e4m3 by hand: 1.0 = 0x38, 0.5 = 0x30, -2 = 0xc0, 448 = 0x7e (the largest finite), 2^-6 = 0x08
+    (smallest normal), 2^-9 = 0x01 (smallest subnormal); halfway values go to the even mantissa;
+    -0 keeps its sign; every finite byte encodes back to itself."""
+    enc = O.fp8_e4m3_encode
+    f = lambda *v: np.array(v, np.float32)
+    assert enc(f(1.0, 0.5, -2.0, 448.0, 2.0 ** -6, 2.0 ** -9)).tolist() == [0x38, 0x30, 0xC0, 0x7E, 0x08, 0x01]
+    assert enc(f(1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -11, -0.0)).tolist() == [0x38, 0x3A, 0x00, 0x01, 0x80]
+    assert O.fp8_e4m3_value(np.array([0x38, 0x7E, 0x01, 0xC0])).tolist() == [1.0, 448.0, 2.0 ** -9, -2.0]
+    assert np.isnan(O.fp8_e4m3_value(np.array([0x7F, 0xFF]))).all()
+    b = np.arange(256)
+    fin = np.isfinite(O.fp8_e4m3_value(b))
+    assert np.array_equal(enc(O.fp8_e4m3_value(b[fin]).astype(np.float32)), b[fin].astype(np.uint8))
+
+
+def test_quantize_fp8_exact_on_its_grid_and_error_bound():
+    """Rows of e4m3 values times 2^k whose largest magnitude is 448 * 2^k have scale 2^k and are
+    reproduced exactly; on random rows the error is within half a mantissa step (2^-4 relative) in
+    the normal range and 2^-10 scale below it; the largest |w| maps to +-448."""
+    rng = np.random.default_rng(21)
+    table = O.fp8_e4m3_value(np.arange(256))
+    finite = table[np.isfinite(table)]
+    vals = rng.choice(finite, size=(2, 16, 96))
+    vals[..., 5] = 448.0
+    k = rng.integers(-12, -4, size=(2, 16, 1))
+    w = (vals * 2.0 ** k).astype(np.float32)
+    codes, scales = O.quantize_weights(w, "f8")
+    assert np.array_equal(scales, (2.0 ** k[..., 0]).astype(np.float32))
+    assert np.array_equal(O.dequantize_weights(codes, scales), w.astype(np.float64))
+    w = I.bf16_bits_to_f32(I.round_to_bf16_bits(rng.normal(0.0, 0.02, size=(3, 32, 256)).astype(np.float32)))
+    w[0, 0] = 0.0
+    codes, scales = O.quantize_weights(w, "f8")
+    assert scales[0, 0] == 0 and not codes[0, 0].any()
+    deq = O.dequantize_weights(codes, scales)
+    q = np.abs(w / np.where(scales > 0, scales, 1)[..., None])
+    err = np.abs(deq - w.astype(np.float64))
+    sc = scales.astype(np.float64)[..., None]
+    normal = q >= 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(w.astype(np.float64))[normal] * (1 + 2.0 ** -20) + 1e-30)
+    assert np.all(err[~normal] <= np.broadcast_to(2.0 ** -10 * sc, err.shape)[~normal] * (1 + 2.0 ** -20))
+    at_max = np.take_along_axis(codes, np.abs(w).argmax(-1)[..., None], -1)[..., 0]
+    assert np.all((at_max[scales > 0] & 0x7F) == 0x7E)
