@@ -7,7 +7,7 @@ synthetic tokens already resident in HBM.
 Prints ONE JSON line. `value` is whole-layer tokens/s on the headline workload (the 16,384-token
 Qwen3-VL-30B-A3B prefill layer). `roofline` reports the grouped gate_up GEMM (the dominant kernel),
 timed with events on its launch stream inside the timed steps. `decode` adds the 64-token decode
-layer (weight-read bound). `quantized_experts` repeats both with int8 and int4 expert weights
+layer (weight-read bound). `quantized_experts` repeats both with int8, int4 and fp8 expert weights
 (one scale per weight row). `backward` times moe_backward on both workloads. `cpu_baseline` times
 the CPU oracle on a bounded token sample.
 """
@@ -124,7 +124,7 @@ def time_variants(B, chain, cfg, dev, steps):
                 dropped_share=round(1.0 - kept / (N * k), 4))
 
 
-LAYOUT_NAMES = {0: "rows", 1: "packed", 2: "int8", 3: "int4"}
+LAYOUT_NAMES = {0: "rows", 1: "packed", 2: "int8", 3: "int4", 4: "fp8"}
 
 
 def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, data=None, extras=True):
@@ -132,7 +132,8 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, da
     bracketed by events on its stream (its duration comes from the timed region itself); without,
     the timed steps carry no events (a recorded event idles the GPU for a few microseconds, which
     matters at decode sizes) and the gate_up duration comes from a second run of `steps` steps.
-    layout: 1 packed bf16 experts (rows if the shape cannot be packed), 2 / 3 int8 / int4 experts."""
+    layout: 1 packed bf16 experts (rows if the shape cannot be packed), 2 / 3 / 4 int8 / int4 / fp8
+    experts."""
     import torch
     from mixture_experts_layer_10_amd import binding as B
     from mixture_experts_layer_10_amd import inputs as I
@@ -183,7 +184,7 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, da
     ms_per_step = wall * 1e3 / steps
     stats = time_router_stats(B, chain, cfg, dev, steps) if extras else None
     variants = time_variants(B, chain, cfg, dev, steps) if extras else None
-    alg = algorithmic(shape, touched, {2: 8, 3: 4}.get(cfg.weight_layout))
+    alg = algorithmic(shape, touched, {2: 8, 3: 4, 4: 8}.get(cfg.weight_layout))
     log(f"[bench] {name}: {ms_per_step:.3f} ms/step (gpu {gpu_ms / steps:.3f}), gate_up {gate_up_ms:.3f} ms, "
         f"touched {touched}/{shape.n_experts}")
     return dict(shape=shape, data=data, cfg=cfg, stats=stats, variants=variants, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
@@ -193,11 +194,11 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, da
 
 
 def quantized_runs(args, runs):
-    """Weight-only quantised experts (int8 and int4, one fp32 scale per weight row; router and
+    """Weight-only quantised experts (int8, int4 and fp8 e4m3, one fp32 scale per weight row; router and
     activations bf16) on the same inputs as the bf16 runs: step time, HBM fraction of the quantised
     algorithmic bytes, stored expert bytes, and the layer output's deviation from the bf16 layer."""
     out = {}
-    for bits, layout in ((8, 2), (4, 3)):
+    for bits, layout in ((8, 2), (4, 3), ("f8", 4)):
         res = {}
         for wl, base in runs.items():
             decode = wl == "decode"
@@ -211,7 +212,7 @@ def quantized_runs(args, runs):
                  "alg_gbs": round(q["alg"]["bytes"] / st / 1e9, 1),
                  "hbm_frac": round(q["alg"]["bytes"] / st / 1e9 / PEAK_HBM_GBS, 4),
                  "gate_up_ms": round(q["gate_up_ms"], 4),
-                 "expert_weight_bytes": int(sh.n_experts * (3 * sh.hidden * sh.inter * bits // 8
+                 "expert_weight_bytes": int(sh.n_experts * (3 * sh.hidden * sh.inter * (4 if bits == 4 else 8) // 8
                                                             + (2 * sh.inter + sh.hidden) * 4)),
                  "y_rms_rel_vs_bf16": round(float(np.sqrt(np.mean(d * d))) / ref_rms, 5),
                  "y_maxabs_rel_vs_bf16": round(float(np.abs(d).max()) / ref_rms, 5)}
@@ -220,7 +221,7 @@ def quantized_runs(args, runs):
             else:
                 r["gate_up_tflops"] = round(q["alg"]["gate_up_flops"] / (q["gate_up_ms"] / 1e3) / 1e12, 1)
             res[wl] = r
-        out[f"int{bits}"] = res
+        out["fp8" if bits == "f8" else f"int{bits}"] = res
     return out
 
 

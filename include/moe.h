@@ -37,14 +37,16 @@
  * with hidden, inter and shared_inter multiples of 128 and n_experts a multiple of 16.
  * w_shared_gate is a vector and keeps its layout.
  *
- * Quantised experts (moe_config.weight_layout = MOE_LAYOUT_Q8 or MOE_LAYOUT_Q4; weight-only
- * quantisation of the experts with the router kept in bf16: "Qwen3-VL-MoE" Keras port, section
- * "Lower memory"; "27. Mixture of experts", section "Dispatch" and stretch exercise 3): gate_up,
+ * Quantised experts (moe_config.weight_layout = MOE_LAYOUT_Q8, MOE_LAYOUT_Q4 or MOE_LAYOUT_F8;
+ * weight-only quantisation of the experts with the router kept in bf16: "Qwen3-VL-MoE" Keras port,
+ * section "Lower memory"; "27. Mixture of experts", section "Dispatch" and stretch exercise 3;
+ * "Qwen3-VL + MoE: train to deploy", the FP8 copy of the 30B model): gate_up,
  * down, shared_gate_up and shared_down each hold a quantised stack made by moe_quantize_weights
  * (with the same n_groups, rows and cols the expert entry points see), w_router is packed as for
  * MOE_LAYOUT_PACKED and w_shared_gate keeps its layout. Same shape rules as MOE_LAYOUT_PACKED. The
- * layer then computes with the weights code * scale: the integer codes enter the matrix cores
- * exactly (as bf16) and each output column's fp32 sum is multiplied by its row's scale.
+ * layer then computes with the weights code * scale (for FP8, the e4m3 value of the code times the
+ * scale): the codes enter the matrix cores exactly (as bf16) and each output column's fp32 sum is
+ * multiplied by its row's scale.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -66,7 +68,9 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_PACKED = 1, MOE_LAYOUT_Q8 = 2, MOE_LAYOUT_Q4 = 3 } moe_weight_layout;
+typedef enum {
+  MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_PACKED = 1, MOE_LAYOUT_Q8 = 2, MOE_LAYOUT_Q4 = 3, MOE_LAYOUT_F8 = 4
+} moe_weight_layout;
 
 /* Shape and options of one MoE layer. Refuses, never defaults: every field must be set
  * (the config-ingestion lesson of "27. Mixture of experts", section "Qwen3-MoE", Note). */
@@ -185,19 +189,22 @@ int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int6
                      void* dst, void* stream);
 
 /* Weight-only quantisation of a row-major bf16 stack src [G, R, K] (R % 16 == 0, K % 32 == 0)
- * into dst, once at model load. b = 8 (cfg.weight_layout MOE_LAYOUT_Q8) or 4 (MOE_LAYOUT_Q4); cfg
- * gives dtype (must be bf16) and weight_layout, its other fields are not used.
+ * into dst, once at model load. b = 8 (cfg.weight_layout MOE_LAYOUT_Q8 or MOE_LAYOUT_F8) or 4
+ * (MOE_LAYOUT_Q4); cfg gives dtype (must be bf16) and weight_layout, its other fields are not used.
  * Rule, per output row r (symmetric absmax, one scale per row; the pages give the bit widths, not
  * the quantiser):
  *   m = max |w| over the row, scale = m / Q in fp32 (IEEE division), Q = 127 (b = 8) or 7 (b = 4)
  *   code = clamp(rint(w / scale), -Q, Q), the fp32 quotient rounded to nearest, ties to even;
  *   an all-zero row has scale 0 and codes 0.
+ * FP8 (MOE_LAYOUT_F8): scale = m / 448 and code = the OCP e4m3 byte (1 sign, 4 exponent bits with
+ *   bias 7, 3 mantissa bits, subnormals below 2^-6) nearest to clamp(w / scale, -448, 448), ties to
+ *   the even mantissa, the sign of zero kept; an all-zero row has scale 0 and codes 0.
  * dst layout (moe_quantized_bytes() bytes, 16-byte aligned, not overlapping src):
  *   codes: G R K b / 8 bytes in the block order of moe_pack_weights: block (g, rb, kb) of rows
  *     rb*16 .. +15 and columns kb*32 .. +31 takes 64 b bytes at ((g * R/16 + rb) * K/32 + kb) * 64 b;
  *     its slot l (b bytes, l = 0..63) holds the codes of row rb*16 + l % 16, columns
- *     kb*32 + 8 (l / 16) + i, i = 0..7, two's complement: b = 8 byte i, b = 4 bits 4i..4i+3 (byte
- *     i / 2, low nibble first);
+ *     kb*32 + 8 (l / 16) + i, i = 0..7: b = 8 byte i (two's complement, or the e4m3 byte for
+ *     FP8), b = 4 bits 4i..4i+3 (two's complement; byte i / 2, low nibble first);
  *   scales: fp32 [G, R] from byte G R K b / 8 on. */
 int moe_quantized_bytes(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, size_t* bytes);
 int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src,

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "_lib", "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
-MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED, MOE_LAYOUT_Q8, MOE_LAYOUT_Q4 = 0, 1, 2, 3
+MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED, MOE_LAYOUT_Q8, MOE_LAYOUT_Q4, MOE_LAYOUT_F8 = 0, 1, 2, 3, 4
 
 # Every symbol include/moe.h declares.
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",

@@ -166,6 +166,20 @@ __device__ __forceinline__ u32x4 codes4_to_bf16(uint32_t c) {
   return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 
+// FP8 (OCP e4m3) codes -> bf16, exactly (3-bit mantissa, exponents 2^-9 .. 2^8 inside bf16's range):
+// code i in byte i, converted by the hardware e4m3 -> fp32 instruction two at a time.
+__device__ __forceinline__ u32x4 codesf8_to_bf16(u32x2 c) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c[h]), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c[h]), true);
+    r[2 * h] = pack_bf16x2(lo[0], lo[1]);
+    r[2 * h + 1] = pack_bf16x2(hi[0], hi[1]);
+  }
+  return r;
+}
+
 // s_waitcnt immediate for vmcnt(n) alone (bits 3:0 and 15:14; expcnt and lgkmcnt at "no wait").
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 

@@ -284,8 +284,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int A_GROUPS = BM / 16;
   constexpr int A_INS = (A_GROUPS + NW - 1) / NW, B_INS = BNB / 16 / NW;
   constexpr int OUT_COLS = kSwiGLU ? BNB / 2 : BNB;
-  constexpr int QB = kQ ? 64 * kQ : 1024;                 // bytes of one 16 x 32 weight block
-  constexpr int B_DMA = kQ == 8 ? 2 * B_INS : B_INS;       // weight DMA instructions per wave per stage
+  constexpr int QS = kQ ? code_slot(kQ) : 16;              // bytes per lane slot of a weight block
+  constexpr int QB = 64 * QS;                              // bytes of one 16 x 32 weight block
+  constexpr int B_DMA = QS == 8 ? 2 * B_INS : B_INS;       // weight DMA instructions per wave per stage
   constexpr int PER_STAGE = A_INS + B_DMA;
   static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
   static_assert(A_INS * NW == A_GROUPS || A_INS == 1, "A rows must split into 16-row DMA groups");
@@ -296,10 +297,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * kSK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA2[BM * kSK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA3[BM * kSK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BNB * kSK * (kQ ? kQ : 16) / 16];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BNB * kSK * (kQ ? kQ : 16) / 16];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BNB * kSK * (kQ ? kQ : 16) / 16];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB3[BNB * kSK * (kQ ? kQ : 16) / 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BNB * kSK * QS / 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BNB * kSK * QS / 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BNB * kSK * QS / 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB3[BNB * kSK * QS / 16];
   __shared__ int s_pref[1025];
   __shared__ int s_off[1025];           // group row offsets (no global round trip per tile)
   __shared__ int s_tmp[16];
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     const int pc = ((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 3;
     koA[kk] = (wm * TM * 32 + (lane & 31)) * kSK + pc;
     if constexpr (kQ != 0)
-      koB[kk] = (rb0 / 16 + ((lane >> 4) & 1)) * QB + ((lane & 15) + 16 * (2 * kk + (lane >> 5))) * kQ;
+      koB[kk] = (rb0 / 16 + ((lane >> 4) & 1)) * QB + ((lane & 15) + 16 * (2 * kk + (lane >> 5))) * QS;
     else
       koB[kk] = kPacked ? rb0 * kSK + ((lane >> 4) & 1) * 512 + (lane & 15) * 8 + (2 * kk + (lane >> 5)) * 128
                         : (rb0 + (lane & 31)) * kSK + pc;
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     if constexpr (kQ != 0) {
       // the weight row of this lane's column in block j (columns past the output width read a
       // valid row; their outputs are never stored)
-      const float* S = reinterpret_cast<const float*>(static_cast<const char*>(a.w) + quant_code_bytes(G, R, K, kQ)) +
+      const float* S = reinterpret_cast<const float*>(static_cast<const char*>(a.w) + quant_code_bytes(G, R, K, code_bits(kQ))) +
                        static_cast<int64_t>(g) * R;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -407,7 +408,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
           rb = min(T.c0 / 16 + grp, NOUT / 16 - 1);
         }
         if constexpr (kQ != 0)
-          T.srcQ[j] = static_cast<const char*>(a.w) + quant_code_bytes(g, R, K, kQ) +
+          T.srcQ[j] = static_cast<const char*>(a.w) + quant_code_bytes(g, R, K, code_bits(kQ)) +
                       static_cast<int64_t>(rb) * (K / kSK) * QB + lane * 4;
         else
           T.srcB[j] = Wg + static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8;
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         const char* src = T.srcQ[j] + static_cast<int64_t>(ks) * QB;
         char* dst = reinterpret_cast<char*>(sb) + (wave * B_INS + j) * QB;
         dma4(src, dst);
-        if constexpr (kQ == 8) dma4(src + 256, dst + 256);
+        if constexpr (QS == 8) dma4(src + 256, dst + 256);
       } else {
         dma16(T.srcB[j] + (kPacked ? ks * 512 : kb), sb + (wave * B_INS + j) * 512);
       }
@@ -465,9 +466,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
       for (int j = 0; j < TN; ++j) {
         constexpr int H = TN / 2;
         const int rowoff = kSwiGLU ? (j < H ? j * 32 : BNB / 2 + (j - H) * 32) : j * 32;
-        if constexpr (kQ == 8)
+        if constexpr (kQ == kQInt8)
           fb[j] = codes8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
-        else if constexpr (kQ == 4)
+        else if constexpr (kQ == kQFp8)
+          fb[j] = codesf8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
+        else if constexpr (kQ == kQInt4)
           fb[j] = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
         else
           fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
@@ -582,11 +585,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 template <int kQ> struct WRaw { typedef u32x4 T; };          // bf16: 8 values = 16 bytes per lane
 template <> struct WRaw<8> { typedef u32x2 T; };              // int8: 8 codes = 8 bytes
 template <> struct WRaw<4> { typedef uint32_t T; };           // int4: 8 codes = 4 bytes
+template <> struct WRaw<kQFp8> { typedef u32x2 T; };          // fp8: 8 codes = 8 bytes
 
 template <int kQ>
 __device__ __forceinline__ u32x4 to_bf16_frag(typename WRaw<kQ>::T v) {
-  if constexpr (kQ == 8) return codes8_to_bf16(v);
-  else if constexpr (kQ == 4) return codes4_to_bf16(v);
+  if constexpr (kQ == kQInt8) return codes8_to_bf16(v);
+  else if constexpr (kQ == kQInt4) return codes4_to_bf16(v);
+  else if constexpr (kQ == kQFp8) return codesf8_to_bf16(v);
   else return v;
 }
 
@@ -627,20 +632,20 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   // wrow[j]: this lane's weight bytes of k-step 0 of block j; k-step ks is WSTEP bytes further.
   // packed: a column block's 16 rows are one row block; k-step ks of it is one block in lane order.
   const char* wrow[NB];
-  constexpr int WSTEP = kQ ? 64 * kQ : (kPacked ? 1024 : 64);
+  constexpr int WSTEP = kQ ? 64 * code_slot(kQ) : (kPacked ? 1024 : 64);
   const char* Wg = static_cast<const char*>(a.w) +
-                   (kQ ? quant_code_bytes(g, R, K, kQ) : static_cast<int64_t>(g) * R * K * 2);
+                   (kQ ? quant_code_bytes(g, R, K, code_bits(kQ)) : static_cast<int64_t>(g) * R * K * 2);
   float scl[NB];                             // quantised: the scale of each block's row for this lane
   const float* S = nullptr;
   if constexpr (kQ != 0)
-    S = reinterpret_cast<const float*>(static_cast<const char*>(a.w) + quant_code_bytes(a.G, R, K, kQ)) +
+    S = reinterpret_cast<const float*>(static_cast<const char*>(a.w) + quant_code_bytes(a.G, R, K, code_bits(kQ))) +
         static_cast<int64_t>(g) * R;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int cb = min(cb0 + j / NS, ncb - 1);
     const int up = (j % NS) * a.I;           // SwiGLU: the up rows follow the I gate rows
     if constexpr (kPacked) {
-      constexpr int SLOT = kQ ? kQ : 16;     // bytes per lane slot
+      constexpr int SLOT = kQ ? code_slot(kQ) : 16;   // bytes per lane slot
       wrow[j] = Wg + static_cast<int64_t>(up / 16 + cb) * (K / 32) * WSTEP + lane * SLOT;
     } else {
       wrow[j] = Wg + (static_cast<int64_t>(up + min(cb * 16 + (lane & 15), NOUT - 1)) * K + kg) * 2;
@@ -885,7 +890,7 @@ static void launch_stream(const GemmArgs& a, hipStream_t st) {
   constexpr int out_cols = kSwiGLU ? BNB / 2 : BNB;
   const int NOUT = kSwiGLU ? a.I : a.D;
   const int n_tiles = (NOUT + out_cols - 1) / out_cols;
-  constexpr int lds = 4 * (BM * 2 + BNB * (kQ ? kQ : 16) / 8) * kSK;
+  constexpr int lds = 4 * (BM * 2 + BNB * (kQ ? code_bits(kQ) : 16) / 8) * kSK;
   // Short-row tiles (few rows per group) are pure weight streams: one workgroup per tile lets the
   // dispatcher start a new tile wherever one finishes instead of running fixed rounds with a
   // half-empty last round. Tall tiles keep a persistent grid (one prologue per workgroup).
@@ -929,6 +934,10 @@ static void launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.qbits == 4) {
     if (small_rows(a)) return launch_wstream<kSwiGLU, true, 4>(a, st);
     return launch_stream<2, 4, 4, 2, kSwiGLU, true, 4>(a, st);
+  }
+  if (a.qbits == kQFp8) {
+    if (small_rows(a)) return launch_wstream<kSwiGLU, true, kQFp8>(a, st);
+    return launch_stream<2, 4, 4, 2, kSwiGLU, true, kQFp8>(a, st);
   }
   if (a.packed) {
     if (small_rows(a)) return launch_wstream<kSwiGLU, true>(a, st);

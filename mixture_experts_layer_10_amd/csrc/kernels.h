@@ -58,7 +58,7 @@ struct GemmArgs {
   int D, I;
   bool bf16;
   bool packed;            // w in the packed layout (bf16, K % 128 == 0, rows % 16 == 0)
-  int qbits;              // 0: bf16 weights; 8 or 4: w is a quantised stack (codes, then scales)
+  int qbits;              // code kind: 0 bf16 weights; kQInt8 / kQInt4 / kQFp8: a quantised stack
 };
 void launch_gate_up(const GemmArgs& a, hipStream_t st);
 void launch_down(const GemmArgs& a, hipStream_t st);
@@ -73,7 +73,11 @@ void launch_pack(const uint16_t* src, uint16_t* dst, int64_t G, int R, int K, hi
 // * 64 b, slot l (b bytes) = row rb*16 + l % 16, columns kb*32 + 8 (l / 16) .. + 7; then one fp32
 // scale per row, [G, R], from byte G R K b / 8 on.
 __host__ __device__ inline int64_t quant_code_bytes(int64_t G, int64_t R, int64_t K, int bits) { return G * R * K * bits / 8; }
-void launch_quantize(const uint16_t* src, uint8_t* dst, int64_t G, int R, int K, int bits, hipStream_t st);
+// Code kinds (GemmArgs::qbits and kernel template arguments): bits per code, FP8 marked apart.
+constexpr int kQInt8 = 8, kQInt4 = 4, kQFp8 = 9;
+__host__ __device__ constexpr int code_bits(int kind) { return kind == kQFp8 ? 8 : kind; }    // 0 for bf16
+__host__ __device__ constexpr int code_slot(int kind) { return code_bits(kind); }           // bytes per lane slot
+void launch_quantize(const uint16_t* src, uint8_t* dst, int64_t G, int R, int K, int kind, hipStream_t st);
 
 struct CombineArgs {
   const float* out_perm;

@@ -54,10 +54,16 @@ constexpr int64_t kMaxExperts = 512;
 
 static size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
-// Bits per expert-weight code of a quantised layout, 0 for bf16 / fp32 weights.
-static int quant_bits(const moe_config* c) {
-  return c->weight_layout == MOE_LAYOUT_Q8 ? 8 : c->weight_layout == MOE_LAYOUT_Q4 ? 4 : 0;
+// Code kind of a quantised layout (kQInt8, kQInt4, kQFp8), 0 for bf16 / fp32 weights.
+static int quant_kind(const moe_config* c) {
+  switch (c->weight_layout) {
+    case MOE_LAYOUT_Q8: return kQInt8;
+    case MOE_LAYOUT_Q4: return kQInt4;
+    case MOE_LAYOUT_F8: return kQFp8;
+    default: return 0;
+  }
 }
+static int quant_bits(const moe_config* c) { return code_bits(quant_kind(c)); }
 
 // Weight loads are 16 bytes wide (bf16 rows, packed blocks, quantised codes and scales).
 static int check_weight_align(const void* p, const char* name) {
@@ -77,8 +83,8 @@ static int validate_config(const moe_config* c) {
   if (c->shared_inter < 0) return fail(MOE_ERR_INVALID_ARG, "shared_inter = %lld < 0", (long long)c->shared_inter);
   if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1)
     return fail(MOE_ERR_INVALID_ARG, "norm_topk_prob = %d (must be 0 or 1)", c->norm_topk_prob);
-  if (c->weight_layout < MOE_LAYOUT_ROWS || c->weight_layout > MOE_LAYOUT_Q4)
-    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d (must be 0, 1, 2 or 3)", c->weight_layout);
+  if (c->weight_layout < MOE_LAYOUT_ROWS || c->weight_layout > MOE_LAYOUT_F8)
+    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d (must be 0 to 4)", c->weight_layout);
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
   if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "out_dtype %d not supported", c->out_dtype);
@@ -231,7 +237,7 @@ static GemmArgs gemm_args(const moe_config* c, int64_t n_groups, int64_t inter, 
   a.I = static_cast<int>(inter);
   a.bf16 = c->dtype == MOE_BF16;
   a.packed = c->weight_layout != MOE_LAYOUT_ROWS;
-  a.qbits = quant_bits(c);
+  a.qbits = quant_kind(c);
   return a;
 }
 
@@ -485,7 +491,7 @@ int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int6
 static int quant_shape_checks(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols) {
   if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
   if (quant_bits(cfg) == 0)
-    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d is not a quantised layout (2 or 3)", cfg->weight_layout);
+    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d is not a quantised layout (2, 3 or 4)", cfg->weight_layout);
   if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "quantisation needs dtype bf16");
   if (n_groups < 0 || rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
   if (rows % 16 || cols % 32)
@@ -516,7 +522,7 @@ int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, 
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15)
     return fail(MOE_ERR_UNSUPPORTED, "src and dst must be 16-byte aligned");
   launch_quantize(static_cast<const uint16_t*>(src), static_cast<uint8_t*>(dst), n_groups, static_cast<int>(rows),
-                  static_cast<int>(cols), bits, static_cast<hipStream_t>(stream));
+                  static_cast<int>(cols), quant_kind(cfg), static_cast<hipStream_t>(stream));
   MOE_TRY(check_launch("moe_quantize_weights"));
   return ok();
 }

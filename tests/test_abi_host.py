@@ -63,7 +63,8 @@ def test_workspace_bytes_host_only(lib):
     ("inter", 0, B.MOE_ERR_INVALID_ARG),
     ("shared_inter", -8, B.MOE_ERR_INVALID_ARG),
     ("norm_topk_prob", 2, B.MOE_ERR_INVALID_ARG),
-    ("weight_layout", 4, B.MOE_ERR_INVALID_ARG),
+    ("weight_layout", 5, B.MOE_ERR_INVALID_ARG),
+    ("weight_layout", 4, B.MOE_ERR_UNSUPPORTED),      # FP8: the packed shape rules
     ("weight_layout", -1, B.MOE_ERR_INVALID_ARG),
     ("weight_layout", 2, B.MOE_ERR_UNSUPPORTED),      # quantised: the packed shape rules
     ("weight_layout", 1, B.MOE_ERR_UNSUPPORTED),      # packed needs widths that are multiples of 128
@@ -117,7 +118,7 @@ def test_pack_refuses_before_launch(lib):
     B.moe_pack_weights(c, 0, 32, 64, None, None, stream=0)       # nothing to pack: no-op
 
 
-@pytest.mark.parametrize("layout,bits", [(B.MOE_LAYOUT_Q8, 8), (B.MOE_LAYOUT_Q4, 4)])
+@pytest.mark.parametrize("layout,bits", [(B.MOE_LAYOUT_Q8, 8), (B.MOE_LAYOUT_Q4, 4), (B.MOE_LAYOUT_F8, 8)])
 def test_quantized_bytes_and_layout_rules(lib, layout, bits):
     c = B.make_config(64, 256, 16, 2, 128, shared_inter=384, layout=layout)
     assert B.moe_workspace_bytes(c) > 0
@@ -131,7 +132,7 @@ def test_quantized_bytes_and_layout_rules(lib, layout, bits):
             B.moe_workspace_bytes(bad)
         assert ei.value.status == B.MOE_ERR_UNSUPPORTED
     with pytest.raises(B.MoeError) as ei:
-        B.moe_workspace_bytes(c.copy(weight_layout=4))
+        B.moe_workspace_bytes(c.copy(weight_layout=5))
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
 
 

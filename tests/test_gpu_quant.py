@@ -1,4 +1,4 @@
-"""Weight-only quantised experts (MOE_LAYOUT_Q8 / MOE_LAYOUT_Q4) on the GPU, against the oracle.
+"""Weight-only quantised experts (MOE_LAYOUT_Q8 / Q4 / F8) on the GPU, against the oracle.
 
 * moe_quantize_weights: codes and scales bit for bit against the oracle's quantiser (both sides
   decide the integer codes with the same float32 divisions), laid out by the documented order
@@ -20,7 +20,9 @@ from test_gpu_parity import data_of, say
 
 pytestmark = pytest.mark.gpu
 
-LAYOUT = {8: B.MOE_LAYOUT_Q8, 4: B.MOE_LAYOUT_Q4}
+LAYOUT = {8: B.MOE_LAYOUT_Q8, 4: B.MOE_LAYOUT_Q4, "f8": B.MOE_LAYOUT_F8}
+BITS = [8, 4, "f8"]
+SEED = {8: 8, 4: 4, "f8": 9}
 
 
 def quant_reference_bytes(codes, scales, bits):
@@ -29,7 +31,9 @@ def quant_reference_bytes(codes, scales, bits):
     then the fp32 scales as [G, R]."""
     G, R, K = codes.shape
     slots = codes.reshape(G, R // 16, 16, K // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1, 8)
-    if bits == 8:
+    if bits == "f8":
+        code_bytes = slots.astype(np.uint8).reshape(-1)
+    elif bits == 8:
         code_bytes = slots.astype(np.int8).view(np.uint8).reshape(-1)
     else:
         nib = (slots.astype(np.int16) & 0xF).astype(np.uint8)
@@ -63,11 +67,11 @@ def quant_stack(cfg, w_dev, G, R, K):
     return q
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("G,R,K", [(1, 16, 32), (3, 48, 96), (2, 1536, 2048), (5, 2048, 768)])
 def test_quantize_weights_bit_exact(bits, G, R, K):
-    say(f"[quantize] int{bits} {G}x{R}x{K}")
-    rng = np.random.default_rng(G * 100 + R + K + bits)
+    say(f"[quantize] {bits} {G}x{R}x{K}")
+    rng = np.random.default_rng(G * 100 + R + K + SEED[bits])
     w = rng.normal(0.0, 0.02, size=(G, R, K)).astype(np.float32)
     w[0, 0, :] = 0.0                                      # an all-zero row
     w[-1, -1, :] *= 1e-30                                 # a row of tiny (still normal) values
@@ -80,7 +84,7 @@ def test_quantize_weights_bit_exact(bits, G, R, K):
     ref = quant_reference_bytes(codes, scales, bits)
     gb = got.cpu().numpy()
     assert gb.size == ref.size
-    n_codes = G * R * K * bits // 8
+    n_codes = G * R * K * (4 if bits == 4 else 8) // 8
     bad = np.nonzero(gb[:n_codes] != ref[:n_codes])[0]
     assert bad.size == 0, f"{bad.size} code bytes differ, first at {bad[:5]}"
     assert np.array_equal(gb[n_codes:], ref[n_codes:])
@@ -94,7 +98,7 @@ def _ffn(cfg, G, I_, R, x, ridx, off, gu, dn):
     return h, out
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("D,I_,rows", [
     (256, 128, [300, 0, 5, 257, 1, 64, 513]),       # tall groups: 256-row tiles, LDS streaming
     (384, 256, [700, 3, 260]),                      # down output 384 wide: a half-empty column tile
@@ -102,12 +106,12 @@ def _ffn(cfg, G, I_, R, x, ridx, off, gu, dn):
     (384, 256, [17, 40, 0, 9]),
 ])
 def test_quant_ffn_vs_oracle(bits, D, I_, rows):
-    say(f"[quant ffn] int{bits} D={D} I={I_} rows={rows}")
+    say(f"[quant ffn] {bits} D={D} I={I_} rows={rows}")
     G = len(rows)
     offsets = np.zeros(G + 1, np.int64)
     offsets[1:] = np.cumsum(rows)
     R = int(offsets[-1])
-    d = I.make_inputs(I.custom_shape("qffn", R, D, G, 1, I_, seed=400 + D + bits))
+    d = I.make_inputs(I.custom_shape("qffn", R, D, G, 1, I_, seed=400 + D + SEED[bits]))
     dev = B.to_device(d.store)
     cfg = B.make_config(R, D, 16, 1, I_, layout=LAYOUT[bits])
     gu = quant_stack(cfg, dev["gate_up"], G, 2 * I_, D)
@@ -143,10 +147,10 @@ def quant_data(name):
     return data_of(name)
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("name,n_sample", [("small", 64), ("decode", 64), ("prefill", 96), ("fanout", 96)])
 def test_quant_forward_vs_oracle(bits, name, n_sample):
-    say(f"[quant forward] int{bits} {name}")
+    say(f"[quant forward] {bits} {name}")
     d, dev = quant_data(name)
     s = d.shape
     N, k = s.n_tokens, s.top_k
