@@ -244,8 +244,10 @@ def time_backward(base, steps, warmup):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        B.moe_backward(cfg, dev["x"], dev["w_router"], dev["gate_up"], dev["down"], dy, outs["dx"], outs["dw_router"],
-                       outs["dgate_up"], outs["ddown"], ws)
+        B.moe_backward(cfg, dev["x"], dev["w_router"], dev["gate_up"], dev["down"], dev.get("shared_gate_up"),
+                       dev.get("shared_down"), dev.get("w_shared_gate"), dy, outs["dx"], outs["dw_router"],
+                       outs["dgate_up"], outs["ddown"], outs.get("dshared_gate_up"), outs.get("dshared_down"),
+                       outs.get("dw_shared_gate"), ws)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps

@@ -221,19 +221,26 @@ int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, 
  *   experts  with a = x G_e^T, b = x U_e^T, h = silu(a) b and the row's gradient w dy:
  *            dh = w dy Dn_e, da = dh b silu'(a), db = dh silu(a),
  *            dDn_e = sum (w dy)^T h, dG_e = sum da^T x, dU_e = sum db^T x, dx += da G_e + db U_e
+ *   shared   the same with all N tokens, row weight g = sigmoid(w_s . x) (1 without w_s), and for
+ *            the gate dz = (dy . shared(x)) g (1 - g): dw_s = sum dz x, dx += dz w_s
  * The forward's routing, grouping and pre-activations are recomputed from x (nothing is kept from a
  * moe_forward call). Matrix-core inputs are bf16 (h, w dy, da, db and dlogits rounded once),
  * accumulation fp32; the sums over an expert's rows run in row order, deterministic.
- *   cfg: dtype bf16, weight_layout MOE_LAYOUT_ROWS, shared_inter 0 (else MOE_ERR_UNSUPPORTED)
+ *   cfg: dtype bf16, weight_layout MOE_LAYOUT_ROWS (else MOE_ERR_UNSUPPORTED)
  *   x [N, D], w_router [E, D], gate_up [E, 2I, D], down [E, D, I], dy [N, D]   (bf16, row-major)
+ *   shared_gate_up [2I_s, D], shared_down [D, I_s], w_shared_gate [D] (bf16): as moe_forward
+ *     (required iff shared_inter > 0; w_shared_gate may be NULL: ungated)
  *   dx [N, D], dw_router [E, D], dgate_up [E, 2I, D], ddown [E, D, I]       (fp32, overwritten;
  *     an expert that received no token gets zeros)
+ *   dshared_gate_up [2I_s, D], dshared_down [D, I_s] (fp32; iff shared_inter > 0),
+ *   dw_shared_gate [D] (fp32; iff w_shared_gate)
  *   ws, ws_bytes: at least moe_backward_workspace_bytes() bytes, 256-byte aligned
  * All tensors 16-byte aligned. */
 int moe_backward_workspace_bytes(const moe_config* cfg, size_t* bytes);
 int moe_backward(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
-                 const void* dy, float* dx, float* dw_router, float* dgate_up, float* ddown, void* ws,
-                 size_t ws_bytes, void* stream);
+                 const void* shared_gate_up, const void* shared_down, const void* w_shared_gate, const void* dy,
+                 float* dx, float* dw_router, float* dgate_up, float* ddown, float* dshared_gate_up,
+                 float* dshared_down, float* dw_shared_gate, void* ws, size_t ws_bytes, void* stream);
 
 /* Router load statistics and the Switch-style balance loss ("Qwen3-VL + MoE: train to deploy",
  * section "An auxiliary balance loss", its N read as the number of experts):

@@ -100,7 +100,7 @@ def load(path: str = LIB_PATH):
         "moe_quantized_bytes": (ctypes.c_int, [_CFG, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_quantize_weights": (ctypes.c_int, [_CFG, _I64, _I64, _I64, _P, _P, _P]),
         "moe_backward_workspace_bytes": (ctypes.c_int, [_CFG, ctypes.POINTER(ctypes.c_size_t)]),
-        "moe_backward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "moe_backward": (ctypes.c_int, [_CFG] + [_P] * 16 + [ctypes.c_size_t, _P]),
         "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     }
     for name, (res, args) in sig.items():
@@ -208,23 +208,33 @@ def moe_backward_workspace_bytes(cfg) -> int:
     return n.value
 
 
-def moe_backward(cfg, x, w_router, gate_up, down, dy, dx, dw_router, dgate_up, ddown, ws, ws_bytes=None, stream=None):
+def moe_backward(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_shared_gate, dy, dx, dw_router,
+                 dgate_up, ddown, dshared_gate_up, dshared_down, dw_shared_gate, ws, ws_bytes=None, stream=None):
     _check("moe_backward", load().moe_backward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(gate_up), _ptr(down),
-                                               _ptr(dy), _ptr(dx), _ptr(dw_router), _ptr(dgate_up), _ptr(ddown),
+                                               _ptr(shared_gate_up), _ptr(shared_down), _ptr(w_shared_gate), _ptr(dy),
+                                               _ptr(dx), _ptr(dw_router), _ptr(dgate_up), _ptr(ddown),
+                                               _ptr(dshared_gate_up), _ptr(dshared_down), _ptr(dw_shared_gate),
                                                _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
 
 
 def backward(cfg: MoeConfig, dev: dict, dy, ws=None, stream=None):
-    """Run moe_backward on the tensors of ``dev``; returns dict(dx, dw_router, dgate_up, ddown) (fp32)."""
+    """Run moe_backward on the tensors of ``dev``; returns the fp32 gradients dx, dw_router, dgate_up,
+    ddown (and dshared_gate_up, dshared_down, dw_shared_gate when the shapes have them)."""
     import torch
     x = dev["x"]
     out = {"dx": torch.empty(x.shape, dtype=torch.float32, device=x.device)}
-    for name, key in (("dw_router", "w_router"), ("dgate_up", "gate_up"), ("ddown", "down")):
+    pairs = [("dw_router", "w_router"), ("dgate_up", "gate_up"), ("ddown", "down")]
+    if cfg.shared_inter:
+        pairs += [("dshared_gate_up", "shared_gate_up"), ("dshared_down", "shared_down")]
+        if dev.get("w_shared_gate") is not None:
+            pairs.append(("dw_shared_gate", "w_shared_gate"))
+    for name, key in pairs:
         out[name] = torch.empty(dev[key].shape, dtype=torch.float32, device=x.device)
     if ws is None:
         ws = torch.empty(max(moe_backward_workspace_bytes(cfg), 256), dtype=torch.uint8, device=x.device)
-    moe_backward(cfg, x, dev["w_router"], dev["gate_up"], dev["down"], dy, out["dx"], out["dw_router"], out["dgate_up"],
-                 out["ddown"], ws, stream=stream)
+    moe_backward(cfg, x, dev["w_router"], dev["gate_up"], dev["down"], dev.get("shared_gate_up"), dev.get("shared_down"),
+                 dev.get("w_shared_gate"), dy, out["dx"], out["dw_router"], out["dgate_up"], out["ddown"],
+                 out.get("dshared_gate_up"), out.get("dshared_down"), out.get("dw_shared_gate"), ws, stream=stream)
     return out
 
 

@@ -169,15 +169,16 @@ void launch_scatter_assign(const int32_t* slot_pos, const float* weights, float*
 
 // One wave per sorted row p: from z = [a | b] (fp32) and dhu = dy[token] Dn_e (fp32):
 //   h = bf16(silu(a) b)                 (the forward's rounding)
-//   dw[assign_of[p]] = sum_i dhu_i h_i  (= dy . expert output)
+//   dw[assign_of[p]] = sum_i dhu_i h_i  (= dy . expert output; index p without assign_of)
 //   dh = w dhu, da = dh b silu'(a), db = dh silu(a) -> dab = bf16([da | db])
+// Rows at or past *n_rows (when given) are skipped.
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ z, const float* __restrict__ dhu,
                                                          const float* __restrict__ w_perm, const int32_t* __restrict__ assign_of,
                                                          const int32_t* __restrict__ n_rows, int64_t A, int I,
                                                          uint16_t* __restrict__ h, uint16_t* __restrict__ dab,
                                                          float* __restrict__ dw) {
   const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (p >= A || p >= *n_rows) return;
+  if (p >= A || (n_rows && p >= *n_rows)) return;
   const int lane = threadIdx.x & 63;
   const float w = w_perm[p];
   const float* zp = z + p * 2 * I;
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
     *reinterpret_cast<uint2*>(dab + p * 2 * I + I + i) = dbv;
   }
   dot = wave_sum(dot);
-  if (lane == 0) dw[assign_of[p]] = dot;
+  if (lane == 0) dw[assign_of ? assign_of[p] : p] = dot;
 }
 
 void launch_swiglu_bwd(const float* z, const float* dhu, const float* w_perm, const int32_t* assign_of, const int32_t* n_rows,
@@ -265,6 +266,46 @@ void launch_router_bwd(const float* logits, const float* weights, const int32_t*
                        int Ep, int k, int norm, uint16_t* dlogit, hipStream_t st) {
   if (N <= 0) return;
   router_bwd_kernel<<<static_cast<unsigned>((N + 3) / 4), 256, 0, st>>>(logits, weights, experts, dw, N, E, Ep, k, norm, dlogit);
+}
+
+// Shared-expert gate g = sigmoid(w_s . x): dz[n] = (dy[n] . s[n]) g (1 - g) in fp32, and the same
+// rounded to bf16 in a zero-padded row of qpad entries (the operand of dw_s = sum_n dz[n] x[n]).
+__global__ __launch_bounds__(256) void shared_gate_bwd_kernel(const float* __restrict__ sdot, const float* __restrict__ g,
+                                                              int64_t N, int64_t qpad, float* __restrict__ dz,
+                                                              uint16_t* __restrict__ dz_row) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (n >= qpad) return;
+  float v = 0.f;
+  if (n < N) {
+    v = sdot[n] * g[n] * (1.0f - g[n]);
+    dz[n] = v;
+  }
+  dz_row[n] = f32_to_bf16(v);
+}
+
+void launch_shared_gate_bwd(const float* sdot, const float* g, int64_t N, int64_t qpad, float* dz, uint16_t* dz_row,
+                            hipStream_t st) {
+  shared_gate_bwd_kernel<<<static_cast<unsigned>((qpad + 255) / 256), 256, 0, st>>>(sdot, g, N, qpad, dz, dz_row);
+}
+
+// acc[n][d] += add[n][d] (+ dz[n] w_s[d] when dz is given; w_s bf16): the shared expert's and its
+// gate's input gradients joined to the router's before the final gather.
+__global__ __launch_bounds__(256) void add_rows_kernel(float* __restrict__ acc, const float* __restrict__ add,
+                                                       const float* __restrict__ dz, const uint16_t* __restrict__ ws,
+                                                       int64_t N, int D) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= N * D) return;
+  const int64_t n = i / D;
+  const int d = static_cast<int>(i - n * D);
+  float v = acc[i] + add[i];
+  if (dz) v = fmaf(dz[n], bf16_to_f32(ws[d]), v);
+  acc[i] = v;
+}
+
+void launch_add_rows(float* acc, const float* add, const float* dz, const uint16_t* ws, int64_t N, int D, hipStream_t st) {
+  const int64_t n = N * D;
+  if (n <= 0) return;
+  add_rows_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(acc, add, dz, ws, N, D);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -109,6 +109,9 @@ void launch_scatter_assign(const int32_t* slot_pos, const float* weights, float*
                            int64_t A, hipStream_t st);
 void launch_swiglu_bwd(const float* z, const float* dhu, const float* w_perm, const int32_t* assign_of, const int32_t* n_rows,
                        int64_t A, int I, uint16_t* h, uint16_t* dab, float* dw, hipStream_t st);
+void launch_shared_gate_bwd(const float* sdot, const float* g, int64_t N, int64_t qpad, float* dz, uint16_t* dz_row,
+                            hipStream_t st);
+void launch_add_rows(float* acc, const float* add, const float* dz, const uint16_t* ws, int64_t N, int D, hipStream_t st);
 void launch_router_bwd(const float* logits, const float* weights, const int32_t* experts, const float* dw, int64_t N, int E,
                        int Ep, int k, int norm, uint16_t* dlogit, hipStream_t st);
 void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32_t* poff, int64_t qtot, int G, int M, int Nn,

@@ -263,13 +263,13 @@ static int combine_impl(const moe_config* c, const float* out_perm, const float*
 struct BwdLayout {
   size_t route_partial, logits, weights, experts, counts, offsets, block_counts, token_of, slot_pos, w_perm, assign_of,
       ones, dw, poff, z, dhu, h, dab, dx_rows, dlogit, dxr, dnT, guT, wrT, doT, xgT, hT, dabT, dlogitT, xT, spoff,
-      wr_part, total;
+      wr_part, sh_scale, zs, dhus, hs, dabs, sdot, dz, dz_row, dxs, sdnT, sguT, dysT, hsT, dabsT, total;
   int64_t Ep, Qs, Ns;
 };
 
 static BwdLayout bwd_layout_of(const moe_config* c) {
   BwdLayout L{};
-  const int64_t N = c->n_tokens, A = N * c->top_k, E = c->n_experts, D = c->hidden, I = c->inter;
+  const int64_t N = c->n_tokens, A = N * c->top_k, E = c->n_experts, D = c->hidden, I = c->inter, Is = c->shared_inter;
   L.Ep = (E + 7) / 8 * 8;
   L.Qs = (A + 64 * E + 7) / 8 * 8;
   L.Ns = (N + 63) / 64 * 64;
@@ -306,7 +306,22 @@ static BwdLayout bwd_layout_of(const moe_config* c) {
   L.dlogitT = take(L.Ep * L.Ns * 2);
   L.xT = take(D * L.Ns * 2);
   L.spoff = take((kWgradSlices + 1) * 4);
-  L.wr_part = take(static_cast<int64_t>(kWgradSlices) * E * D * 4);
+  L.wr_part = take(static_cast<int64_t>(kWgradSlices) * std::max(E, 2 * Is) * D * 4);
+  // shared expert: one more group over all N tokens
+  L.sh_scale = take(Is ? N * 4 : 0);
+  L.zs = take(N * 2 * Is * 4);
+  L.dhus = take(N * Is * 4);
+  L.hs = take(N * Is * 2);
+  L.dabs = take(N * 2 * Is * 2);
+  L.sdot = take(Is ? N * 4 : 0);
+  L.dz = take(Is ? N * 4 : 0);
+  L.dz_row = take(Is ? L.Ns * 2 : 0);
+  L.dxs = take(Is ? N * D * 4 : 0);
+  L.sdnT = take(Is * D * 2);
+  L.sguT = take(D * 2 * Is * 2);
+  L.dysT = take(Is ? D * L.Ns * 2 : 0);
+  L.hsT = take(Is * L.Ns * 2);
+  L.dabsT = take(2 * Is * L.Ns * 2);
   L.total = at;
   return L;
 }
@@ -315,7 +330,6 @@ static int backward_checks(const moe_config* c) {
   MOE_TRY(validate_config(c));
   if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs dtype bf16");
   if (c->weight_layout != MOE_LAYOUT_ROWS) return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs row-layout weights");
-  if (c->shared_inter != 0) return fail(MOE_ERR_UNSUPPORTED, "the backward pass has no shared expert");
   return MOE_OK;
 }
 
@@ -535,17 +549,24 @@ int moe_backward_workspace_bytes(const moe_config* cfg, size_t* bytes) {
 }
 
 int moe_backward(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
-                 const void* dy, float* dx, float* dw_router, float* dgate_up, float* ddown, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 const void* shared_gate_up, const void* shared_down, const void* w_shared_gate, const void* dy,
+                 float* dx, float* dw_router, float* dgate_up, float* ddown, float* dshared_gate_up,
+                 float* dshared_down, float* dw_shared_gate, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(backward_checks(cfg));
   if (cfg->n_tokens == 0) return ok();
   if (!x || !w_router || !gate_up || !down || !dy) return fail(MOE_ERR_INVALID_ARG, "x, w_router, gate_up, down or dy is NULL");
   if (!dx || !dw_router || !dgate_up || !ddown) return fail(MOE_ERR_INVALID_ARG, "dx, dw_router, dgate_up or ddown is NULL");
-  for (const void* p : {x, w_router, gate_up, down, dy})
+  const bool shared = cfg->shared_inter > 0, gated = shared && w_shared_gate;
+  if (shared && (!shared_gate_up || !shared_down || !dshared_gate_up || !dshared_down))
+    return fail(MOE_ERR_INVALID_ARG, "shared_inter > 0 needs shared_gate_up, shared_down and their gradients");
+  if (!shared && (shared_gate_up || shared_down || w_shared_gate || dshared_gate_up || dshared_down || dw_shared_gate))
+    return fail(MOE_ERR_INVALID_ARG, "shared expert tensors given with shared_inter == 0");
+  if ((w_shared_gate == nullptr) != (dw_shared_gate == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "w_shared_gate and dw_shared_gate must be both set or both NULL");
+  for (const void* p : {x, w_router, gate_up, down, dy, shared_gate_up, shared_down, w_shared_gate})
     if (reinterpret_cast<uintptr_t>(p) & 15) return fail(MOE_ERR_UNSUPPORTED, "inputs must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(dx) | reinterpret_cast<uintptr_t>(dw_router) | reinterpret_cast<uintptr_t>(dgate_up) |
-       reinterpret_cast<uintptr_t>(ddown)) & 15)
-    return fail(MOE_ERR_UNSUPPORTED, "gradient outputs must be 16-byte aligned");
+  for (const float* p : {dx, dw_router, dgate_up, ddown, dshared_gate_up, dshared_down, dw_shared_gate})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return fail(MOE_ERR_UNSUPPORTED, "gradient outputs must be 16-byte aligned");
   const BwdLayout L = bwd_layout_of(cfg);
   if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, L.total);
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MOE_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
@@ -562,7 +583,8 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   int32_t* token_of = I32(L.token_of);
 
   // forward pieces: routing (with logits), grouping, pre-activations z = [a | b]
-  MOE_TRY(route_impl(cfg, x, w_router, nullptr, F(L.logits), F(L.weights), I32(L.experts), nullptr,
+  float* g = gated ? F(L.sh_scale) : nullptr;                 // shared-expert gate sigmoid(w_s . x)
+  MOE_TRY(route_impl(cfg, x, w_router, gated ? w_shared_gate : nullptr, F(L.logits), F(L.weights), I32(L.experts), g,
                      route_partial_bytes(cfg) ? F(L.route_partial) : nullptr, st));
   MOE_TRY(permute_impl(cfg, I32(L.experts), nullptr, I32(L.counts), offsets, token_of, I32(L.slot_pos), nullptr,
                        I32(L.block_counts), st));
@@ -581,6 +603,20 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
                     cfg->norm_topk_prob, H16(L.dlogit), st);
   launch_down(nt_args(H16(L.dab), nullptr, offsets, E, A, H16(L.guT), D, 2 * I, F(L.dx_rows)), st);
   launch_down(nt_args(H16(L.dlogit), nullptr, nullptr, 1, N, H16(L.wrT), D, Ep, F(L.dxr)), st);
+  const int Is = static_cast<int>(cfg->shared_inter);
+  if (shared) {
+    // the shared expert as one group of all N tokens with row weight g (1 ungated), then its gate
+    launch_transpose_mat(static_cast<const uint16_t*>(shared_down), H16(L.sdnT), 1, D, Is, D, st);
+    launch_transpose_mat(static_cast<const uint16_t*>(shared_gate_up), H16(L.sguT), 1, 2 * Is, D, 2 * Is, st);
+    launch_down(nt_args(x, nullptr, nullptr, 1, N, shared_gate_up, 2 * Is, D, F(L.zs)), st);
+    launch_down(nt_args(dy, nullptr, nullptr, 1, N, H16(L.sdnT), Is, D, F(L.dhus)), st);
+    launch_swiglu_bwd(F(L.zs), F(L.dhus), gated ? g : F(L.ones), nullptr, nullptr, N, Is, H16(L.hs), H16(L.dabs),
+                      F(L.sdot), st);
+    launch_down(nt_args(H16(L.dabs), nullptr, nullptr, 1, N, H16(L.sguT), D, 2 * Is, F(L.dxs)), st);
+    if (gated) launch_shared_gate_bwd(F(L.sdot), g, N, L.Ns, F(L.dz), H16(L.dz_row), st);
+    launch_add_rows(F(L.dxr), F(L.dxs), gated ? F(L.dz) : nullptr, static_cast<const uint16_t*>(w_shared_gate), N, D, st);
+    MOE_TRY(check_launch("moe_backward (shared expert)"));
+  }
   moe_config c32 = *cfg;
   c32.out_dtype = MOE_F32;
   MOE_TRY(combine_impl(&c32, F(L.dx_rows), F(L.ones), I32(L.slot_pos), F(L.dxr), nullptr, dx, st));
@@ -596,6 +632,19 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   launch_wgrad(H16(L.doT), H16(L.hT), L.Qs, poff, 0, E, D, I, ddown, st);
   launch_wgrad(H16(L.dabT), H16(L.xgT), L.Qs, poff, 0, E, 2 * I, D, dgate_up, st);
   launch_wgrad_split(H16(L.dlogitT), H16(L.xT), L.Ns, L.Ns, E, D, kWgradSlices, I32(L.spoff), F(L.wr_part), dw_router, st);
+  if (shared) {
+    launch_transpose_rows(static_cast<const uint16_t*>(dy), D, nullptr, g, nullptr, nullptr, 1, static_cast<int>(N), L.Ns,
+                          H16(L.dysT), L.Ns, st);
+    launch_transpose_rows(H16(L.hs), Is, nullptr, nullptr, nullptr, nullptr, 1, static_cast<int>(N), L.Ns, H16(L.hsT), L.Ns, st);
+    launch_transpose_rows(H16(L.dabs), 2 * Is, nullptr, nullptr, nullptr, nullptr, 1, static_cast<int>(N), L.Ns, H16(L.dabsT),
+                          L.Ns, st);
+    launch_wgrad_split(H16(L.dysT), H16(L.hsT), L.Ns, L.Ns, D, Is, kWgradSlices, I32(L.spoff), F(L.wr_part), dshared_down, st);
+    launch_wgrad_split(H16(L.dabsT), H16(L.xT), L.Ns, L.Ns, 2 * Is, D, kWgradSlices, I32(L.spoff), F(L.wr_part),
+                       dshared_gate_up, st);
+    if (gated)
+      launch_wgrad_split(H16(L.dz_row), H16(L.xT), L.Ns, L.Ns, 1, D, kWgradSlices, I32(L.spoff), F(L.wr_part),
+                         dw_shared_gate, st);
+  }
   MOE_TRY(check_launch("moe_backward (weight gradients)"));
   return ok();
 }

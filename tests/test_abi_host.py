@@ -167,18 +167,24 @@ def test_backward_rules_and_workspace(lib):
     c = B.make_config(64, 256, 12, 2, 128)
     n = B.moe_backward_workspace_bytes(c)
     assert n > 64 * 2 * 2 * 128 * 4                               # at least the recomputed pre-activations
+    assert B.moe_backward_workspace_bytes(c.copy(shared_inter=128)) > n
     for bad, what in ((c.copy(dtype=B.MOE_F32, out_dtype=B.MOE_F32), "bf16"),
-                      (B.make_config(64, 256, 16, 2, 128, packed=True), "row-layout"),
-                      (c.copy(shared_inter=128), "shared")):
+                      (B.make_config(64, 256, 16, 2, 128, packed=True), "row-layout")):
         with pytest.raises(B.MoeError) as ei:
             B.moe_backward_workspace_bytes(bad)
         assert ei.value.status == B.MOE_ERR_UNSUPPORTED and what in str(ei.value)
-    args = [FAKE] * 5 + [FAKE * 2] * 4
+    args = [FAKE] * 4 + [None] * 3 + [FAKE] + [FAKE * 2] * 4 + [None] * 3
     with pytest.raises(B.MoeError) as ei:                          # no workspace
         B.moe_backward(c, *args, None, 0, stream=0)
     assert ei.value.status == B.MOE_ERR_WORKSPACE
+    no_dy = list(args)
+    no_dy[7] = None
     with pytest.raises(B.MoeError) as ei:
-        B.moe_backward(c, *args[:4], None, *args[5:], FAKE * 4, n, stream=0)
+        B.moe_backward(c, *no_dy, FAKE * 4, n, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    cs = c.copy(shared_inter=128)
+    with pytest.raises(B.MoeError) as ei:                          # shared expert without its gradients
+        B.moe_backward(cs, *args[:4], FAKE, FAKE, None, *args[7:], FAKE * 4, 1 << 40, stream=0)
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
     B.moe_backward(c.copy(n_tokens=0), *args, None, 0, stream=0)  # no tokens: no-op
 

@@ -33,6 +33,8 @@ SHAPES = {
     "keras_like": I.custom_shape("bwd_keras", 512, 2048, 60, 4, 1408, seed=53),      # E = 60, wide experts
     "tall": I.custom_shape("bwd_tall", 3000, 512, 8, 2, 256, seed=54),               # long per-expert sums
     "norm_off": I.custom_shape("bwd_nonorm", 64, 256, 16, 4, 128, norm_topk_prob=False, seed=55),
+    "shared_gated": I.custom_shape("bwd_sh", 300, 256, 32, 4, 128, shared_inter=256, seed=56),
+    "shared_ungated": I.custom_shape("bwd_sh_u", 130, 384, 16, 2, 128, shared_inter=128, seed=57, shared_gated=False),
 }
 
 
@@ -53,9 +55,16 @@ def run_and_compare(d, dev):
     cfg = B.config_for(s)
     g = B.backward(cfg, dev, bf16_dev(dy_np))
     torch.cuda.synchronize()
+    sh = {}
+    if s.shared_inter:
+        sh = dict(shared_gate_up=d.values("shared_gate_up"), shared_down=d.values("shared_down"),
+                  w_shared_gate=d.values("w_shared_gate"))
     ref = O.backward(d.values("x"), d.values("w_router"), d.expert_view("gate_up"), d.expert_view("down"),
-                     s.top_k, dy_np, s.norm_topk_prob)
-    for name, key in (("dx", "dx"), ("dw_router", "dw_router"), ("dgate_up", "dgate_up"), ("ddown", "ddown")):
+                     s.top_k, dy_np, s.norm_topk_prob, **sh)
+    names = ["dx", "dw_router", "dgate_up", "ddown"] + [n for n in ("dshared_gate_up", "dshared_down", "dw_shared_gate")
+                                                            if n in g]
+    assert ("dw_shared_gate" in g) == ("dw_shared_gate" in ref)
+    for name, key in ((n, n) for n in names):
         got = g[name].cpu().numpy().astype(np.float64)
         want = np.asarray(ref[key], np.float64).reshape(got.shape)
         assert np.isfinite(got).all(), name
@@ -78,7 +87,7 @@ def test_backward_vs_oracle(name):
     run_and_compare(d, B.to_device(d.store))
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "fanout"])
 def test_backward_full_size(name):
     # prefill: 256-row GEMM tiles and a 16,263-row sum for the hottest expert's weight gradients
     say(f"[backward] {name} (full size)")
