@@ -16,39 +16,61 @@ namespace moe {
 
 constexpr int kTT = 64;          // transpose tile
 
-// out[g][c][r] = in[g][r][c] for r < R, 0 for R <= r < Rp (bf16). One 64 x 64 tile per workgroup;
-// rows of 16-byte chunks both ways, staged through LDS with a one-element pad per row.
-__global__ __launch_bounds__(256) void transpose_mat_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+// 16-byte chunks of a row of T (bf16 bits or fp32 bits) <-> its CH elements.
+template <typename T> struct Chunk {
+  static constexpr int CH = 16 / static_cast<int>(sizeof(T));
+  __device__ static void unpack(u32x4 v, T* e) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      e[i] = sizeof(T) == 2 ? static_cast<T>(v[i >> 1] >> (16 * (i & 1))) : static_cast<T>(v[i]);
+  }
+  __device__ static u32x4 pack(const T* e) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = sizeof(T) == 2 ? (static_cast<uint32_t>(e[2 * i]) | (static_cast<uint32_t>(e[2 * i + 1]) << 16))
+                            : static_cast<uint32_t>(e[i]);
+    return v;
+  }
+};
+
+// out[g][c][r] = in[g][r][c] for r < R, 0 for R <= r < Rp (T = bf16 or fp32 bits). One 64 x 64
+// tile per workgroup; rows of 16-byte chunks both ways, staged through LDS with a pad per row.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_mat_kernel(const T* __restrict__ in, T* __restrict__ out,
                                                             int R, int C, int Rp) {
-  __shared__ uint16_t s[kTT][kTT + 2];
+  constexpr int CH = Chunk<T>::CH, NC = kTT / CH;
+  __shared__ T s[kTT][kTT + 2];
   const int64_t g = blockIdx.z;
   const int r0 = blockIdx.y * kTT, c0 = blockIdx.x * kTT, tid = threadIdx.x;
-  const uint16_t* src = in + g * R * static_cast<int64_t>(C);
-  for (int t = tid; t < kTT * (kTT / 8); t += 256) {
-    const int rr = t >> 3, ch = (t & 7) * 8;
+  const T* src = in + g * R * static_cast<int64_t>(C);
+  for (int t = tid; t < kTT * NC; t += 256) {
+    const int rr = t / NC, ch = (t % NC) * CH;
     const int r = r0 + rr, c = c0 + ch;
     u32x4 v = {0, 0, 0, 0};
     if (r < R && c < C) v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * C + c);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[rr][ch + i] = static_cast<uint16_t>(v[i >> 1] >> (16 * (i & 1)));
+    Chunk<T>::unpack(v, &s[rr][ch]);
   }
   __syncthreads();
-  uint16_t* dst = out + g * C * static_cast<int64_t>(Rp);
-  for (int t = tid; t < kTT * (kTT / 8); t += 256) {
-    const int cc = t >> 3, ch = (t & 7) * 8;
+  T* dst = out + g * C * static_cast<int64_t>(Rp);
+  for (int t = tid; t < kTT * NC; t += 256) {
+    const int cc = t / NC, ch = (t % NC) * CH;
     const int c = c0 + cc, r = r0 + ch;
     if (c >= C || r >= Rp) continue;
-    u32x4 v;
+    T e[CH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = static_cast<uint32_t>(s[ch + 2 * i][cc]) | (static_cast<uint32_t>(s[ch + 2 * i + 1][cc]) << 16);
-    *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(c) * Rp + r) = v;
+    for (int i = 0; i < CH; ++i) e[i] = s[ch + i][cc];
+    *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(c) * Rp + r) = Chunk<T>::pack(e);
   }
 }
 
-void launch_transpose_mat(const uint16_t* in, uint16_t* out, int64_t G, int R, int C, int Rp, hipStream_t st) {
+void launch_transpose_mat(const void* in, void* out, int64_t G, int R, int C, int Rp, bool f32, hipStream_t st) {
   if (G <= 0 || R <= 0 || C <= 0) return;
   dim3 grid((C + kTT - 1) / kTT, (Rp + kTT - 1) / kTT, static_cast<unsigned>(G));
-  transpose_mat_kernel<<<grid, 256, 0, st>>>(in, out, R, C, Rp);
+  if (f32)
+    transpose_mat_kernel<uint32_t><<<grid, 256, 0, st>>>(static_cast<const uint32_t*>(in), static_cast<uint32_t*>(out), R, C, Rp);
+  else
+    transpose_mat_kernel<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C, Rp);
 }
 
 // Per-expert row ranges padded to multiples of 64: poff[g] = sum_{g' < g} roundup(counts[g'], 64).
@@ -78,13 +100,15 @@ void launch_pad_offsets(const int32_t* counts, int32_t* poff, int G, hipStream_t
 // sorted row p = off[g] + q - poff[g] if that lies inside the group, else zero. The source row is
 // token_of[p] when gathering, the value is scaled by scale[p] when given (rounded to bf16 once).
 // With off == nullptr there is one group of n1 rows padded to qtot.
-__global__ __launch_bounds__(256) void transpose_rows_kernel(const uint16_t* __restrict__ src, int M,
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const T* __restrict__ src, int M,
                                                              const int32_t* __restrict__ gather,
                                                              const float* __restrict__ scale,
                                                              const int32_t* __restrict__ off,
                                                              const int32_t* __restrict__ poff, int G, int n1,
-                                                             int64_t qmax, uint16_t* __restrict__ out, int64_t ld) {
-  __shared__ uint16_t s[kTT][kTT + 2];
+                                                             int64_t qmax, T* __restrict__ out, int64_t ld) {
+  constexpr int CH = Chunk<T>::CH, NC = kTT / CH;
+  __shared__ T s[kTT][kTT + 2];
   __shared__ int s_src[kTT];
   __shared__ float s_scl[kTT];
   const int64_t q0 = static_cast<int64_t>(blockIdx.x) * kTT;
@@ -111,8 +135,8 @@ __global__ __launch_bounds__(256) void transpose_rows_kernel(const uint16_t* __r
     s_scl[tid] = p < 0 ? 0.f : (scale ? scale[p] : 1.f);
   }
   __syncthreads();
-  for (int t = tid; t < kTT * (kTT / 8); t += 256) {
-    const int qq = t >> 3, ch = (t & 7) * 8;
+  for (int t = tid; t < kTT * NC; t += 256) {
+    const int qq = t / NC, ch = (t % NC) * CH;
     const int m = m0 + ch;
     const int srow = s_src[qq];
     u32x4 v = {0, 0, 0, 0};
@@ -121,32 +145,40 @@ __global__ __launch_bounds__(256) void transpose_rows_kernel(const uint16_t* __r
       const float sc = s_scl[qq];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float lo = bf16_to_f32(static_cast<uint16_t>(v[i] & 0xffff)) * sc;
-        const float hi = bf16_to_f32(static_cast<uint16_t>(v[i] >> 16)) * sc;
-        v[i] = pack_bf16x2(lo, hi);
+        if constexpr (sizeof(T) == 2) {
+          const float lo = bf16_to_f32(static_cast<uint16_t>(v[i] & 0xffff)) * sc;
+          const float hi = bf16_to_f32(static_cast<uint16_t>(v[i] >> 16)) * sc;
+          v[i] = pack_bf16x2(lo, hi);
+        } else {
+          v[i] = __float_as_uint(__uint_as_float(v[i]) * sc);
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[qq][ch + i] = static_cast<uint16_t>(v[i >> 1] >> (16 * (i & 1)));
+    Chunk<T>::unpack(v, &s[qq][ch]);
   }
   __syncthreads();
-  for (int t = tid; t < kTT * (kTT / 8); t += 256) {
-    const int mm = t >> 3, ch = (t & 7) * 8;
+  for (int t = tid; t < kTT * NC; t += 256) {
+    const int mm = t / NC, ch = (t % NC) * CH;
     const int m = m0 + mm;
     const int64_t q = q0 + ch;
     if (m >= M || q >= qtot) continue;
-    u32x4 v;
+    T e[CH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = static_cast<uint32_t>(s[ch + 2 * i][mm]) | (static_cast<uint32_t>(s[ch + 2 * i + 1][mm]) << 16);
-    *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(m) * ld + q) = v;
+    for (int i = 0; i < CH; ++i) e[i] = s[ch + i][mm];
+    *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(m) * ld + q) = Chunk<T>::pack(e);
   }
 }
 
-void launch_transpose_rows(const uint16_t* src, int M, const int32_t* gather, const float* scale, const int32_t* off,
-                           const int32_t* poff, int G, int n1, int64_t qmax, uint16_t* out, int64_t ld, hipStream_t st) {
+void launch_transpose_rows(const void* src, int M, const int32_t* gather, const float* scale, const int32_t* off,
+                           const int32_t* poff, int G, int n1, int64_t qmax, void* out, int64_t ld, bool f32, hipStream_t st) {
   if (qmax <= 0 || M <= 0) return;
   dim3 grid(static_cast<unsigned>((qmax + kTT - 1) / kTT), (M + kTT - 1) / kTT);
-  transpose_rows_kernel<<<grid, 256, 0, st>>>(src, M, gather, scale, off, poff, G, n1, qmax, out, ld);
+  if (f32)
+    transpose_rows_kernel<uint32_t><<<grid, 256, 0, st>>>(static_cast<const uint32_t*>(src), M, gather, scale, off, poff, G,
+                                                          n1, qmax, static_cast<uint32_t*>(out), ld);
+  else
+    transpose_rows_kernel<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(src), M, gather, scale, off, poff, G,
+                                                          n1, qmax, static_cast<uint16_t*>(out), ld);
 }
 
 // w_perm[slot_pos[a]] = weights[a], assign_of[slot_pos[a]] = a; ones[a] = 1.
@@ -172,10 +204,12 @@ void launch_scatter_assign(const int32_t* slot_pos, const float* weights, float*
 //   dw[assign_of[p]] = sum_i dhu_i h_i  (= dy . expert output; index p without assign_of)
 //   dh = w dhu, da = dh b silu'(a), db = dh silu(a) -> dab = bf16([da | db])
 // Rows at or past *n_rows (when given) are skipped.
+// kF32: fp32 layers keep h, da and db in fp32 (no rounding).
+template <bool kF32>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ z, const float* __restrict__ dhu,
                                                          const float* __restrict__ w_perm, const int32_t* __restrict__ assign_of,
                                                          const int32_t* __restrict__ n_rows, int64_t A, int I,
-                                                         uint16_t* __restrict__ h, uint16_t* __restrict__ dab,
+                                                         void* __restrict__ h_out, void* __restrict__ dab_out,
                                                          float* __restrict__ dw) {
   const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (p >= A || (n_rows && p >= *n_rows)) return;
@@ -193,39 +227,54 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
     for (int t = 0; t < 4; ++t) {
       const float a = av[t], b = bv[t];
       const float s = 1.0f / (1.0f + __expf(-a));
-      hh[t] = bf16_to_f32(f32_to_bf16(a * s * b));
+      hh[t] = kF32 ? a * s * b : bf16_to_f32(f32_to_bf16(a * s * b));
       dot = fmaf(gv[t], hh[t], dot);
       const float dh = w * gv[t];
       da[t] = dh * b * (s * (1.0f + a * (1.0f - s)));
       db[t] = dh * a * s;
     }
-    uint2 hv, dav, dbv;
-    hv.x = pack_bf16x2(hh[0], hh[1]);
-    hv.y = pack_bf16x2(hh[2], hh[3]);
-    dav.x = pack_bf16x2(da[0], da[1]);
-    dav.y = pack_bf16x2(da[2], da[3]);
-    dbv.x = pack_bf16x2(db[0], db[1]);
-    dbv.y = pack_bf16x2(db[2], db[3]);
-    *reinterpret_cast<uint2*>(h + p * I + i) = hv;
-    *reinterpret_cast<uint2*>(dab + p * 2 * I + i) = dav;
-    *reinterpret_cast<uint2*>(dab + p * 2 * I + I + i) = dbv;
+    if constexpr (kF32) {
+      float* h = static_cast<float*>(h_out);
+      float* dab = static_cast<float*>(dab_out);
+      *reinterpret_cast<f32x4*>(h + p * I + i) = f32x4{hh[0], hh[1], hh[2], hh[3]};
+      *reinterpret_cast<f32x4*>(dab + p * 2 * I + i) = f32x4{da[0], da[1], da[2], da[3]};
+      *reinterpret_cast<f32x4*>(dab + p * 2 * I + I + i) = f32x4{db[0], db[1], db[2], db[3]};
+    } else {
+      uint16_t* h = static_cast<uint16_t*>(h_out);
+      uint16_t* dab = static_cast<uint16_t*>(dab_out);
+      uint2 hv, dav, dbv;
+      hv.x = pack_bf16x2(hh[0], hh[1]);
+      hv.y = pack_bf16x2(hh[2], hh[3]);
+      dav.x = pack_bf16x2(da[0], da[1]);
+      dav.y = pack_bf16x2(da[2], da[3]);
+      dbv.x = pack_bf16x2(db[0], db[1]);
+      dbv.y = pack_bf16x2(db[2], db[3]);
+      *reinterpret_cast<uint2*>(h + p * I + i) = hv;
+      *reinterpret_cast<uint2*>(dab + p * 2 * I + i) = dav;
+      *reinterpret_cast<uint2*>(dab + p * 2 * I + I + i) = dbv;
+    }
   }
   dot = wave_sum(dot);
   if (lane == 0) dw[assign_of ? assign_of[p] : p] = dot;
 }
 
 void launch_swiglu_bwd(const float* z, const float* dhu, const float* w_perm, const int32_t* assign_of, const int32_t* n_rows,
-                       int64_t A, int I, uint16_t* h, uint16_t* dab, float* dw, hipStream_t st) {
+                       int64_t A, int I, void* h, void* dab, float* dw, bool f32, hipStream_t st) {
   if (A <= 0) return;
-  swiglu_bwd_kernel<<<static_cast<unsigned>((A + 3) / 4), 256, 0, st>>>(z, dhu, w_perm, assign_of, n_rows, A, I, h, dab, dw);
+  const unsigned grid = static_cast<unsigned>((A + 3) / 4);
+  if (f32)
+    swiglu_bwd_kernel<true><<<grid, 256, 0, st>>>(z, dhu, w_perm, assign_of, n_rows, A, I, h, dab, dw);
+  else
+    swiglu_bwd_kernel<false><<<grid, 256, 0, st>>>(z, dhu, w_perm, assign_of, n_rows, A, I, h, dab, dw);
 }
 
 // One wave per token: p = softmax(logits) in fp32, the gradient of the kept (renormalised) weights
 // back to the logits; dlogit [N, Ep] bf16, zero in the padding columns E <= e < Ep.
+template <bool kF32>
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ logits, const float* __restrict__ weights,
                                                          const int32_t* __restrict__ experts, const float* __restrict__ dw,
                                                          int64_t N, int E, int Ep, int k, int norm,
-                                                         uint16_t* __restrict__ dlogit) {
+                                                         void* __restrict__ dlogit) {
   const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
   const int lane = threadIdx.x & 63;
@@ -258,21 +307,27 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
       const float pe = __expf(lg[e] - mx) * inv;
       g = pe * (dp - t);
     }
-    dlogit[n * Ep + e] = f32_to_bf16(g);
+    if constexpr (kF32) static_cast<float*>(dlogit)[n * Ep + e] = g;
+    else static_cast<uint16_t*>(dlogit)[n * Ep + e] = f32_to_bf16(g);
   }
 }
 
 void launch_router_bwd(const float* logits, const float* weights, const int32_t* experts, const float* dw, int64_t N, int E,
-                       int Ep, int k, int norm, uint16_t* dlogit, hipStream_t st) {
+                       int Ep, int k, int norm, void* dlogit, bool f32, hipStream_t st) {
   if (N <= 0) return;
-  router_bwd_kernel<<<static_cast<unsigned>((N + 3) / 4), 256, 0, st>>>(logits, weights, experts, dw, N, E, Ep, k, norm, dlogit);
+  const unsigned grid = static_cast<unsigned>((N + 3) / 4);
+  if (f32)
+    router_bwd_kernel<true><<<grid, 256, 0, st>>>(logits, weights, experts, dw, N, E, Ep, k, norm, dlogit);
+  else
+    router_bwd_kernel<false><<<grid, 256, 0, st>>>(logits, weights, experts, dw, N, E, Ep, k, norm, dlogit);
 }
 
 // Shared-expert gate g = sigmoid(w_s . x): dz[n] = (dy[n] . s[n]) g (1 - g) in fp32, and the same
 // rounded to bf16 in a zero-padded row of qpad entries (the operand of dw_s = sum_n dz[n] x[n]).
+template <bool kF32>
 __global__ __launch_bounds__(256) void shared_gate_bwd_kernel(const float* __restrict__ sdot, const float* __restrict__ g,
                                                               int64_t N, int64_t qpad, float* __restrict__ dz,
-                                                              uint16_t* __restrict__ dz_row) {
+                                                              void* __restrict__ dz_row) {
   const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (n >= qpad) return;
   float v = 0.f;
@@ -280,32 +335,41 @@ __global__ __launch_bounds__(256) void shared_gate_bwd_kernel(const float* __res
     v = sdot[n] * g[n] * (1.0f - g[n]);
     dz[n] = v;
   }
-  dz_row[n] = f32_to_bf16(v);
+  if constexpr (kF32) static_cast<float*>(dz_row)[n] = v;
+  else static_cast<uint16_t*>(dz_row)[n] = f32_to_bf16(v);
 }
 
-void launch_shared_gate_bwd(const float* sdot, const float* g, int64_t N, int64_t qpad, float* dz, uint16_t* dz_row,
+void launch_shared_gate_bwd(const float* sdot, const float* g, int64_t N, int64_t qpad, float* dz, void* dz_row, bool f32,
                             hipStream_t st) {
-  shared_gate_bwd_kernel<<<static_cast<unsigned>((qpad + 255) / 256), 256, 0, st>>>(sdot, g, N, qpad, dz, dz_row);
+  const unsigned grid = static_cast<unsigned>((qpad + 255) / 256);
+  if (f32)
+    shared_gate_bwd_kernel<true><<<grid, 256, 0, st>>>(sdot, g, N, qpad, dz, dz_row);
+  else
+    shared_gate_bwd_kernel<false><<<grid, 256, 0, st>>>(sdot, g, N, qpad, dz, dz_row);
 }
 
-// acc[n][d] += add[n][d] (+ dz[n] w_s[d] when dz is given; w_s bf16): the shared expert's and its
-// gate's input gradients joined to the router's before the final gather.
+// acc[n][d] += add[n][d] (+ dz[n] w_s[d] when dz is given; w_s bf16 or fp32): the shared expert's
+// and its gate's input gradients joined to the router's before the final gather.
 __global__ __launch_bounds__(256) void add_rows_kernel(float* __restrict__ acc, const float* __restrict__ add,
-                                                       const float* __restrict__ dz, const uint16_t* __restrict__ ws,
-                                                       int64_t N, int D) {
+                                                       const float* __restrict__ dz, const void* __restrict__ ws,
+                                                       bool ws_f32, int64_t N, int D) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= N * D) return;
   const int64_t n = i / D;
   const int d = static_cast<int>(i - n * D);
   float v = acc[i] + add[i];
-  if (dz) v = fmaf(dz[n], bf16_to_f32(ws[d]), v);
+  if (dz) {
+    const float w = ws_f32 ? static_cast<const float*>(ws)[d] : bf16_to_f32(static_cast<const uint16_t*>(ws)[d]);
+    v = fmaf(dz[n], w, v);
+  }
   acc[i] = v;
 }
 
-void launch_add_rows(float* acc, const float* add, const float* dz, const uint16_t* ws, int64_t N, int D, hipStream_t st) {
+void launch_add_rows(float* acc, const float* add, const float* dz, const void* ws, bool ws_f32, int64_t N, int D,
+                     hipStream_t st) {
   const int64_t n = N * D;
   if (n <= 0) return;
-  add_rows_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(acc, add, dz, ws, N, D);
+  add_rows_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(acc, add, dz, ws, ws_f32, N, D);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -405,6 +469,39 @@ void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32
   if (G <= 0 || M <= 0 || Nn <= 0) return;
   dim3 grid((Nn + kWB - 1) / kWB, (M + kWB - 1) / kWB, static_cast<unsigned>(G));
   gemm_wgrad_kernel<<<grid, 256, 0, st>>>(A, Bm, ld, poff, qtot, M, Nn, out);
+}
+
+// fp32 weight gradient (fp32 layers): the same sums with FMAs, one output per thread of a 16 x 16
+// tile, 64-wide k-slices through LDS, in q order (deterministic).
+__global__ __launch_bounds__(256) void gemm_wgrad_f32_kernel(const float* __restrict__ Am, const float* __restrict__ Bm,
+                                                             int64_t ld, const int32_t* __restrict__ poff, int64_t qtot,
+                                                             int M, int Nn, float* __restrict__ out) {
+  __shared__ float sA[16][kWK + 1];
+  __shared__ float sB[16][kWK + 1];
+  const int g = blockIdx.z;
+  const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 16, tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int64_t q0 = poff ? poff[g] : 0;
+  const int64_t q1 = poff ? poff[g + 1] : qtot;
+  float acc = 0.f;
+  for (int64_t qb = q0; qb < q1; qb += kWK) {
+    for (int i = tid; i < 16 * kWK; i += 256) {
+      const int r = i / kWK, c = i % kWK;
+      sA[r][c] = m0 + r < M ? Am[static_cast<int64_t>(m0 + r) * ld + qb + c] : 0.f;
+      sB[r][c] = n0 + r < Nn ? Bm[static_cast<int64_t>(n0 + r) * ld + qb + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < kWK; ++c) acc = fmaf(sA[ty][c], sB[tx][c], acc);
+    __syncthreads();
+  }
+  if (m0 + ty < M && n0 + tx < Nn) out[static_cast<int64_t>(g) * M * Nn + static_cast<int64_t>(m0 + ty) * Nn + n0 + tx] = acc;
+}
+
+void launch_wgrad_f32(const float* A, const float* Bm, int64_t ld, const int32_t* poff, int64_t qtot, int G, int M, int Nn,
+                      float* out, hipStream_t st) {
+  if (G <= 0 || M <= 0 || Nn <= 0) return;
+  dim3 grid((Nn + 15) / 16, (M + 15) / 16, static_cast<unsigned>(G));
+  gemm_wgrad_f32_kernel<<<grid, 256, 0, st>>>(A, Bm, ld, poff, qtot, M, Nn, out);
 }
 
 // Split reduction for a single long group (the router's sum over all tokens): slice s covers

@@ -100,22 +100,26 @@ void launch_stats(const float* logits, const int32_t* counts, float* f, float* P
 // Selection-bias nudge: bias[e] -= gamma * sign(counts[e] - A / E).
 void launch_bias_update(const int32_t* counts, float* bias, float gamma, int64_t A, int E, hipStream_t st);
 
-// Backward pass helpers (backward.hip).
-void launch_transpose_mat(const uint16_t* in, uint16_t* out, int64_t G, int R, int C, int Rp, hipStream_t st);
+// Backward pass helpers (backward.hip). f32: the layer's dtype is fp32 (elements of 4 bytes, no
+// rounding of the intermediates); otherwise bf16.
+void launch_transpose_mat(const void* in, void* out, int64_t G, int R, int C, int Rp, bool f32, hipStream_t st);
 void launch_pad_offsets(const int32_t* counts, int32_t* poff, int G, hipStream_t st);
-void launch_transpose_rows(const uint16_t* src, int M, const int32_t* gather, const float* scale, const int32_t* off,
-                           const int32_t* poff, int G, int n1, int64_t qmax, uint16_t* out, int64_t ld, hipStream_t st);
+void launch_transpose_rows(const void* src, int M, const int32_t* gather, const float* scale, const int32_t* off,
+                           const int32_t* poff, int G, int n1, int64_t qmax, void* out, int64_t ld, bool f32, hipStream_t st);
 void launch_scatter_assign(const int32_t* slot_pos, const float* weights, float* w_perm, int32_t* assign_of, float* ones,
                            int64_t A, hipStream_t st);
 void launch_swiglu_bwd(const float* z, const float* dhu, const float* w_perm, const int32_t* assign_of, const int32_t* n_rows,
-                       int64_t A, int I, uint16_t* h, uint16_t* dab, float* dw, hipStream_t st);
-void launch_shared_gate_bwd(const float* sdot, const float* g, int64_t N, int64_t qpad, float* dz, uint16_t* dz_row,
+                       int64_t A, int I, void* h, void* dab, float* dw, bool f32, hipStream_t st);
+void launch_shared_gate_bwd(const float* sdot, const float* g, int64_t N, int64_t qpad, float* dz, void* dz_row, bool f32,
                             hipStream_t st);
-void launch_add_rows(float* acc, const float* add, const float* dz, const uint16_t* ws, int64_t N, int D, hipStream_t st);
+void launch_add_rows(float* acc, const float* add, const float* dz, const void* ws, bool ws_f32, int64_t N, int D,
+                     hipStream_t st);
 void launch_router_bwd(const float* logits, const float* weights, const int32_t* experts, const float* dw, int64_t N, int E,
-                       int Ep, int k, int norm, uint16_t* dlogit, hipStream_t st);
+                       int Ep, int k, int norm, void* dlogit, bool f32, hipStream_t st);
 void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32_t* poff, int64_t qtot, int G, int M, int Nn,
                   float* out, hipStream_t st);
+void launch_wgrad_f32(const float* A, const float* Bm, int64_t ld, const int32_t* poff, int64_t qtot, int G, int M, int Nn,
+                      float* out, hipStream_t st);
 constexpr int kWgradSlices = 16;     // split of a single long reduction (poff: kWgradSlices + 1 entries)
 void launch_wgrad_split(const uint16_t* A, const uint16_t* Bm, int64_t ld, int64_t qtot, int M, int Nn, int S,
                         int32_t* poff, float* part, float* out, hipStream_t st);

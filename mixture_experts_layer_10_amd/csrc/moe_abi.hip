@@ -270,6 +270,7 @@ struct BwdLayout {
 static BwdLayout bwd_layout_of(const moe_config* c) {
   BwdLayout L{};
   const int64_t N = c->n_tokens, A = N * c->top_k, E = c->n_experts, D = c->hidden, I = c->inter, Is = c->shared_inter;
+  const int64_t eb = static_cast<int64_t>(elem_bytes(c->dtype));      // layer-dtype intermediates
   L.Ep = (E + 7) / 8 * 8;
   L.Qs = (A + 64 * E + 7) / 8 * 8;
   L.Ns = (N + 63) / 64 * 64;
@@ -291,51 +292,50 @@ static BwdLayout bwd_layout_of(const moe_config* c) {
   L.poff = take((E + 1) * 4);
   L.z = take(A * 2 * I * 4);
   L.dhu = take(A * I * 4);
-  L.h = take(A * I * 2);
-  L.dab = take(A * 2 * I * 2);
+  L.h = take(A * I * eb);
+  L.dab = take(A * 2 * I * eb);
   L.dx_rows = take(A * D * 4);
-  L.dlogit = take(N * L.Ep * 2);
+  L.dlogit = take(N * L.Ep * eb);
   L.dxr = take(N * D * 4);
-  L.dnT = take(E * I * D * 2);
-  L.guT = take(E * D * 2 * I * 2);
-  L.wrT = take(D * L.Ep * 2);
-  L.doT = take(D * L.Qs * 2);
-  L.xgT = take(D * L.Qs * 2);
-  L.hT = take(I * L.Qs * 2);
-  L.dabT = take(2 * I * L.Qs * 2);
-  L.dlogitT = take(L.Ep * L.Ns * 2);
-  L.xT = take(D * L.Ns * 2);
+  L.dnT = take(E * I * D * eb);
+  L.guT = take(E * D * 2 * I * eb);
+  L.wrT = take(D * L.Ep * eb);
+  L.doT = take(D * L.Qs * eb);
+  L.xgT = take(D * L.Qs * eb);
+  L.hT = take(I * L.Qs * eb);
+  L.dabT = take(2 * I * L.Qs * eb);
+  L.dlogitT = take(L.Ep * L.Ns * eb);
+  L.xT = take(D * L.Ns * eb);
   L.spoff = take((kWgradSlices + 1) * 4);
   L.wr_part = take(static_cast<int64_t>(kWgradSlices) * std::max(E, 2 * Is) * D * 4);
   // shared expert: one more group over all N tokens
   L.sh_scale = take(Is ? N * 4 : 0);
   L.zs = take(N * 2 * Is * 4);
   L.dhus = take(N * Is * 4);
-  L.hs = take(N * Is * 2);
-  L.dabs = take(N * 2 * Is * 2);
+  L.hs = take(N * Is * eb);
+  L.dabs = take(N * 2 * Is * eb);
   L.sdot = take(Is ? N * 4 : 0);
   L.dz = take(Is ? N * 4 : 0);
-  L.dz_row = take(Is ? L.Ns * 2 : 0);
+  L.dz_row = take(Is ? L.Ns * eb : 0);
   L.dxs = take(Is ? N * D * 4 : 0);
-  L.sdnT = take(Is * D * 2);
-  L.sguT = take(D * 2 * Is * 2);
-  L.dysT = take(Is ? D * L.Ns * 2 : 0);
-  L.hsT = take(Is * L.Ns * 2);
-  L.dabsT = take(2 * Is * L.Ns * 2);
+  L.sdnT = take(Is * D * eb);
+  L.sguT = take(D * 2 * Is * eb);
+  L.dysT = take(Is ? D * L.Ns * eb : 0);
+  L.hsT = take(Is * L.Ns * eb);
+  L.dabsT = take(2 * Is * L.Ns * eb);
   L.total = at;
   return L;
 }
 
 static int backward_checks(const moe_config* c) {
   MOE_TRY(validate_config(c));
-  if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs dtype bf16");
   if (c->weight_layout != MOE_LAYOUT_ROWS) return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs row-layout weights");
   return MOE_OK;
 }
 
 // The [out, in] grouped GEMM (fp32 output) on arbitrary operands: out[p] = X[row p] W_g^T, K = k_in.
 static GemmArgs nt_args(const void* x, const int32_t* row_index, const int32_t* offsets, int G, int64_t max_rows,
-                        const void* w, int n_out, int k_in, void* out) {
+                        const void* w, int n_out, int k_in, void* out, bool bf16) {
   GemmArgs a{};
   a.x = x;
   a.row_index = row_index;
@@ -346,7 +346,7 @@ static GemmArgs nt_args(const void* x, const int32_t* row_index, const int32_t* 
   a.G = G;
   a.D = n_out;      // the down form: NOUT = D, K = I
   a.I = k_in;
-  a.bf16 = true;
+  a.bf16 = bf16;
   return a;
 }
 
@@ -574,7 +574,8 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   char* base = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
-  auto H16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
+  auto PV = [&](size_t off) { return static_cast<void*>(base + off); };        // layer-dtype buffers
+  const bool f32 = cfg->dtype == MOE_F32, bf = !f32;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t N = cfg->n_tokens, A = N * cfg->top_k;
   const int E = static_cast<int>(cfg->n_experts), D = static_cast<int>(cfg->hidden), I = static_cast<int>(cfg->inter);
@@ -590,31 +591,32 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
                        I32(L.block_counts), st));
   launch_scatter_assign(I32(L.slot_pos), F(L.weights), F(L.w_perm), I32(L.assign_of), F(L.ones), A, st);
   launch_pad_offsets(I32(L.counts), I32(L.poff), E, st);
-  launch_transpose_mat(static_cast<const uint16_t*>(down), H16(L.dnT), E, D, I, D, st);       // [E, I, D]
-  launch_transpose_mat(static_cast<const uint16_t*>(gate_up), H16(L.guT), E, 2 * I, D, 2 * I, st);  // [E, D, 2I]
-  launch_transpose_mat(static_cast<const uint16_t*>(w_router), H16(L.wrT), 1, E, D, Ep, st);  // [D, Ep]
+  launch_transpose_mat(down, PV(L.dnT), E, D, I, D, f32, st);                   // [E, I, D]
+  launch_transpose_mat(gate_up, PV(L.guT), E, 2 * I, D, 2 * I, f32, st);          // [E, D, 2I]
+  launch_transpose_mat(w_router, PV(L.wrT), 1, E, D, Ep, f32, st);               // [D, Ep]
   MOE_TRY(check_launch("moe_backward (setup)"));
-  launch_down(nt_args(x, token_of, offsets, E, A, gate_up, 2 * I, D, F(L.z)), st);
-  launch_down(nt_args(dy, token_of, offsets, E, A, H16(L.dnT), I, D, F(L.dhu)), st);
+  launch_down(nt_args(x, token_of, offsets, E, A, gate_up, 2 * I, D, F(L.z), bf), st);
+  launch_down(nt_args(dy, token_of, offsets, E, A, PV(L.dnT), I, D, F(L.dhu), bf), st);
   MOE_TRY(check_launch("moe_backward (recompute)"));
   // expert and router gradients of the activations
-  launch_swiglu_bwd(F(L.z), F(L.dhu), F(L.w_perm), I32(L.assign_of), offsets + E, A, I, H16(L.h), H16(L.dab), F(L.dw), st);
+  launch_swiglu_bwd(F(L.z), F(L.dhu), F(L.w_perm), I32(L.assign_of), offsets + E, A, I, PV(L.h), PV(L.dab), F(L.dw), f32,
+                    st);
   launch_router_bwd(F(L.logits), F(L.weights), I32(L.experts), F(L.dw), N, E, Ep, static_cast<int>(cfg->top_k),
-                    cfg->norm_topk_prob, H16(L.dlogit), st);
-  launch_down(nt_args(H16(L.dab), nullptr, offsets, E, A, H16(L.guT), D, 2 * I, F(L.dx_rows)), st);
-  launch_down(nt_args(H16(L.dlogit), nullptr, nullptr, 1, N, H16(L.wrT), D, Ep, F(L.dxr)), st);
+                    cfg->norm_topk_prob, PV(L.dlogit), f32, st);
+  launch_down(nt_args(PV(L.dab), nullptr, offsets, E, A, PV(L.guT), D, 2 * I, F(L.dx_rows), bf), st);
+  launch_down(nt_args(PV(L.dlogit), nullptr, nullptr, 1, N, PV(L.wrT), D, Ep, F(L.dxr), bf), st);
   const int Is = static_cast<int>(cfg->shared_inter);
   if (shared) {
     // the shared expert as one group of all N tokens with row weight g (1 ungated), then its gate
-    launch_transpose_mat(static_cast<const uint16_t*>(shared_down), H16(L.sdnT), 1, D, Is, D, st);
-    launch_transpose_mat(static_cast<const uint16_t*>(shared_gate_up), H16(L.sguT), 1, 2 * Is, D, 2 * Is, st);
-    launch_down(nt_args(x, nullptr, nullptr, 1, N, shared_gate_up, 2 * Is, D, F(L.zs)), st);
-    launch_down(nt_args(dy, nullptr, nullptr, 1, N, H16(L.sdnT), Is, D, F(L.dhus)), st);
-    launch_swiglu_bwd(F(L.zs), F(L.dhus), gated ? g : F(L.ones), nullptr, nullptr, N, Is, H16(L.hs), H16(L.dabs),
-                      F(L.sdot), st);
-    launch_down(nt_args(H16(L.dabs), nullptr, nullptr, 1, N, H16(L.sguT), D, 2 * Is, F(L.dxs)), st);
-    if (gated) launch_shared_gate_bwd(F(L.sdot), g, N, L.Ns, F(L.dz), H16(L.dz_row), st);
-    launch_add_rows(F(L.dxr), F(L.dxs), gated ? F(L.dz) : nullptr, static_cast<const uint16_t*>(w_shared_gate), N, D, st);
+    launch_transpose_mat(shared_down, PV(L.sdnT), 1, D, Is, D, f32, st);
+    launch_transpose_mat(shared_gate_up, PV(L.sguT), 1, 2 * Is, D, 2 * Is, f32, st);
+    launch_down(nt_args(x, nullptr, nullptr, 1, N, shared_gate_up, 2 * Is, D, F(L.zs), bf), st);
+    launch_down(nt_args(dy, nullptr, nullptr, 1, N, PV(L.sdnT), Is, D, F(L.dhus), bf), st);
+    launch_swiglu_bwd(F(L.zs), F(L.dhus), gated ? g : F(L.ones), nullptr, nullptr, N, Is, PV(L.hs), PV(L.dabs),
+                      F(L.sdot), f32, st);
+    launch_down(nt_args(PV(L.dabs), nullptr, nullptr, 1, N, PV(L.sguT), D, 2 * Is, F(L.dxs), bf), st);
+    if (gated) launch_shared_gate_bwd(F(L.sdot), g, N, L.Ns, F(L.dz), PV(L.dz_row), f32, st);
+    launch_add_rows(F(L.dxr), F(L.dxs), gated ? F(L.dz) : nullptr, w_shared_gate, f32, N, D, st);
     MOE_TRY(check_launch("moe_backward (shared expert)"));
   }
   moe_config c32 = *cfg;
@@ -622,28 +624,35 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   MOE_TRY(combine_impl(&c32, F(L.dx_rows), F(L.ones), I32(L.slot_pos), F(L.dxr), nullptr, dx, st));
   // weight gradients over each expert's rows (padded transposes), then over the tokens for W_r
   const int32_t* poff = I32(L.poff);
-  launch_transpose_rows(static_cast<const uint16_t*>(dy), D, token_of, F(L.w_perm), offsets, poff, E, 0, L.Qs, H16(L.doT), L.Qs, st);
-  launch_transpose_rows(static_cast<const uint16_t*>(x), D, token_of, nullptr, offsets, poff, E, 0, L.Qs, H16(L.xgT), L.Qs, st);
-  launch_transpose_rows(H16(L.h), I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, H16(L.hT), L.Qs, st);
-  launch_transpose_rows(H16(L.dab), 2 * I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, H16(L.dabT), L.Qs, st);
-  launch_transpose_rows(H16(L.dlogit), Ep, nullptr, nullptr, nullptr, nullptr, 1, static_cast<int>(N), L.Ns, H16(L.dlogitT), L.Ns, st);
-  launch_transpose_rows(static_cast<const uint16_t*>(x), D, nullptr, nullptr, nullptr, nullptr, 1, static_cast<int>(N), L.Ns, H16(L.xT), L.Ns, st);
+  const int n1 = static_cast<int>(N);
+  launch_transpose_rows(dy, D, token_of, F(L.w_perm), offsets, poff, E, 0, L.Qs, PV(L.doT), L.Qs, f32, st);
+  launch_transpose_rows(x, D, token_of, nullptr, offsets, poff, E, 0, L.Qs, PV(L.xgT), L.Qs, f32, st);
+  launch_transpose_rows(PV(L.h), I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, PV(L.hT), L.Qs, f32, st);
+  launch_transpose_rows(PV(L.dab), 2 * I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, PV(L.dabT), L.Qs, f32, st);
+  launch_transpose_rows(PV(L.dlogit), Ep, nullptr, nullptr, nullptr, nullptr, 1, n1, L.Ns, PV(L.dlogitT), L.Ns, f32, st);
+  launch_transpose_rows(x, D, nullptr, nullptr, nullptr, nullptr, 1, n1, L.Ns, PV(L.xT), L.Ns, f32, st);
   MOE_TRY(check_launch("moe_backward (transposes)"));
-  launch_wgrad(H16(L.doT), H16(L.hT), L.Qs, poff, 0, E, D, I, ddown, st);
-  launch_wgrad(H16(L.dabT), H16(L.xgT), L.Qs, poff, 0, E, 2 * I, D, dgate_up, st);
-  launch_wgrad_split(H16(L.dlogitT), H16(L.xT), L.Ns, L.Ns, E, D, kWgradSlices, I32(L.spoff), F(L.wr_part), dw_router, st);
+  // out[g] = A_g B_g^T over the padded rows: matrix cores for bf16, FMAs for fp32 layers; one long
+  // group (the sums over all tokens) split in slices on the bf16 path
+  auto wgrad = [&](size_t a_off, size_t b_off, int64_t ld, const int32_t* po, int G, int M, int Nn, float* out) {
+    if (f32)
+      launch_wgrad_f32(F(a_off), F(b_off), ld, po, po ? 0 : ld, G, M, Nn, out, st);
+    else if (po)
+      launch_wgrad(static_cast<const uint16_t*>(PV(a_off)), static_cast<const uint16_t*>(PV(b_off)), ld, po, 0, G, M, Nn, out, st);
+    else
+      launch_wgrad_split(static_cast<const uint16_t*>(PV(a_off)), static_cast<const uint16_t*>(PV(b_off)), ld, ld, M, Nn,
+                         kWgradSlices, I32(L.spoff), F(L.wr_part), out, st);
+  };
+  wgrad(L.doT, L.hT, L.Qs, poff, E, D, I, ddown);
+  wgrad(L.dabT, L.xgT, L.Qs, poff, E, 2 * I, D, dgate_up);
+  wgrad(L.dlogitT, L.xT, L.Ns, nullptr, 1, E, D, dw_router);
   if (shared) {
-    launch_transpose_rows(static_cast<const uint16_t*>(dy), D, nullptr, g, nullptr, nullptr, 1, static_cast<int>(N), L.Ns,
-                          H16(L.dysT), L.Ns, st);
-    launch_transpose_rows(H16(L.hs), Is, nullptr, nullptr, nullptr, nullptr, 1, static_cast<int>(N), L.Ns, H16(L.hsT), L.Ns, st);
-    launch_transpose_rows(H16(L.dabs), 2 * Is, nullptr, nullptr, nullptr, nullptr, 1, static_cast<int>(N), L.Ns, H16(L.dabsT),
-                          L.Ns, st);
-    launch_wgrad_split(H16(L.dysT), H16(L.hsT), L.Ns, L.Ns, D, Is, kWgradSlices, I32(L.spoff), F(L.wr_part), dshared_down, st);
-    launch_wgrad_split(H16(L.dabsT), H16(L.xT), L.Ns, L.Ns, 2 * Is, D, kWgradSlices, I32(L.spoff), F(L.wr_part),
-                       dshared_gate_up, st);
-    if (gated)
-      launch_wgrad_split(H16(L.dz_row), H16(L.xT), L.Ns, L.Ns, 1, D, kWgradSlices, I32(L.spoff), F(L.wr_part),
-                         dw_shared_gate, st);
+    launch_transpose_rows(dy, D, nullptr, g, nullptr, nullptr, 1, n1, L.Ns, PV(L.dysT), L.Ns, f32, st);
+    launch_transpose_rows(PV(L.hs), Is, nullptr, nullptr, nullptr, nullptr, 1, n1, L.Ns, PV(L.hsT), L.Ns, f32, st);
+    launch_transpose_rows(PV(L.dabs), 2 * Is, nullptr, nullptr, nullptr, nullptr, 1, n1, L.Ns, PV(L.dabsT), L.Ns, f32, st);
+    wgrad(L.dysT, L.hsT, L.Ns, nullptr, 1, D, Is, dshared_down);
+    wgrad(L.dabsT, L.xT, L.Ns, nullptr, 1, 2 * Is, D, dshared_gate_up);
+    if (gated) wgrad(L.dz_row, L.xT, L.Ns, nullptr, 1, 1, D, dw_shared_gate);
   }
   MOE_TRY(check_launch("moe_backward (weight gradients)"));
   return ok();

@@ -168,8 +168,8 @@ def test_backward_rules_and_workspace(lib):
     n = B.moe_backward_workspace_bytes(c)
     assert n > 64 * 2 * 2 * 128 * 4                               # at least the recomputed pre-activations
     assert B.moe_backward_workspace_bytes(c.copy(shared_inter=128)) > n
-    for bad, what in ((c.copy(dtype=B.MOE_F32, out_dtype=B.MOE_F32), "bf16"),
-                      (B.make_config(64, 256, 16, 2, 128, packed=True), "row-layout")):
+    assert B.moe_backward_workspace_bytes(c.copy(dtype=B.MOE_F32, out_dtype=B.MOE_F32)) > n   # fp32 intermediates
+    for bad, what in ((B.make_config(64, 256, 16, 2, 128, packed=True), "row-layout"),):
         with pytest.raises(B.MoeError) as ei:
             B.moe_backward_workspace_bytes(bad)
         assert ei.value.status == B.MOE_ERR_UNSUPPORTED and what in str(ei.value)
