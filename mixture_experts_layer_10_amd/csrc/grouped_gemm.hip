@@ -289,6 +289,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int B_DMA = QS == 8 ? 2 * B_INS : B_INS;       // weight DMA instructions per wave per stage
   constexpr int PER_STAGE = A_INS + B_DMA;
   static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
+  // bf16 weights enter the matrix cores as the row operand, so a lane's accumulators hold one token
+  // and runs of four consecutive output columns (stored as one 8- or 16-byte vector); quantised
+  // weights keep the activation rows there, so that a lane's outputs share one weight-row scale.
+  constexpr bool kSwap = kQ == 0;
   static_assert(A_INS * NW == A_GROUPS || A_INS == 1, "A rows must split into 16-row DMA groups");
   static_assert(B_INS * 16 * NW == BNB, "B rows must split into 16-row DMA groups");
   static_assert(!kSwiGLU || TN % 2 == 0, "SwiGLU pairs gate blocks with up blocks");
@@ -444,6 +448,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     }
   };
 
+  // DMA instruction n of issue() alone (n < PER_STAGE, in issue()'s order)
+  auto issue_one = [&](const Tile& T, int ks, uint16_t* sa, uint16_t* sb, int n) {
+    if (n < A_INS) {
+      dma16(T.srcA[n] + ks * kSK, sa + ((wave * A_INS + n) % A_GROUPS) * 512);
+    } else if constexpr (kQ != 0) {
+      const int b = n - A_INS, j = QS == 8 ? b / 2 : b, half = QS == 8 ? b % 2 : 0;
+      dma4(T.srcQ[j] + static_cast<int64_t>(ks) * QB + half * 256,
+           reinterpret_cast<char*>(sb) + (wave * B_INS + j) * QB + half * 256);
+    } else {
+      const int j = n - A_INS;
+      dma16(T.srcB[j] + (kPacked ? ks * 512 : ks * kSK), sb + (wave * B_INS + j) * 512);
+    }
+  };
+
   // wait for stage s (later stages may stay in flight), then sync the workgroup: after this, stage
   // s is visible to every wave and every wave has finished reading stage s - 1's buffer. Loads
   // retire in order, so "at most n outstanding" implies stage s has landed even with the previous
@@ -456,7 +474,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     lds_barrier();
   };
   f32x16 acc[TM][TN];
-  auto compute = [&](const uint16_t* sa, const uint16_t* sb, int live) {
+  // One stage's matrix-core steps; with dma, stage dks of the current tile goes to (dsa, dsb), one
+  // DMA instruction after each group of steps (issued together, the DMA instructions of all waves
+  // queue behind one another in the CU's load path and hold up every wave's steps).
+  auto compute = [&](const uint16_t* sa, const uint16_t* sb, int live, const Tile& T, bool dma, int dks, uint16_t* dsa,
+                     uint16_t* dsb) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 fa[TM], fb[TN];
@@ -476,12 +498,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
           fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
         if (i < live) {
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+          for (int j = 0; j < TN; ++j) acc[i][j] = kSwap ? mfma32(fb[j], fa[i], acc[i][j]) : mfma32(fa[i], fb[j], acc[i][j]);
         }
+        if (kk * TM + i < PER_STAGE && dma) issue_one(T, dks, dsa, dsb, kk * TM + i);
+      }
     }
+#pragma unroll
+    for (int n = 2 * TM; n < PER_STAGE; ++n)          // more instructions than groups (short tiles)
+      if (dma) issue_one(T, dks, dsa, dsb, n);
   };
 
   // Tiles are software-pipelined: the next tile's first three stages go out as soon as every wave
@@ -503,23 +530,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     for (int ks = 0; ks < ksteps; ks += 4) {
       const bool last = ks + 4 >= ksteps;
       wait_stage(ks);
-      if (ks + 3 < ksteps) issue(cur, ks + 3, sA3, sB3);
       if (last) nxt = make_tile(r + 1);
-      compute(sA0, sB0, cur.live);
+      compute(sA0, sB0, cur.live, cur, ks + 3 < ksteps, ks + 3, sA3, sB3);
       wait_stage(ks + 1);
-      if (ks + 4 < ksteps) issue(cur, ks + 4, sA0, sB0);
-      compute(sA1, sB1, cur.live);
+      compute(sA1, sB1, cur.live, cur, ks + 4 < ksteps, ks + 4, sA0, sB0);
       wait_stage(ks + 2);
-      if (ks + 5 < ksteps) issue(cur, ks + 5, sA1, sB1);
-      compute(sA2, sB2, cur.live);
+      compute(sA2, sB2, cur.live, cur, ks + 5 < ksteps, ks + 5, sA1, sB1);
       wait_stage(ks + 3);                 // the last stage: everything this wave issued has landed
-      if (ks + 6 < ksteps) issue(cur, ks + 6, sA2, sB2);
       if (last && nxt.valid) {
         issue(nxt, 0, sA0, sB0);
         issue(nxt, 1, sA1, sB1);
         issue(nxt, 2, sA2, sB2);
       }
-      compute(sA3, sB3, cur.live);
+      compute(sA3, sB3, cur.live, cur, ks + 6 < ksteps, ks + 6, sA2, sB2);
     }
     // Epilogue. The next tile writes buffer 3 only after its first barrier, which every wave
     // reaches after finishing these reads of buffer 3.
@@ -531,7 +554,53 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] *= cur.sc[j];
     }
-    if constexpr (kSwiGLU) {
+    if constexpr (kSwap) {
+      // block (i, j): token m0 + (wm TM + i) 32 + lane % 32; element e is output column
+      // 8 (e / 4) + 4 (lane / 32) + e % 4 of the block
+      const bool vec = NOUT % 4 == 0;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int rr = m0 + (wm * TM + i) * 32 + (lane & 31);
+        if (rr >= rows) continue;
+        if constexpr (kSwiGLU) {
+          uint16_t* Hrow = static_cast<uint16_t*>(a.out) + (row0 + rr) * NOUT;
+          constexpr int H = TN / 2;
+#pragma unroll
+          for (int j = 0; j < H; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int col = c0 + (wn * H + j) * 32 + 8 * q + 4 * (lane >> 5);
+              uint16_t v[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) v[t] = f32_to_bf16(silu(acc[i][j][4 * q + t]) * acc[i][j + H][4 * q + t]);
+              if (vec && col + 3 < NOUT) {
+                *reinterpret_cast<u32x2*>(Hrow + col) = u32x2{v[0] | (static_cast<uint32_t>(v[1]) << 16),
+                                                              v[2] | (static_cast<uint32_t>(v[3]) << 16)};
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  if (col + t < NOUT) Hrow[col + t] = v[t];
+              }
+            }
+        } else {
+          float* Orow = static_cast<float*>(a.out) + (row0 + rr) * NOUT;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int col = c0 + (wn * TN + j) * 32 + 8 * q + 4 * (lane >> 5);
+              const f32x16& c = acc[i][j];
+              if (vec && col + 3 < NOUT) {
+                *reinterpret_cast<f32x4*>(Orow + col) = f32x4{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  if (col + t < NOUT) Orow[col + t] = c[4 * q + t];
+              }
+            }
+        }
+      }
+    } else if constexpr (kSwiGLU) {
       uint16_t* Hh = static_cast<uint16_t*>(a.out);
       constexpr int H = TN / 2;
 #pragma unroll
