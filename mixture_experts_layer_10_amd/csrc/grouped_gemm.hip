@@ -17,6 +17,7 @@
 // share their A rows and their expert's weights. Workgroup w runs on XCD w % 8; the list is cut into
 // runs of (grid / 8) consecutive tiles per XCD, so tiles that share data share an L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -276,6 +277,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------------------------
 constexpr int kSK = 32;
 
+// f(integral_constant<L>) for L = min(live, LMAX): one compiled copy of a loop per live-block count.
+template <int LMAX, typename F>
+__device__ __forceinline__ void dispatch_live(int live, F&& f) {
+  if constexpr (LMAX == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (live >= LMAX) f(std::integral_constant<int, LMAX>{});
+    else dispatch_live<LMAX - 1>(live, f);
+  }
+}
+
 template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32, NT = WM * WN * 64, NW = WM * WN;
@@ -293,6 +305,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   // and runs of four consecutive output columns (stored as one 8- or 16-byte vector); quantised
   // weights keep the activation rows there, so that a lane's outputs share one weight-row scale.
   constexpr bool kSwap = kQ == 0;
+  constexpr bool kEarlyReads = true;
   static_assert(A_INS * NW == A_GROUPS || A_INS == 1, "A rows must split into 16-row DMA groups");
   static_assert(B_INS * 16 * NW == BNB, "B rows must split into 16-row DMA groups");
   static_assert(!kSwiGLU || TN % 2 == 0, "SwiGLU pairs gate blocks with up blocks");
@@ -462,53 +475,104 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     }
   };
 
-  // wait for stage s (later stages may stay in flight), then sync the workgroup: after this, stage
-  // s is visible to every wave and every wave has finished reading stage s - 1's buffer. Loads
-  // retire in order, so "at most n outstanding" implies stage s has landed even with the previous
-  // tile's epilogue stores still counted.
-  auto wait_stage = [&](int s) {
-    const int ahead = min(2, ksteps - 1 - s);
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(W2);
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(W1);
-    else __builtin_amdgcn_s_waitcnt(W0);
+  // wait for the oldest stage in flight while n later stages may stay in flight, then sync the
+  // workgroup: after this the stage is visible to every wave and every wave has finished reading the
+  // previous stage's buffer. Loads retire in order, so "at most n stages outstanding" implies the
+  // stage has landed even with the previous tile's epilogue stores still counted. Inside a tile's
+  // k-loop n = 2; its last group of four stages waits with 2, 2, 1, 0.
+  // The wait includes lgkmcnt(0): the compiler may place matrix-core steps after the barrier, and the
+  // fragment reads feeding them must not still be pending once other waves may refill the buffer.
+  auto wait_stage = [&](auto Nc) __attribute__((always_inline)) {
+    constexpr int n = decltype(Nc)::value;
+    __builtin_amdgcn_s_waitcnt((n == 2 ? W2 : n == 1 ? W1 : W0) & ~(0xF << 8));
     lds_barrier();
   };
   f32x16 acc[TM][TN];
-  // One stage's matrix-core steps; with dma, stage dks of the current tile goes to (dsa, dsb), one
-  // DMA instruction after each group of steps (issued together, the DMA instructions of all waves
-  // queue behind one another in the CU's load path and hold up every wave's steps).
-  auto compute = [&](const uint16_t* sa, const uint16_t* sb, int live, const Tile& T, bool dma, int dks, uint16_t* dsa,
-                     uint16_t* dsb) {
+  // One stage's matrix-core steps for the first L 32-row blocks of this wave; with kDma, stage dks
+  // of tile T goes to (dsa, dsb), one DMA instruction after each group of steps (issued together,
+  // the DMA instructions of all waves queue behind one another in the CU's load path and hold up
+  // every wave's steps). L and kDma are compile-time, so no branch sits between the steps.
+  auto compute = [&](auto Lc, auto Dc, const uint16_t* sa, const uint16_t* sb, const Tile& T, int dks, uint16_t* dsa,
+                     uint16_t* dsb) __attribute__((always_inline)) {
+    constexpr int L = decltype(Lc)::value;
+    constexpr bool kDma = decltype(Dc)::value;
+    // both k-steps' fragments are read first (the reads of the second overlap the first's steps)
+    u32x4 fa[2][TM], fb[2][TN];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      u32x4 fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&sa[koA[kk] + i * 32 * kSK]);
+      for (int i = 0; i < L; ++i) fa[kk][i] = *reinterpret_cast<const u32x4*>(&sa[koA[kk] + i * 32 * kSK]);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         constexpr int H = TN / 2;
         const int rowoff = kSwiGLU ? (j < H ? j * 32 : BNB / 2 + (j - H) * 32) : j * 32;
         if constexpr (kQ == kQInt8)
-          fb[j] = codes8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
+          fb[kk][j] = codes8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
         else if constexpr (kQ == kQFp8)
-          fb[j] = codesf8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
+          fb[kk][j] = codesf8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
         else if constexpr (kQ == kQInt4)
-          fb[j] = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
+          fb[kk][j] = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
         else
-          fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
+          fb[kk][j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
       }
+    }
+    if constexpr (kEarlyReads) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        if (i < live) {
+        if (i < L) {
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = kSwap ? mfma32(fb[j], fa[i], acc[i][j]) : mfma32(fa[i], fb[j], acc[i][j]);
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = kSwap ? mfma32(fb[kk][j], fa[kk][i], acc[i][j]) : mfma32(fa[kk][i], fb[kk][j], acc[i][j]);
         }
-        if (kk * TM + i < PER_STAGE && dma) issue_one(T, dks, dsa, dsb, kk * TM + i);
+        if (kDma && kk * TM + i < PER_STAGE) issue_one(T, dks, dsa, dsb, kk * TM + i);
       }
     }
 #pragma unroll
     for (int n = 2 * TM; n < PER_STAGE; ++n)          // more instructions than groups (short tiles)
-      if (dma) issue_one(T, dks, dsa, dsb, n);
+      if (kDma) issue_one(T, dks, dsa, dsb, n);
+  };
+  constexpr std::integral_constant<int, 0> n0{};
+  constexpr std::integral_constant<int, 1> n1{};
+  constexpr std::integral_constant<int, 2> n2{};
+  constexpr std::true_type dma{};
+  constexpr std::false_type no_dma{};
+
+  // One tile's k-loop for L live 32-row blocks of this wave (a copy per L, chosen once per tile).
+  // Every copy clears all accumulators, the skipped blocks too, so that each defines them all and
+  // the register allocator keeps them in place across the copies.
+  auto kloop = [&](auto Lc, const Tile& cur, Tile& nxt, int r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    int ks = 0;
+    for (; ks + 4 < ksteps; ks += 4) {
+      wait_stage(n2);
+      compute(Lc, dma, sA0, sB0, cur, ks + 3, sA3, sB3);
+      wait_stage(n2);
+      compute(Lc, dma, sA1, sB1, cur, ks + 4, sA0, sB0);
+      wait_stage(n2);
+      compute(Lc, dma, sA2, sB2, cur, ks + 5, sA1, sB1);
+      wait_stage(n2);
+      compute(Lc, dma, sA3, sB3, cur, ks + 6, sA2, sB2);
+    }
+    // the last four stages: only the first still issues one of this tile's stages
+    wait_stage(n2);
+    nxt = make_tile(r + 1);
+    compute(Lc, dma, sA0, sB0, cur, ks + 3, sA3, sB3);
+    wait_stage(n2);
+    compute(Lc, no_dma, sA1, sB1, cur, 0, sA0, sB0);
+    wait_stage(n1);
+    compute(Lc, no_dma, sA2, sB2, cur, 0, sA1, sB1);
+    wait_stage(n0);                       // everything this wave issued has landed
+    if (nxt.valid) {
+      issue(nxt, 0, sA0, sB0);
+      issue(nxt, 1, sA1, sB1);
+      issue(nxt, 2, sA2, sB2);
+    }
+    compute(Lc, no_dma, sA3, sB3, cur, 0, sA2, sB2);
   };
 
   // Tiles are software-pipelined: the next tile's first three stages go out as soon as every wave
@@ -521,29 +585,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     issue(cur, 2, sA2, sB2);
   }
   for (int r = 0; cur.valid; ++r) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
     Tile nxt;
     nxt.valid = false;
-    for (int ks = 0; ks < ksteps; ks += 4) {
-      const bool last = ks + 4 >= ksteps;
-      wait_stage(ks);
-      if (last) nxt = make_tile(r + 1);
-      compute(sA0, sB0, cur.live, cur, ks + 3 < ksteps, ks + 3, sA3, sB3);
-      wait_stage(ks + 1);
-      compute(sA1, sB1, cur.live, cur, ks + 4 < ksteps, ks + 4, sA0, sB0);
-      wait_stage(ks + 2);
-      compute(sA2, sB2, cur.live, cur, ks + 5 < ksteps, ks + 5, sA1, sB1);
-      wait_stage(ks + 3);                 // the last stage: everything this wave issued has landed
-      if (last && nxt.valid) {
-        issue(nxt, 0, sA0, sB0);
-        issue(nxt, 1, sA1, sB1);
-        issue(nxt, 2, sA2, sB2);
-      }
-      compute(sA3, sB3, cur.live, cur, ks + 6 < ksteps, ks + 6, sA2, sB2);
-    }
+    dispatch_live<TM>(cur.live, [&](auto Lc) __attribute__((always_inline)) { kloop(Lc, cur, nxt, r); });
     // Epilogue. The next tile writes buffer 3 only after its first barrier, which every wave
     // reaches after finishing these reads of buffer 3.
     const int64_t row0 = cur.row0, rows = cur.rows;
