@@ -27,17 +27,11 @@ namespace moe {
 // ---------------------------------------------------------------------------------------------
 // Tile list shared by both kernels.
 // ---------------------------------------------------------------------------------------------
-template <int NT>
-__device__ void build_tile_prefix(const int32_t* offsets, int G, int64_t max_rows, int BM, int n_tiles,
-                                  int* s_pref, int* s_tmp) {
-  // s_pref[g] = sum_{g' < g} ceil(rows_g' / BM) * n_tiles, for g = 0..G. G <= 2 * NT.
+// s_pref[g] = sum_{g' < g} tiles_of(g'), for g = 0..G (G <= 2 * NT); ends with a barrier.
+template <int NT, typename F>
+__device__ void tile_prefix_scan(F tiles_of, int G, int* s_pref, int* s_tmp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto tiles_of = [&](int g) -> int {
-    if (g >= G) return 0;
-    const int64_t rows = offsets ? static_cast<int64_t>(offsets[g + 1] - offsets[g]) : max_rows;
-    return static_cast<int>((rows + BM - 1) / BM) * n_tiles;
-  };
-  const int v0 = tiles_of(2 * tid), v1 = tiles_of(2 * tid + 1);
+  const int v0 = 2 * tid < G ? tiles_of(2 * tid) : 0, v1 = 2 * tid + 1 < G ? tiles_of(2 * tid + 1) : 0;
   const int own = v0 + v1;
   int inc = own;
 #pragma unroll
@@ -56,6 +50,85 @@ __device__ void build_tile_prefix(const int32_t* offsets, int G, int64_t max_row
   // (written separately because G may equal 2 * NT, one past the last slot the loop covers)
   if (tid == NT - 1) s_pref[G] = before + inc;
   __syncthreads();
+}
+
+// s_pref[g] = sum_{g' < g} ceil(rows_g' / BM) * n_tiles, for g = 0..G. G <= 2 * NT.
+template <int NT>
+__device__ void build_tile_prefix(const int32_t* offsets, int G, int64_t max_rows, int BM, int n_tiles,
+                                  int* s_pref, int* s_tmp) {
+  tile_prefix_scan<NT>(
+      [&](int g) {
+        const int64_t rows = offsets ? static_cast<int64_t>(offsets[g + 1] - offsets[g]) : max_rows;
+        return static_cast<int>((rows + BM - 1) / BM) * n_tiles;
+      },
+      G, s_pref, s_tmp);
+}
+
+// Tile list of the streaming kernel, the most work first. A tile costs about the number of its
+// 32-row blocks that hold rows (those without rows skip their matrix-core steps). The list holds
+// first every tile whose BM / 32 blocks all hold rows (group order, m-tile, n-tile fastest), then
+// each group's last m-tile where it is shorter, ordered by its number of row blocks, most first
+// (equal counts in group order), n-tile fastest. Dealt out round by round, the list leaves the
+// cheap tiles for the last rounds, which then end together instead of on whichever full tiles
+// fall last in group order.
+// s_pref[g] = sum_{g' < g} (full m-tiles of g') * n_tiles, s_pref[G] = their total;
+// s_plist[i] = the group of short m-tile i in list order. Returns the number of short m-tiles.
+// G <= 2 * NT; s_cnt holds 2 * NT / 64 * 8 ints. Ends with a barrier.
+template <int NT, int BM>
+__device__ int build_tile_lists(const int32_t* offsets, int G, int64_t max_rows, int n_tiles, int* s_pref,
+                                int* s_plist, int* s_tmp, int* s_cnt) {
+  constexpr int NW = NT / 64, LB = BM / 32;
+  static_assert(LB <= 8, "eight block counts per slot");
+  auto rows_of = [&](int g) -> int64_t {
+    return offsets ? static_cast<int64_t>(offsets[g + 1] - offsets[g]) : max_rows;
+  };
+  tile_prefix_scan<NT>(
+      [&](int g) {
+        const int64_t c = rows_of(g), rem = c % BM;
+        return static_cast<int>(c / BM + (rem > BM - 32 ? 1 : 0)) * n_tiles;
+      },
+      G, s_pref, s_tmp);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // groups g = tid + k NT; slot k NW + wave holds groups 64 (k NW + wave) .. + 63 (group order)
+  int cls[2];
+  uint64_t same[2] = {0, 0};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int g = tid + k * NT;
+    cls[k] = 0;
+    if (g < G) {
+      const int64_t rem = rows_of(g) % BM;
+      if (rem > 0 && rem <= BM - 32) cls[k] = static_cast<int>((rem + 31) / 32);
+    }
+#pragma unroll
+    for (int L = 1; L < LB; ++L) {
+      const uint64_t m = __ballot(cls[k] == L);
+      if (cls[k] == L) same[k] = m;
+      if (lane == 0) s_cnt[(k * NW + wave) * 8 + L] = __popcll(m);
+    }
+  }
+  __syncthreads();
+  int total[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int slot = 0; slot < 2 * NW; ++slot)
+#pragma unroll
+    for (int L = 1; L < LB; ++L) total[L] += s_cnt[slot * 8 + L];
+  int n_short = 0;
+#pragma unroll
+  for (int L = 1; L < LB; ++L) n_short += total[L];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = cls[k];
+    if (c == 0) continue;
+    int rank = 0;
+#pragma unroll
+    for (int L = 1; L < LB; ++L)
+      if (L > c) rank += total[L];
+    for (int slot = 0; slot < k * NW + wave; ++slot) rank += s_cnt[slot * 8 + c];
+    rank += __popcll(same[k] & ((1ull << lane) - 1));
+    s_plist[rank] = tid + k * NT;
+  }
+  __syncthreads();
+  return n_short;
 }
 
 __device__ __forceinline__ int find_group(const int* s_pref, int G, int t) {
@@ -321,6 +394,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   __shared__ int s_pref[1025];
   __shared__ int s_off[1025];           // group row offsets (no global round trip per tile)
   __shared__ int s_tmp[16];
+  __shared__ int s_plist[1024];         // groups of the short m-tiles, in list order
+  __shared__ int s_cnt[2 * NW * 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -331,8 +406,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   const int n_tiles = (NOUT + OUT_COLS - 1) / OUT_COLS;
   for (int g = tid; g <= G; g += NT)
     s_off[g] = a.offsets ? a.offsets[g] : (g == 0 ? 0 : static_cast<int>(a.max_rows));
-  build_tile_prefix<NT>(a.offsets, G, a.max_rows, BM, n_tiles, s_pref, s_tmp);   // ends with a barrier
-  const int total = s_pref[G];
+  const int n_short = build_tile_lists<NT, BM>(a.offsets, G, a.max_rows, n_tiles, s_pref, s_plist, s_tmp, s_cnt);
+  const int total_full = s_pref[G];
+  const int total = total_full + n_short * n_tiles;
   const int P = gridDim.x;
   const uint16_t* X = static_cast<const uint16_t*>(a.x);
   const uint16_t* W = static_cast<const uint16_t*>(a.w);
@@ -373,14 +449,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   };
   auto make_tile = [&](int r) {
     Tile T;
-    const int t = tile_of_round(r, blockIdx.x, P);
+    // round r deals tiles r P .. r P + P - 1, in alternate directions in alternate rounds (a
+    // workgroup that drew a more expensive tile in one round draws a cheaper one in the next)
+    const int t = tile_of_round(r, (r & 1) ? P - 1 - static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x), P);
     T.valid = r * P < total && t < total;             // t grows with r: past the list, nothing follows
     if (!T.valid) return T;
-    const int g = find_group(s_pref, G, t);
-    const int local = t - s_pref[g];
+    int g, mt, nt;
+    if (t < total_full) {
+      g = find_group(s_pref, G, t);
+      const int local = t - s_pref[g];
+      mt = local / n_tiles;
+      nt = local - mt * n_tiles;
+    } else {
+      const int u = t - total_full, i = u / n_tiles;
+      g = min(max(s_plist[i], 0), G - 1);             // (a permutation of the short groups; kept in range)
+      nt = u - i * n_tiles;
+      mt = (s_off[g + 1] - s_off[g]) / BM;            // the group's last, short m-tile
+    }
     T.row0 = s_off[g];
     T.rows = static_cast<int64_t>(s_off[g + 1]) - T.row0;   // > 0: empty groups own no tiles
-    const int mt = local / n_tiles, nt = local - mt * n_tiles;
     T.m0 = mt * BM;
     T.c0 = nt * OUT_COLS;
     // 32-row blocks of this wave that hold real rows (uniform across the wave)
