@@ -15,7 +15,8 @@
 // ceil(rows_g / BM) * n_tiles from the device-side offsets (no host round trip), then walks the
 // tile list. Tile t -> (group by binary search, m-tile, n-tile), n fastest, so neighbouring tiles
 // share their A rows and their expert's weights. Workgroup w runs on XCD w % 8; the list is cut into
-// runs of (grid / 8) consecutive tiles per XCD, so tiles that share data share an L2.
+// runs of (grid / 8) consecutive tiles per XCD, so tiles that share data share an L2. The streaming
+// kernel orders its list longest first (build_tile_lists) and deals it in alternate directions.
 #include <algorithm>
 #include <type_traits>
 
@@ -343,8 +344,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
 // 16 consecutive rows at one chunk cover a 256-byte window's 16 slots. One DMA instruction writes
 // 64 lanes x 16 bytes = 16 rows contiguously, so the swizzle is applied to the global side: lane l
 // fetches chunk (l & 3) ^ (((l >> 2) >> 2) & 3) of row l >> 2.
-// 32-row blocks of a tile that lie past the group's last row skip their matrix-core steps.
-// Quantised weights (kQ = 8 or 4): each stage's weight blocks (64 kQ bytes of codes per 16 x 32)
+// 32-row blocks of a tile that lie past the group's last row skip their matrix-core steps: the
+// k-loop is compiled once per number of such blocks a wave has live (chosen once per tile), with
+// the DMA and wait depths fixed per position, so no branch sits between two barriers.
+// Quantised weights (kQ = 8, 4 or FP8): each stage's weight blocks (64 kQ bytes of codes per 16 x 32)
 // move with 4-byte-per-lane DMA; fragments are converted to bf16 exactly as they are read, and each
 // output column is multiplied by its weight row's scale in the epilogue.
 // ---------------------------------------------------------------------------------------------
