@@ -529,4 +529,113 @@ void launch_wgrad_split(const uint16_t* A, const uint16_t* Bm, int64_t ld, int64
   sum_slices_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(part, S, n, out);
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Grouped product with the weights read in their stored [K][N] layout, for short groups (the
+// backward's dh = dy Dn and dx rows = [da | db] GU when each expert holds a few rows):
+//   out[p][n] = sum_k X[row(p)][k] W[g][k][n]   for the rows p of group g, out fp32,
+// row(p) = row_index[p] when given. A wave owns 128 columns (two per lane) of one group and walks
+// k: one 4-byte weight load per lane and k (a 256-byte run of the weight row), in chunks of 16 k
+// with the next chunk's loads in flight during this chunk's products. The group's rows sit in LDS
+// in their own layout, so consecutive k pair up in one dword; a byte permute pairs the weights of
+// one column for the same two k, and one bf16 dot-product instruction (two products added to an
+// fp32 sum) covers them. The loop is compiled once per row count (1..8); a group of more than eight
+// rows takes several passes over its weights. No transposed weight copy is needed. K % 32 == 0,
+// K <= kKsMaxK.
+// ---------------------------------------------------------------------------------------------
+constexpr int kKsRows = 8, kKsUnroll = 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int R>
+__device__ __forceinline__ void kstream_pass(const uint16_t* __restrict__ sX, const uint32_t* __restrict__ wg, bool col_ok,
+                                             int K, int NW, float* __restrict__ orow0, int N, int c) {
+  float acc[R][2];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
+  auto load = [&](uint32_t* wv, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kKsUnroll; ++u) wv[u] = __builtin_nontemporal_load(wg + static_cast<int64_t>(k0 + u) * NW);
+  };
+  auto math = [&](const uint32_t* wv, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kKsUnroll / 8; ++q) {              // eight k at a time
+      u32x4 xv[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) xv[r] = *reinterpret_cast<const u32x4*>(&sX[r * K + k0 + 8 * q]);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {                         // k pair (k0 + 8 q + 2 h, + 1)
+        const uint32_t a = wv[8 * q + 2 * h], b = wv[8 * q + 2 * h + 1];
+        const uint32_t wc0 = __builtin_amdgcn_perm(b, a, 0x05040100u);   // column c: (W[k][c], W[k+1][c])
+        const uint32_t wc1 = __builtin_amdgcn_perm(b, a, 0x07060302u);   // column c + 1
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          acc[r][0] = dot2_bf16(xv[r][h], wc0, acc[r][0]);
+          acc[r][1] = dot2_bf16(xv[r][h], wc1, acc[r][1]);
+        }
+      }
+    }
+  };
+  // two chunks of weight rows in registers: the next chunk's loads go out before this chunk's
+  // products (past the end they re-read the last chunk, in bounds and unused)
+  uint32_t wa[kKsUnroll], wb[kKsUnroll];
+  load(wa, 0);
+  for (int k0 = 0; k0 < K; k0 += 2 * kKsUnroll) {
+    load(wb, min(k0 + kKsUnroll, K - kKsUnroll));
+    math(wa, k0);
+    load(wa, min(k0 + 2 * kKsUnroll, K - kKsUnroll));
+    math(wb, k0 + kKsUnroll);
+  }
+  if (col_ok) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) *reinterpret_cast<float2*>(orow0 + static_cast<int64_t>(r) * N + c) = make_float2(acc[r][0], acc[r][1]);
+  }
+}
+
+__global__ __launch_bounds__(256) void gemm_kstream_kernel(const uint16_t* __restrict__ X, const int32_t* __restrict__ row_index,
+                                                           const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
+                                                           int K, int N, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kKsMaxK * kKsRows];
+  const int g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = offsets[g];
+  const int rows = offsets[g + 1] - static_cast<int>(r0);
+  const int c = (blockIdx.x * 4 + wave) * 128 + 2 * lane;       // this lane's columns c, c + 1
+  const bool col_ok = c < N;                                     // N is even
+  // lanes past N read column 0 (in bounds) and store nothing
+  const uint32_t* wg = reinterpret_cast<const uint32_t*>(W + static_cast<int64_t>(g) * K * N + (col_ok ? c : 0));
+  const int NW = N / 2;                                          // weight row stride in 4-byte units
+  for (int pass = 0; pass < rows; pass += kKsRows) {
+    const int R = min(kKsRows, rows - pass);
+    for (int idx = tid; idx < R * (K / 8); idx += 256) {         // rows pass .. pass + R - 1, 16 bytes at a time
+      const int r = idx / (K / 8), k8 = idx - r * (K / 8);
+      const int64_t p = r0 + pass + r;
+      const int64_t src = row_index ? row_index[p] : p;
+      *reinterpret_cast<u32x4*>(&sX[r * K + k8 * 8]) = *reinterpret_cast<const u32x4*>(X + src * K + k8 * 8);
+    }
+    __syncthreads();
+    float* orow0 = out + (r0 + pass) * N;
+    switch (R) {
+      case 1: kstream_pass<1>(sX, wg, col_ok, K, NW, orow0, N, c); break;
+      case 2: kstream_pass<2>(sX, wg, col_ok, K, NW, orow0, N, c); break;
+      case 3: kstream_pass<3>(sX, wg, col_ok, K, NW, orow0, N, c); break;
+      case 4: kstream_pass<4>(sX, wg, col_ok, K, NW, orow0, N, c); break;
+      case 5: kstream_pass<5>(sX, wg, col_ok, K, NW, orow0, N, c); break;
+      case 6: kstream_pass<6>(sX, wg, col_ok, K, NW, orow0, N, c); break;
+      case 7: kstream_pass<7>(sX, wg, col_ok, K, NW, orow0, N, c); break;
+      default: kstream_pass<8>(sX, wg, col_ok, K, NW, orow0, N, c); break;
+    }
+    __syncthreads();                                             // before the next pass restages
+  }
+}
+
+void launch_kstream(const uint16_t* X, const int32_t* row_index, const int32_t* offsets, int G, const uint16_t* W, int K,
+                    int N, float* out, hipStream_t st) {
+  if (G <= 0 || K <= 0 || N <= 0) return;
+  dim3 grid((N + 511) / 512, static_cast<unsigned>(G));
+  gemm_kstream_kernel<<<grid, 256, 0, st>>>(X, row_index, offsets, W, K, N, out);
+}
+
 }  // namespace moe

@@ -124,6 +124,12 @@ constexpr int kWgradSlices = 16;     // split of a single long reduction (poff: 
 void launch_wgrad_split(const uint16_t* A, const uint16_t* Bm, int64_t ld, int64_t qtot, int M, int Nn, int S,
                         int32_t* poff, float* part, float* out, hipStream_t st);
 
+// Grouped product over short groups with W[g] stored [K][N] (no transposed copy): out[p][n] =
+// sum_k X[row(p)][k] W[g][k][n] (bf16 in, fp32 out). K <= kKsMaxK, K % 32 == 0, N even.
+constexpr int kKsMaxK = 2048;
+void launch_kstream(const uint16_t* X, const int32_t* row_index, const int32_t* offsets, int G, const uint16_t* W, int K,
+                    int N, float* out, hipStream_t st);
+
 int device_cu_count();
 
 }  // namespace moe

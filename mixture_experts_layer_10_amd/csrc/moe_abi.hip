@@ -591,19 +591,31 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
                        I32(L.block_counts), st));
   launch_scatter_assign(I32(L.slot_pos), F(L.weights), F(L.w_perm), I32(L.assign_of), F(L.ones), A, st);
   launch_pad_offsets(I32(L.counts), I32(L.poff), E, st);
-  launch_transpose_mat(down, PV(L.dnT), E, D, I, D, f32, st);                   // [E, I, D]
-  launch_transpose_mat(gate_up, PV(L.guT), E, 2 * I, D, 2 * I, f32, st);          // [E, D, 2I]
+  // Short groups (a few rows per expert) read the weights in their stored layout (launch_kstream);
+  // otherwise the [out, in] grouped GEMMs run on transposed copies.
+  const bool short_groups = bf && A <= 64LL * E;
+  const bool ks_dh = short_groups && D % 32 == 0 && D <= kKsMaxK;
+  const bool ks_dx = short_groups && (2 * I) % 32 == 0 && 2 * I <= kKsMaxK;
+  if (!ks_dh) launch_transpose_mat(down, PV(L.dnT), E, D, I, D, f32, st);                 // [E, I, D]
+  if (!ks_dx) launch_transpose_mat(gate_up, PV(L.guT), E, 2 * I, D, 2 * I, f32, st);        // [E, D, 2I]
   launch_transpose_mat(w_router, PV(L.wrT), 1, E, D, Ep, f32, st);               // [D, Ep]
   MOE_TRY(check_launch("moe_backward (setup)"));
   launch_down(nt_args(x, token_of, offsets, E, A, gate_up, 2 * I, D, F(L.z), bf), st);
-  launch_down(nt_args(dy, token_of, offsets, E, A, PV(L.dnT), I, D, F(L.dhu), bf), st);
+  if (ks_dh)
+    launch_kstream(static_cast<const uint16_t*>(dy), token_of, offsets, E, static_cast<const uint16_t*>(down), D, I, F(L.dhu), st);
+  else
+    launch_down(nt_args(dy, token_of, offsets, E, A, PV(L.dnT), I, D, F(L.dhu), bf), st);
   MOE_TRY(check_launch("moe_backward (recompute)"));
   // expert and router gradients of the activations
   launch_swiglu_bwd(F(L.z), F(L.dhu), F(L.w_perm), I32(L.assign_of), offsets + E, A, I, PV(L.h), PV(L.dab), F(L.dw), f32,
                     st);
   launch_router_bwd(F(L.logits), F(L.weights), I32(L.experts), F(L.dw), N, E, Ep, static_cast<int>(cfg->top_k),
                     cfg->norm_topk_prob, PV(L.dlogit), f32, st);
-  launch_down(nt_args(PV(L.dab), nullptr, offsets, E, A, PV(L.guT), D, 2 * I, F(L.dx_rows), bf), st);
+  if (ks_dx)
+    launch_kstream(static_cast<const uint16_t*>(PV(L.dab)), nullptr, offsets, E, static_cast<const uint16_t*>(gate_up), 2 * I,
+                   D, F(L.dx_rows), st);
+  else
+    launch_down(nt_args(PV(L.dab), nullptr, offsets, E, A, PV(L.guT), D, 2 * I, F(L.dx_rows), bf), st);
   launch_down(nt_args(PV(L.dlogit), nullptr, nullptr, 1, N, PV(L.wrT), D, Ep, F(L.dxr), bf), st);
   const int Is = static_cast<int>(cfg->shared_inter);
   if (shared) {
