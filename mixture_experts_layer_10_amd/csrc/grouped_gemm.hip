@@ -364,7 +364,7 @@ __device__ __forceinline__ void dispatch_live(int live, F&& f) {
   }
 }
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32, NT = WM * WN * 64, NW = WM * WN;
   // DMA instructions per wave per stage; with fewer 16-row A groups than waves (BM = 32), waves
@@ -377,6 +377,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int B_DMA = QS == 8 ? 2 * B_INS : B_INS;       // weight DMA instructions per wave per stage
   constexpr int PER_STAGE = A_INS + B_DMA;
   static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
+  static_assert(!kWKN || (!kSwiGLU && !kPacked && kQ == 0 && BNB == 256), "[K][N] weights: bf16 down form, 256 columns");
   // bf16 weights enter the matrix cores as the row operand, so a lane's accumulators hold one token
   // and runs of four consecutive output columns (stored as one 8- or 16-byte vector); quantised
   // weights keep the activation rows there, so that a lane's outputs share one weight-row scale.
@@ -437,6 +438,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
                         : (rb0 + (lane & 31)) * kSK + pc;
   }
   const int R = kSwiGLU ? 2 * a.I : a.D;              // weight rows per group
+  // [K][NOUT] weights: a stage holds 32 k-rows of the tile's 256 columns (512 bytes per row, 32-byte
+  // chunks swizzled by (2 row) & 7). The operand for columns n0 .. n0 + 31 comes from two transpose
+  // loads (ds_read_b64_tr_b16): in each 16-lane group G, lane 16 G + 4 a + b receives element b of
+  // the 8-byte pieces addressed by lanes 16 G + a + 4 t, t = 0..3. Address lane 16 G + r therefore
+  // points at k-row 8 (G / 2) + r / 4 (+ 4 in the second load), columns 16 (G % 2) + 4 (r % 4) .. + 3,
+  // and lane l ends up with column l % 32 at k 8 (l / 32) .. + 7, the layout of the plain read. A
+  // half-wave touches four rows by two chunks, which the swizzle spreads over all 64 banks.
+  auto read_wkn = [&](const uint16_t* sb, int kk, int n0) __attribute__((always_inline)) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int gq = lane >> 4, rq = lane & 15;
+    const int krow = kk * 16 + 8 * (gq >> 1) + (rq >> 2);
+    const int ncol = n0 + 16 * (gq & 1) + 4 * (rq & 3);
+    u32x2 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kr = krow + 4 * h;
+      const int idx = kr * 256 + (((ncol >> 4) ^ ((2 * kr) & 7)) << 4) + (ncol & 15);
+      const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(sb) + idx));
+      v[h] = __builtin_bit_cast(u32x2, t);
+    }
+    return u32x4{v[0][0], v[0][1], v[1][0], v[1][1]};
+  };
   constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
 
   // One tile's fixed data. make_tile reads the group table in LDS and, for gathered rows, the row
@@ -519,6 +543,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
                       static_cast<int64_t>(rb) * (K / kSK) * QB + lane * 4;
         else
           T.srcB[j] = Wg + static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8;
+      } else if constexpr (kWKN) {
+        // weights [K][NOUT]: DMA group grp carries k-rows 2 grp and 2 grp + 1 of the stage (512 bytes
+        // each); lane l fetches 16 bytes of row 2 grp + l / 32 into physical 32-byte chunk (l % 32) / 2,
+        // which holds logical chunk ((l % 32) / 2) ^ ((2 row) & 7) (the transpose-read swizzle);
+        // columns past NOUT read a valid chunk, and their outputs are never stored
+        const int row = 2 * grp + (lane >> 5);
+        const int chunk = ((lane & 31) >> 1) ^ ((2 * row) & 7);
+        const int n = min(T.c0 + chunk * 16 + (lane & 1) * 8, NOUT - 8);
+        T.srcB[j] = Wg + static_cast<int64_t>(row) * NOUT + n;
       } else {
         const int rr = grp * 16 + lrow;
         int wrow;
@@ -546,7 +579,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         dma4(src, dst);
         if constexpr (QS == 8) dma4(src + 256, dst + 256);
       } else {
-        dma16(T.srcB[j] + (kPacked ? ks * 512 : kb), sb + (wave * B_INS + j) * 512);
+        dma16(T.srcB[j] + (kWKN ? static_cast<int64_t>(kb) * NOUT : kPacked ? ks * 512 : kb), sb + (wave * B_INS + j) * 512);
       }
     }
   };
@@ -561,7 +594,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
            reinterpret_cast<char*>(sb) + (wave * B_INS + j) * QB + half * 256);
     } else {
       const int j = n - A_INS;
-      dma16(T.srcB[j] + (kPacked ? ks * 512 : ks * kSK), sb + (wave * B_INS + j) * 512);
+      dma16(T.srcB[j] + (kWKN ? static_cast<int64_t>(ks) * kSK * NOUT : kPacked ? ks * 512 : ks * kSK),
+            sb + (wave * B_INS + j) * 512);
     }
   };
 
@@ -602,6 +636,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
           fb[kk][j] = codesf8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
         else if constexpr (kQ == kQInt4)
           fb[kk][j] = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
+        else if constexpr (kWKN)
+          fb[kk][j] = read_wkn(sb, kk, rb0 + rowoff);
         else
           fb[kk][j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
       }
@@ -1087,7 +1123,7 @@ static void launch_bf16(const GemmArgs& a, hipStream_t st) {
   gemm_bf16_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, C::NT, 0, st>>>(a);
 }
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false>
 static void launch_stream(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32;
   constexpr int out_cols = kSwiGLU ? BNB / 2 : BNB;
@@ -1100,7 +1136,7 @@ static void launch_stream(const GemmArgs& a, hipStream_t st) {
   const int64_t ub = tile_upper_bound(a, BM, n_tiles);
   const unsigned grid = BM <= 32 ? static_cast<unsigned>(std::max<int64_t>(ub, 1))
                                  : persistent_grid(ub, lds <= 76 * 1024 ? 2 : 1);
-  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked, kQ><<<grid, WM * WN * 64, 0, st>>>(a);
+  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked, kQ, kWKN><<<grid, WM * WN * 64, 0, st>>>(a);
 }
 
 template <bool kSwiGLU>
@@ -1128,6 +1164,10 @@ static bool streamable(const GemmArgs& a, bool gate_up) { return ((gate_up ? a.D
 template <bool kSwiGLU>
 static void launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (!a.bf16) return launch_f32<kSwiGLU>(a, st);
+  if constexpr (!kSwiGLU) {
+    // [K][N] weights (the caller checks wkn_streamable first)
+    if (a.wkn) return launch_stream<2, 4, 4, 2, false, false, 0, true>(a, st);
+  }
   const int K = kSwiGLU ? a.D : a.I;
   const bool stream = streamable(a, kSwiGLU);
   if (a.qbits == 8) {
@@ -1150,6 +1190,8 @@ static void launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (small_rows(a)) return stream ? launch_stream<1, 1, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<1, 1, 4, 2, kSwiGLU>(a, st);
   return stream ? launch_stream<2, 4, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<2, 4, 4, 2, kSwiGLU>(a, st);
 }
+
+bool wkn_streamable(const GemmArgs& a) { return a.bf16 && !small_rows(a) && a.I % 128 == 0 && a.D % 8 == 0; }
 
 void launch_gate_up(const GemmArgs& a, hipStream_t st) { launch_gemm<true>(a, st); }
 void launch_down(const GemmArgs& a, hipStream_t st) { launch_gemm<false>(a, st); }

@@ -59,9 +59,13 @@ struct GemmArgs {
   bool bf16;
   bool packed;            // w in the packed layout (bf16, K % 128 == 0, rows % 16 == 0)
   int qbits;              // code kind: 0 bf16 weights; kQInt8 / kQInt4 / kQFp8: a quantised stack
+  bool wkn;               // down form, bf16 rows: w stored [G, K, NOUT] (read with LDS transpose loads)
 };
 void launch_gate_up(const GemmArgs& a, hipStream_t st);
 void launch_down(const GemmArgs& a, hipStream_t st);
+// whether launch_down takes a.wkn (weights [G, K, NOUT]) for these arguments: bf16, tall groups,
+// K % 128 == 0 and NOUT % 8 == 0
+bool wkn_streamable(const GemmArgs& a);
 
 // Packed weight layout: a [G, R, K] bf16 matrix (R % 16 == 0, K % 32 == 0) stored as 16 x 32
 // fragments, fragment (g, rb, kb) at element ((g * R/16 + rb) * K/32 + kb) * 512, each 1 KB in

@@ -350,6 +350,19 @@ static GemmArgs nt_args(const void* x, const int32_t* row_index, const int32_t* 
   return a;
 }
 
+// The same product with W_g stored [k_in, n_out] (a layer weight in its own layout, used transposed):
+// read in place where the streaming kernel takes that layout, else through a transposed copy in tmp.
+static GemmArgs kn_args(const void* x, const int32_t* row_index, const int32_t* offsets, int G, int64_t max_rows,
+                        const void* w_kn, void* tmp, int n_out, int k_in, void* out, bool bf16, hipStream_t st) {
+  GemmArgs a = nt_args(x, row_index, offsets, G, max_rows, w_kn, n_out, k_in, out, bf16);
+  a.wkn = wkn_streamable(a);
+  if (!a.wkn) {
+    launch_transpose_mat(w_kn, tmp, G, k_in, n_out, k_in, !bf16, st);
+    a.w = tmp;
+  }
+  return a;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -591,20 +604,22 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
                        I32(L.block_counts), st));
   launch_scatter_assign(I32(L.slot_pos), F(L.weights), F(L.w_perm), I32(L.assign_of), F(L.ones), A, st);
   launch_pad_offsets(I32(L.counts), I32(L.poff), E, st);
-  // Short groups (a few rows per expert) read the weights in their stored layout (launch_kstream);
-  // otherwise the [out, in] grouped GEMMs run on transposed copies.
+  // The products with transposed weights (dh = dy W_down, dx = [da | db] W_gate_up) read the weights
+  // in their stored layout: short groups (a few rows per expert) through launch_kstream, tall groups
+  // through the streaming GEMM's [K][N] mode; other shapes through transposed copies (kn_args).
   const bool short_groups = bf && A <= 64LL * E;
   const bool ks_dh = short_groups && D % 32 == 0 && D <= kKsMaxK;
   const bool ks_dx = short_groups && (2 * I) % 32 == 0 && 2 * I <= kKsMaxK;
-  if (!ks_dh) launch_transpose_mat(down, PV(L.dnT), E, D, I, D, f32, st);                 // [E, I, D]
-  if (!ks_dx) launch_transpose_mat(gate_up, PV(L.guT), E, 2 * I, D, 2 * I, f32, st);        // [E, D, 2I]
+  GemmArgs dh_args{}, dx_args{};
+  if (!ks_dh) dh_args = kn_args(dy, token_of, offsets, E, A, down, PV(L.dnT), I, D, F(L.dhu), bf, st);
+  if (!ks_dx) dx_args = kn_args(PV(L.dab), nullptr, offsets, E, A, gate_up, PV(L.guT), D, 2 * I, F(L.dx_rows), bf, st);
   launch_transpose_mat(w_router, PV(L.wrT), 1, E, D, Ep, f32, st);               // [D, Ep]
   MOE_TRY(check_launch("moe_backward (setup)"));
   launch_down(nt_args(x, token_of, offsets, E, A, gate_up, 2 * I, D, F(L.z), bf), st);
   if (ks_dh)
     launch_kstream(static_cast<const uint16_t*>(dy), token_of, offsets, E, static_cast<const uint16_t*>(down), D, I, F(L.dhu), st);
   else
-    launch_down(nt_args(dy, token_of, offsets, E, A, PV(L.dnT), I, D, F(L.dhu), bf), st);
+    launch_down(dh_args, st);
   MOE_TRY(check_launch("moe_backward (recompute)"));
   // expert and router gradients of the activations
   launch_swiglu_bwd(F(L.z), F(L.dhu), F(L.w_perm), I32(L.assign_of), offsets + E, A, I, PV(L.h), PV(L.dab), F(L.dw), f32,
@@ -615,18 +630,18 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
     launch_kstream(static_cast<const uint16_t*>(PV(L.dab)), nullptr, offsets, E, static_cast<const uint16_t*>(gate_up), 2 * I,
                    D, F(L.dx_rows), st);
   else
-    launch_down(nt_args(PV(L.dab), nullptr, offsets, E, A, PV(L.guT), D, 2 * I, F(L.dx_rows), bf), st);
+    launch_down(dx_args, st);
   launch_down(nt_args(PV(L.dlogit), nullptr, nullptr, 1, N, PV(L.wrT), D, Ep, F(L.dxr), bf), st);
   const int Is = static_cast<int>(cfg->shared_inter);
   if (shared) {
     // the shared expert as one group of all N tokens with row weight g (1 ungated), then its gate
-    launch_transpose_mat(shared_down, PV(L.sdnT), 1, D, Is, D, f32, st);
-    launch_transpose_mat(shared_gate_up, PV(L.sguT), 1, 2 * Is, D, 2 * Is, f32, st);
+    const GemmArgs dhs_args = kn_args(dy, nullptr, nullptr, 1, N, shared_down, PV(L.sdnT), Is, D, F(L.dhus), bf, st);
+    const GemmArgs dxs_args = kn_args(PV(L.dabs), nullptr, nullptr, 1, N, shared_gate_up, PV(L.sguT), D, 2 * Is, F(L.dxs), bf, st);
     launch_down(nt_args(x, nullptr, nullptr, 1, N, shared_gate_up, 2 * Is, D, F(L.zs), bf), st);
-    launch_down(nt_args(dy, nullptr, nullptr, 1, N, PV(L.sdnT), Is, D, F(L.dhus), bf), st);
+    launch_down(dhs_args, st);
     launch_swiglu_bwd(F(L.zs), F(L.dhus), gated ? g : F(L.ones), nullptr, nullptr, N, Is, PV(L.hs), PV(L.dabs),
                       F(L.sdot), f32, st);
-    launch_down(nt_args(PV(L.dabs), nullptr, nullptr, 1, N, PV(L.sguT), D, 2 * Is, F(L.dxs), bf), st);
+    launch_down(dxs_args, st);
     if (gated) launch_shared_gate_bwd(F(L.sdot), g, N, L.Ns, F(L.dz), PV(L.dz_row), f32, st);
     launch_add_rows(F(L.dxr), F(L.dxs), gated ? F(L.dz) : nullptr, w_shared_gate, f32, N, D, st);
     MOE_TRY(check_launch("moe_backward (shared expert)"));
