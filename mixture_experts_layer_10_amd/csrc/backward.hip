@@ -5,10 +5,14 @@
 //             dx_rows = [da | db] GU_e, dDn_e = sum_p (w dy)^T h, dGU_e = sum_p [da | db]^T X_p
 //   router    dp_sel = (dw - sum_j dw_j w_j) / S (renormalised) or dw, dlogit = p (dp - sum p dp),
 //             dW_r = dlogit^T x, dx += dlogit W_r
-// The contractions over D, I or E run on the grouped GEMM kernels in their [out, in] form on
-// transposed weight copies; the weight gradients, whose contraction runs over each expert's rows,
-// use gemm_wgrad_kernel on transposed activation copies whose per-expert row ranges are padded to
-// multiples of 64 with zeros. This file holds those transposes and the elementwise steps.
+// The contractions over D, I or E run on the grouped GEMM kernels in their [out, in] form; for bf16
+// layers dh and dx read the weights in their stored [K][N] layout (gemm_kstream_kernel for short
+// groups, the streaming GEMM's LDS-transpose mode for tall ones), other shapes use transposed weight
+// copies. The experts' weight gradients, whose contraction runs over each expert's rows, read those
+// rows in place (gemm_wgrad_rows_kernel, bf16 with D and I multiples of 8); the other weight
+// gradients use gemm_wgrad_kernel on transposed activation copies whose per-group row ranges are
+// padded to multiples of 64 with zeros. This file holds those kernels, the transposes and the
+// elementwise steps.
 #include "common.h"
 #include "kernels.h"
 
@@ -469,6 +473,171 @@ void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32
   if (G <= 0 || M <= 0 || Nn <= 0) return;
   dim3 grid((Nn + kWB - 1) / kWB, (M + kWB - 1) / kWB, static_cast<unsigned>(G));
   gemm_wgrad_kernel<<<grid, 256, 0, st>>>(A, Bm, ld, poff, qtot, M, Nn, out);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Weight-gradient GEMM on the rows in place (no transposed copies): for group g with rows
+// p in [off[g], off[g+1]),
+//   out[g][m][n] = sum_p bf16(s(p) Am[ra(p)][m]) * Bm[rb(p)][n],
+// ra(p) = ga ? ga[p] : p, rb(p) = gb ? gb[p] : p, s(p) = scale ? scale[p] : 1 (the product rounded to
+// bf16 once, as the transposed copies round it). Tiles of 128 x 128 as in gemm_wgrad_kernel; a k-step
+// is 64 rows, staged as [64 rows][128 columns] (256 bytes per row, 32-byte chunks swizzled by
+// (2 row) & 7) and read with lds_tr_frag, so the fragments, and the sums in their k order, are those
+// of gemm_wgrad_kernel on the zero-padded transposed copies. Rows past the group enter as zeros. Each
+// thread moves 16 bytes of four rows per operand and step; the row indices and scales of step
+// ks + 1 are loaded during step ks - 1, the rows themselves during step ks.
+// Requires M % 8 == 0 and Nn % 8 == 0 (16-byte row pieces).
+// ---------------------------------------------------------------------------------------------
+template <bool kGA, bool kGB, bool kScale>
+__global__ __launch_bounds__(256) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kWK * kWB];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kWK * kWB];
+  const int g = w.order ? w.order[blockIdx.z] : static_cast<int>(blockIdx.z);
+  const int m0 = blockIdx.y * kWB, n0 = blockIdx.x * kWB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t p0 = w.off[g];
+  const int64_t cnt = static_cast<int64_t>(w.off[g + 1]) - p0;
+  const int ksteps = static_cast<int>((cnt + kWK - 1) / kWK);
+  const int c = tid & 15;                                   // 16-byte piece of a 256-byte row
+  const int colA = min(m0 + c * 8, w.M - 8), colB = min(n0 + c * 8, w.Nn - 8);   // pieces past M or Nn: unused
+  // LDS element offset of this thread's piece in row q = (tid >> 4) + 16 j
+  int so[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = (tid >> 4) + 16 * j;
+    so[j] = q * kWB + ((((c >> 1) ^ ((2 * q) & 7))) << 4) + (c & 1) * 8;
+  }
+  // Every load is issued unconditionally (rows past the group read the group's last row, and are
+  // zeroed by a select before the LDS store): loads guarded per lane compile into branches.
+  int ia[4], ib[4];
+  bool ok[4], ok_st[4];
+  float sc[4], sc_st[4];
+  auto gidx = [&](int ks) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t q = static_cast<int64_t>(ks) * kWK + (tid >> 4) + 16 * j;
+      ok[j] = q < cnt;
+      const int64_t p = p0 + min(q, cnt - 1);
+      ia[j] = kGA ? w.ga[p] : static_cast<int>(p);
+      ib[j] = kGB ? w.gb[p] : static_cast<int>(p);
+      sc[j] = kScale ? w.scale[p] : 1.f;
+    }
+  };
+  u32x4 ra[4], rb[4];
+  auto gload = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = *reinterpret_cast<const u32x4*>(w.A + static_cast<int64_t>(ia[j]) * w.lda + colA);
+      rb[j] = *reinterpret_cast<const u32x4*>(w.B + static_cast<int64_t>(ib[j]) * w.ldb + colB);
+      sc_st[j] = sc[j];
+      ok_st[j] = ok[j];
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 v = ra[j], u = rb[j];
+      if constexpr (kScale) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = pack_bf16x2(bf16_to_f32(static_cast<uint16_t>(v[i] & 0xffff)) * sc_st[j],
+                             bf16_to_f32(static_cast<uint16_t>(v[i] >> 16)) * sc_st[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = ok_st[j] ? v[i] : 0u;
+        u[i] = ok_st[j] ? u[i] : 0u;
+      }
+      *reinterpret_cast<u32x4*>(&sA[buf][so[j]]) = v;
+      *reinterpret_cast<u32x4*>(&sB[buf][so[j]]) = u;
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  if (ksteps > 0) {
+    gidx(0);
+    gload();
+    if (ksteps > 1) gidx(1);
+    sstore(0);
+    __syncthreads();
+  }
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < ksteps) {
+      gload();                                  // rows of step ks + 1 (indices loaded a step ago)
+      if (ks + 2 < ksteps) gidx(ks + 2);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kWK / 16; ++kk) {
+      u32x4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = lds_tr_frag<kWB>(sA[buf], kk, wm * 64 + i * 32, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = lds_tr_frag<kWB>(sB[buf], kk, wn * 64 + j * 32, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+    }
+    if (ks + 1 < ksteps) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  float* og = w.out + static_cast<int64_t>(g) * w.M * w.Nn;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    if (n >= w.Nn) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * 64 + i * 32 + acc_row(e, lane);
+        if (m < w.M) og[static_cast<int64_t>(m) * w.Nn + n] = acc[i][j][e];
+      }
+  }
+}
+
+// Groups ranked by row count, largest first (ties: lower index first). Workgroups start in
+// blockIdx order, so with this order the longest sums start first and the short ones fill in
+// behind them, instead of a late long group running alone at the end.
+__global__ __launch_bounds__(1024) void group_order_kernel(const int32_t* __restrict__ counts, int G,
+                                                           int32_t* __restrict__ order) {
+  __shared__ int s_c[1024];
+  for (int g = threadIdx.x; g < G; g += 1024) s_c[g] = counts[g];
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += 1024) {
+    const int c = s_c[g];
+    int rank = 0;
+    for (int h = 0; h < G; ++h) rank += (s_c[h] > c || (s_c[h] == c && h < g)) ? 1 : 0;
+    order[rank] = g;
+  }
+}
+
+void launch_group_order(const int32_t* counts, int G, int32_t* order, hipStream_t st) {
+  if (G <= 0 || G > 1024) return;
+  group_order_kernel<<<1, 1024, 0, st>>>(counts, G, order);
+}
+
+void launch_wgrad_rows(const WgradRowsArgs& w, int G, hipStream_t st) {
+  if (G <= 0 || w.M <= 0 || w.Nn <= 0) return;
+  dim3 grid((w.Nn + kWB - 1) / kWB, (w.M + kWB - 1) / kWB, static_cast<unsigned>(G));
+  // one compiled copy per combination of gathers and scale (the expert products use (A, scale) for
+  // dDn and (B) for dGU)
+  const int sel = (w.ga ? 4 : 0) | (w.gb ? 2 : 0) | (w.scale ? 1 : 0);
+  switch (sel) {
+    case 0: gemm_wgrad_rows_kernel<false, false, false><<<grid, 256, 0, st>>>(w); break;
+    case 1: gemm_wgrad_rows_kernel<false, false, true><<<grid, 256, 0, st>>>(w); break;
+    case 2: gemm_wgrad_rows_kernel<false, true, false><<<grid, 256, 0, st>>>(w); break;
+    case 3: gemm_wgrad_rows_kernel<false, true, true><<<grid, 256, 0, st>>>(w); break;
+    case 4: gemm_wgrad_rows_kernel<true, false, false><<<grid, 256, 0, st>>>(w); break;
+    case 5: gemm_wgrad_rows_kernel<true, false, true><<<grid, 256, 0, st>>>(w); break;
+    case 6: gemm_wgrad_rows_kernel<true, true, false><<<grid, 256, 0, st>>>(w); break;
+    default: gemm_wgrad_rows_kernel<true, true, true><<<grid, 256, 0, st>>>(w); break;
+  }
 }
 
 // fp32 weight gradient (fp32 layers): the same sums with FMAs, one output per thread of a 16 x 16

@@ -44,6 +44,31 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
 }
 
+// A 32x32x16 operand from an LDS tile stored k-major: ROW bf16 per k-row, 32-byte chunks placed at
+// chunk ^ ((2 row) & 7). Returns what a plain read of the [n][k] layout gives: lane l holds column
+// n0 + l % 32 at k = 16 kk + 8 (l / 32) .. + 7. ds_read_b64_tr_b16 hands lane 16 G + 4 a + b (16-lane
+// group G) element b of the 8-byte pieces addressed by lanes 16 G + a + 4 t, t = 0..3, so address
+// lane 16 G + r points at k-row 16 kk + 8 (G / 2) + r / 4 (+ 4 in the second read) and columns
+// n0 + 16 (G % 2) + 4 (r % 4) .. + 3. A half-wave touches four consecutive rows by two chunks; the
+// swizzle puts those eight chunks on distinct banks when ROW * 2 bytes is a multiple of 256.
+template <int ROW>
+__device__ __forceinline__ u32x4 lds_tr_frag(const uint16_t* s, int kk, int n0, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int gq = lane >> 4, rq = lane & 15;
+  const int krow = kk * 16 + 8 * (gq >> 1) + (rq >> 2);
+  const int ncol = n0 + 16 * (gq & 1) + 4 * (rq & 3);
+  u32x2 v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kr = krow + 4 * h;
+    const int idx = kr * ROW + (((ncol >> 4) ^ ((2 * kr) & 7)) << 4) + (ncol & 15);
+    const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(s) + idx));
+    v[h] = __builtin_bit_cast(u32x2, t);
+  }
+  return u32x4{v[0][0], v[0][1], v[1][0], v[1][1]};
+}
+
 // Accumulator layout of the 32x32 matrix-core result: element i of lane l holds
 // row 8*(i/4) + 4*(l/32) + (i%4), column l % 32.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }

@@ -439,28 +439,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   }
   const int R = kSwiGLU ? 2 * a.I : a.D;              // weight rows per group
   // [K][NOUT] weights: a stage holds 32 k-rows of the tile's 256 columns (512 bytes per row, 32-byte
-  // chunks swizzled by (2 row) & 7). The operand for columns n0 .. n0 + 31 comes from two transpose
-  // loads (ds_read_b64_tr_b16): in each 16-lane group G, lane 16 G + 4 a + b receives element b of
-  // the 8-byte pieces addressed by lanes 16 G + a + 4 t, t = 0..3. Address lane 16 G + r therefore
-  // points at k-row 8 (G / 2) + r / 4 (+ 4 in the second load), columns 16 (G % 2) + 4 (r % 4) .. + 3,
-  // and lane l ends up with column l % 32 at k 8 (l / 32) .. + 7, the layout of the plain read. A
-  // half-wave touches four rows by two chunks, which the swizzle spreads over all 64 banks.
-  auto read_wkn = [&](const uint16_t* sb, int kk, int n0) __attribute__((always_inline)) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const int gq = lane >> 4, rq = lane & 15;
-    const int krow = kk * 16 + 8 * (gq >> 1) + (rq >> 2);
-    const int ncol = n0 + 16 * (gq & 1) + 4 * (rq & 3);
-    u32x2 v[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kr = krow + 4 * h;
-      const int idx = kr * 256 + (((ncol >> 4) ^ ((2 * kr) & 7)) << 4) + (ncol & 15);
-      const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(sb) + idx));
-      v[h] = __builtin_bit_cast(u32x2, t);
-    }
-    return u32x4{v[0][0], v[0][1], v[1][0], v[1][1]};
-  };
+  // chunks swizzled by (2 row) & 7); lds_tr_frag assembles each weight operand with two transpose
+  // reads, in the layout of the plain read.
   constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
 
   // One tile's fixed data. make_tile reads the group table in LDS and, for gathered rows, the row
@@ -637,7 +617,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         else if constexpr (kQ == kQInt4)
           fb[kk][j] = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
         else if constexpr (kWKN)
-          fb[kk][j] = read_wkn(sb, kk, rb0 + rowoff);
+          fb[kk][j] = lds_tr_frag<256>(sb, kk, rb0 + rowoff, lane);
         else
           fb[kk][j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
       }

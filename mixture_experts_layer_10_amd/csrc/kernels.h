@@ -124,6 +124,25 @@ void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32
                   float* out, hipStream_t st);
 void launch_wgrad_f32(const float* A, const float* Bm, int64_t ld, const int32_t* poff, int64_t qtot, int G, int M, int Nn,
                       float* out, hipStream_t st);
+// Weight gradients from the rows in place: out[g] = sum over the rows p of group g (off) of
+// bf16(s(p) A[ra(p)]) (x) B[rb(p)] (outer product, [M, Nn] fp32); ra / rb gather through ga / gb
+// when given, s = scale[p] when given. bf16 only; M % 8 == 0, Nn % 8 == 0.
+struct WgradRowsArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const int32_t* ga;
+  const float* scale;
+  const uint16_t* B;
+  int64_t ldb;
+  const int32_t* gb;
+  const int32_t* off;
+  const int32_t* order;   // optional: workgroup z computes group order[z] (largest groups first)
+  int M, Nn;
+  float* out;
+};
+void launch_wgrad_rows(const WgradRowsArgs& w, int G, hipStream_t st);
+// order[0 .. G) = the groups by row count, largest first, ties by index (G <= 1024)
+void launch_group_order(const int32_t* counts, int G, int32_t* order, hipStream_t st);
 constexpr int kWgradSlices = 16;     // split of a single long reduction (poff: kWgradSlices + 1 entries)
 void launch_wgrad_split(const uint16_t* A, const uint16_t* Bm, int64_t ld, int64_t qtot, int M, int Nn, int S,
                         int32_t* poff, float* part, float* out, hipStream_t st);

@@ -258,11 +258,17 @@ static int combine_impl(const moe_config* c, const float* out_perm, const float*
   return check_launch("moe_combine");
 }
 
+// The experts' weight gradients read their rows in place (gemm_wgrad_rows_kernel) for bf16 layers
+// with D and I multiples of 8; other layers go through padded transposed copies.
+static bool rows_wgrad_of(const moe_config* c) {
+  return c->dtype == MOE_BF16 && c->hidden % 8 == 0 && c->inter % 8 == 0;
+}
+
 // Backward workspace: routing and permutation state, the recomputed pre-activations, the
 // gradients' intermediates, transposed weight copies and the padded transposed activations.
 struct BwdLayout {
   size_t route_partial, logits, weights, experts, counts, offsets, block_counts, token_of, slot_pos, w_perm, assign_of,
-      ones, dw, poff, z, dhu, h, dab, dx_rows, dlogit, dxr, dnT, guT, wrT, doT, xgT, hT, dabT, dlogitT, xT, spoff,
+      ones, dw, poff, gorder, z, dhu, h, dab, dx_rows, dlogit, dxr, dnT, guT, wrT, doT, xgT, hT, dabT, dlogitT, xT, spoff,
       wr_part, sh_scale, zs, dhus, hs, dabs, sdot, dz, dz_row, dxs, sdnT, sguT, dysT, hsT, dabsT, total;
   int64_t Ep, Qs, Ns;
 };
@@ -290,6 +296,7 @@ static BwdLayout bwd_layout_of(const moe_config* c) {
   L.ones = take(A * 4);
   L.dw = take(A * 4);
   L.poff = take((E + 1) * 4);
+  L.gorder = take(E * 4);
   L.z = take(A * 2 * I * 4);
   L.dhu = take(A * I * 4);
   L.h = take(A * I * eb);
@@ -300,10 +307,11 @@ static BwdLayout bwd_layout_of(const moe_config* c) {
   L.dnT = take(E * I * D * eb);
   L.guT = take(E * D * 2 * I * eb);
   L.wrT = take(D * L.Ep * eb);
-  L.doT = take(D * L.Qs * eb);
-  L.xgT = take(D * L.Qs * eb);
-  L.hT = take(I * L.Qs * eb);
-  L.dabT = take(2 * I * L.Qs * eb);
+  const int64_t tq = rows_wgrad_of(c) ? 0 : L.Qs;     // padded expert rows of the transposed copies
+  L.doT = take(D * tq * eb);
+  L.xgT = take(D * tq * eb);
+  L.hT = take(I * tq * eb);
+  L.dabT = take(2 * I * tq * eb);
   L.dlogitT = take(L.Ep * L.Ns * eb);
   L.xT = take(D * L.Ns * eb);
   L.spoff = take((kWgradSlices + 1) * 4);
@@ -649,13 +657,17 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   moe_config c32 = *cfg;
   c32.out_dtype = MOE_F32;
   MOE_TRY(combine_impl(&c32, F(L.dx_rows), F(L.ones), I32(L.slot_pos), F(L.dxr), nullptr, dx, st));
-  // weight gradients over each expert's rows (padded transposes), then over the tokens for W_r
+  // weight gradients over each expert's rows (bf16 with D, I multiples of 8: read in place;
+  // otherwise through padded transposes), then over the tokens for W_r
   const int32_t* poff = I32(L.poff);
   const int n1 = static_cast<int>(N);
-  launch_transpose_rows(dy, D, token_of, F(L.w_perm), offsets, poff, E, 0, L.Qs, PV(L.doT), L.Qs, f32, st);
-  launch_transpose_rows(x, D, token_of, nullptr, offsets, poff, E, 0, L.Qs, PV(L.xgT), L.Qs, f32, st);
-  launch_transpose_rows(PV(L.h), I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, PV(L.hT), L.Qs, f32, st);
-  launch_transpose_rows(PV(L.dab), 2 * I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, PV(L.dabT), L.Qs, f32, st);
+  const bool rows_wgrad = rows_wgrad_of(cfg);
+  if (!rows_wgrad) {
+    launch_transpose_rows(dy, D, token_of, F(L.w_perm), offsets, poff, E, 0, L.Qs, PV(L.doT), L.Qs, f32, st);
+    launch_transpose_rows(x, D, token_of, nullptr, offsets, poff, E, 0, L.Qs, PV(L.xgT), L.Qs, f32, st);
+    launch_transpose_rows(PV(L.h), I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, PV(L.hT), L.Qs, f32, st);
+    launch_transpose_rows(PV(L.dab), 2 * I, nullptr, nullptr, offsets, poff, E, 0, L.Qs, PV(L.dabT), L.Qs, f32, st);
+  }
   launch_transpose_rows(PV(L.dlogit), Ep, nullptr, nullptr, nullptr, nullptr, 1, n1, L.Ns, PV(L.dlogitT), L.Ns, f32, st);
   launch_transpose_rows(x, D, nullptr, nullptr, nullptr, nullptr, 1, n1, L.Ns, PV(L.xT), L.Ns, f32, st);
   MOE_TRY(check_launch("moe_backward (transposes)"));
@@ -670,8 +682,40 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
       launch_wgrad_split(static_cast<const uint16_t*>(PV(a_off)), static_cast<const uint16_t*>(PV(b_off)), ld, ld, M, Nn,
                          kWgradSlices, I32(L.spoff), F(L.wr_part), out, st);
   };
-  wgrad(L.doT, L.hT, L.Qs, poff, E, D, I, ddown);
-  wgrad(L.dabT, L.xgT, L.Qs, poff, E, 2 * I, D, dgate_up);
+  if (rows_wgrad) {
+    // dDn_e = sum_p (w dy[token])^T h, dGU_e = sum_p [da | db]^T x[token]
+    // tall groups: the longest sums start first (short groups have no long tail to avoid)
+    static_assert(kMaxExperts <= 1024, "launch_group_order ranks up to 1024 groups");
+    if (!short_groups) launch_group_order(I32(L.counts), static_cast<int>(E), I32(L.gorder), st);
+    WgradRowsArgs wd{};
+    wd.order = short_groups ? nullptr : I32(L.gorder);
+    wd.A = static_cast<const uint16_t*>(dy);
+    wd.lda = D;
+    wd.ga = token_of;
+    wd.scale = F(L.w_perm);
+    wd.B = static_cast<const uint16_t*>(PV(L.h));
+    wd.ldb = I;
+    wd.off = offsets;
+    wd.M = D;
+    wd.Nn = I;
+    wd.out = ddown;
+    launch_wgrad_rows(wd, E, st);
+    WgradRowsArgs wg{};
+    wg.order = wd.order;
+    wg.A = static_cast<const uint16_t*>(PV(L.dab));
+    wg.lda = 2 * I;
+    wg.B = static_cast<const uint16_t*>(x);
+    wg.ldb = D;
+    wg.gb = token_of;
+    wg.off = offsets;
+    wg.M = 2 * I;
+    wg.Nn = D;
+    wg.out = dgate_up;
+    launch_wgrad_rows(wg, E, st);
+  } else {
+    wgrad(L.doT, L.hT, L.Qs, poff, E, D, I, ddown);
+    wgrad(L.dabT, L.xgT, L.Qs, poff, E, 2 * I, D, dgate_up);
+  }
   wgrad(L.dlogitT, L.xT, L.Ns, nullptr, 1, E, D, dw_router);
   if (shared) {
     launch_transpose_rows(dy, D, nullptr, g, nullptr, nullptr, 1, n1, L.Ns, PV(L.dysT), L.Ns, f32, st);

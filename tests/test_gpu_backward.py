@@ -33,6 +33,9 @@ SHAPES = {
     "ragged_e12": I.custom_shape("bwd_e12", 37, 384, 12, 3, 256, seed=52),          # E padded to 16 for W_r^T
     "keras_like": I.custom_shape("bwd_keras", 512, 2048, 60, 4, 1408, seed=53),      # E = 60, wide experts
     "tall": I.custom_shape("bwd_tall", 3000, 512, 8, 2, 256, seed=54),               # long per-expert sums
+    # tall groups, I = 200: dh reads Dn in its [D, I] layout with a last column tile of 200 columns
+    # (a half-filled 32-byte chunk at the edge); dx (K = 2I = 400) goes through the transposed copy
+    "tall_cols200": I.custom_shape("bwd_c200", 2000, 256, 8, 2, 200, seed=59),
     "norm_off": I.custom_shape("bwd_nonorm", 64, 256, 16, 4, 128, norm_topk_prob=False, seed=55),
     "shared_gated": I.custom_shape("bwd_sh", 300, 256, 32, 4, 128, shared_inter=256, seed=56),
     "shared_ungated": I.custom_shape("bwd_sh_u", 130, 384, 16, 2, 128, shared_inter=128, seed=57, shared_gated=False),
