@@ -1130,10 +1130,8 @@ static void launch_f32(const GemmArgs& a, hipStream_t st) {
 
 // Rows per group decide the tile height: few rows per expert (decode) -> 32-row tiles with wide
 // weight tiles; many rows -> 256 x 256 tiles.
-static bool small_rows(const GemmArgs& a) {
-  if (!a.offsets) return a.max_rows <= 64;
-  return a.max_rows <= 64LL * a.G;
-}
+static bool small_rows_of(bool grouped, int64_t max_rows, int G) { return grouped ? max_rows <= 64LL * G : max_rows <= 64; }
+static bool small_rows(const GemmArgs& a) { return small_rows_of(a.offsets != nullptr, a.max_rows, a.G); }
 
 // Streaming path when K is a multiple of 128 (four 32-wide stages per loop trip); the
 // register-staged kernel covers the other K.
@@ -1145,7 +1143,7 @@ template <bool kSwiGLU>
 static void launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (!a.bf16) return launch_f32<kSwiGLU>(a, st);
   if constexpr (!kSwiGLU) {
-    // [K][N] weights (the caller checks wkn_streamable first)
+    // [K][N] weights (set only where wkn_streamable holds)
     if (a.wkn) return launch_stream<2, 4, 4, 2, false, false, 0, true>(a, st);
   }
   const int K = kSwiGLU ? a.D : a.I;
@@ -1171,7 +1169,9 @@ static void launch_gemm(const GemmArgs& a, hipStream_t st) {
   return stream ? launch_stream<2, 4, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<2, 4, 4, 2, kSwiGLU>(a, st);
 }
 
-bool wkn_streamable(const GemmArgs& a) { return a.bf16 && !small_rows(a) && a.I % 128 == 0 && a.D % 8 == 0; }
+bool wkn_streamable(bool bf16, bool grouped, int64_t max_rows, int G, int k_in, int n_out) {
+  return bf16 && !small_rows_of(grouped, max_rows, G) && k_in % 128 == 0 && n_out % 8 == 0;
+}
 
 void launch_gate_up(const GemmArgs& a, hipStream_t st) { launch_gemm<true>(a, st); }
 void launch_down(const GemmArgs& a, hipStream_t st) { launch_gemm<false>(a, st); }

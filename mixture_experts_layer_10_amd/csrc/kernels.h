@@ -63,9 +63,10 @@ struct GemmArgs {
 };
 void launch_gate_up(const GemmArgs& a, hipStream_t st);
 void launch_down(const GemmArgs& a, hipStream_t st);
-// whether launch_down takes a.wkn (weights [G, K, NOUT]) for these arguments: bf16, tall groups,
-// K % 128 == 0 and NOUT % 8 == 0
-bool wkn_streamable(const GemmArgs& a);
+// whether launch_down takes a.wkn (weights [G, K, NOUT]) for the down form with K = k_in, NOUT = n_out
+// over max_rows rows (in G groups when grouped, i.e. with offsets): bf16, tall groups, K % 128 == 0
+// and NOUT % 8 == 0
+bool wkn_streamable(bool bf16, bool grouped, int64_t max_rows, int G, int k_in, int n_out);
 
 // Packed weight layout: a [G, R, K] bf16 matrix (R % 16 == 0, K % 32 == 0) stored as 16 x 32
 // fragments, fragment (g, rb, kb) at element ((g * R/16 + rb) * K/32 + kb) * 512, each 1 KB in

@@ -258,10 +258,32 @@ static int combine_impl(const moe_config* c, const float* out_perm, const float*
   return check_launch("moe_combine");
 }
 
-// The experts' weight gradients read their rows in place (gemm_wgrad_rows_kernel) for bf16 layers
-// with D and I multiples of 8; other layers go through padded transposed copies.
-static bool rows_wgrad_of(const moe_config* c) {
-  return c->dtype == MOE_BF16 && c->hidden % 8 == 0 && c->inter % 8 == 0;
+// Which backward products read their operands in place and which go through transposed copies;
+// one decision serves both the workspace layout (no room for copies that are not made) and the
+// launches.
+//   dh = dy Dn_e and dx rows = [da | db] GU_e (weights used transposed): short groups (a few rows
+//   per expert) through launch_kstream, tall groups through the streaming GEMM's [K][N] mode, other
+//   shapes through transposed weight copies; likewise the shared expert's two (one group of N rows).
+//   The experts' weight gradients read their rows in place for bf16 layers with D and I multiples
+//   of 8, else padded transposed copies of the rows.
+struct BwdPlan {
+  bool short_groups, ks_dh, ks_dx, copy_dn, copy_gu, copy_sdn, copy_sgu, rows_wgrad;
+};
+
+static BwdPlan bwd_plan_of(const moe_config* c) {
+  const int64_t N = c->n_tokens, A = N * c->top_k, E = c->n_experts, D = c->hidden, I = c->inter, Is = c->shared_inter;
+  const bool bf = c->dtype == MOE_BF16;
+  const int e = static_cast<int>(E), d = static_cast<int>(D), i = static_cast<int>(I), is = static_cast<int>(Is);
+  BwdPlan P{};
+  P.short_groups = bf && A <= 64LL * E;
+  P.ks_dh = P.short_groups && D % 32 == 0 && D <= kKsMaxK;
+  P.ks_dx = P.short_groups && (2 * I) % 32 == 0 && 2 * I <= kKsMaxK;
+  P.copy_dn = !P.ks_dh && !wkn_streamable(bf, true, A, e, d, i);
+  P.copy_gu = !P.ks_dx && !wkn_streamable(bf, true, A, e, 2 * i, d);
+  P.copy_sdn = Is > 0 && !wkn_streamable(bf, false, N, 1, d, is);
+  P.copy_sgu = Is > 0 && !wkn_streamable(bf, false, N, 1, 2 * is, d);
+  P.rows_wgrad = bf && D % 8 == 0 && I % 8 == 0;
+  return P;
 }
 
 // Backward workspace: routing and permutation state, the recomputed pre-activations, the
@@ -304,10 +326,11 @@ static BwdLayout bwd_layout_of(const moe_config* c) {
   L.dx_rows = take(A * D * 4);
   L.dlogit = take(N * L.Ep * eb);
   L.dxr = take(N * D * 4);
-  L.dnT = take(E * I * D * eb);
-  L.guT = take(E * D * 2 * I * eb);
+  const BwdPlan P = bwd_plan_of(c);
+  L.dnT = take(P.copy_dn ? E * I * D * eb : 0);
+  L.guT = take(P.copy_gu ? E * D * 2 * I * eb : 0);
   L.wrT = take(D * L.Ep * eb);
-  const int64_t tq = rows_wgrad_of(c) ? 0 : L.Qs;     // padded expert rows of the transposed copies
+  const int64_t tq = P.rows_wgrad ? 0 : L.Qs;         // padded expert rows of the transposed copies
   L.doT = take(D * tq * eb);
   L.xgT = take(D * tq * eb);
   L.hT = take(I * tq * eb);
@@ -326,8 +349,8 @@ static BwdLayout bwd_layout_of(const moe_config* c) {
   L.dz = take(Is ? N * 4 : 0);
   L.dz_row = take(Is ? L.Ns * eb : 0);
   L.dxs = take(Is ? N * D * 4 : 0);
-  L.sdnT = take(Is * D * eb);
-  L.sguT = take(D * 2 * Is * eb);
+  L.sdnT = take(P.copy_sdn ? Is * D * eb : 0);
+  L.sguT = take(P.copy_sgu ? D * 2 * Is * eb : 0);
   L.dysT = take(Is ? D * L.Ns * eb : 0);
   L.hsT = take(Is * L.Ns * eb);
   L.dabsT = take(2 * Is * L.Ns * eb);
@@ -359,12 +382,13 @@ static GemmArgs nt_args(const void* x, const int32_t* row_index, const int32_t* 
 }
 
 // The same product with W_g stored [k_in, n_out] (a layer weight in its own layout, used transposed):
-// read in place where the streaming kernel takes that layout, else through a transposed copy in tmp.
+// read in place by the streaming kernel's [K][N] mode, or (copy, as BwdPlan decides) through a
+// transposed copy in tmp.
 static GemmArgs kn_args(const void* x, const int32_t* row_index, const int32_t* offsets, int G, int64_t max_rows,
-                        const void* w_kn, void* tmp, int n_out, int k_in, void* out, bool bf16, hipStream_t st) {
+                        const void* w_kn, bool copy, void* tmp, int n_out, int k_in, void* out, bool bf16, hipStream_t st) {
   GemmArgs a = nt_args(x, row_index, offsets, G, max_rows, w_kn, n_out, k_in, out, bf16);
-  a.wkn = wkn_streamable(a);
-  if (!a.wkn) {
+  a.wkn = !copy;
+  if (copy) {
     launch_transpose_mat(w_kn, tmp, G, k_in, n_out, k_in, !bf16, st);
     a.w = tmp;
   }
@@ -615,12 +639,12 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   // The products with transposed weights (dh = dy W_down, dx = [da | db] W_gate_up) read the weights
   // in their stored layout: short groups (a few rows per expert) through launch_kstream, tall groups
   // through the streaming GEMM's [K][N] mode; other shapes through transposed copies (kn_args).
-  const bool short_groups = bf && A <= 64LL * E;
-  const bool ks_dh = short_groups && D % 32 == 0 && D <= kKsMaxK;
-  const bool ks_dx = short_groups && (2 * I) % 32 == 0 && 2 * I <= kKsMaxK;
+  const BwdPlan P = bwd_plan_of(cfg);
+  const bool short_groups = P.short_groups, ks_dh = P.ks_dh, ks_dx = P.ks_dx;
   GemmArgs dh_args{}, dx_args{};
-  if (!ks_dh) dh_args = kn_args(dy, token_of, offsets, E, A, down, PV(L.dnT), I, D, F(L.dhu), bf, st);
-  if (!ks_dx) dx_args = kn_args(PV(L.dab), nullptr, offsets, E, A, gate_up, PV(L.guT), D, 2 * I, F(L.dx_rows), bf, st);
+  if (!ks_dh) dh_args = kn_args(dy, token_of, offsets, E, A, down, P.copy_dn, PV(L.dnT), I, D, F(L.dhu), bf, st);
+  if (!ks_dx)
+    dx_args = kn_args(PV(L.dab), nullptr, offsets, E, A, gate_up, P.copy_gu, PV(L.guT), D, 2 * I, F(L.dx_rows), bf, st);
   launch_transpose_mat(w_router, PV(L.wrT), 1, E, D, Ep, f32, st);               // [D, Ep]
   MOE_TRY(check_launch("moe_backward (setup)"));
   launch_down(nt_args(x, token_of, offsets, E, A, gate_up, 2 * I, D, F(L.z), bf), st);
@@ -643,8 +667,10 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   const int Is = static_cast<int>(cfg->shared_inter);
   if (shared) {
     // the shared expert as one group of all N tokens with row weight g (1 ungated), then its gate
-    const GemmArgs dhs_args = kn_args(dy, nullptr, nullptr, 1, N, shared_down, PV(L.sdnT), Is, D, F(L.dhus), bf, st);
-    const GemmArgs dxs_args = kn_args(PV(L.dabs), nullptr, nullptr, 1, N, shared_gate_up, PV(L.sguT), D, 2 * Is, F(L.dxs), bf, st);
+    const GemmArgs dhs_args =
+        kn_args(dy, nullptr, nullptr, 1, N, shared_down, P.copy_sdn, PV(L.sdnT), Is, D, F(L.dhus), bf, st);
+    const GemmArgs dxs_args =
+        kn_args(PV(L.dabs), nullptr, nullptr, 1, N, shared_gate_up, P.copy_sgu, PV(L.sguT), D, 2 * Is, F(L.dxs), bf, st);
     launch_down(nt_args(x, nullptr, nullptr, 1, N, shared_gate_up, 2 * Is, D, F(L.zs), bf), st);
     launch_down(dhs_args, st);
     launch_swiglu_bwd(F(L.zs), F(L.dhus), gated ? g : F(L.ones), nullptr, nullptr, N, Is, PV(L.hs), PV(L.dabs),
@@ -661,7 +687,7 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   // otherwise through padded transposes), then over the tokens for W_r
   const int32_t* poff = I32(L.poff);
   const int n1 = static_cast<int>(N);
-  const bool rows_wgrad = rows_wgrad_of(cfg);
+  const bool rows_wgrad = P.rows_wgrad;
   if (!rows_wgrad) {
     launch_transpose_rows(dy, D, token_of, F(L.w_perm), offsets, poff, E, 0, L.Qs, PV(L.doT), L.Qs, f32, st);
     launch_transpose_rows(x, D, token_of, nullptr, offsets, poff, E, 0, L.Qs, PV(L.xgT), L.Qs, f32, st);
