@@ -322,7 +322,7 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
     packed = "true" if main_run["cfg"].weight_layout else "false"
-    kname = f"gemm_stream_kernel<2,4,4,2,true,{packed},0,false>" if prefill_like else f"gemm_wstream_kernel<1,true,{packed},0>"
+    kname = f"gemm_stream_kernel<2,4,4,2,true,{packed},0,false,false>" if prefill_like else f"gemm_wstream_kernel<1,true,{packed},0>"
     roof["kernel"] = kname + (" (grouped gate_up + SwiGLU)" if prefill_like else " (grouped gate_up + SwiGLU, weight streaming)")
     if args.workload == "prefill":
         roof["traffic"] = measured_traffic(kname)

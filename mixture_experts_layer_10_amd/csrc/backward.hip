@@ -262,6 +262,21 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
   if (lane == 0) dw[assign_of ? assign_of[p] : p] = dot;
 }
 
+// dw[assign_of[p]] = the sum of row p's per-block partials, in block order (one thread per row).
+__global__ __launch_bounds__(256) void dw_sum_kernel(const float* __restrict__ dwp, int nb, const int32_t* __restrict__ assign_of,
+                                                     int64_t A, float* __restrict__ dw) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (p >= A) return;
+  float s = 0.f;
+  for (int c = 0; c < nb; ++c) s += dwp[p * nb + c];
+  dw[assign_of ? assign_of[p] : p] = s;
+}
+
+void launch_dw_sum(const float* dwp, int nb, const int32_t* assign_of, int64_t A, float* dw, hipStream_t st) {
+  if (A <= 0) return;
+  dw_sum_kernel<<<static_cast<unsigned>((A + 255) / 256), 256, 0, st>>>(dwp, nb, assign_of, A, dw);
+}
+
 void launch_swiglu_bwd(const float* z, const float* dhu, const float* w_perm, const int32_t* assign_of, const int32_t* n_rows,
                        int64_t A, int I, void* h, void* dab, float* dw, bool f32, hipStream_t st) {
   if (A <= 0) return;

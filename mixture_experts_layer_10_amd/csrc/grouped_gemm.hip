@@ -364,7 +364,7 @@ __device__ __forceinline__ void dispatch_live(int live, F&& f) {
   }
 }
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false, bool kBwd = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32, NT = WM * WN * 64, NW = WM * WN;
   // DMA instructions per wave per stage; with fewer 16-row A groups than waves (BM = 32), waves
@@ -378,6 +378,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int PER_STAGE = A_INS + B_DMA;
   static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
   static_assert(!kWKN || (!kSwiGLU && !kPacked && kQ == 0 && BNB == 256), "[K][N] weights: bf16 down form, 256 columns");
+  static_assert(!kBwd || (kSwiGLU && kQ == 0 && !kWKN), "SwiGLU backward: bf16 gate_up form");
   // bf16 weights enter the matrix cores as the row operand, so a lane's accumulators hold one token
   // and runs of four consecutive output columns (stored as one 8- or 16-byte vector); quantised
   // weights keep the activation rows there, so that a lane's outputs share one weight-row scale.
@@ -712,7 +713,65 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
       for (int i = 0; i < TM; ++i) {
         const int rr = m0 + (wm * TM + i) * 32 + (lane & 31);
         if (rr >= rows) continue;
-        if constexpr (kSwiGLU) {
+        if constexpr (kBwd) {
+          // SwiGLU backward of this row's columns (the formulas of swiglu_bwd_kernel); lanes l and
+          // l ^ 32 hold the two halves of each 32-column block, so one exchange completes its dot
+          const int64_t p = row0 + rr;
+          uint16_t* Hrow = static_cast<uint16_t*>(a.out) + p * NOUT;
+          uint16_t* DArow = static_cast<uint16_t*>(a.bwd_dab) + p * 2 * NOUT;
+          const float* Grow = a.bwd_dhu + p * NOUT;
+          const float wp = a.bwd_w[p];
+          const int nb = (NOUT + 31) / 32;
+          constexpr int H = TN / 2;
+#pragma unroll
+          for (int j = 0; j < H; ++j) {
+            const int blk = c0 / 32 + wn * H + j;
+            float dot = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int col = c0 + (wn * H + j) * 32 + 8 * q + 4 * (lane >> 5);
+              const bool full = vec && col + 3 < NOUT;
+              float g[4];
+              if (full) {
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(Grow + col);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) g[t] = gv[t];
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) g[t] = col + t < NOUT ? Grow[col + t] : 0.f;
+              }
+              uint16_t hv[4], dav[4], dbv[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const float av = acc[i][j][4 * q + t], bv = acc[i][j + H][4 * q + t];
+                const float s = 1.0f / (1.0f + __expf(-av));
+                hv[t] = f32_to_bf16(av * s * bv);
+                dot = fmaf(g[t], bf16_to_f32(hv[t]), dot);
+                const float dh = wp * g[t];
+                dav[t] = f32_to_bf16(dh * bv * (s * (1.0f + av * (1.0f - s))));
+                dbv[t] = f32_to_bf16(dh * av * s);
+              }
+              if (full) {
+                *reinterpret_cast<u32x2*>(Hrow + col) = u32x2{hv[0] | (static_cast<uint32_t>(hv[1]) << 16),
+                                                              hv[2] | (static_cast<uint32_t>(hv[3]) << 16)};
+                *reinterpret_cast<u32x2*>(DArow + col) = u32x2{dav[0] | (static_cast<uint32_t>(dav[1]) << 16),
+                                                               dav[2] | (static_cast<uint32_t>(dav[3]) << 16)};
+                *reinterpret_cast<u32x2*>(DArow + NOUT + col) = u32x2{dbv[0] | (static_cast<uint32_t>(dbv[1]) << 16),
+                                                                      dbv[2] | (static_cast<uint32_t>(dbv[3]) << 16)};
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  if (col + t < NOUT) {
+                    Hrow[col + t] = hv[t];
+                    DArow[col + t] = dav[t];
+                    DArow[NOUT + col + t] = dbv[t];
+                  }
+              }
+            }
+            dot += __shfl_xor(dot, 32, 64);
+            if (lane < 32 && blk < nb) a.bwd_dwp[p * nb + blk] = dot;
+          }
+        } else if constexpr (kSwiGLU) {
           uint16_t* Hrow = static_cast<uint16_t*>(a.out) + (row0 + rr) * NOUT;
           constexpr int H = TN / 2;
 #pragma unroll
@@ -1103,7 +1162,7 @@ static void launch_bf16(const GemmArgs& a, hipStream_t st) {
   gemm_bf16_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, C::NT, 0, st>>>(a);
 }
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false, bool kBwd = false>
 static void launch_stream(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32;
   constexpr int out_cols = kSwiGLU ? BNB / 2 : BNB;
@@ -1116,7 +1175,7 @@ static void launch_stream(const GemmArgs& a, hipStream_t st) {
   const int64_t ub = tile_upper_bound(a, BM, n_tiles);
   const unsigned grid = BM <= 32 ? static_cast<unsigned>(std::max<int64_t>(ub, 1))
                                  : persistent_grid(ub, lds <= 76 * 1024 ? 2 : 1);
-  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked, kQ, kWKN><<<grid, WM * WN * 64, 0, st>>>(a);
+  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked, kQ, kWKN, kBwd><<<grid, WM * WN * 64, 0, st>>>(a);
 }
 
 template <bool kSwiGLU>
@@ -1145,6 +1204,9 @@ static void launch_gemm(const GemmArgs& a, hipStream_t st) {
   if constexpr (!kSwiGLU) {
     // [K][N] weights (set only where wkn_streamable holds)
     if (a.wkn) return launch_stream<2, 4, 4, 2, false, false, 0, true>(a, st);
+  } else {
+    // SwiGLU backward epilogue (set only where bwd_fusable holds)
+    if (a.bwd_dab) return launch_stream<2, 4, 4, 2, true, false, 0, false, true>(a, st);
   }
   const int K = kSwiGLU ? a.D : a.I;
   const bool stream = streamable(a, kSwiGLU);
@@ -1167,6 +1229,10 @@ static void launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (small_rows(a) && K % 32 == 0) return launch_wstream<kSwiGLU, false>(a, st);
   if (small_rows(a)) return stream ? launch_stream<1, 1, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<1, 1, 4, 2, kSwiGLU>(a, st);
   return stream ? launch_stream<2, 4, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<2, 4, 4, 2, kSwiGLU>(a, st);
+}
+
+bool bwd_fusable(bool bf16, bool grouped, int64_t max_rows, int G, int D, int I) {
+  return bf16 && !small_rows_of(grouped, max_rows, G) && D % 128 == 0 && I % 4 == 0;
 }
 
 bool wkn_streamable(bool bf16, bool grouped, int64_t max_rows, int G, int k_in, int n_out) {

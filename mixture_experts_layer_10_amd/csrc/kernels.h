@@ -60,13 +60,26 @@ struct GemmArgs {
   bool packed;            // w in the packed layout (bf16, K % 128 == 0, rows % 16 == 0)
   int qbits;              // code kind: 0 bf16 weights; kQInt8 / kQInt4 / kQFp8: a quantised stack
   bool wkn;               // down form, bf16 rows: w stored [G, K, NOUT] (read with LDS transpose loads)
+  // gate_up form, bf16 rows, tall groups: the SwiGLU backward in the epilogue when bwd_dab is set.
+  // With [a | b] the tile's pre-activations, s = 1 / (1 + exp(-a)) and dh = w[p] dhu:
+  // out = h = bf16(a s b), bwd_dab = bf16([dh b s (1 + a (1 - s)) | dh a s]), and
+  // bwd_dwp[p][c] = sum of dhu h over columns 32 c .. 32 c + 31 (fp32 partials of dw)
+  const float* bwd_dhu;   // [rows, I] fp32
+  const float* bwd_w;     // [rows]
+  void* bwd_dab;          // [rows, 2I] bf16
+  float* bwd_dwp;         // [rows, ceil(I / 32)] fp32
 };
+// dw[assign_of[p]] = sum over c of dwp[p][c], in column order (p < A)
+void launch_dw_sum(const float* dwp, int nb, const int32_t* assign_of, int64_t A, float* dw, hipStream_t st);
 void launch_gate_up(const GemmArgs& a, hipStream_t st);
 void launch_down(const GemmArgs& a, hipStream_t st);
 // whether launch_down takes a.wkn (weights [G, K, NOUT]) for the down form with K = k_in, NOUT = n_out
 // over max_rows rows (in G groups when grouped, i.e. with offsets): bf16, tall groups, K % 128 == 0
 // and NOUT % 8 == 0
 bool wkn_streamable(bool bf16, bool grouped, int64_t max_rows, int G, int k_in, int n_out);
+// whether launch_gate_up takes the SwiGLU backward epilogue (bwd_dab set) for a gate_up product of
+// width D and I over max_rows rows (row-layout bf16 weights): tall groups, D % 128 == 0, I % 4 == 0
+bool bwd_fusable(bool bf16, bool grouped, int64_t max_rows, int G, int D, int I);
 
 // Packed weight layout: a [G, R, K] bf16 matrix (R % 16 == 0, K % 32 == 0) stored as 16 x 32
 // fragments, fragment (g, rb, kb) at element ((g * R/16 + rb) * K/32 + kb) * 512, each 1 KB in

@@ -266,8 +266,10 @@ static int combine_impl(const moe_config* c, const float* out_perm, const float*
 //   shapes through transposed weight copies; likewise the shared expert's two (one group of N rows).
 //   The experts' weight gradients read their rows in place for bf16 layers with D and I multiples
 //   of 8, else padded transposed copies of the rows.
+//   Tall groups (bf16, D % 128 == 0): the SwiGLU backward runs in the epilogue of the recomputed
+//   gate_up product (no fp32 pre-activations z in memory), dw from per-block partials.
 struct BwdPlan {
-  bool short_groups, ks_dh, ks_dx, copy_dn, copy_gu, copy_sdn, copy_sgu, rows_wgrad;
+  bool short_groups, ks_dh, ks_dx, copy_dn, copy_gu, copy_sdn, copy_sgu, rows_wgrad, fused_swiglu;
 };
 
 static BwdPlan bwd_plan_of(const moe_config* c) {
@@ -283,6 +285,7 @@ static BwdPlan bwd_plan_of(const moe_config* c) {
   P.copy_sdn = Is > 0 && !wkn_streamable(bf, false, N, 1, d, is);
   P.copy_sgu = Is > 0 && !wkn_streamable(bf, false, N, 1, 2 * is, d);
   P.rows_wgrad = bf && D % 8 == 0 && I % 8 == 0;
+  P.fused_swiglu = bwd_fusable(bf, true, A, e, d, i);
   return P;
 }
 
@@ -290,7 +293,7 @@ static BwdPlan bwd_plan_of(const moe_config* c) {
 // gradients' intermediates, transposed weight copies and the padded transposed activations.
 struct BwdLayout {
   size_t route_partial, logits, weights, experts, counts, offsets, block_counts, token_of, slot_pos, w_perm, assign_of,
-      ones, dw, poff, gorder, z, dhu, h, dab, dx_rows, dlogit, dxr, dnT, guT, wrT, doT, xgT, hT, dabT, dlogitT, xT, spoff,
+      ones, dw, poff, gorder, z, dwp, dhu, h, dab, dx_rows, dlogit, dxr, dnT, guT, wrT, doT, xgT, hT, dabT, dlogitT, xT, spoff,
       wr_part, sh_scale, zs, dhus, hs, dabs, sdot, dz, dz_row, dxs, sdnT, sguT, dysT, hsT, dabsT, total;
   int64_t Ep, Qs, Ns;
 };
@@ -319,14 +322,15 @@ static BwdLayout bwd_layout_of(const moe_config* c) {
   L.dw = take(A * 4);
   L.poff = take((E + 1) * 4);
   L.gorder = take(E * 4);
-  L.z = take(A * 2 * I * 4);
+  const BwdPlan P = bwd_plan_of(c);
+  L.z = take(P.fused_swiglu ? 0 : A * 2 * I * 4);
+  L.dwp = take(P.fused_swiglu ? A * ((I + 31) / 32) * 4 : 0);
   L.dhu = take(A * I * 4);
   L.h = take(A * I * eb);
   L.dab = take(A * 2 * I * eb);
   L.dx_rows = take(A * D * 4);
   L.dlogit = take(N * L.Ep * eb);
   L.dxr = take(N * D * 4);
-  const BwdPlan P = bwd_plan_of(c);
   L.dnT = take(P.copy_dn ? E * I * D * eb : 0);
   L.guT = take(P.copy_gu ? E * D * 2 * I * eb : 0);
   L.wrT = take(D * L.Ep * eb);
@@ -647,15 +651,25 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
     dx_args = kn_args(PV(L.dab), nullptr, offsets, E, A, gate_up, P.copy_gu, PV(L.guT), D, 2 * I, F(L.dx_rows), bf, st);
   launch_transpose_mat(w_router, PV(L.wrT), 1, E, D, Ep, f32, st);               // [D, Ep]
   MOE_TRY(check_launch("moe_backward (setup)"));
-  launch_down(nt_args(x, token_of, offsets, E, A, gate_up, 2 * I, D, F(L.z), bf), st);
+  if (!P.fused_swiglu) launch_down(nt_args(x, token_of, offsets, E, A, gate_up, 2 * I, D, F(L.z), bf), st);
   if (ks_dh)
     launch_kstream(static_cast<const uint16_t*>(dy), token_of, offsets, E, static_cast<const uint16_t*>(down), D, I, F(L.dhu), st);
   else
     launch_down(dh_args, st);
+  // expert and router gradients of the activations: h, [da | db] and dw = dhu . h
+  if (P.fused_swiglu) {
+    GemmArgs gu = gemm_args(cfg, E, I, A, x, token_of, offsets, gate_up, PV(L.h));
+    gu.bwd_dhu = F(L.dhu);
+    gu.bwd_w = F(L.w_perm);
+    gu.bwd_dab = PV(L.dab);
+    gu.bwd_dwp = F(L.dwp);
+    launch_gate_up(gu, st);
+    launch_dw_sum(F(L.dwp), static_cast<int>((I + 31) / 32), I32(L.assign_of), A, F(L.dw), st);
+  } else {
+    launch_swiglu_bwd(F(L.z), F(L.dhu), F(L.w_perm), I32(L.assign_of), offsets + E, A, I, PV(L.h), PV(L.dab), F(L.dw),
+                      f32, st);
+  }
   MOE_TRY(check_launch("moe_backward (recompute)"));
-  // expert and router gradients of the activations
-  launch_swiglu_bwd(F(L.z), F(L.dhu), F(L.w_perm), I32(L.assign_of), offsets + E, A, I, PV(L.h), PV(L.dab), F(L.dw), f32,
-                    st);
   launch_router_bwd(F(L.logits), F(L.weights), I32(L.experts), F(L.dw), N, E, Ep, static_cast<int>(cfg->top_k),
                     cfg->norm_topk_prob, PV(L.dlogit), f32, st);
   if (ks_dx)
