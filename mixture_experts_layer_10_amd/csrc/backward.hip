@@ -495,64 +495,83 @@ void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32
 // p in [off[g], off[g+1]),
 //   out[g][m][n] = sum_p bf16(s(p) Am[ra(p)][m]) * Bm[rb(p)][n],
 // ra(p) = ga ? ga[p] : p, rb(p) = gb ? gb[p] : p, s(p) = scale ? scale[p] : 1 (the product rounded to
-// bf16 once, as the transposed copies round it). Tiles of 128 x 128 as in gemm_wgrad_kernel; a k-step
-// is 64 rows, staged as [64 rows][128 columns] (256 bytes per row, 32-byte chunks swizzled by
-// (2 row) & 7) and read with lds_tr_frag, so the fragments, and the sums in their k order, are those
-// of gemm_wgrad_kernel on the zero-padded transposed copies. Rows past the group enter as zeros. Each
-// thread moves 16 bytes of four rows per operand and step; the row indices and scales of step
-// ks + 1 are loaded during step ks - 1, the rows themselves during step ks.
+// bf16 once, as the transposed copies round it). Tiles of 256 (M) x 128 (N), four waves of 128 x 64
+// (4 x 2 blocks of 32 x 32, so each fragment read feeds 1.33 matrix-core steps); a k-step is 32 rows,
+// staged as [32 rows][256 or 128 columns] (32-byte chunks swizzled by (2 row) & 7) and read with
+// lds_tr_frag, so the fragments, and the sums in their k order, are those of gemm_wgrad_kernel on
+// the zero-padded transposed copies. Two buffers take 48 KB, three workgroups per CU. Rows past the
+// group enter as zeros. Per step a thread moves 16 bytes of four A rows and two B rows; the row
+// indices and scales of step ks + 1 are loaded during step ks - 1, the rows themselves during ks.
 // Requires M % 8 == 0 and Nn % 8 == 0 (16-byte row pieces).
 // ---------------------------------------------------------------------------------------------
+constexpr int kRM = 256, kRN = 128, kRK = 32;   // rows kernel: tile M x N, rows per k-step
+
 template <bool kGA, bool kGB, bool kScale>
 __global__ __launch_bounds__(256) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kWK * kWB];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kWK * kWB];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kRK * kRM];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kRK * kRN];
   const int g = w.order ? w.order[blockIdx.z] : static_cast<int>(blockIdx.z);
-  const int m0 = blockIdx.y * kWB, n0 = blockIdx.x * kWB;
+  const int m0 = blockIdx.y * kRM, n0 = blockIdx.x * kRN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;                // wave tile: 128 of M x 64 of N
   const int64_t p0 = w.off[g];
   const int64_t cnt = static_cast<int64_t>(w.off[g + 1]) - p0;
-  const int ksteps = static_cast<int>((cnt + kWK - 1) / kWK);
-  const int c = tid & 15;                                   // 16-byte piece of a 256-byte row
-  const int colA = min(m0 + c * 8, w.M - 8), colB = min(n0 + c * 8, w.Nn - 8);   // pieces past M or Nn: unused
-  // LDS element offset of this thread's piece in row q = (tid >> 4) + 16 j
-  int so[4];
+  const int ksteps = static_cast<int>((cnt + kRK - 1) / kRK);
+  // A: rows (tid >> 5) + 8 j (j < 4), 16-byte piece ca = tid % 32 of the row's 512 bytes;
+  // B: rows (tid >> 4) + 16 j (j < 2), piece cb = tid % 16 of 256 bytes
+  const int ca = tid & 31, cb = tid & 15;
+  const int colA = min(m0 + ca * 8, w.M - 8), colB = min(n0 + cb * 8, w.Nn - 8);   // pieces past M or Nn: unused
+  int soA[4], soB[2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    const int q = (tid >> 5) + 8 * j;
+    soA[j] = q * kRM + ((((ca >> 1) ^ ((2 * q) & 7))) << 4) + (ca & 1) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
     const int q = (tid >> 4) + 16 * j;
-    so[j] = q * kWB + ((((c >> 1) ^ ((2 * q) & 7))) << 4) + (c & 1) * 8;
+    soB[j] = q * kRN + ((((cb >> 1) ^ ((2 * q) & 7))) << 4) + (cb & 1) * 8;
   }
   // Every load is issued unconditionally (rows past the group read the group's last row, and are
   // zeroed by a select before the LDS store): loads guarded per lane compile into branches.
-  int ia[4], ib[4];
-  bool ok[4], ok_st[4];
+  int ia[4], ib[2];
+  bool oka[4], okb[2], oka_st[4], okb_st[2];
   float sc[4], sc_st[4];
   auto gidx = [&](int ks) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t q = static_cast<int64_t>(ks) * kWK + (tid >> 4) + 16 * j;
-      ok[j] = q < cnt;
+      const int64_t q = static_cast<int64_t>(ks) * kRK + (tid >> 5) + 8 * j;
+      oka[j] = q < cnt;
       const int64_t p = p0 + min(q, cnt - 1);
       ia[j] = kGA ? w.ga[p] : static_cast<int>(p);
-      ib[j] = kGB ? w.gb[p] : static_cast<int>(p);
       sc[j] = kScale ? w.scale[p] : 1.f;
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t q = static_cast<int64_t>(ks) * kRK + (tid >> 4) + 16 * j;
+      okb[j] = q < cnt;
+      const int64_t p = p0 + min(q, cnt - 1);
+      ib[j] = kGB ? w.gb[p] : static_cast<int>(p);
+    }
   };
-  u32x4 ra[4], rb[4];
+  u32x4 ra[4], rb[2];
   auto gload = [&]() {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       ra[j] = *reinterpret_cast<const u32x4*>(w.A + static_cast<int64_t>(ia[j]) * w.lda + colA);
-      rb[j] = *reinterpret_cast<const u32x4*>(w.B + static_cast<int64_t>(ib[j]) * w.ldb + colB);
       sc_st[j] = sc[j];
-      ok_st[j] = ok[j];
+      oka_st[j] = oka[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      rb[j] = *reinterpret_cast<const u32x4*>(w.B + static_cast<int64_t>(ib[j]) * w.ldb + colB);
+      okb_st[j] = okb[j];
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x4 v = ra[j], u = rb[j];
+      u32x4 v = ra[j];
       if constexpr (kScale) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -560,17 +579,20 @@ __global__ __launch_bounds__(256) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
                              bf16_to_f32(static_cast<uint16_t>(v[i] >> 16)) * sc_st[j]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = ok_st[j] ? v[i] : 0u;
-        u[i] = ok_st[j] ? u[i] : 0u;
-      }
-      *reinterpret_cast<u32x4*>(&sA[buf][so[j]]) = v;
-      *reinterpret_cast<u32x4*>(&sB[buf][so[j]]) = u;
+      for (int i = 0; i < 4; ++i) v[i] = oka_st[j] ? v[i] : 0u;
+      *reinterpret_cast<u32x4*>(&sA[buf][soA[j]]) = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 u = rb[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = okb_st[j] ? u[i] : 0u;
+      *reinterpret_cast<u32x4*>(&sB[buf][soB[j]]) = u;
     }
   };
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   if (ksteps > 0) {
@@ -587,14 +609,14 @@ __global__ __launch_bounds__(256) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
       if (ks + 2 < ksteps) gidx(ks + 2);
     }
 #pragma unroll
-    for (int kk = 0; kk < kWK / 16; ++kk) {
-      u32x4 fa[2], fb[2];
+    for (int kk = 0; kk < kRK / 16; ++kk) {
+      u32x4 fa[4], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = lds_tr_frag<kWB>(sA[buf], kk, wm * 64 + i * 32, lane);
+      for (int i = 0; i < 4; ++i) fa[i] = lds_tr_frag<kRM>(sA[buf], kk, wm * 128 + i * 32, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = lds_tr_frag<kWB>(sB[buf], kk, wn * 64 + j * 32, lane);
+      for (int j = 0; j < 2; ++j) fb[j] = lds_tr_frag<kRN>(sB[buf], kk, wn * 64 + j * 32, lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
     }
@@ -607,10 +629,10 @@ __global__ __launch_bounds__(256) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
     const int n = n0 + wn * 64 + j * 32 + (lane & 31);
     if (n >= w.Nn) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 64 + i * 32 + acc_row(e, lane);
+        const int m = m0 + wm * 128 + i * 32 + acc_row(e, lane);
         if (m < w.M) og[static_cast<int64_t>(m) * w.Nn + n] = acc[i][j][e];
       }
   }
@@ -639,7 +661,7 @@ void launch_group_order(const int32_t* counts, int G, int32_t* order, hipStream_
 
 void launch_wgrad_rows(const WgradRowsArgs& w, int G, hipStream_t st) {
   if (G <= 0 || w.M <= 0 || w.Nn <= 0) return;
-  dim3 grid((w.Nn + kWB - 1) / kWB, (w.M + kWB - 1) / kWB, static_cast<unsigned>(G));
+  dim3 grid((w.Nn + kRN - 1) / kRN, (w.M + kRM - 1) / kRM, static_cast<unsigned>(G));
   // one compiled copy per combination of gathers and scale (the expert products use (A, scale) for
   // dDn and (B) for dGU)
   const int sel = (w.ga ? 4 : 0) | (w.gb ? 2 : 0) | (w.scale ? 1 : 0);
