@@ -11,8 +11,10 @@
 // copies. The experts' weight gradients, whose contraction runs over each expert's rows, read those
 // rows in place (gemm_wgrad_rows_kernel, bf16 with D and I multiples of 8); the other weight
 // gradients use gemm_wgrad_kernel on transposed activation copies whose per-group row ranges are
-// padded to multiples of 64 with zeros. This file holds those kernels, the transposes and the
-// elementwise steps.
+// padded to multiples of 64 with zeros. For tall groups the SwiGLU backward (h, da, db, dw) runs in
+// the epilogue of the recomputed gate_up product (grouped_gemm.hip) and dw_sum_kernel adds its
+// per-block partials; otherwise swiglu_bwd_kernel does it from z. This file holds those kernels,
+// the transposes and the elementwise steps.
 #include "common.h"
 #include "kernels.h"
 
