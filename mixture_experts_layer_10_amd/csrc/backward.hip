@@ -497,52 +497,49 @@ void launch_wgrad(const uint16_t* A, const uint16_t* Bm, int64_t ld, const int32
 // p in [off[g], off[g+1]),
 //   out[g][m][n] = sum_p bf16(s(p) Am[ra(p)][m]) * Bm[rb(p)][n],
 // ra(p) = ga ? ga[p] : p, rb(p) = gb ? gb[p] : p, s(p) = scale ? scale[p] : 1 (the product rounded to
-// bf16 once, as the transposed copies round it). Tiles of 256 (M) x 128 (N), four waves of 128 x 64
-// (4 x 2 blocks of 32 x 32, so each fragment read feeds 1.33 matrix-core steps); a k-step is 32 rows,
-// staged as [32 rows][256 or 128 columns] (32-byte chunks swizzled by (2 row) & 7) and read with
-// lds_tr_frag, so the fragments, and the sums in their k order, are those of gemm_wgrad_kernel on
-// the zero-padded transposed copies. Two buffers take 48 KB, three workgroups per CU. Rows past the
-// group enter as zeros. Per step a thread moves 16 bytes of four A rows and two B rows; the row
-// indices and scales of step ks + 1 are loaded during step ks - 1, the rows themselves during ks.
+// bf16 once, as the transposed copies round it). Tiles of 256 x 256 (each of a group's rows is
+// read once per 256 columns of the other operand: those re-reads, not the matrix cores, bound the
+// kernel), eight waves of 128 x 64 (4 x 2 blocks of 32 x 32, each fragment read feeding 1.33
+// matrix-core steps); a k-step is 32 rows, staged as [32 rows][256 columns] per operand (32-byte
+// chunks swizzled by (2 row) & 7) and read with lds_tr_frag, so the fragments, and the sums in their
+// k order, are those of gemm_wgrad_kernel on the zero-padded transposed copies. Two buffers take
+// 64 KB. Rows past the group enter as zeros. Per step a thread moves 16 bytes of two A rows and two
+// B rows; the row indices and scales of step ks + 1 are loaded during step ks - 1, the rows
+// themselves during ks.
 // Requires M % 8 == 0 and Nn % 8 == 0 (16-byte row pieces).
 // ---------------------------------------------------------------------------------------------
-constexpr int kRM = 256, kRN = 128, kRK = 32;   // rows kernel: tile M x N, rows per k-step
+constexpr int kRM = 256, kRN = 256, kRK = 32;   // rows kernel: tile M x N, rows per k-step
 
 template <bool kGA, bool kGB, bool kScale>
-__global__ __launch_bounds__(256) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
+__global__ __launch_bounds__(512) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kRK * kRM];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kRK * kRN];
   const int g = w.order ? w.order[blockIdx.z] : static_cast<int>(blockIdx.z);
   const int m0 = blockIdx.y * kRM, n0 = blockIdx.x * kRN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;                // wave tile: 128 of M x 64 of N
+  const int wm = wave >> 2, wn = wave & 3;                // wave tile: 128 of M x 64 of N
   const int64_t p0 = w.off[g];
   const int64_t cnt = static_cast<int64_t>(w.off[g + 1]) - p0;
   const int ksteps = static_cast<int>((cnt + kRK - 1) / kRK);
-  // A: rows (tid >> 5) + 8 j (j < 4), 16-byte piece ca = tid % 32 of the row's 512 bytes;
-  // B: rows (tid >> 4) + 16 j (j < 2), piece cb = tid % 16 of 256 bytes
-  const int ca = tid & 31, cb = tid & 15;
+  // A and B: rows (tid >> 5) + 16 j (j < 2), 16-byte piece c = tid % 32 of the row's 512 bytes
+  const int ca = tid & 31, cb = tid & 31;
   const int colA = min(m0 + ca * 8, w.M - 8), colB = min(n0 + cb * 8, w.Nn - 8);   // pieces past M or Nn: unused
-  int soA[4], soB[2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = (tid >> 5) + 8 * j;
-    soA[j] = q * kRM + ((((ca >> 1) ^ ((2 * q) & 7))) << 4) + (ca & 1) * 8;
-  }
+  int soA[2], soB[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int q = (tid >> 4) + 16 * j;
+    const int q = (tid >> 5) + 16 * j;
+    soA[j] = q * kRM + ((((ca >> 1) ^ ((2 * q) & 7))) << 4) + (ca & 1) * 8;
     soB[j] = q * kRN + ((((cb >> 1) ^ ((2 * q) & 7))) << 4) + (cb & 1) * 8;
   }
   // Every load is issued unconditionally (rows past the group read the group's last row, and are
   // zeroed by a select before the LDS store): loads guarded per lane compile into branches.
-  int ia[4], ib[2];
-  bool oka[4], okb[2], oka_st[4], okb_st[2];
-  float sc[4], sc_st[4];
+  int ia[2], ib[2];
+  bool oka[2], okb[2], oka_st[2], okb_st[2];
+  float sc[2], sc_st[2];
   auto gidx = [&](int ks) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t q = static_cast<int64_t>(ks) * kRK + (tid >> 5) + 8 * j;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t q = static_cast<int64_t>(ks) * kRK + (tid >> 5) + 16 * j;
       oka[j] = q < cnt;
       const int64_t p = p0 + min(q, cnt - 1);
       ia[j] = kGA ? w.ga[p] : static_cast<int>(p);
@@ -550,16 +547,16 @@ __global__ __launch_bounds__(256) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int64_t q = static_cast<int64_t>(ks) * kRK + (tid >> 4) + 16 * j;
+      const int64_t q = static_cast<int64_t>(ks) * kRK + (tid >> 5) + 16 * j;
       okb[j] = q < cnt;
       const int64_t p = p0 + min(q, cnt - 1);
       ib[j] = kGB ? w.gb[p] : static_cast<int>(p);
     }
   };
-  u32x4 ra[4], rb[2];
+  u32x4 ra[2], rb[2];
   auto gload = [&]() {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       ra[j] = *reinterpret_cast<const u32x4*>(w.A + static_cast<int64_t>(ia[j]) * w.lda + colA);
       sc_st[j] = sc[j];
       oka_st[j] = oka[j];
@@ -572,7 +569,7 @@ __global__ __launch_bounds__(256) void gemm_wgrad_rows_kernel(WgradRowsArgs w) {
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       u32x4 v = ra[j];
       if constexpr (kScale) {
 #pragma unroll
@@ -668,14 +665,14 @@ void launch_wgrad_rows(const WgradRowsArgs& w, int G, hipStream_t st) {
   // dDn and (B) for dGU)
   const int sel = (w.ga ? 4 : 0) | (w.gb ? 2 : 0) | (w.scale ? 1 : 0);
   switch (sel) {
-    case 0: gemm_wgrad_rows_kernel<false, false, false><<<grid, 256, 0, st>>>(w); break;
-    case 1: gemm_wgrad_rows_kernel<false, false, true><<<grid, 256, 0, st>>>(w); break;
-    case 2: gemm_wgrad_rows_kernel<false, true, false><<<grid, 256, 0, st>>>(w); break;
-    case 3: gemm_wgrad_rows_kernel<false, true, true><<<grid, 256, 0, st>>>(w); break;
-    case 4: gemm_wgrad_rows_kernel<true, false, false><<<grid, 256, 0, st>>>(w); break;
-    case 5: gemm_wgrad_rows_kernel<true, false, true><<<grid, 256, 0, st>>>(w); break;
-    case 6: gemm_wgrad_rows_kernel<true, true, false><<<grid, 256, 0, st>>>(w); break;
-    default: gemm_wgrad_rows_kernel<true, true, true><<<grid, 256, 0, st>>>(w); break;
+    case 0: gemm_wgrad_rows_kernel<false, false, false><<<grid, 512, 0, st>>>(w); break;
+    case 1: gemm_wgrad_rows_kernel<false, false, true><<<grid, 512, 0, st>>>(w); break;
+    case 2: gemm_wgrad_rows_kernel<false, true, false><<<grid, 512, 0, st>>>(w); break;
+    case 3: gemm_wgrad_rows_kernel<false, true, true><<<grid, 512, 0, st>>>(w); break;
+    case 4: gemm_wgrad_rows_kernel<true, false, false><<<grid, 512, 0, st>>>(w); break;
+    case 5: gemm_wgrad_rows_kernel<true, false, true><<<grid, 512, 0, st>>>(w); break;
+    case 6: gemm_wgrad_rows_kernel<true, true, false><<<grid, 512, 0, st>>>(w); break;
+    default: gemm_wgrad_rows_kernel<true, true, true><<<grid, 512, 0, st>>>(w); break;
   }
 }
 
