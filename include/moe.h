@@ -134,7 +134,9 @@ int moe_router_bias_update(const moe_config* cfg, const int32_t* counts, float* 
  * assignment order), with no atomics on ranks, so the result is deterministic ("27. Mixture of
  * experts", section "Dispatch", grouped dispatch steps 1-2; stretch exercise 2 for the row-offset
  * prefix sum).
- *   experts [N, k] int32 in [0, E)                 (ids outside that range: undefined result)
+ *   experts [N, k] int32 in [0, E)                 an id outside [0, E) is dropped: not counted,
+ *                                                  given no row, slot_pos = -1 (moe_combine then
+ *                                                  skips it, as a capacity drop)
  *   counts [E], offsets [E+1] int32                rows of expert e are [offsets[e], offsets[e+1])
  *   token_of [N*k] int32                           token each sorted row came from
  *   slot_pos [N*k] int32                           sorted row of assignment a (inverse permutation)
@@ -224,11 +226,12 @@ int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, 
  *   shared   the same with all N tokens, row weight g = sigmoid(w_s . x) (1 without w_s), and for
  *            the gate dz = (dy . shared(x)) g (1 - g): dw_s = sum dz x, dx += dz w_s
  * The forward's routing, grouping and pre-activations are recomputed from x (nothing is kept from a
- * moe_forward call). Matrix-core inputs are bf16 (h, w dy, da, db and dlogits rounded once),
- * accumulation fp32; the sums over an expert's rows run in row order, deterministic.
- *   cfg: dtype bf16, weight_layout MOE_LAYOUT_ROWS (else MOE_ERR_UNSUPPORTED)
- *   x [N, D], w_router [E, D], gate_up [E, 2I, D], down [E, D, I], dy [N, D]   (bf16, row-major)
- *   shared_gate_up [2I_s, D], shared_down [D, I_s], w_shared_gate [D] (bf16): as moe_forward
+ * moe_forward call). bf16 layers: matrix-core inputs are bf16 (h, w dy, da, db and dlogits rounded
+ * once), accumulation fp32. fp32 layers: every intermediate stays fp32 (FMA weight-gradient kernel).
+ * The sums over an expert's rows run in row order, deterministic.
+ *   cfg: dtype bf16 or fp32, weight_layout MOE_LAYOUT_ROWS (else MOE_ERR_UNSUPPORTED)
+ *   x [N, D], w_router [E, D], gate_up [E, 2I, D], down [E, D, I], dy [N, D]   (cfg.dtype, row-major)
+ *   shared_gate_up [2I_s, D], shared_down [D, I_s], w_shared_gate [D] (cfg.dtype): as moe_forward
  *     (required iff shared_inter > 0; w_shared_gate may be NULL: ungated)
  *   dx [N, D], dw_router [E, D], dgate_up [E, 2I, D], ddown [E, D, I]       (fp32, overwritten;
  *     an expert that received no token gets zeros)
@@ -268,8 +271,11 @@ int moe_combine(const moe_config* cfg, const float* out_perm, const float* weigh
                 const int32_t* slot_pos, const float* shared_out, const float* shared_scale, void* y,
                 void* stream);
 
-/* The whole block: moe_route (with ws) -> moe_permute -> moe_expert_ffn over the routed groups (rows gathered
- * straight from x) -> [shared expert as one more group over all N rows] -> moe_combine.
+/* The whole block ("27. Mixture of experts", section "The shared expert", SparseMoeBlock.forward:
+ * router, then the experts on their routed rows (section "Dispatch", the grouped form), then the
+ * weighted sum back into each token plus the gated shared term): moe_route (with ws) -> moe_permute -> moe_expert_ffn over the
+ * routed groups (rows gathered straight from x) -> [shared expert as one more group over all N rows]
+ * -> moe_combine. y has x's shape [N, D].
  *   shared_gate_up, shared_down: required iff cfg.shared_inter > 0; w_shared_gate may be NULL
  *     (ungated shared expert, scale 1)
  *   y [N, D] (out_dtype); weights_out [N, k] fp32 / experts_out [N, k] int32: optional copies

@@ -5,6 +5,9 @@
 // Deterministic by construction: ranks come from ordered ballots inside a wave and ordered
 // per-wave counts inside a round, never from atomics (LDS atomics only build counts, whose value
 // does not depend on order).
+// An expert id outside [0, E) (never produced by the router; possible from a caller's own ids) is
+// treated as a dropped pair: it is not counted, takes no row and gets slot_pos -1, so no index
+// derived from it reaches memory.
 // Capacity limit ("Qwen3-VL + MoE: train to deploy", section "Capacity limits"): an expert keeps
 // its first `capacity` assignments in assignment order. Counts and offsets cover the kept rows;
 // since positions are handed out in assignment order, an assignment is kept exactly when its
@@ -26,7 +29,10 @@ __global__ __launch_bounds__(kPermThreads) void perm_count_kernel(PermuteArgs a)
   __syncthreads();
   const int64_t lo = static_cast<int64_t>(blockIdx.x) * kPermChunk;
   const int64_t hi = min<int64_t>(lo + kPermChunk, a.A);
-  for (int64_t i = lo + threadIdx.x; i < hi; i += kPermThreads) atomicAdd(&s_cnt[a.experts[i]], 1);
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kPermThreads) {
+    const int e = a.experts[i];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&s_cnt[e], 1);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPermThreads) a.block_counts[blockIdx.x * static_cast<int64_t>(E) + e] = s_cnt[e];
 }
@@ -119,8 +125,10 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(PermuteArgs 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t base = lo; base < hi; base += kPermThreads) {
     const int64_t i = base + tid;
-    const bool valid = i < hi;
-    const int e = valid ? a.experts[i] : 0;
+    const int e_in = i < hi ? a.experts[i] : 0;
+    const bool in_range = static_cast<unsigned>(e_in) < static_cast<unsigned>(E);
+    const bool valid = i < hi && in_range;
+    const int e = valid ? e_in : 0;
     uint64_t m = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool set = (e >> bit) & 1;
@@ -146,6 +154,8 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(PermuteArgs 
       const bool kept = pos < s_end[e];
       if (kept) a.token_of[pos] = static_cast<int32_t>(i / a.k);
       a.slot_pos[i] = kept ? pos : -1;
+    } else if (!in_range) {
+      a.slot_pos[i] = -1;                     // an id outside [0, E): dropped
     }
   }
 }
@@ -165,7 +175,10 @@ __global__ __launch_bounds__(512) void perm_small_kernel(PermuteArgs a, int nbit
   for (int w = 0; w < 8; ++w)
     if (tid < E) s_wcnt[w][tid] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < A; i += 512) atomicAdd(&s_pos[a.experts[i]], 1);
+  for (int64_t i = tid; i < A; i += 512) {
+    const int e = a.experts[i];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&s_pos[e], 1);
+  }
   __syncthreads();
   const int total = tid < E ? static_cast<int>(min<int64_t>(s_pos[tid], a.capacity)) : 0;   // kept rows
   int inc = total;
@@ -190,8 +203,10 @@ __global__ __launch_bounds__(512) void perm_small_kernel(PermuteArgs a, int nbit
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t base = 0; base < A; base += 512) {
     const int64_t i = base + tid;
-    const bool valid = i < A;
-    const int e = valid ? a.experts[i] : 0;
+    const int e_in = i < A ? a.experts[i] : 0;
+    const bool in_range = static_cast<unsigned>(e_in) < static_cast<unsigned>(E);
+    const bool valid = i < A && in_range;
+    const int e = valid ? e_in : 0;
     uint64_t m = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool set = (e >> bit) & 1;
@@ -217,6 +232,8 @@ __global__ __launch_bounds__(512) void perm_small_kernel(PermuteArgs a, int nbit
       const bool kept = pos < s_end[e];
       if (kept) a.token_of[pos] = static_cast<int32_t>(i / a.k);
       a.slot_pos[i] = kept ? pos : -1;
+    } else if (!in_range) {
+      a.slot_pos[i] = -1;                     // an id outside [0, E): dropped
     }
   }
 }

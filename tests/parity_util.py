@@ -73,3 +73,37 @@ def oracle_layer(data: I.MoeInputs, tokens=None, routing=None):
                   w_shared_gate=data.values("w_shared_gate"))
     return O.forward_grouped(x, data.values("w_router"), data.expert_view("gate_up"), data.expert_view("down"),
                              s.top_k, s.norm_topk_prob, routing=routing, **kw)
+
+
+def check_permute_invariants(experts, counts, offsets, token_of, slot_pos, n_experts, top_k):
+    """Host-side invariants of a grouping, whatever the ids:
+      * offsets start at 0, never decrease, and their differences are the counts;
+      * the kept assignments' rows are a bijection onto [0, offsets[E]);
+      * a kept assignment's row lies in its own expert's range, and token_of of that row is its token;
+      * inside an expert, rows follow assignment order (the grouping is stable);
+      * dropped assignments (capacity, or an id outside [0, E), which is always dropped) have slot_pos -1.
+    Returns the kept assignment ids and their rows."""
+    experts = np.asarray(experts).reshape(-1).astype(np.int64)
+    counts, offsets = np.asarray(counts, np.int64), np.asarray(offsets, np.int64)
+    token_of, slot_pos = np.asarray(token_of, np.int64), np.asarray(slot_pos, np.int64)
+    A, E = experts.size, n_experts
+    assert counts.shape == (E,) and offsets.shape == (E + 1,)
+    assert offsets[0] == 0 and np.all(np.diff(offsets) >= 0), "offsets do not rise from 0"
+    assert np.array_equal(np.diff(offsets), counts), "counts are not the offset differences"
+    total = int(offsets[-1])
+    assert 0 <= total <= A
+    sp = slot_pos[:A]
+    assert np.all(sp >= -1)
+    bad = (experts < 0) | (experts >= E)
+    assert np.all(sp[bad] == -1), "an id outside [0, E) was given a row"
+    kept = sp >= 0
+    a_idx = np.nonzero(kept)[0]
+    pos = sp[kept]
+    assert np.array_equal(np.sort(pos), np.arange(total)), "kept rows are not a bijection onto [0, offsets[E])"
+    e_k = experts[kept]
+    assert np.all(pos >= offsets[e_k]) and np.all(pos < offsets[e_k + 1]), "a row outside its expert's range"
+    assert np.array_equal(token_of[pos], a_idx // top_k), "token_of does not invert slot_pos"
+    by_row = np.argsort(pos)                       # assignments in row order
+    same_e = np.diff(e_k[by_row]) == 0
+    assert np.all(np.diff(a_idx[by_row])[same_e] > 0), "rows of one expert out of assignment order"
+    return a_idx, pos

@@ -9,7 +9,7 @@ import torch
 import oracle as O
 from mixture_experts_layer_10_amd import binding as B
 from mixture_experts_layer_10_amd import inputs as I
-from parity_util import GAP, W_TOL, rel_err, to_np, y_tolerance
+from parity_util import GAP, W_TOL, check_permute_invariants, rel_err, to_np, y_tolerance
 from test_gpu_parity import data_of, say
 
 pytestmark = pytest.mark.gpu
@@ -88,6 +88,7 @@ def test_permute_capped_bit_exact(N, k, E, cap):
     B.moe_permute_capped(cfg, cap, torch.from_numpy(experts).cuda(), x, counts, offsets, token_of, slot_pos, x_perm,
                          B.alloc_workspace(cfg))
     torch.cuda.synchronize()
+    check_permute_invariants(experts, to_np(counts), to_np(offsets), to_np(token_of), to_np(slot_pos), E, k)
     c_ref, o_ref, t_ref, s_ref = oracle_capped_permute(experts, E, cap)
     assert np.array_equal(to_np(counts), c_ref)
     assert np.array_equal(to_np(offsets), o_ref)
@@ -99,6 +100,8 @@ def test_permute_capped_bit_exact(N, k, E, cap):
 
 @pytest.mark.parametrize("name,frac", [("odd", 0.5), ("keras", 0.6), ("decode", 0.8), ("odd_f32", 0.7)])
 def test_capped_layer(name, frac):
+    """The oracle's routing goes through moe_permute_capped -> moe_expert_ffn -> moe_combine (the
+    forced choice), so no expected value depends on the GPU's own routing."""
     say(f"[capped layer] {name} capacity {frac} x mean load")
     d, dev = data_of(name)
     s = d.shape
@@ -106,10 +109,10 @@ def test_capped_layer(name, frac):
     N, k, E, D, Iw = s.n_tokens, s.top_k, s.n_experts, s.hidden, s.inter
     A = N * k
     capacity = max(1, int(frac * A / E))
-    w = torch.empty((N, k), dtype=torch.float32, device="cuda")
-    e = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    _, _, w_ref, e_ref = O.route(d.values("x"), d.values("w_router"), k, s.norm_topk_prob)
+    w = torch.from_numpy(np.asarray(w_ref, np.float32)).cuda()
+    e = torch.from_numpy(np.asarray(e_ref, np.int32)).cuda()
     ws = B.alloc_workspace(cfg)
-    B.moe_route(cfg, dev["x"], dev["w_router"], None, None, w, e, None, ws)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     token_of = torch.empty(A, dtype=torch.int32, device="cuda")
@@ -121,10 +124,11 @@ def test_capped_layer(name, frac):
     y = torch.empty((N, D), dtype=torch.float32, device="cuda")
     B.moe_combine(cfg, out, w, slot_pos, None, None, y)
     torch.cuda.synchronize()
-    we, ee = to_np(w).astype(np.float64), to_np(e)
-    keep = O.capacity_keep(ee, E, capacity)
+    check_permute_invariants(e_ref, to_np(counts), to_np(offsets), to_np(token_of), to_np(slot_pos), E, k)
+    keep = O.capacity_keep(e_ref, E, capacity)
     assert (~keep).any(), "the capacity should drop something"
-    y_ref = O.forward_capacity(d.values("x"), we, ee, d.expert_view("gate_up"), d.expert_view("down"), keep)
+    y_ref = O.forward_capacity(d.values("x"), np.asarray(w_ref, np.float32).astype(np.float64), e_ref,
+                               d.expert_view("gate_up"), d.expert_view("down"), keep)
     got = to_np(y)
     assert np.isfinite(got).all()
     err = rel_err(got, y_ref)

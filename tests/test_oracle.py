@@ -303,6 +303,35 @@ def test_switch_aux_loss_closed_forms():
     assert abs(loss - E) < 1e-12
 
 
+def test_switch_aux_loss_top_k_assignments():
+    # f_e counts the N*k token-to-expert assignments, so it sums to 1 for every k and balanced
+    # top-k routing still scores 1 (reading f as a fraction of the N tokens would give k).
+    E, k = 8, 2
+    experts = np.array([[(2 * n) % E, (2 * n + 1) % E] for n in range(E)])      # each expert twice
+    probs = np.full((E, E), 1.0 / E)
+    loss, f, P = O.switch_aux_loss(probs, experts, E)
+    assert abs(f.sum() - 1.0) < 1e-15 and np.allclose(f, 1.0 / E, rtol=0, atol=1e-15)
+    assert abs(loss - 1.0) < 1e-12
+    # collapsed onto experts 0 and 1 with probability 1/2 each: E * (1/2 * 1/2 + 1/2 * 1/2) = E / 2
+    probs = np.zeros((10, E))
+    probs[:, :2] = 0.5
+    loss, f, _ = O.switch_aux_loss(probs, np.tile([0, 1], (10, 1)), E)
+    assert np.array_equal(f[:2], [0.5, 0.5]) and abs(loss - E / 2) < 1e-12
+    # brute force on a skewed k = 3 routing: the loss is E times the mean, over all N*k
+    # assignments, of the mean probability of the assignment's expert
+    rng = np.random.default_rng(31)
+    N, k, E = 9, 3, 5
+    experts = np.stack([rng.choice(E, k, replace=False) for _ in range(N)])
+    probs = rng.dirichlet(np.ones(E), size=N)
+    loss, _, _ = O.switch_aux_loss(probs, experts, E)
+    total = 0.0
+    for n in range(N):
+        for j in range(k):
+            e = int(experts[n, j])
+            total += sum(probs[m][e] for m in range(N)) / N
+    assert abs(loss - E * total / (N * k)) < 1e-12
+
+
 def test_k_gap():
     p = np.array([[0.1, 0.5, 0.3, 0.1]])
     assert O.k_gap(p, 2)[0] == pytest.approx(0.2)
