@@ -285,6 +285,24 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
                 const void* w_shared_gate, void* y, float* weights_out, int32_t* experts_out,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_forward with the same arguments minus the workspace.
+ * It calls no hipMalloc / hipFree (nor any allocating routine) and runs the kernels of moe_forward
+ * (results bitwise equal) on a scratch array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each device it runs on, from that device's first call until the process ends.
+ *   Limit: moe_workspace_bytes(cfg) must not exceed MOE_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. the
+ *     512-token, 60-expert layer of the Keras port, or decode batches of a few hundred tokens at
+ *     D = 2048, k = 8); a larger layer returns MOE_ERR_WORKSPACE before anything is enqueued.
+ *   Every call on one device shares that device's scratch, which keeps the last call's contents
+ *     (nothing in it needs clearing: each call writes what it reads). Calls that overlap on one
+ *     device (different streams, or threads without ordering) race on it: order them.
+ *   The device is the current HIP device; stream must belong to it. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up,
+                        const void* down, const void* shared_gate_up, const void* shared_down,
+                        const void* w_shared_gate, void* y, float* weights_out, int32_t* experts_out,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,9 @@ MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED, MOE_LAYOUT_Q8, MOE_LAYOUT_Q4, MOE_LAYOUT_F8 
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_pack_weights", "moe_router_stats",
             "moe_combine", "moe_forward", "moe_route_sigmoid", "moe_router_bias_update", "moe_permute_capped",
-            "moe_quantized_bytes", "moe_quantize_weights", "moe_backward_workspace_bytes", "moe_backward"]
+            "moe_quantized_bytes", "moe_quantize_weights", "moe_backward_workspace_bytes", "moe_backward",
+            "moe_forward_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20      # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -102,6 +104,7 @@ def load(path: str = LIB_PATH):
         "moe_backward_workspace_bytes": (ctypes.c_int, [_CFG, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_backward": (ctypes.c_int, [_CFG] + [_P] * 16 + [ctypes.c_size_t, _P]),
         "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "moe_forward_noalloc": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -275,6 +278,14 @@ def moe_forward(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_
                                              _ptr(shared_gate_up), _ptr(shared_down), _ptr(w_shared_gate), _ptr(y),
                                              _ptr(weights_out), _ptr(experts_out), _ptr(ws), nbytes,
                                              _stream(stream)))
+
+
+def moe_forward_noalloc(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_shared_gate, y,
+                        weights_out, experts_out, stream=None):
+    _check("moe_forward_noalloc",
+           load().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(gate_up), _ptr(down),
+                                      _ptr(shared_gate_up), _ptr(shared_down), _ptr(w_shared_gate), _ptr(y),
+                                      _ptr(weights_out), _ptr(experts_out), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------------------------

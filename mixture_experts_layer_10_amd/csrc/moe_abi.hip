@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
@@ -397,6 +398,31 @@ static GemmArgs kn_args(const void* x, const int32_t* row_index, const int32_t* 
     a.w = tmp;
   }
   return a;
+}
+
+// Scratch of moe_forward_noalloc: a fixed device array, so that the call allocates nothing. Each
+// device holds its own copy at its own address; the host-side name is only a stand-in, so its
+// device address is looked up once per device (with that device current) and kept.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(MOE_ERR_HIP, "moe_forward_noalloc: no current device");
+  if (dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "moe_forward_noalloc: device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "moe_forward_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace moe
@@ -804,11 +830,10 @@ int moe_combine(const moe_config* cfg, const float* out_perm, const float* weigh
   return ok();
 }
 
-int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
-                const void* shared_gate_up, const void* shared_down, const void* w_shared_gate, void* y,
-                float* weights_out, int32_t* experts_out, void* ws, size_t ws_bytes, void* stream) {
-  MOE_TRY(validate_config(cfg));
-  if (cfg->n_tokens == 0) return ok();
+// Argument checks of moe_forward that do not involve the workspace.
+static int forward_checks(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up,
+                          const void* down, const void* shared_gate_up, const void* shared_down,
+                          const void* w_shared_gate, void* y) {
   if (!x || !w_router || !gate_up || !down || !y) return fail(MOE_ERR_INVALID_ARG, "x, w_router, gate_up, down or y is NULL");
   MOE_TRY(check_weight_align(gate_up, "gate_up"));
   MOE_TRY(check_weight_align(down, "down"));
@@ -818,10 +843,14 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
     return fail(MOE_ERR_INVALID_ARG, "shared_inter > 0 needs shared_gate_up and shared_down");
   if (cfg->shared_inter == 0 && (shared_gate_up || shared_down || w_shared_gate))
     return fail(MOE_ERR_INVALID_ARG, "shared expert tensors given with shared_inter == 0");
-  const Layout L = layout_of(cfg);
-  if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, L.total);
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MOE_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+  return MOE_OK;
+}
 
+// The block on a checked, large-enough, 256-byte aligned workspace.
+static int forward_impl(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
+                        const void* shared_gate_up, const void* shared_down, const void* w_shared_gate, void* y,
+                        float* weights_out, int32_t* experts_out, void* ws, void* stream) {
+  const Layout L = layout_of(cfg);
   char* base = static_cast<char*>(ws);
   float* weights = weights_out ? weights_out : reinterpret_cast<float*>(base + L.weights);
   int32_t* experts = experts_out ? experts_out : reinterpret_cast<int32_t*>(base + L.experts);
@@ -855,6 +884,35 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
   }
   MOE_TRY(combine_impl(cfg, out, weights, slot_pos, sh_out, shared_scale, y, st));
   return ok();
+}
+
+int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
+                const void* shared_gate_up, const void* shared_down, const void* w_shared_gate, void* y,
+                float* weights_out, int32_t* experts_out, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (cfg->n_tokens == 0) return ok();
+  MOE_TRY(forward_checks(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_shared_gate, y));
+  const size_t need = layout_of(cfg).total;
+  if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MOE_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+  return forward_impl(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_shared_gate, y, weights_out,
+                      experts_out, ws, stream);
+}
+
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up,
+                        const void* down, const void* shared_gate_up, const void* shared_down,
+                        const void* w_shared_gate, void* y, float* weights_out, int32_t* experts_out, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (cfg->n_tokens == 0) return ok();
+  MOE_TRY(forward_checks(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_shared_gate, y));
+  const size_t need = layout_of(cfg).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "moe_forward_noalloc: this layer needs %zu bytes of scratch, above the library's "
+                "fixed %zu (use moe_forward with a caller workspace)", need, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  MOE_TRY(noalloc_scratch(&ws));
+  return forward_impl(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_shared_gate, y, weights_out,
+                      experts_out, ws, stream);
 }
 
 }  // extern "C"

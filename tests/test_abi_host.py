@@ -28,7 +28,7 @@ def header_functions():
 
 def test_header_symbols_all_exported(lib):
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -248,6 +248,20 @@ def test_forward_workspace_checks(lib):
         B.moe_forward(cs, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, FAKE,
                       B.moe_workspace_bytes(cs), stream=0)
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
+
+
+def test_forward_noalloc_refuses_before_launch(lib):
+    # the scratch limit is checked on the host: a layer needing more returns MOE_ERR_WORKSPACE
+    big = B.make_config(16384, 2048, 128, 8, 768)
+    assert B.moe_workspace_bytes(big) > B.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_noalloc(big, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, stream=0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE and "scratch" in str(ei.value)
+    c = B.make_config(64, 128, 8, 2, 64)
+    with pytest.raises(B.MoeError) as ei:                    # y missing
+        B.moe_forward_noalloc(c, FAKE, FAKE, FAKE, FAKE, None, None, None, None, None, None, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    B.moe_forward_noalloc(c.copy(n_tokens=0), None, None, None, None, None, None, None, None, None, None, stream=0)
 
 
 def test_permute_and_ffn_argument_checks(lib):
