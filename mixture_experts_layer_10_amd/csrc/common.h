@@ -165,6 +165,16 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 #endif
 }
 
+// dma16 with the non-temporal hint: for data read once (it enters L2 with the lowest priority, so a
+// stream of it does not evict lines that other workgroups still reuse).
+__device__ __forceinline__ void dma16_nt(const void* src, const void* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)lds_dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(base) : "memory");
+#endif
+}
+
 // The same for 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes land at lds_dst + 4 l, so
 // one instruction fills 256 bytes of LDS contiguously.
 __device__ __forceinline__ void dma4(const void* src, const void* lds_dst) {

@@ -26,6 +26,75 @@ namespace moe {
 
 constexpr int kRouteThreads = 256;
 
+// Partial dot product x_row . w over d = g, g + G, ... in 16-byte chunks (G lanes share a row; the
+// caller adds the G partials). Four chunks of each operand are loaded before any is used, so a
+// lane keeps eight loads in flight instead of one dependent load per element.
+template <int G>
+__device__ float row_dot_part(const void* x_row, const void* w, int D, bool bf16, int g) {
+  const bool vec = ((reinterpret_cast<uintptr_t>(x_row) | reinterpret_cast<uintptr_t>(w)) & 15) == 0;
+  float z[4] = {0.f, 0.f, 0.f, 0.f};
+  if (bf16 && vec && (D & 7) == 0) {
+    const u32x4* xv = static_cast<const u32x4*>(x_row);
+    const u32x4* wv = static_cast<const u32x4*>(w);
+    const int nc = D >> 3;
+    int c = g;
+    auto acc8 = [](float zz, u32x4 xa, u32x4 wa) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zz = fmaf(__uint_as_float(xa[i] << 16), __uint_as_float(wa[i] << 16), zz);
+        zz = fmaf(__uint_as_float(xa[i] & 0xffff0000u), __uint_as_float(wa[i] & 0xffff0000u), zz);
+      }
+      return zz;
+    };
+    for (; c + 3 * G < nc; c += 4 * G) {
+      u32x4 xa[4], wa[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xa[u] = xv[c + u * G];
+        wa[u] = wv[c + u * G];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) z[u] = acc8(z[u], xa[u], wa[u]);
+    }
+    for (; c < nc; c += G) z[0] = acc8(z[0], xv[c], wv[c]);
+  } else if (!bf16 && vec && (D & 3) == 0) {
+    const f32x4* xv = static_cast<const f32x4*>(x_row);
+    const f32x4* wv = static_cast<const f32x4*>(w);
+    const int nc = D >> 2;
+    int c = g;
+    for (; c + 3 * G < nc; c += 4 * G) {
+      f32x4 xa[4], wa[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xa[u] = xv[c + u * G];
+        wa[u] = wv[c + u * G];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[u] = fmaf(xa[u][i], wa[u][i], z[u]);
+    }
+    for (; c < nc; c += G) {
+      const f32x4 xa = xv[c], wa = wv[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[0] = fmaf(xa[i], wa[i], z[0]);
+    }
+  } else if (bf16) {
+    const uint16_t* xr = static_cast<const uint16_t*>(x_row);
+    const uint16_t* ws = static_cast<const uint16_t*>(w);
+    for (int d = g; d < D; d += G) z[0] = fmaf(bf16_to_f32(xr[d]), bf16_to_f32(ws[d]), z[0]);
+  } else {
+    const float* xr = static_cast<const float*>(x_row);
+    const float* ws = static_cast<const float*>(w);
+    for (int d = g; d < D; d += G) z[0] = fmaf(xr[d], ws[d], z[0]);
+  }
+  return (z[0] + z[1]) + (z[2] + z[3]);
+}
+
+__device__ __forceinline__ const void* x_row_of(const RouteArgs& a, int64_t n) {
+  return static_cast<const char*>(a.x) + n * a.D * (a.bf16 ? 2 : 4);
+}
+
 // Softmax, top-k and outputs for token rows [0, n_rows) of a workgroup whose logits sit in
 // s_logit[t * cols + e]. sel_p / sel_e: per-wave scratch of 512 entries each. A lane holds
 // experts lane + 64 j, j < 2 EP (E <= 128 EP).
@@ -98,16 +167,7 @@ __device__ void route_select(const RouteArgs& a, const float* s_logit, int cols,
       a.experts[n * k + r] = sel_e[r];
     }
     if (a.w_shared_gate) {
-      float z = 0.f;
-      if (a.bf16) {
-        const uint16_t* xr = static_cast<const uint16_t*>(a.x) + n * D;
-        const uint16_t* ws = static_cast<const uint16_t*>(a.w_shared_gate);
-        for (int d = lane; d < D; d += kWave) z = fmaf(bf16_to_f32(xr[d]), bf16_to_f32(ws[d]), z);
-      } else {
-        const float* xr = static_cast<const float*>(a.x) + n * D;
-        const float* ws = static_cast<const float*>(a.w_shared_gate);
-        for (int d = lane; d < D; d += kWave) z = fmaf(xr[d], ws[d], z);
-      }
+      float z = row_dot_part<kWave>(x_row_of(a, n), a.w_shared_gate, D, a.bf16, lane);
       z = wave_sum_dpp(z);
       if (lane == 0) a.shared_scale[n] = 1.f / (1.f + expf(-z));
     }
@@ -236,18 +296,7 @@ __device__ void route_select16(const RouteArgs& a, const float* s_logit, int col
     }
     if (a.w_shared_gate) {                                         // 16 lanes per token
       float z = 0.f;
-      if (valid) {
-        const int64_t n = n0 + t;
-        if (a.bf16) {
-          const uint16_t* xr = static_cast<const uint16_t*>(a.x) + n * D;
-          const uint16_t* ws = static_cast<const uint16_t*>(a.w_shared_gate);
-          for (int d = j; d < D; d += 16) z = fmaf(bf16_to_f32(xr[d]), bf16_to_f32(ws[d]), z);
-        } else {
-          const float* xr = static_cast<const float*>(a.x) + n * D;
-          const float* ws = static_cast<const float*>(a.w_shared_gate);
-          for (int d = j; d < D; d += 16) z = fmaf(xr[d], ws[d], z);
-        }
-      }
+      if (valid) z = row_dot_part<16>(x_row_of(a, n0 + t), a.w_shared_gate, D, a.bf16, j);
       z += xor16f<1>(z);
       z += xor16f<2>(z);
       z += xor16f<4>(z);
@@ -501,6 +550,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_stream_kernel(RouteArgs a
 // Eight waves: wave w takes expert blocks (w % 4) + 4 b over half h = w / 4 of the contraction;
 // the halves are added in the order h = 0 + h = 1. LDS: 16-byte chunk c of row r sits at
 // c ^ (r & 15), so the 16 rows one ds_read_b128 serves together hit 16 distinct bank slots.
+// Long batches: the shared-expert gate of each token of the x tile, from the tile in LDS (chunk c
+// of row r at c ^ (r & 15)) and w_s in 16-byte chunks; one wave per token. Called while every wave
+// still reads the tile.
+__device__ void xs_shared_gate(const RouteArgs& a, const uint16_t* sX, int64_t n0, int n_rows, int nw) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, D = a.D, nc = D >> 3;
+  const u32x4* ws = static_cast<const u32x4*>(a.w_shared_gate);
+  for (int t = wave; t < n_rows; t += nw) {
+    float z[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = lane; c0 < nc; c0 += 4 * kWave) {
+      u32x4 xa[4], wa[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = min(c0 + u * kWave, nc - 1);
+        xa[u] = *reinterpret_cast<const u32x4*>(&sX[t * D + ((c ^ (t & 15)) << 3)]);
+        wa[u] = ws[c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (c0 + u * kWave >= nc) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[u] = fmaf(__uint_as_float(xa[u][i] << 16), __uint_as_float(wa[u][i] << 16), z[u]);
+          z[u] = fmaf(__uint_as_float(xa[u][i] & 0xffff0000u), __uint_as_float(wa[u][i] & 0xffff0000u), z[u]);
+        }
+      }
+    }
+    const float zz = wave_sum_dpp((z[0] + z[1]) + (z[2] + z[3]));
+    if (lane == 0) a.shared_scale[n0 + t] = 1.f / (1.f + expf(-zz));
+  }
+}
+
 constexpr int kXsMaxD = 2048;
 constexpr int kXsThreads = 512;
 
@@ -524,7 +604,7 @@ __global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
   for (int i = wave; i < kRtTok * IPR; i += kXsThreads / 64) {
     const int r = i / IPR, q = i - r * IPR;
     const int64_t n = min<int64_t>(n0 + r, a.N - 1);
-    dma16(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
+    dma16_nt(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
   }
   // weight rows of this wave's blocks; lane: row lane % 32, k-group lane / 32; k from kh * D / 2
   const int ks0 = kh * (D / 32);                            // first 16-wide k-step of this half
@@ -575,6 +655,9 @@ __global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
     if (q + 2 < full) loadw(0, (q + 2) * U);
     math(1, (q + 1) * U);
   }
+  const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
+  const bool gate_here = a.w_shared_gate && (reinterpret_cast<uintptr_t>(a.w_shared_gate) & 15) == 0;
+  if (gate_here) xs_shared_gate(a, sX, n0, n_rows, kXsThreads / 64);
   __syncthreads();                                          // every wave is done reading the x tile
   float* hi = reinterpret_cast<float*>(sX);
   if (kh == 1) {
@@ -603,8 +686,9 @@ __global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
-  select_tokens<EP>(a, s_logit, EPAD, n0, n_rows, s_selp, s_sele, kXsThreads / 64);
+  RouteArgs sel = a;
+  if (gate_here) sel.w_shared_gate = nullptr;               // the gate is done
+  select_tokens<EP>(sel, s_logit, EPAD, n0, n_rows, s_selp, s_sele, kXsThreads / 64);
 }
 
 // E <= 128: the same x tile with 16x16x32 matrix-core steps. Wave w owns experts 16 w .. + 15
@@ -625,7 +709,7 @@ __global__ __launch_bounds__(kXsThreads) void route_xs16_kernel(RouteArgs a) {
   for (int i = wave; i < kRtTok * IPR; i += kXsThreads / 64) {
     const int r = i / IPR, q = i - r * IPR;
     const int64_t n = min<int64_t>(n0 + r, a.N - 1);
-    dma16(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
+    dma16_nt(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
   }
   const bool active = wave * 16 < E;                        // uniform
   // packed weights: block (wave, s) is this wave's 16 rows at k-step s, 1 KB in lane order
@@ -660,6 +744,9 @@ __global__ __launch_bounds__(kXsThreads) void route_xs16_kernel(RouteArgs a) {
     if (q + 2 < full) loadw(0, (q + 2) * U);
     math(1, (q + 1) * U);
   }
+  const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
+  const bool gate_here = a.w_shared_gate && (reinterpret_cast<uintptr_t>(a.w_shared_gate) & 15) == 0;
+  if (gate_here) xs_shared_gate(a, sX, n0, n_rows, kXsThreads / 64);
   __syncthreads();                                          // every wave is done reading the x tile
   float* s_logit = reinterpret_cast<float*>(sX);            // [kRtTok][EPAD]
   if (active) {
@@ -669,8 +756,9 @@ __global__ __launch_bounds__(kXsThreads) void route_xs16_kernel(RouteArgs a) {
       for (int i = 0; i < 4; ++i) s_logit[(tb * 16 + 4 * (lane >> 4) + i) * EPAD + wave * 16 + (lane & 15)] = acc[tb][i];
   }
   __syncthreads();
-  const int n_rows = static_cast<int>(min<int64_t>(kRtTok, a.N - n0));
-  route_select16<1>(a, s_logit, EPAD, n0, n_rows, kXsThreads / 64);
+  RouteArgs sel = a;
+  if (gate_here) sel.w_shared_gate = nullptr;               // the gate is done
+  route_select16<1>(sel, s_logit, EPAD, n0, n_rows, kXsThreads / 64);
 }
 
 // Long bf16 batches with a suitable width take the x-stationary kernel (one workgroup per CU, so
