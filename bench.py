@@ -7,15 +7,20 @@ synthetic tokens already resident in HBM.
 Prints ONE JSON line. `value` is whole-layer tokens/s on the headline workload (the 16,384-token
 Qwen3-VL-30B-A3B prefill layer). `roofline` reports the grouped gate_up GEMM (the dominant kernel),
 timed with events on its launch stream inside the timed steps. `decode` adds the 64-token decode
-layer (weight-read bound). `quantized_experts` repeats both with int8, int4 and fp8 expert weights
-(one scale per weight row). `backward` times moe_backward on both workloads. `cpu_baseline` times
-the CPU oracle on a bounded token sample.
+layer (weight-read bound). `configs` reports every workload (tiny, keras, decode, prefill, fanout):
+per-step GPU time (median, p10, p90), tokens/s, TFLOP/s, GB/s, the binding roofline and its
+fraction, and the CPU oracle's tokens/s on all host threads and on one. `ceilings` holds the
+measured read rate and register-only matrix-core rate of this machine beside the published peaks.
+`quantized_experts` repeats prefill and decode with int8, int4 and fp8 expert weights (one scale per
+weight row). `backward` times moe_backward on both workloads. `cpu_baseline` times the CPU oracle
+on a bounded token sample of the headline workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -28,6 +33,7 @@ import numpy as np  # noqa: E402
 METRIC = "MoE-layer tokens/s; % bf16 MFMA peak (prefill), % HBM GB/s (decode)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector (the fp32 layer's FMA kernels)
 
 
 def log(msg):
@@ -187,7 +193,8 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, da
     alg = algorithmic(shape, touched, {2: 8, 3: 4, 4: 8}.get(cfg.weight_layout))
     log(f"[bench] {name}: {ms_per_step:.3f} ms/step (gpu {gpu_ms / steps:.3f}), gate_up {gate_up_ms:.3f} ms, "
         f"touched {touched}/{shape.n_experts}")
-    return dict(shape=shape, data=data, cfg=cfg, stats=stats, variants=variants, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
+    return dict(shape=shape, data=data, cfg=cfg, chain=chain, stats=stats, variants=variants, ms_per_step=ms_per_step,
+                gpu_ms_per_step=gpu_ms / steps,
                 y=y_ref.float().cpu().numpy(),
                 gate_up_ms=gate_up_ms, touched=touched, counts=counts, alg=alg,
                 tokens_per_s=shape.n_tokens / (ms_per_step / 1e3))
@@ -258,6 +265,145 @@ def time_backward(base, steps, warmup):
             "workspace_bytes": int(ws.numel()), "weight_layout": "rows"}
 
 
+def step_stats(chain, samples, per):
+    """GPU time per step over `samples` event-bracketed blocks of `per` back-to-back steps (blocks,
+    so that at decode sizes the events' own idle time is spread over several steps): median, p10
+    and p90 in ms."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    chain.step()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        for _ in range(per):
+            chain.step()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) / per for a, b in ev])
+    return {"median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
+            "p90": round(float(np.percentile(t, 90)), 4), "samples": samples, "steps_per_sample": per}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_oracle_rates(data, runs, one_thread_s=4.0):
+    """The CPU oracle (grouped form, fp64) on this workload: all host BLAS threads over every token
+    (median of `runs` runs), and one thread over a seeded token sample sized to about one_thread_s
+    seconds. Returns tokens/s for both and what each timed."""
+    import oracle as O
+    s = data.shape
+    w_router, gate_up, down = data.values("w_router"), data.values("gate_up"), data.values("down")   # converted outside the timing
+    kw = {}
+    if s.shared_inter:
+        kw = dict(shared_gate_up=data.values("shared_gate_up"), shared_down=data.values("shared_down"),
+                  w_shared_gate=data.values("w_shared_gate") if s.shared_gated else None)
+
+    def run(toks):
+        x = data.token_rows(toks)
+        t0 = time.perf_counter()
+        O.forward_grouped(x, w_router, gate_up, down, s.top_k, s.norm_topk_prob, **kw)
+        return time.perf_counter() - t0
+
+    all_toks = np.arange(s.n_tokens)
+    t_all = float(np.median([run(all_toks) for _ in range(runs)]))
+    rng = np.random.default_rng(0)
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:
+        limiter = None
+    try:
+        n = min(16, s.n_tokens)
+        dt = run(np.sort(rng.choice(s.n_tokens, n, replace=False)))
+        n1 = int(min(s.n_tokens, max(n, n * one_thread_s / max(dt, 1e-4))))
+        t1 = run(np.sort(rng.choice(s.n_tokens, n1, replace=False)))
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    return {"tokens_per_s": round(s.n_tokens / t_all, 1), "threads": blas_threads(), "runs": runs,
+            "tokens_per_s_1thread": round(n1 / t1, 1), "sample_1thread": f"{n1} of {s.n_tokens} tokens"}
+
+
+def summarize_config(run, stats, cpu):
+    """One workload's line of the configs block: rates at the median step time and the binding
+    roofline (the larger of FLOPs / peak and bytes / HBM bandwidth, over the measured time)."""
+    alg, sh = run["alg"], run["shape"]
+    t = stats["median"] / 1e3
+    peak = PEAK_FP32_TFLOPS if sh.dtype == "f32" else PEAK_BF16_TFLOPS
+    t_flop, t_byte = alg["flops"] / (peak * 1e12), alg["bytes"] / (PEAK_HBM_GBS * 1e9)
+    return {"shape": {"n_tokens": sh.n_tokens, "hidden": sh.hidden, "n_experts": sh.n_experts, "top_k": sh.top_k,
+                      "inter": sh.inter, "shared_inter": sh.shared_inter, "dtype": sh.dtype},
+            "weight_layout": LAYOUT_NAMES[run["cfg"].weight_layout],
+            "ms_per_step": stats, "ms_per_step_wall_mean": round(run["ms_per_step"], 4),
+            "tokens_per_s": round(sh.n_tokens / t, 1),
+            "tflops": round(alg["flops"] / t / 1e12, 3), "alg_gbs": round(alg["bytes"] / t / 1e9, 1),
+            "alg_flops": alg["flops"], "alg_bytes": alg["bytes"],
+            "compute_peak_tflops": peak, "compute_frac": round(t_flop / t, 4), "hbm_frac": round(t_byte / t, 4),
+            "bound": ("mfma" if sh.dtype == "bf16" else "fp32 alu") if t_flop >= t_byte else "hbm",
+            "roofline_frac": round(max(t_flop, t_byte) / t, 4),
+            "experts_touched": run["touched"], "max_rows_per_expert": int(run["counts"].max()),
+            "cpu_oracle": cpu}
+
+
+def measured_ceilings():
+    """Read rate of a streaming kernel over 4 GiB and the register-only bf16 matrix-core rate."""
+    import ctypes
+    import torch
+    from mixture_experts_layer_10_amd import build as BUILD
+    lib = ctypes.CDLL(BUILD.PROBE_PATH)
+    lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    st = torch.cuda.current_stream().cuda_stream
+    nbytes, grid = 4 << 30, 1024
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4 * grid, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / 1e3)
+        return float(np.median(out))
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+
+    t_read = timed(lambda: check(lib.probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, st)))
+    iters = 20000
+    t_mfma = timed(lambda: check(lib.probe_mfma(sink.data_ptr(), iters, grid, st)))
+    flops = grid * 4 * 4 * iters * 32 * 32 * 16 * 2
+    del buf
+    return {"read_gbs": round(nbytes / t_read / 1e9, 1), "read_frac_of_peak": round(nbytes / t_read / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1),
+            "mfma_frac_of_peak": round(flops / t_mfma / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "what": "probe/ceilings.hip: 16-byte nontemporal reads of 4 GiB, 1,024 workgroups; 32x32x16 bf16 "
+                    "matrix-core steps on register operands, four chains per wave, 16 waves per CU"}
+
+
 def cpu_baseline(data, target_s=15.0):
     """The CPU oracle (grouped form, fp64) on a seeded token sample of the same workload."""
     import oracle as O
@@ -298,6 +444,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant", action="store_true", help="skip the int8 / int4 expert runs")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload configs block")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured read / matrix-core ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy a 256 MiB buffer once (a kernel of known traffic for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -357,6 +505,8 @@ def main():
         "router_stats": main_run["stats"],
         "routing_variants": main_run["variants"],
     }
+    out["ms_per_step_gpu"] = step_stats(main_run["chain"], args.steps, 1)
+    dec = None
     if not args.no_decode and args.workload != "decode":
         dec = run_workload("decode", max(args.steps, 50), args.warmup, args.out_dtype, inner_events=False)
         ds = dec["ms_per_step"] / 1e3
@@ -373,6 +523,29 @@ def main():
             out["backward"] = {"prefill": time_backward(main_run, args.steps, args.warmup),
                                "decode": time_backward(dec, max(args.steps, 50), args.warmup)}
             log(f"[bench] backward: {out['backward']}")
+    if not args.no_configs:
+        configs = {}
+        for wl in ("tiny", "keras", "decode", "prefill", "fanout"):
+            if wl == args.workload:
+                r = main_run
+            elif wl == "decode" and dec is not None:
+                r = dec
+            else:
+                r = run_workload(wl, args.steps, args.warmup, args.out_dtype, inner_events=False, extras=False)
+            small = r["shape"].n_tokens * r["shape"].top_k <= 8192
+            st = step_stats(r["chain"], 20, 10 if small else 1)
+            cpu = None if args.no_cpu_baseline else cpu_oracle_rates(r["data"], 1 if wl == "prefill" else 3)
+            configs[wl] = summarize_config(r, st, cpu)
+            log(f"[bench] config {wl}: {configs[wl]['ms_per_step']} ms, {configs[wl]['bound']} "
+                f"{configs[wl]['roofline_frac']}, cpu {cpu}")
+            if r is not main_run and r is not dec:
+                del r
+        out["configs"] = configs
+        if not args.no_cpu_baseline:
+            out["cpu_model"] = cpu_model()
+    if not args.no_ceilings:
+        out["ceilings"] = measured_ceilings()
+        log(f"[bench] ceilings: {out['ceilings']}")
     if args.copy_calibration:
         src = torch.ones(64 * 2**20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

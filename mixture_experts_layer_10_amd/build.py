@@ -3,7 +3,8 @@
     python -m mixture_experts_layer_10_amd.build [--jobs N]
 
 Every .hip file under csrc/ is compiled separately with hipcc (parallel), then linked into one
-shared library exporting the C ABI declared in include/moe.h.
+shared library exporting the C ABI declared in include/moe.h. probe/ceilings.hip (the benchmark's
+measured read and matrix-core ceilings, not part of the ABI) becomes _lib/libmoe_probe.so.
 """
 from __future__ import annotations
 
@@ -21,6 +22,8 @@ OUT_DIR = os.path.join(PKG, "_lib")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(OUT_DIR, LIB_NAME)
+PROBE_SRC = os.path.join(PKG, "probe", "ceilings.hip")
+PROBE_PATH = os.path.join(OUT_DIR, "libmoe_probe.so")
 
 ARCH = "gfx950"
 HIP_FLAGS = [
@@ -64,8 +67,15 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    # the measured-ceiling probes of the benchmark: a small library of their own
+    ptmp = PROBE_PATH + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-o", ptmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(ptmp, PROBE_PATH)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources")
+        print(f"built {LIB_PATH} from {len(srcs)} sources, and {PROBE_PATH}")
     return LIB_PATH
 
 
