@@ -133,13 +133,18 @@ def time_variants(B, chain, cfg, dev, steps):
 LAYOUT_NAMES = {0: "rows", 1: "packed", 2: "int8", 3: "int4", 4: "fp8"}
 
 
-def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, data=None, extras=True):
+EXPERT_OUT = {"f32": 0, "f16s": 1}
+
+
+def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, data=None, extras=True, expert_out="f16s"):
     """Times `steps` whole-path steps. With inner_events the gate_up launch of every timed step is
     bracketed by events on its stream (its duration comes from the timed region itself); without,
     the timed steps carry no events (a recorded event idles the GPU for a few microseconds, which
     matters at decode sizes) and the gate_up duration comes from a second run of `steps` steps.
     layout: 1 packed bf16 experts (rows if the shape cannot be packed), 2 / 3 / 4 int8 / int4 / fp8
-    experts."""
+    experts. expert_out: "f16s" keeps the per-assignment expert outputs as fp16 values with a
+    power-of-two exponent per 16 columns where the layer allows it (bf16 rows or packed weights,
+    D % 16 == 0), else fp32; "f32" always fp32."""
     import torch
     from mixture_experts_layer_10_amd import binding as B
     from mixture_experts_layer_10_amd import inputs as I
@@ -159,8 +164,10 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, da
         torch.cuda.synchronize()
     else:
         cfg = B.config_for(shape, out_dtype)
+    if EXPERT_OUT[expert_out] and B.f16s_supported(cfg):
+        cfg = cfg.copy(expert_out=B.MOE_EXPERT_OUT_F16S)
     log(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s (weight layout "
-        f"{LAYOUT_NAMES[cfg.weight_layout]})")
+        f"{LAYOUT_NAMES[cfg.weight_layout]}, expert outputs {'f16s' if cfg.expert_out else 'f32'})")
     chain = Chain(cfg, dev)
     y_ref = B.forward(cfg, dev)
     for _ in range(warmup):
@@ -351,6 +358,7 @@ def summarize_config(run, stats, cpu):
     return {"shape": {"n_tokens": sh.n_tokens, "hidden": sh.hidden, "n_experts": sh.n_experts, "top_k": sh.top_k,
                       "inter": sh.inter, "shared_inter": sh.shared_inter, "dtype": sh.dtype},
             "weight_layout": LAYOUT_NAMES[run["cfg"].weight_layout],
+            "expert_out": "f16s" if run["cfg"].expert_out else "f32",
             "ms_per_step": stats, "ms_per_step_wall_mean": round(run["ms_per_step"], 4),
             "tokens_per_s": round(sh.n_tokens / t, 1),
             "tflops": round(alg["flops"] / t / 1e12, 3), "alg_gbs": round(alg["bytes"] / t / 1e9, 1),
@@ -444,6 +452,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant", action="store_true", help="skip the int8 / int4 expert runs")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--expert-out", default="f16s", choices=sorted(EXPERT_OUT),
+                    help="form of the per-assignment expert outputs (f16s where the layer allows it)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload configs block")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured read / matrix-core ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -457,7 +467,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    main_run = run_workload(args.workload, args.steps, args.warmup, args.out_dtype)
+    main_run = run_workload(args.workload, args.steps, args.warmup, args.out_dtype, expert_out=args.expert_out)
     shape, alg = main_run["shape"], main_run["alg"]
     gemm_s = main_run["gate_up_ms"] / 1e3
     prefill_like = alg["gate_up_flops"] / alg["gate_up_bytes"] > 500
@@ -494,6 +504,7 @@ def main():
                    "shared_inter": shape.shared_inter, "norm_topk_prob": shape.norm_topk_prob,
                    "zipf_s": shape.zipf_s, "out_dtype": args.out_dtype, "seed": shape.seed,
                    "weight_layout": "packed" if main_run["cfg"].weight_layout else "rows",
+                   "expert_out": "f16s" if main_run["cfg"].expert_out else "f32",
                    "parallelism": "none (1 GPU)"},
         "layer": {"tflops": round(alg["flops"] / layer_s / 1e12, 2),
                   "mfma_frac": round(alg["flops"] / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -508,7 +519,8 @@ def main():
     out["ms_per_step_gpu"] = step_stats(main_run["chain"], args.steps, 1)
     dec = None
     if not args.no_decode and args.workload != "decode":
-        dec = run_workload("decode", max(args.steps, 50), args.warmup, args.out_dtype, inner_events=False)
+        dec = run_workload("decode", max(args.steps, 50), args.warmup, args.out_dtype, inner_events=False,
+                           expert_out=args.expert_out)
         ds = dec["ms_per_step"] / 1e3
         out["decode"] = {"workload": "decode", "tokens_per_s": round(dec["tokens_per_s"], 1),
                          "ms_per_step": round(dec["ms_per_step"], 4),
@@ -531,7 +543,8 @@ def main():
             elif wl == "decode" and dec is not None:
                 r = dec
             else:
-                r = run_workload(wl, args.steps, args.warmup, args.out_dtype, inner_events=False, extras=False)
+                r = run_workload(wl, args.steps, args.warmup, args.out_dtype, inner_events=False, extras=False,
+                                 expert_out=args.expert_out)
             small = r["shape"].n_tokens * r["shape"].top_k <= 8192
             st = step_stats(r["chain"], 20, 10 if small else 1)
             cpu = None if args.no_cpu_baseline else cpu_oracle_rates(r["data"], 1 if wl == "prefill" else 3)

@@ -47,6 +47,19 @@
  * layer then computes with the weights code * scale (for FP8, the e4m3 value of the code times the
  * scale): the codes enter the matrix cores exactly (as bf16) and each output column's fp32 sum is
  * multiplied by its row's scale.
+ *
+ * Expert outputs (moe_config.expert_out): the per-assignment outputs out[p, :] that the down
+ * projection writes and moe_combine weights and sums ("27. Mixture of experts", section "Dispatch",
+ * grouped steps 3-4). MOE_EXPERT_OUT_F32 (0): fp32 rows [rows, D]. MOE_EXPERT_OUT_F16S (1): each
+ * row is D fp16 values followed by D / 16 int8 exponents, padded to a multiple of 16 bytes:
+ *   row stride S = round_up(2 D + D / 16, 16) bytes; value of column c = fp16[c] * 2^exp[c / 16];
+ *   exp of a 16-column group = clamp(floor(log2 m) - 14, -128, 127) for the group's largest |v| = m
+ *   (0 when m = 0), so every scaled value is below 2^15 (at most 2^15 once rounded) and in range;
+ *   fp16[c] = v * 2^-exp rounded to nearest, ties to even (the only rounding: 2^-11 relative,
+ *   against 2^-8 for a bf16 output). Non-finite outputs are not supported (inputs are finite).
+ * It halves the bytes the down projection writes and moe_combine reads. bf16 layers with D % 16 == 0
+ * and weight_layout MOE_LAYOUT_ROWS or MOE_LAYOUT_PACKED only (else MOE_ERR_UNSUPPORTED). An
+ * expert-output buffer sized [rows, D] fp32 holds either form (S <= 4 D).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -72,6 +85,8 @@ typedef enum {
   MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_PACKED = 1, MOE_LAYOUT_Q8 = 2, MOE_LAYOUT_Q4 = 3, MOE_LAYOUT_F8 = 4
 } moe_weight_layout;
 
+typedef enum { MOE_EXPERT_OUT_F32 = 0, MOE_EXPERT_OUT_F16S = 1 } moe_expert_out;
+
 /* Shape and options of one MoE layer. Refuses, never defaults: every field must be set
  * (the config-ingestion lesson of "27. Mixture of experts", section "Qwen3-MoE", Note). */
 typedef struct {
@@ -86,6 +101,7 @@ typedef struct {
   int32_t out_dtype;      /* moe_dtype of y                                                   */
   int32_t weight_layout;  /* moe_weight_layout of the weights (see "Packed weights" and
                              "Quantised experts" above)                                       */
+  int32_t expert_out;     /* moe_expert_out: form of the expert outputs (see "Expert outputs") */
 } moe_config;
 
 /* Human-readable name of a status code. Never NULL. */
@@ -167,7 +183,8 @@ int moe_permute_capped(const moe_config* cfg, int64_t capacity, const int32_t* e
  *   offsets [G+1] int32 on device, offsets[0] == 0 and non-decreasing, or NULL for one group of
  *     max_rows rows
  *   gate_up [G, 2I, D], down [G, D, I] (dtype)
- *   h [max_rows, I] (dtype; bf16 when dtype is bf16, the matrix-core input), out [max_rows, D] fp32
+ *   h [max_rows, I] (dtype; bf16 when dtype is bf16, the matrix-core input), out: max_rows expert-
+ *   output rows in the form cfg.expert_out selects ([max_rows, D] fp32, or rows of S bytes)
  * Accumulation is fp32; with bf16 the SwiGLU product is rounded to bf16 once (the second GEMM's
  * input). Rows at or past offsets[G] are left untouched. */
 int moe_expert_gate_up(const moe_config* cfg, int64_t n_groups, int64_t inter, int64_t max_rows,
@@ -264,8 +281,11 @@ int moe_router_stats(const moe_config* cfg, const float* logits, const int32_t* 
  *                                  (+ shared_scale[n] * shared_out[n]),
  * summed in fp32 in slot order j = 0..k-1, then the shared term, rounded once to out_dtype.
  * A gather per token (no atomics): deterministic.
- *   out_perm [N*k, D] fp32, weights [N, k] fp32, slot_pos [N*k] int32 (-1: a dropped pair, skipped)
- *   shared_out [N, D] fp32 or NULL; shared_scale [N] fp32 or NULL (NULL with shared_out: scale 1)
+ *   out_perm: N*k expert-output rows in the form cfg.expert_out selects ([N*k, D] fp32 or rows of
+ *     S bytes, see "Expert outputs"), weights [N, k] fp32, slot_pos [N*k] int32 (-1: a dropped pair,
+ *     skipped)
+ *   shared_out: N rows in the same form, or NULL; shared_scale [N] fp32 or NULL (NULL with
+ *     shared_out: scale 1)
  *   y [N, D] (out_dtype) */
 int moe_combine(const moe_config* cfg, const float* out_perm, const float* weights,
                 const int32_t* slot_pos, const float* shared_out, const float* shared_scale, void* y,

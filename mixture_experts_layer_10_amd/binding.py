@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG, "_lib", "libmoe_mi355x.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED, MOE_LAYOUT_Q8, MOE_LAYOUT_Q4, MOE_LAYOUT_F8 = 0, 1, 2, 3, 4
+MOE_EXPERT_OUT_F32, MOE_EXPERT_OUT_F16S = 0, 1
 
 # Every symbol include/moe.h declares.
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
@@ -40,7 +41,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("n_experts", ctypes.c_int64),
                 ("top_k", ctypes.c_int64), ("inter", ctypes.c_int64), ("shared_inter", ctypes.c_int64),
                 ("norm_topk_prob", ctypes.c_int32), ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("expert_out", ctypes.c_int32)]
 
     def copy(self, **kw):
         c = MoeConfig()
@@ -50,19 +51,25 @@ class MoeConfig(ctypes.Structure):
 
 
 def make_config(n_tokens, hidden, n_experts, top_k, inter, shared_inter=0, norm_topk_prob=True,
-                dtype="bf16", out_dtype=None, packed=False, layout=None) -> MoeConfig:
-    """layout: a MOE_LAYOUT_* value; default rows, or packed when ``packed``."""
+                dtype="bf16", out_dtype=None, packed=False, layout=None, expert_out=MOE_EXPERT_OUT_F32) -> MoeConfig:
+    """layout: a MOE_LAYOUT_* value; default rows, or packed when ``packed``. expert_out: a
+    MOE_EXPERT_OUT_* value (the form of the per-assignment expert outputs)."""
     dt = {"bf16": MOE_BF16, "f32": MOE_F32}
     if layout is None:
         layout = MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_ROWS
     return MoeConfig(n_tokens, hidden, n_experts, top_k, inter, shared_inter, int(bool(norm_topk_prob)),
-                     dt[dtype], dt[out_dtype or dtype], layout)
+                     dt[dtype], dt[out_dtype or dtype], layout, expert_out)
 
 
-def config_for(shape, out_dtype=None, packed=False, layout=None) -> MoeConfig:
+def config_for(shape, out_dtype=None, packed=False, layout=None, expert_out=MOE_EXPERT_OUT_F32) -> MoeConfig:
     """MoeConfig for an inputs.MoeShape."""
     return make_config(shape.n_tokens, shape.hidden, shape.n_experts, shape.top_k, shape.inter,
-                       shape.shared_inter, shape.norm_topk_prob, shape.dtype, out_dtype, packed, layout)
+                       shape.shared_inter, shape.norm_topk_prob, shape.dtype, out_dtype, packed, layout, expert_out)
+
+
+def f16s_supported(cfg: MoeConfig) -> bool:
+    """Whether MOE_EXPERT_OUT_F16S applies (bf16, D % 16 == 0, row or packed bf16 weights)."""
+    return cfg.dtype == MOE_BF16 and cfg.hidden % 16 == 0 and cfg.weight_layout in (MOE_LAYOUT_ROWS, MOE_LAYOUT_PACKED)
 
 
 def packable(cfg: MoeConfig) -> bool:

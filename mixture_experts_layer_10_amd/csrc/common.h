@@ -215,6 +215,28 @@ __device__ __forceinline__ u32x4 codesf8_to_bf16(u32x2 c) {
   return r;
 }
 
+// fp16 form of expert outputs: the exponent of a 16-column group whose largest magnitude is m:
+// floor(log2 m) - 14 (so every value scaled by 2^-exp is below 2^15), at least -128; 0 when m is
+// zero or not finite.
+__device__ __forceinline__ int f16s_exp(float m) {
+  const int be = static_cast<int>((__float_as_uint(m) >> 23) & 0xff);   // m >= 0
+  if (m == 0.f || be == 0xff) return 0;
+  return max(be - 127 - 14, -128);
+}
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// v * 2^-e rounded to fp16 (nearest, ties to even), two at a time
+__device__ __forceinline__ uint32_t pack_f16x2_scaled(float a, float b, int e) {
+  const f16x2 v = {static_cast<_Float16>(ldexpf(a, -e)), static_cast<_Float16>(ldexpf(b, -e))};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f16_scaled(float a, int e) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(ldexpf(a, -e)));
+}
+// the value of an fp16 code (bits) with exponent e, exactly
+__device__ __forceinline__ float f16_unscale(uint16_t bits, int e) {
+  return ldexpf(static_cast<float>(__builtin_bit_cast(_Float16, bits)), e);
+}
+
 // s_waitcnt immediate for vmcnt(n) alone (bits 3:0 and 15:14; expcnt and lgkmcnt at "no wait").
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 

@@ -317,6 +317,32 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs a) {
             }
           }
       }
+    } else if (a.out_f16s) {
+      // fp16 form: the 16 lanes of a DPP row hold 16 consecutive columns of one output row
+      // (NOUT % 16 == 0, so a group is wholly in or out)
+      const int64_t rb = f16s_row_bytes(NOUT);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = c0 + (wn * TN + j) * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float v = acc[i][j][e];
+            float m = fabsf(v);
+            m = fmaxf(m, xor16f<1>(m));
+            m = fmaxf(m, xor16f<2>(m));
+            m = fmaxf(m, xor16f<4>(m));
+            m = fmaxf(m, xor16f<8>(m));
+            const int ex = f16s_exp(m);
+            const int rr = m0 + (wm * TM + i) * 32 + acc_row(e, lane);
+            if (col < NOUT && rr < rows) {
+              char* Ob = static_cast<char*>(a.out) + (row0 + rr) * rb;
+              *reinterpret_cast<uint16_t*>(Ob + 2 * col) = f16_scaled(v, ex);
+              if ((lane & 15) == 0) Ob[2 * NOUT + col / 16] = static_cast<char>(ex);
+            }
+          }
+      }
     } else {
       float* O = static_cast<float*>(a.out);
 #pragma unroll
@@ -791,6 +817,31 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
                   if (col + t < NOUT) Hrow[col + t] = v[t];
               }
             }
+        } else if (a.out_f16s) {
+          // fp16 form: a 16-column group of this row is runs q = 2 g, 2 g + 1 of lanes l and l ^ 32
+          // (the same row); its exponent comes from the pair's largest magnitude
+          char* Ob = static_cast<char*>(a.out) + (row0 + rr) * f16s_row_bytes(NOUT);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const f32x16& c = acc[i][j];
+              float m = 0.f;
+#pragma unroll
+              for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(c[8 * g + t]));
+              m = fmaxf(m, __shfl_xor(m, 32, kWave));
+              const int ex = f16s_exp(m);
+              const int gcol = c0 + (wn * TN + j) * 32 + 16 * g;   // NOUT % 16 == 0: in or out whole
+              if (gcol < NOUT) {
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) {
+                  const int q = 2 * g + qq, col = gcol + 8 * qq + 4 * (lane >> 5);
+                  *reinterpret_cast<u32x2*>(Ob + 2 * col) =
+                      u32x2{pack_f16x2_scaled(c[4 * q], c[4 * q + 1], ex), pack_f16x2_scaled(c[4 * q + 2], c[4 * q + 3], ex)};
+                }
+                if (lane < 32) Ob[2 * NOUT + gcol / 16] = static_cast<char>(ex);
+              }
+            }
         } else {
           float* Orow = static_cast<float*>(a.out) + (row0 + rr) * NOUT;
 #pragma unroll
@@ -997,6 +1048,33 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
       for (int b = 0; b < MB; ++b)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[b][j] *= scl[j];
+    }
+    if constexpr (!kSwiGLU && kQ == 0) {
+      if (a.out_f16s) {
+        // fp16 form: the 16 lanes of a DPP row hold one row's 16 columns of the task (NOUT % 16 == 0)
+        const int64_t rb = f16s_row_bytes(NOUT);
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v = acc[b][c][i];
+              float m = fabsf(v);
+              m = fmaxf(m, xor16f<1>(m));
+              m = fmaxf(m, xor16f<2>(m));
+              m = fmaxf(m, xor16f<4>(m));
+              m = fmaxf(m, xor16f<8>(m));
+              const int ex = f16s_exp(m);
+              const int64_t rr = m0 + b * 16 + 4 * (lane >> 4) + i;
+              if (rr < rows && col[c] < NOUT) {
+                char* Ob = static_cast<char*>(a.out) + (row0 + rr) * rb;
+                *reinterpret_cast<uint16_t*>(Ob + 2 * col[c]) = f16_scaled(v, ex);
+                if ((lane & 15) == 0) Ob[2 * NOUT + col[c] / 16] = static_cast<char>(ex);
+              }
+            }
+        continue;
+      }
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c) {

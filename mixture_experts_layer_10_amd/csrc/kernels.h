@@ -60,6 +60,8 @@ struct GemmArgs {
   bool packed;            // w in the packed layout (bf16, K % 128 == 0, rows % 16 == 0)
   int qbits;              // code kind: 0 bf16 weights; kQInt8 / kQInt4 / kQFp8: a quantised stack
   bool wkn;               // down form, bf16 rows: w stored [G, K, NOUT] (read with LDS transpose loads)
+  bool out_f16s;          // down form, bf16: out rows are fp16 values + an int8 exponent per 16 columns
+                          // (f16s_row_bytes(NOUT) bytes per row), else fp32 rows
   // gate_up form, bf16 rows, tall groups: the SwiGLU backward in the epilogue when bwd_dab is set.
   // With [a | b] the tile's pre-activations, s = 1 / (1 + exp(-a)) and dh = w[p] dhu:
   // out = h = bf16(a s b), bwd_dab = bf16([dh b s (1 + a (1 - s)) | dh a s]), and
@@ -97,6 +99,10 @@ __host__ __device__ constexpr int code_bits(int kind) { return kind == kQFp8 ? 8
 __host__ __device__ constexpr int code_slot(int kind) { return code_bits(kind); }           // bytes per lane slot
 void launch_quantize(const uint16_t* src, uint8_t* dst, int64_t G, int R, int K, int kind, hipStream_t st);
 
+// Expert-output rows in the fp16 form: NOUT fp16 values, then NOUT / 16 int8 exponents (value of
+// column c = fp16[c] * 2^exp[c / 16]), padded to 16 bytes. NOUT % 16 == 0.
+__host__ __device__ constexpr int64_t f16s_row_bytes(int64_t nout) { return (2 * nout + nout / 16 + 15) / 16 * 16; }
+
 struct CombineArgs {
   const float* out_perm;
   const float* weights;
@@ -107,6 +113,7 @@ struct CombineArgs {
   int64_t N;
   int D, k;
   bool out_bf16;
+  bool in_f16s;               // out_perm and shared_out rows in the fp16 form (f16s_row_bytes(D) bytes)
 };
 void launch_combine(const CombineArgs& a, hipStream_t st);
 

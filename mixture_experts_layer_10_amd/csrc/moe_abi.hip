@@ -101,6 +101,14 @@ static int validate_config(const moe_config* c) {
     if (c->n_experts % 16)
       return fail(MOE_ERR_UNSUPPORTED, "packed weights need n_experts = %lld to be a multiple of 16", (long long)c->n_experts);
   }
+  if (c->expert_out != MOE_EXPERT_OUT_F32 && c->expert_out != MOE_EXPERT_OUT_F16S)
+    return fail(MOE_ERR_INVALID_ARG, "expert_out = %d (must be 0 or 1)", c->expert_out);
+  if (c->expert_out == MOE_EXPERT_OUT_F16S) {
+    if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fp16 expert outputs need dtype bf16");
+    if (c->hidden % 16) return fail(MOE_ERR_UNSUPPORTED, "fp16 expert outputs need hidden %% 16 == 0 (got %lld)", (long long)c->hidden);
+    if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_PACKED)
+      return fail(MOE_ERR_UNSUPPORTED, "fp16 expert outputs need row or packed bf16 weights");
+  }
   if (c->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts = %lld > %lld", (long long)c->n_experts, (long long)kMaxExperts);
   if (c->hidden > (1 << 20) || c->inter > (1 << 20) || c->shared_inter > (1 << 20))
     return fail(MOE_ERR_UNSUPPORTED, "hidden/inter above 2^20");
@@ -239,7 +247,14 @@ static GemmArgs gemm_args(const moe_config* c, int64_t n_groups, int64_t inter, 
   a.bf16 = c->dtype == MOE_BF16;
   a.packed = c->weight_layout != MOE_LAYOUT_ROWS;
   a.qbits = quant_kind(c);
+  a.out_f16s = c->expert_out == MOE_EXPERT_OUT_F16S;
   return a;
+}
+
+// Expert-output rows are 16-byte vectors in either form.
+static int check_out_align(const void* p, const char* name) {
+  if (reinterpret_cast<uintptr_t>(p) & 15) return fail(MOE_ERR_UNSUPPORTED, "%s at %p is not 16-byte aligned", name, p);
+  return MOE_OK;
 }
 
 static int combine_impl(const moe_config* c, const float* out_perm, const float* weights, const int32_t* slot_pos,
@@ -255,6 +270,7 @@ static int combine_impl(const moe_config* c, const float* out_perm, const float*
   a.D = static_cast<int>(c->hidden);
   a.k = static_cast<int>(c->top_k);
   a.out_bf16 = c->out_dtype == MOE_BF16;
+  a.in_f16s = c->expert_out == MOE_EXPERT_OUT_F16S;
   launch_combine(a, st);
   return check_launch("moe_combine");
 }
@@ -533,6 +549,7 @@ int moe_expert_down(const moe_config* cfg, int64_t n_groups, int64_t inter, int6
   if (max_rows == 0) return ok();
   if (!h || !down || !out) return fail(MOE_ERR_INVALID_ARG, "h, down or out is NULL");
   MOE_TRY(check_weight_align(down, "down"));
+  MOE_TRY(check_out_align(out, "out"));
   launch_down(gemm_args(cfg, n_groups, inter, max_rows, h, nullptr, offsets, down, out), static_cast<hipStream_t>(stream));
   MOE_TRY(check_launch("moe_expert_down"));
   return ok();
@@ -546,6 +563,7 @@ int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64
   if (!x || !gate_up || !down || !h || !out) return fail(MOE_ERR_INVALID_ARG, "x, gate_up, down, h or out is NULL");
   MOE_TRY(check_weight_align(gate_up, "gate_up"));
   MOE_TRY(check_weight_align(down, "down"));
+  MOE_TRY(check_out_align(out, "out"));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   launch_gate_up(gemm_args(cfg, n_groups, inter, max_rows, x, row_index, offsets, gate_up, h), st);
   MOE_TRY(check_launch("moe_expert_ffn (gate_up)"));
@@ -826,6 +844,8 @@ int moe_combine(const moe_config* cfg, const float* out_perm, const float* weigh
   if (cfg->n_tokens == 0) return ok();
   if (!out_perm || !weights || !slot_pos || !y) return fail(MOE_ERR_INVALID_ARG, "out_perm, weights, slot_pos or y is NULL");
   if (shared_scale && !shared_out) return fail(MOE_ERR_INVALID_ARG, "shared_scale given without shared_out");
+  MOE_TRY(check_out_align(out_perm, "out_perm"));
+  if (shared_out) MOE_TRY(check_out_align(shared_out, "shared_out"));
   MOE_TRY(combine_impl(cfg, out_perm, weights, slot_pos, shared_out, shared_scale, y, static_cast<hipStream_t>(stream)));
   return ok();
 }

@@ -107,3 +107,52 @@ def check_permute_invariants(experts, counts, offsets, token_of, slot_pos, n_exp
     same_e = np.diff(e_k[by_row]) == 0
     assert np.all(np.diff(a_idx[by_row])[same_e] > 0), "rows of one expert out of assignment order"
     return a_idx, pos
+
+
+def f16s_row_bytes(D):
+    """Bytes per expert-output row in the fp16 form: D fp16 values, D / 16 int8 exponents, padded to 16."""
+    return (2 * D + D // 16 + 15) // 16 * 16
+
+
+def decode_f16s(buf, rows, D):
+    """Values (float64 [rows, D]) and exponents (int [rows, D / 16]) of expert-output rows in the fp16
+    form (fp16[c] * 2^exp[c / 16]), read from a uint8 array holding at least rows * f16s_row_bytes(D)
+    bytes. A reader of the published format, nothing of the method."""
+    RB = f16s_row_bytes(D)
+    raw = np.ascontiguousarray(np.asarray(buf, np.uint8).reshape(-1)[:rows * RB]).reshape(rows, RB)
+    vals = raw[:, :2 * D].copy().view(np.float16).astype(np.float64)
+    exps = raw[:, 2 * D:2 * D + D // 16].copy().view(np.int8).astype(np.int64)
+    return vals * np.exp2(np.repeat(exps, 16, axis=1).astype(np.float64)), exps
+
+
+def encode_f16s(values):
+    """The fp16 form of float32 rows [rows, D] (D % 16 == 0), written from the format's definition:
+    per 16-column group, exp = max(floor(log2 m) - 14, -128) for the largest |v| = m (0 if m == 0),
+    code = v * 2^-exp rounded to fp16. Returns a uint8 array of rows * f16s_row_bytes(D) bytes."""
+    v = np.asarray(values, np.float32)
+    rows, D = v.shape
+    g = v.reshape(rows, D // 16, 16)
+    m = np.abs(g).max(axis=2)
+    _, e2 = np.frexp(m)                               # m = f * 2^e2, f in [0.5, 1): floor(log2 m) = e2 - 1
+    exps = np.where(m > 0, np.maximum(e2 - 1 - 14, -128), 0).astype(np.int64)
+    codes = np.ldexp(g.astype(np.float64), -exps[:, :, None]).astype(np.float16).reshape(rows, D)
+    RB = f16s_row_bytes(D)
+    out = np.zeros((rows, RB), np.uint8)
+    out[:, :2 * D] = codes.view(np.uint8).reshape(rows, 2 * D)
+    out[:, 2 * D:2 * D + D // 16] = exps.astype(np.int8).view(np.uint8)
+    return out.reshape(-1)
+
+
+def check_f16s_exponents(buf, rows, D):
+    """Every group's exponent follows the rule: the largest |code| of a non-zero group lies in
+    [2^14, 2^15] (the scaled maximum is below 2^15 and may round up to it) unless the exponent is at
+    its floor -128, and an all-zero group has exponent 0."""
+    RB = f16s_row_bytes(D)
+    raw = np.ascontiguousarray(np.asarray(buf, np.uint8).reshape(-1)[:rows * RB]).reshape(rows, RB)
+    codes = np.abs(raw[:, :2 * D].copy().view(np.float16).astype(np.float64)).reshape(rows, D // 16, 16).max(axis=2)
+    exps = raw[:, 2 * D:2 * D + D // 16].copy().view(np.int8).astype(np.int64)
+    zero = codes == 0
+    assert np.all(exps[zero] == 0), "an all-zero group with a non-zero exponent"
+    nz = ~zero & (exps > -128)
+    assert np.all(codes[nz] >= 2.0 ** 14) and np.all(codes[nz] <= 2.0 ** 15), "an exponent breaks the rule"
+

@@ -35,7 +35,7 @@ def test_header_symbols_all_exported(lib):
 
 
 def test_config_struct_layout_matches_header():
-    assert ctypes.sizeof(B.MoeConfig) == 6 * 8 + 4 * 4
+    assert ctypes.sizeof(B.MoeConfig) == 6 * 8 + 5 * 4 + 4       # five int32 fields, padded to 8 bytes
 
 
 def test_status_strings(lib):
@@ -73,6 +73,8 @@ def test_workspace_bytes_host_only(lib):
     ("hidden", 36, B.MOE_ERR_UNSUPPORTED),             # bf16 rows must be 16-byte vectors
     ("inter", 12, B.MOE_ERR_UNSUPPORTED),
     ("n_experts", 513, B.MOE_ERR_UNSUPPORTED),
+    ("expert_out", 2, B.MOE_ERR_INVALID_ARG),
+    ("expert_out", -1, B.MOE_ERR_INVALID_ARG),
 ])
 def test_config_validation(lib, field, value, status):
     c = B.make_config(64, 128, 8, 2, 64).copy(**{field: value})
@@ -80,6 +82,26 @@ def test_config_validation(lib, field, value, status):
         B.moe_workspace_bytes(c)
     assert ei.value.status == status
     assert field.split("_")[0] in B.last_error() or B.last_error()
+
+
+def test_f16s_expert_out_rules(lib):
+    ok = B.make_config(64, 256, 16, 2, 128, expert_out=B.MOE_EXPERT_OUT_F16S)
+    assert B.moe_workspace_bytes(ok) > 0 and B.f16s_supported(ok)
+    assert B.moe_workspace_bytes(ok.copy(weight_layout=B.MOE_LAYOUT_PACKED)) > 0
+    for bad in (B.make_config(64, 256, 16, 2, 128, dtype="f32", expert_out=1),      # fp32 layers
+                B.make_config(64, 40, 16, 2, 128, expert_out=1),                    # D % 16 != 0
+                B.make_config(64, 256, 16, 2, 128, layout=B.MOE_LAYOUT_Q8, expert_out=1)):
+        assert not B.f16s_supported(bad)
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_workspace_bytes(bad)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "fp16 expert outputs" in str(ei.value)
+    # expert-output buffers are 16-byte vectors: a misaligned out is refused before any launch
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_expert_down(ok, 16, 128, 128, FAKE, FAKE, FAKE, FAKE + 8, stream=0)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "aligned" in str(ei.value)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_combine(ok, FAKE + 4, FAKE, FAKE, None, None, FAKE, stream=0)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
 
 
 def test_packed_layout_rules(lib):

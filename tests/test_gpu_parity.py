@@ -15,8 +15,8 @@ import torch
 import oracle as O
 from mixture_experts_layer_10_amd import binding as B
 from mixture_experts_layer_10_amd import inputs as I
-from parity_util import (GAP, check_permute_invariants, compare_routing, oracle_layer, rel_err, rms, to_np,
-                         y_tolerance)
+from parity_util import (GAP, check_f16s_exponents, check_permute_invariants, compare_routing, decode_f16s,
+                         encode_f16s, f16s_row_bytes, oracle_layer, rel_err, rms, to_np, y_tolerance)
 
 pytestmark = pytest.mark.gpu
 
@@ -268,6 +268,77 @@ def test_combine():
                 assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
 
 
+@pytest.mark.parametrize("D,I_,rows", [
+    (2048, 768, [300, 0, 5, 257, 1, 64, 513]),       # streaming kernel (256 x 256 tiles)
+    (128, 1408, [2, 4, 3, 1]),                       # weight-streaming kernel (few rows per group)
+    (64, 24, [3, 0, 40, 1]),                         # register-staged kernel (K % 128 != 0)
+    (2048, 768, [1, 2, 3, 4, 5, 6, 7, 8]),
+])
+def test_expert_ffn_f16s(D, I_, rows):
+    """Expert outputs in the fp16 form: decoded values against the oracle, the exponent rule, and the
+    bytes equal to the form's definition applied to the fp32 outputs of the same products."""
+    say(f"[ffn f16s] D={D} I={I_} rows={rows}")
+    s = I.custom_shape("ffn", 1, D, 1, 1, I_, dtype="bf16")
+    d, offsets, R, rng = _ffn_case(s, 60 + D, rows)
+    dev = B.to_device(d.store)
+    off = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    outs = {}
+    for eo in (B.MOE_EXPERT_OUT_F32, B.MOE_EXPERT_OUT_F16S):
+        cfg = B.make_config(R, D, len(rows), 1, I_, expert_out=eo)
+        h = torch.empty((R, I_), dtype=torch.bfloat16, device="cuda")
+        out = torch.full((R, D), float("nan"), dtype=torch.float32, device="cuda")
+        B.moe_expert_ffn(cfg, len(rows), I_, R, dev["x"], None, off, dev["gate_up"], dev["down"], h, out)
+        torch.cuda.synchronize()
+        outs[eo] = out
+    raw = outs[B.MOE_EXPERT_OUT_F16S].view(torch.uint8).cpu().numpy().reshape(-1)
+    vals, _ = decode_f16s(raw, R, D)
+    check_f16s_exponents(raw, R, D)
+    ref = O.grouped_expert_ffn(d.values("x")[:R], offsets, d.expert_view("gate_up"), d.expert_view("down"))
+    assert np.isfinite(vals).all()
+    assert rel_err(vals, ref) <= 2e-2, rel_err(vals, ref)
+    f32 = to_np(outs[B.MOE_EXPERT_OUT_F32])
+    assert np.abs(vals - f32).max() <= 2.0 ** -11 * np.abs(f32).max() * 1.0001
+    want = encode_f16s(f32).reshape(R, -1)
+    got = raw[:R * f16s_row_bytes(D)].reshape(R, -1)
+    assert np.array_equal(got[:, :2 * D + D // 16], want[:, :2 * D + D // 16]), "bytes differ from the form's definition"
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_combine_f16s(out_dtype):
+    say(f"[combine f16s] {out_dtype}")
+    rng = np.random.default_rng(8)
+    N, k, E, D = 333, 5, 17, 272
+    experts = _random_experts(N, k, E, 6)
+    _, _, _, _, slot_pos = O.permute(experts, E)
+    slot_pos = slot_pos.copy()
+    slot_pos[[3, 40, 41]] = -1                                  # dropped pairs are skipped
+    scales = np.exp2(rng.integers(-20, 20, (N * k, 1))).astype(np.float32)
+    out_perm = (rng.standard_normal((N * k, D)) * scales).astype(np.float32)
+    out_perm[7, :32] = 0.0                                     # all-zero groups
+    weights = rng.random((N, k)).astype(np.float32)
+    shared = rng.standard_normal((N, D)).astype(np.float32)
+    scale = rng.random(N).astype(np.float32)
+    enc, enc_sh = encode_f16s(out_perm), encode_f16s(shared)
+    ov, _ = decode_f16s(enc, N * k, D)
+    sv, _ = decode_f16s(enc_sh, N, D)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    for sh in (False, True):
+        cfg = B.make_config(N, D, E, k, 8, dtype="bf16", out_dtype=out_dtype, expert_out=B.MOE_EXPERT_OUT_F16S)
+        y = torch.empty((N, D), dtype=B.torch_dtype(cfg.out_dtype), device="cuda")
+        B.moe_combine(cfg, t(enc), t(weights), t(slot_pos.astype(np.int32)), t(enc_sh) if sh else None,
+                      t(scale) if sh else None, y)
+        torch.cuda.synchronize()
+        kept = (slot_pos >= 0).reshape(N, k)          # the oracle's combine has no dropped pairs:
+        ref = O.combine(ov, np.where(kept, weights, 0.0), np.where(slot_pos >= 0, slot_pos, 0),   # weight 0
+                        sv if sh else None, scale if sh else None)
+        got = to_np(y)
+        rowmax = np.abs(ref).max(axis=1, keepdims=True) + 1e-30
+        if out_dtype == "f32":
+            assert np.all(np.abs(got - ref) <= 1e-5 * rowmax)
+        else:
+            assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rowmax)
+
+
 def sample_tokens(N, near_idx, n_sample, seed=0):
     rng = np.random.default_rng(seed)
     base = rng.choice(N, size=min(n_sample, N), replace=False) if N > n_sample else np.arange(N)
@@ -284,10 +355,10 @@ def oracle_of(name):
     return probs, w_ref, e_ref, y_ref
 
 
-def forward_and_check(name, out_dtype):
+def forward_and_check(name, out_dtype, expert_out=B.MOE_EXPERT_OUT_F32):
     d, dev = data_of(name)
     s = d.shape
-    cfg = B.config_for(s, out_dtype)
+    cfg = B.config_for(s, out_dtype, expert_out=expert_out)
     N, k = s.n_tokens, s.top_k
     w = torch.empty((N, k), dtype=torch.float32, device="cuda")
     e = torch.empty((N, k), dtype=torch.int32, device="cuda")
@@ -302,7 +373,7 @@ def forward_and_check(name, out_dtype):
     tol = y_tolerance(s.dtype, out_dtype, y_ref)        # near-tie tokens the GPU routed differently are
     err = rel_err(got[same], y_ref[same])               # checked through the forced choice
     rms_err = rms(got[same] - y_ref[same]) / rms(y_ref)
-    say(f"  {name} out={out_dtype}: tokens checked {same.sum()}/{N}, near ties {near}, "
+    say(f"  {name} out={out_dtype}{' f16s' if expert_out else ''}: tokens checked {same.sum()}/{N}, near ties {near}, "
         f"max|dy|/rms = {err:.3e} (tol {tol:.3e}), rms(dy)/rms = {rms_err:.3e}")
     assert err <= tol
     return d, dev, cfg, y, near_idx, probs, w_ref, e_ref
@@ -346,6 +417,10 @@ def forced_choice_check(d, dev, cfg, near_idx, w_ref, e_ref):
     assert err <= tol
 
 
+def f16s_ok(s):
+    return s.dtype == I.BF16 and s.hidden % 16 == 0
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_forward_small(name):
     say(f"[forward] {name}")
@@ -356,22 +431,29 @@ def test_forward_small(name):
         forced_choice_check(d, dev, cfg, near_idx, w_ref, e_ref)
     if s.dtype == I.BF16:
         forward_and_check(name, "bf16")
+    if f16s_ok(s):                       # expert outputs in the fp16 form
+        for o in ("f32", "bf16"):
+            d, dev, cfg, y, near_idx, probs, w_ref, e_ref = forward_and_check(name, o, B.MOE_EXPERT_OUT_F16S)
+            if len(near_idx):
+                forced_choice_check(d, dev, cfg, near_idx, w_ref, e_ref)
 
 
+@pytest.mark.parametrize("expert_out", [B.MOE_EXPERT_OUT_F32, B.MOE_EXPERT_OUT_F16S], ids=["f32out", "f16s"])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("name", FULL)
-def test_forward_full(name, out_dtype):
-    say(f"[forward] {name} {out_dtype}")
-    d, dev, cfg, y, near_idx, probs, w_ref, e_ref = forward_and_check(name, out_dtype)
+def test_forward_full(name, out_dtype, expert_out):
+    say(f"[forward] {name} {out_dtype} expert_out={expert_out}")
+    d, dev, cfg, y, near_idx, probs, w_ref, e_ref = forward_and_check(name, out_dtype, expert_out)
     if len(near_idx):
         forced_choice_check(d, dev, cfg, near_idx, w_ref, e_ref)
 
 
-@pytest.mark.parametrize("name", ["odd_shared", "keras", "fanout"])
-def test_forward_deterministic(name):
-    say(f"[determinism] {name}")
+@pytest.mark.parametrize("name,expert_out", [("odd_shared", 0), ("keras", 0), ("fanout", 0), ("fanout", 1),
+                                             ("odd_ungated", 1)])
+def test_forward_deterministic(name, expert_out):
+    say(f"[determinism] {name} expert_out={expert_out}")
     d, dev = data_of(name)
-    cfg = B.config_for(d.shape, "f32")
+    cfg = B.config_for(d.shape, "f32", expert_out=expert_out)
     ws = B.alloc_workspace(cfg)
     y1 = B.forward(cfg, dev, ws=ws).clone()
     ws.fill_(0x5A)
@@ -380,14 +462,15 @@ def test_forward_deterministic(name):
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "fanout"])
-def test_decomposed_chain_equals_forward(name):
+@pytest.mark.parametrize("name,expert_out", [("tiny", 0), ("decode", 0), ("fanout", 0), ("decode", 1), ("fanout", 1),
+                                             ("prefill", 1)])
+def test_decomposed_chain_equals_forward(name, expert_out):
     """The ABI chain (route -> permute -> gate_up -> down -> [shared] -> combine) gives the same bits
     as moe_forward: the benchmark times the chain so it can time the expert GEMM on its own."""
-    say(f"[chain] {name}")
+    say(f"[chain] {name} expert_out={expert_out}")
     d, dev = data_of(name)
     s = d.shape
-    cfg = B.config_for(s)
+    cfg = B.config_for(s, expert_out=expert_out)
     y_fwd = B.forward(cfg, dev)
     from mixture_experts_layer_10_amd.chain import Chain
     ch = Chain(cfg, dev)
