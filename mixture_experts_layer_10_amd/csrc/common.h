@@ -175,6 +175,16 @@ __device__ __forceinline__ void dma16_nt(const void* src, const void* lds_dst) {
 #endif
 }
 
+// dma16 from a uniform base (SGPRs) plus this lane's 32-bit byte offset: one VGPR per source
+// instead of a 64-bit address.
+__device__ __forceinline__ void dma16_sv(const void* base, uint32_t voff, const void* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)lds_dst));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory");
+#endif
+}
+
 // The same for 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes land at lds_dst + 4 l, so
 // one instruction fills 256 bytes of LDS contiguously.
 __device__ __forceinline__ void dma4(const void* src, const void* lds_dst) {

@@ -390,7 +390,8 @@ __device__ __forceinline__ void dispatch_live(int live, F&& f) {
   }
 }
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false, bool kBwd = false>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false, bool kBwd = false,
+          bool kPipe = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32, NT = WM * WN * 64, NW = WM * WN;
   // DMA instructions per wave per stage; with fewer 16-row A groups than waves (BM = 32), waves
@@ -427,6 +428,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   __shared__ int s_tmp[16];
   __shared__ int s_plist[1024];         // groups of the short m-tiles, in list order
   __shared__ int s_cnt[2 * NW * 8];
+  // pipelined loop with gathered rows: the next tile's BM row indices, staged by DMA a tile ahead
+  __shared__ __attribute__((aligned(16))) int s_rows[BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -468,38 +471,75 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   // [K][NOUT] weights: a stage holds 32 k-rows of the tile's 256 columns (512 bytes per row, 32-byte
   // chunks swizzled by (2 row) & 7); lds_tr_frag assembles each weight operand with two transpose
   // reads, in the layout of the plain read.
-  constexpr int W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE), W0 = waitcnt_vm(0);
+  constexpr int W3 = waitcnt_vm(3 * PER_STAGE), W2 = waitcnt_vm(2 * PER_STAGE), W1 = waitcnt_vm(PER_STAGE),
+                W0 = waitcnt_vm(0);
+
+  // The pipelined k-loop (plain bf16 weights, rows gathered or not): each k-slice's barrier sits in
+  // its middle, so the next slice's first fragments are read while the current slice's second half
+  // of matrix-core steps runs (see pipe_kloop). Gathered rows need at least 8 k-slices per tile (the
+  // next tile's row indices are staged in LDS a tile ahead).
+  const bool gather = a.row_index != nullptr;
+  static_assert(!kPipe || (kQ == 0 && !kWKN && !kBwd), "the pipelined loop: plain bf16 weights");
+  constexpr bool pipe = kPipe;
 
   // One tile's fixed data. make_tile reads the group table in LDS and, for gathered rows, the row
-  // indices of its A rows (global loads whose values are first used when its DMA is issued).
+  // indices of its A rows (global loads whose values are first used when its DMA is issued; in the
+  // pipelined loop, from s_rows).
   struct Tile {
     bool valid;
     int m0, c0, live;
     int64_t row0, rows;
     const uint16_t* srcA[A_INS];
     const uint16_t* srcB[B_INS];
+    // pipelined loop: the same sources as byte offsets from X (A) and from the group's weights bB (B)
+    uint32_t oA[A_INS], oB[B_INS];
+    const char* bB;
     const char* srcQ[B_INS];          // quantised: this lane's 4 code bytes of k-block 0
     float sc[TN];                     // quantised: scale of each of this lane's output columns
   };
-  auto make_tile = [&](int r) {
-    Tile T;
+  // tile r of this workgroup: (valid, group, m-tile, n-tile) from the tables in LDS
+  struct Coord {
+    bool valid;
+    int g, mt, nt;
+  };
+  auto tile_coord = [&](int r) {
+    Coord C{};
     // round r deals tiles r P .. r P + P - 1, in alternate directions in alternate rounds (a
     // workgroup that drew a more expensive tile in one round draws a cheaper one in the next)
     const int t = tile_of_round(r, (r & 1) ? P - 1 - static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x), P);
-    T.valid = r * P < total && t < total;             // t grows with r: past the list, nothing follows
-    if (!T.valid) return T;
-    int g, mt, nt;
+    C.valid = r * P < total && t < total;             // t grows with r: past the list, nothing follows
+    if (!C.valid) return C;
     if (t < total_full) {
-      g = find_group(s_pref, G, t);
-      const int local = t - s_pref[g];
-      mt = local / n_tiles;
-      nt = local - mt * n_tiles;
+      C.g = find_group(s_pref, G, t);
+      const int local = t - s_pref[C.g];
+      C.mt = local / n_tiles;
+      C.nt = local - C.mt * n_tiles;
     } else {
       const int u = t - total_full, i = u / n_tiles;
-      g = min(max(s_plist[i], 0), G - 1);             // (a permutation of the short groups; kept in range)
-      nt = u - i * n_tiles;
-      mt = (s_off[g + 1] - s_off[g]) / BM;            // the group's last, short m-tile
+      C.g = min(max(s_plist[i], 0), G - 1);           // (a permutation of the short groups; kept in range)
+      C.nt = u - i * n_tiles;
+      C.mt = (s_off[C.g + 1] - s_off[C.g]) / BM;      // the group's last, short m-tile
     }
+    C.g = __builtin_amdgcn_readfirstlane(C.g);        // uniform: the same tile in every lane
+    C.mt = __builtin_amdgcn_readfirstlane(C.mt);
+    C.nt = __builtin_amdgcn_readfirstlane(C.nt);
+    return C;
+  };
+  // pipelined loop, gathered rows: DMA the BM row indices of tile r into s_rows (waves 0 .. BM / 64 - 1,
+  // 4 bytes per lane; rows past the group repeat its last row)
+  auto stage_rows = [&](int r) {
+    const Coord C = tile_coord(r);
+    if (!C.valid || wave >= BM / 64) return;
+    const int64_t row0 = s_off[C.g], rows = static_cast<int64_t>(s_off[C.g + 1]) - row0;
+    const int64_t lr = min<int64_t>(static_cast<int64_t>(C.mt) * BM + wave * 64 + lane, rows - 1);
+    dma4(a.row_index + row0 + lr, s_rows + wave * 64);
+  };
+  auto make_tile = [&](int r) {
+    Tile T;
+    const Coord C = tile_coord(r);
+    T.valid = C.valid;
+    if (!T.valid) return T;
+    const int g = C.g, mt = C.mt, nt = C.nt;
     T.row0 = s_off[g];
     T.rows = static_cast<int64_t>(s_off[g + 1]) - T.row0;   // > 0: empty groups own no tiles
     T.m0 = mt * BM;
@@ -511,8 +551,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
       const int rr = ((wave * A_INS + j) % A_GROUPS) * 16 + lrow;
       const int64_t lr = min<int64_t>(T.m0 + rr, T.rows - 1);   // rows past the group read a valid row
       const int64_t p = T.row0 + lr;
-      const int64_t src = a.row_index ? a.row_index[p] : p;
-      T.srcA[j] = X + src * K + lch * 8;
+      int64_t src = p;
+      if (gather) {
+        if constexpr (pipe) src = s_rows[rr];
+        else src = a.row_index[p];
+      }
+      if constexpr (pipe) T.oA[j] = static_cast<uint32_t>((src * K + lch * 8) * 2);   // x below 4 GB (checked at launch)
+      else T.srcA[j] = X + src * K + lch * 8;
     }
     const uint16_t* Wg = W + static_cast<int64_t>(g) * (kSwiGLU ? 2LL * a.I * a.D : static_cast<int64_t>(a.D) * a.I);
     if constexpr (kQ != 0) {
@@ -548,6 +593,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         if constexpr (kQ != 0)
           T.srcQ[j] = static_cast<const char*>(a.w) + quant_code_bytes(g, R, K, code_bits(kQ)) +
                       static_cast<int64_t>(rb) * (K / kSK) * QB + lane * 4;
+        else if constexpr (pipe)
+          T.oB[j] = static_cast<uint32_t>((static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8) * 2);
         else
           T.srcB[j] = Wg + static_cast<int64_t>(rb) * (K / kSK) * 512 + lane * 8;
       } else if constexpr (kWKN) {
@@ -569,13 +616,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         } else {
           wrow = min(T.c0 + rr, NOUT - 1);
         }
-        T.srcB[j] = Wg + static_cast<int64_t>(wrow) * K + lch * 8;
+        if constexpr (pipe) T.oB[j] = static_cast<uint32_t>((static_cast<int64_t>(wrow) * K + lch * 8) * 2);
+        else T.srcB[j] = Wg + static_cast<int64_t>(wrow) * K + lch * 8;
       }
     }
+    T.bB = reinterpret_cast<const char*>(Wg);
     return T;
   };
   auto issue = [&](const Tile& T, int ks, uint16_t* sa, uint16_t* sb) {
     const int kb = ks * kSK;
+    if constexpr (pipe) {
+#pragma unroll
+      for (int j = 0; j < A_INS; ++j) dma16_sv(X, T.oA[j] + kb * 2, sa + ((wave * A_INS + j) % A_GROUPS) * 512);
+#pragma unroll
+      for (int j = 0; j < B_INS; ++j)
+        dma16_sv(T.bB, T.oB[j] + (kPacked ? ks * 1024 : kb * 2), sb + (wave * B_INS + j) * 512);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) dma16(T.srcA[j] + kb, sa + ((wave * A_INS + j) % A_GROUPS) * 512);
 #pragma unroll
@@ -593,6 +650,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 
   // DMA instruction n of issue() alone (n < PER_STAGE, in issue()'s order)
   auto issue_one = [&](const Tile& T, int ks, uint16_t* sa, uint16_t* sb, int n) {
+    if constexpr (pipe) {
+      if (n < A_INS) dma16_sv(X, T.oA[n] + ks * kSK * 2, sa + ((wave * A_INS + n) % A_GROUPS) * 512);
+      else dma16_sv(T.bB, T.oB[n - A_INS] + (kPacked ? ks * 1024 : ks * kSK * 2), sb + (wave * B_INS + n - A_INS) * 512);
+      return;
+    }
     if (n < A_INS) {
       dma16(T.srcA[n] + ks * kSK, sa + ((wave * A_INS + n) % A_GROUPS) * 512);
     } else if constexpr (kQ != 0) {
@@ -615,7 +677,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   // fragment reads feeding them must not still be pending once other waves may refill the buffer.
   auto wait_stage = [&](auto Nc) __attribute__((always_inline)) {
     constexpr int n = decltype(Nc)::value;
-    __builtin_amdgcn_s_waitcnt((n == 2 ? W2 : n == 1 ? W1 : W0) & ~(0xF << 8));
+    __builtin_amdgcn_s_waitcnt((n == 3 ? W3 : n == 2 ? W2 : n == 1 ? W1 : W0) & ~(0xF << 8));
     lds_barrier();
   };
   f32x16 acc[TM][TN];
@@ -708,19 +770,134 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     compute(Lc, no_dma, sA3, sB3, cur, 0, sA2, sB2);
   };
 
+  // ---- pipelined k-loop (kPipeKind) ----
+  // Slice g (buffer g % 4) runs as: (a) read its second k-step's fragments F1; (b) the first k-step's
+  // steps on F0 (read during the previous slice); (c) wait until stage g + 1 has landed (and F1 is in
+  // registers), barrier; (d) read stage g + 1's first k-step into F0; (e) the second k-step's steps on
+  // F1, with the DMA of stage g + 4 into buffer g % 4, which every wave finished reading before (c).
+  // So the reads of a slice overlap the previous slice's steps instead of following its barrier.
+  // Fragments of every block are read (a dead block's rows hold valid data; its steps are skipped).
+  u32x4 fa0[pipe ? TM : 1], fb0[pipe ? TN : 1];
+  auto read_half = [&](int kk, const uint16_t* sa, const uint16_t* sb, u32x4* fa, u32x4* fb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&sa[koA[kk] + i * 32 * kSK]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      constexpr int H = TN / 2;
+      const int rowoff = kSwiGLU ? (j < H ? j * 32 : BNB / 2 + (j - H) * 32) : j * 32;
+      fb[j] = *reinterpret_cast<const u32x4*>(&sb[koB[kk] + rowoff * kSK]);
+    }
+  };
+  // kDma: issue the DMA of stage dks of T (when dma_on, a uniform flag), one instruction per group
+  auto steps_half = [&](auto Lc, const u32x4* fa, const u32x4* fb, auto Dc, const Tile& T, int dks, uint16_t* dsa,
+                        uint16_t* dsb, bool dma_on = true) __attribute__((always_inline)) {
+    constexpr int L = decltype(Lc)::value;
+    constexpr bool kDma = decltype(Dc)::value;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i < L) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
+      }
+      if (kDma && i < PER_STAGE && dma_on) issue_one(T, dks, dsa, dsb, i);
+    }
+#pragma unroll
+    for (int n = TM; n < PER_STAGE; ++n)
+      if (kDma && dma_on) issue_one(T, dks, dsa, dsb, n);
+  };
+  // one slice in buffer (sa, sb); Wc: the wait for the next slice's stage, HasNext: whether one
+  // follows in this workgroup (then its buffer is (nsa, nsb)); Dc / T / dks: the DMA of (e)
+  // wait_n: with a compile-time Wc, that wait; with Wc = -1, wait 2 when the next tile is valid (its
+  // stages keep the count up) and w_last otherwise (the stream drains)
+  auto pslice = [&](auto Lc, uint16_t* sa, uint16_t* sb, auto Wc, auto HasNext, const uint16_t* nsa,
+                    const uint16_t* nsb, auto Dc, const Tile& T, int dks, bool dma_on = true, int w_last = 2)
+                    __attribute__((always_inline)) {
+    u32x4 fa1[TM], fb1[TN];
+    read_half(1, sa, sb, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    steps_half(Lc, fa0, fb0, std::false_type{}, T, 0, sa, sb);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(HasNext)::value) {
+      if constexpr (decltype(Wc)::value >= 0) {
+        wait_stage(Wc);
+      } else {
+        if (dma_on || w_last == 2) __builtin_amdgcn_s_waitcnt(W2 & ~(0xF << 8));
+        else if (w_last == 1) __builtin_amdgcn_s_waitcnt(W1 & ~(0xF << 8));
+        else __builtin_amdgcn_s_waitcnt(W0 & ~(0xF << 8));
+        lds_barrier();
+      }
+      read_half(0, nsa, nsb, fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    steps_half(Lc, fa1, fb1, Dc, T, dks, sa, sb, dma_on);
+    __builtin_amdgcn_sched_barrier(0);      // the next slice's reads stay after these steps
+  };
+  constexpr std::integral_constant<int, 3> n3{};
+  constexpr std::true_type yes{};
+  constexpr std::false_type no{};
+  // One tile's slices. Stages run four ahead: slice j issues stage j + 4 of this tile, and the last
+  // four slices stage 0-3 of the next tile (made at the start of those four); the next tile's first
+  // fragments are read after this tile's epilogue (so they are not live across it). The last tile
+  // drains with waits 2, 1, 0.
+  auto pipe_kloop = [&](auto Lc, const Tile& cur, Tile& nxt, int r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    if (gather) stage_rows(r + 1);          // the next tile's row indices, landed before its make_tile
+    int ks = 0;
+    for (; ks + 4 < ksteps; ks += 4) {
+      pslice(Lc, sA0, sB0, n2, yes, sA1, sB1, dma, cur, ks + 4);
+      pslice(Lc, sA1, sB1, n2, yes, sA2, sB2, dma, cur, ks + 5);
+      pslice(Lc, sA2, sB2, n2, yes, sA3, sB3, dma, cur, ks + 6);
+      pslice(Lc, sA3, sB3, n2, yes, sA0, sB0, dma, cur, ks + 7);
+    }
+    // the last four slices: stages 0-2 of the next tile if there is one; the last slice has no
+    // barrier after its reads, so stage 3 (into its buffer) and the next tile's first fragments follow
+    // the epilogue. Without a next tile: no DMA and waits 2, 1, 0.
+    nxt = make_tile(r + 1);
+    const bool nv = nxt.valid;
+    constexpr std::integral_constant<int, -1> wsel{};
+    pslice(Lc, sA0, sB0, n2, yes, sA1, sB1, dma, nxt, 0, nv);
+    pslice(Lc, sA1, sB1, wsel, yes, sA2, sB2, dma, nxt, 1, nv, 1);
+    pslice(Lc, sA2, sB2, wsel, yes, sA3, sB3, dma, nxt, 2, nv, 0);
+    pslice(Lc, sA3, sB3, n0, no, sA0, sB0, no_dma, nxt, 0, false);
+  };
+
   // Tiles are software-pipelined: the next tile's first three stages go out as soon as every wave
   // has passed the last stage's barrier (buffers 0-2 are free then), so their latency overlaps the
-  // last k-slice and the epilogue stores instead of following them.
-  Tile cur = make_tile(0);
-  if (cur.valid) {
-    issue(cur, 0, sA0, sB0);
-    issue(cur, 1, sA1, sB1);
-    issue(cur, 2, sA2, sB2);
+  // last k-slice and the epilogue stores instead of following them. (The pipelined loop instead
+  // keeps four stages in flight across tile boundaries.)
+  Tile cur;
+  if constexpr (pipe) {
+    if (gather) {
+      stage_rows(0);
+      wait_stage(n0);
+    }
+    cur = make_tile(0);
+    if (cur.valid) {
+      issue(cur, 0, sA0, sB0);
+      issue(cur, 1, sA1, sB1);
+      issue(cur, 2, sA2, sB2);
+      issue(cur, 3, sA3, sB3);
+      wait_stage(n3);
+      read_half(0, sA0, sB0, fa0, fb0);
+    }
+  } else {
+    cur = make_tile(0);
+    if (cur.valid) {
+      issue(cur, 0, sA0, sB0);
+      issue(cur, 1, sA1, sB1);
+      issue(cur, 2, sA2, sB2);
+    }
   }
   for (int r = 0; cur.valid; ++r) {
     Tile nxt;
     nxt.valid = false;
-    dispatch_live<TM>(cur.live, [&](auto Lc) __attribute__((always_inline)) { kloop(Lc, cur, nxt, r); });
+    if constexpr (pipe)
+      dispatch_live<TM>(cur.live, [&](auto Lc) __attribute__((always_inline)) { pipe_kloop(Lc, cur, nxt, r); });
+    else
+      dispatch_live<TM>(cur.live, [&](auto Lc) __attribute__((always_inline)) { kloop(Lc, cur, nxt, r); });
     // Epilogue. The next tile writes buffer 3 only after its first barrier, which every wave
     // reaches after finishing these reads of buffer 3.
     const int64_t row0 = cur.row0, rows = cur.rows;
@@ -890,6 +1067,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
               if (rr < rows) O[(row0 + rr) * NOUT + col] = acc[i][j][e];
             }
         }
+      }
+    }
+    if constexpr (pipe) {
+      if (nxt.valid) {
+        // stage 0 of the next tile landed (1 and 2 may stay in flight) and every wave is done with
+        // buffer 3: its stage 3 goes there, then its first fragments are read
+        wait_stage(n2);
+        issue(nxt, 3, sA3, sB3);
+        read_half(0, sA0, sB0, fa0, fb0);
       }
     }
     cur = nxt;
@@ -1240,7 +1426,8 @@ static void launch_bf16(const GemmArgs& a, hipStream_t st) {
   gemm_bf16_kernel<WM, TM, WN, TN, kSwiGLU><<<grid, C::NT, 0, st>>>(a);
 }
 
-template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false, bool kBwd = false>
+template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false, bool kBwd = false,
+          bool kPipe = false>
 static void launch_stream(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = WM * TM * 32, BNB = WN * TN * 32;
   constexpr int out_cols = kSwiGLU ? BNB / 2 : BNB;
@@ -1253,7 +1440,7 @@ static void launch_stream(const GemmArgs& a, hipStream_t st) {
   const int64_t ub = tile_upper_bound(a, BM, n_tiles);
   const unsigned grid = BM <= 32 ? static_cast<unsigned>(std::max<int64_t>(ub, 1))
                                  : persistent_grid(ub, lds <= 76 * 1024 ? 2 : 1);
-  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked, kQ, kWKN, kBwd><<<grid, WM * WN * 64, 0, st>>>(a);
+  gemm_stream_kernel<WM, TM, WN, TN, kSwiGLU, kPacked, kQ, kWKN, kBwd, kPipe><<<grid, WM * WN * 64, 0, st>>>(a);
 }
 
 template <bool kSwiGLU>
@@ -1300,12 +1487,19 @@ static void launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (small_rows(a)) return launch_wstream<kSwiGLU, true, kQFp8>(a, st);
     return launch_stream<2, 4, 4, 2, kSwiGLU, true, kQFp8>(a, st);
   }
+  // the pipelined k-loop where it applies: gathered rows need 8 k-slices per tile, and its 32-bit DMA
+  // byte offsets need the activation rows (at most max_rows of them: a gather reads x [N, D] with
+  // N <= max_rows) and one group's weights below 2 GB
+  const bool pipe = (!a.row_index || K / kSK >= 8) && a.max_rows * K * 2 < (1LL << 31) &&
+                    (kSwiGLU ? 2LL * a.I : static_cast<int64_t>(a.D)) * K * 2 < (1LL << 31);
   if (a.packed) {
     if (small_rows(a)) return launch_wstream<kSwiGLU, true>(a, st);
+    if (pipe) return launch_stream<2, 4, 4, 2, kSwiGLU, true, 0, false, false, true>(a, st);
     return launch_stream<2, 4, 4, 2, kSwiGLU, true>(a, st);
   }
   if (small_rows(a) && K % 32 == 0) return launch_wstream<kSwiGLU, false>(a, st);
   if (small_rows(a)) return stream ? launch_stream<1, 1, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<1, 1, 4, 2, kSwiGLU>(a, st);
+  if (stream && pipe) return launch_stream<2, 4, 4, 2, kSwiGLU, false, 0, false, false, true>(a, st);
   return stream ? launch_stream<2, 4, 4, 2, kSwiGLU, false>(a, st) : launch_bf16<2, 4, 4, 2, kSwiGLU>(a, st);
 }
 
