@@ -11,22 +11,26 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Grid-stride read of n16 16-byte vectors, four loads in flight per lane; one word per workgroup
-// is written so the loads are not removed.
+// Read of n16 16-byte vectors, U loads in flight per lane: each workgroup streams one contiguous
+// chunk (256 threads x U vectors per step); one word per workgroup is written so the loads are not
+// removed. kNT: nontemporal loads.
+template <int U, bool kNT>
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16, uint32_t* sink) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t per = (n16 / gridDim.x) & ~static_cast<int64_t>(256 * U - 1);       // this workgroup's share
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * per, hi = lo + per;
   uint32_t acc = 0;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    u32x4 v[4];
+  for (int64_t i = lo + threadIdx.x; i + (U - 1) * 256 < hi; i += U * 256) {
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(&src[i + u * stride]);
+    for (int u = 0; u < U; ++u) v[u] = kNT ? __builtin_nontemporal_load(&src[i + u * 256]) : src[i + u * 256];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n16; i += stride) {
-    const u32x4 v = src[i];
-    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  if (blockIdx.x == 0) {                          // the tail past the workgroups' equal shares
+    for (int64_t i = per * gridDim.x + threadIdx.x; i < n16; i += 256) {
+      const u32x4 v = src[i];
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
   }
   __shared__ uint32_t s[256];
   s[threadIdx.x] = acc;
@@ -63,9 +67,17 @@ extern "C" {
 
 // Reads `bytes` (a multiple of 16) from src with `grid` workgroups of 256 threads; sink holds grid
 // words. Returns 0, or the HIP error of the launch.
-int probe_read(const void* src, int64_t bytes, uint32_t* sink, int grid, void* stream) {
-  if (!src || !sink || bytes < 16 || (bytes & 15) || grid < 1) return -1;
-  read_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4*>(src), bytes / 16, sink);
+// mode: 0 / 1 = 4 / 8 loads in flight per lane, + 2 for nontemporal loads.
+int probe_read(const void* src, int64_t bytes, uint32_t* sink, int grid, int mode, void* stream) {
+  if (!src || !sink || bytes < 16 || (bytes & 15) || grid < 1 || mode < 0 || mode > 3) return -1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4* s16 = static_cast<const u32x4*>(src);
+  switch (mode) {
+    case 0: read_kernel<4, false><<<grid, 256, 0, st>>>(s16, bytes / 16, sink); break;
+    case 1: read_kernel<8, false><<<grid, 256, 0, st>>>(s16, bytes / 16, sink); break;
+    case 2: read_kernel<4, true><<<grid, 256, 0, st>>>(s16, bytes / 16, sink); break;
+    default: read_kernel<8, true><<<grid, 256, 0, st>>>(s16, bytes / 16, sink); break;
+  }
   return static_cast<int>(hipGetLastError());
 }
 
