@@ -133,7 +133,7 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
               void* stream);
 
 /* Sigmoid-score router ("27. Mixture of experts", section "The router", the note on other routers;
- * "Qwen3-VL + MoE: train to deploy", section "Balancing without a loss"): logits as moe_route
+ * "Qwen3-VL + MoE: train to deploy", section "How the router and experts learn", the item on balancing without a loss): logits as moe_route
  * (fp32, never rounded), s = sigmoid(logits) in fp32, the k experts with the largest s + bias
  * (descending, equal keys to the lower index); the bias only picks, so
  * weights = s of the picked experts, divided by their sum when norm_topk_prob.
@@ -162,7 +162,7 @@ int moe_permute(const moe_config* cfg, const int32_t* experts, const void* x, in
                 int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, void* ws,
                 size_t ws_bytes, void* stream);
 
-/* moe_permute with a capacity limit ("Qwen3-VL + MoE: train to deploy", section "Capacity limits"):
+/* moe_permute with a capacity limit ("Qwen3-VL + MoE: train to deploy", section "How the router and experts learn", the item on capacity limits):
  * each expert keeps its first `capacity` (>= 0) assignments in assignment order a = n*k + j; the
  * rest are dropped (their token passes through unchanged). counts/offsets cover the kept rows
  * (offsets[E] = rows kept), token_of and x_perm hold the kept rows only, and slot_pos[a] = -1 for
@@ -263,7 +263,7 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
                  float* dshared_down, float* dw_shared_gate, void* ws, size_t ws_bytes, void* stream);
 
 /* Router load statistics and the Switch-style balance loss ("Qwen3-VL + MoE: train to deploy",
- * section "An auxiliary balance loss", its N read as the number of experts):
+ * section "How the router and experts learn", the item on an auxiliary balance loss, its N read as the number of experts):
  *   f[e] = counts[e] / (N k)                        fraction of the assignments routed to e
  *   P[e] = (1/N) sum_n softmax(logits[n])[e]         mean router probability (fp32 softmax)
  *   loss = E * sum_e f[e] P[e]                        1 for perfectly even routing; the caller

@@ -15,7 +15,8 @@ from typing import Optional
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "_lib", "libmoe_mi355x.so")
+# MOE_LIB_PATH names another build of the same library (the tests' host-sanitizer build)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(PKG, "_lib", "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1

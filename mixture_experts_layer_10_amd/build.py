@@ -79,6 +79,57 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Host AddressSanitizer build for the CPU tests: the same sources with the host code instrumented
+# (device code unchanged), linked against the shared sanitizer runtime, which the test process
+# preloads. It stays under _build/ and is never loaded by the product path.
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_LIB_PATH = os.path.join(ASAN_DIR, "libmoe_mi355x_hostasan.so")
+ASAN_HOST_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+ASAN_LINK_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -shared-libasan".split()
+
+
+def asan_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the ROCm clang."""
+    for clang in ("/opt/rocm/llvm/bin/clang", shutil.which("amdclang") or ""):
+        if clang and os.path.exists(clang):
+            r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            path = r.stdout.strip()
+            if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    raise RuntimeError("AddressSanitizer runtime not found")
+
+
+def _compile_asan(src: str) -> str:
+    obj = os.path.join(ASAN_DIR, os.path.basename(src) + ".o")
+    flags = [f for f in HIP_FLAGS if f != "-O3"]
+    cmd = [hipcc(), *flags, "-O1", *ASAN_HOST_FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build_host_asan(jobs: int | None = None) -> str:
+    """Builds ASAN_LIB_PATH unless it is newer than every source and header."""
+    srcs = sources()
+    inc = os.path.join(ROOT, "include")
+    deps = srcs + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
+        [os.path.join(inc, f) for f in os.listdir(inc)]
+    if os.path.exists(ASAN_LIB_PATH) and os.path.getmtime(ASAN_LIB_PATH) > max(os.path.getmtime(d) for d in deps):
+        return ASAN_LIB_PATH
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile_asan, srcs))
+    tmp = ASAN_LIB_PATH + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *ASAN_LINK_FLAGS, "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ASAN_LIB_PATH)
+    return ASAN_LIB_PATH
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)

@@ -148,10 +148,12 @@ static Layout layout_of(const moe_config* c) {
   L.token_of = take(A * 4);
   L.slot_pos = take(A * 4);
   L.shared_scale = take(Is ? N * 4 : 0);
+  // expert-output rows: D fp32 values, or the fp16 form's f16s_row_bytes(D)
+  const size_t orow = c->expert_out == MOE_EXPERT_OUT_F16S ? static_cast<size_t>(f16s_row_bytes(c->hidden)) : D * 4;
   L.h = take(A * I * eb);
-  L.out = take(A * D * 4);
+  L.out = take(A * orow);
   L.sh_h = take(Is ? N * Is * eb : 0);
-  L.sh_out = take(Is ? N * D * 4 : 0);
+  L.sh_out = take(Is ? N * orow : 0);
   L.total = at;
   return L;
 }

@@ -8,7 +8,7 @@
 // An expert id outside [0, E) (never produced by the router; possible from a caller's own ids) is
 // treated as a dropped pair: it is not counted, takes no row and gets slot_pos -1, so no index
 // derived from it reaches memory.
-// Capacity limit ("Qwen3-VL + MoE: train to deploy", section "Capacity limits"): an expert keeps
+// Capacity limit ("Qwen3-VL + MoE: train to deploy", section "How the router and experts learn", the item on capacity limits): an expert keeps
 // its first `capacity` assignments in assignment order. Counts and offsets cover the kept rows;
 // since positions are handed out in assignment order, an assignment is kept exactly when its
 // position falls before its expert's end offset, and a dropped one gets slot_pos -1.

@@ -1,5 +1,5 @@
 // Router load statistics and the Switch-style balance loss ("Qwen3-VL + MoE: train to deploy",
-// section "An auxiliary balance loss", reading its N as the number of experts; "27. Mixture of
+// section "How the router and experts learn", the item on an auxiliary balance loss, reading its N as the number of experts; "27. Mixture of
 // experts", section "Dispatch", closing paragraph on expert load):
 //   f_e  = counts[e] / (N k)                         fraction of assignments routed to e
 //   P_e  = (1 / N) sum_n softmax(logits[n])_e        mean router probability of e (fp32 softmax)
@@ -94,7 +94,7 @@ void launch_stats(const float* logits, const int32_t* counts, float* f, float* P
   stats_loss_kernel<<<1, 64, 0, st>>>(f, P, loss, E);
 }
 
-// Selection-bias nudge ("Qwen3-VL + MoE: train to deploy", section "Balancing without a loss":
+// Selection-bias nudge ("Qwen3-VL + MoE: train to deploy", section "How the router and experts learn", the item on balancing without a loss:
 // overloaded experts get their bias lowered slightly, idle ones raised): one thread per expert,
 // bias[e] -= gamma * sign(counts[e] - A / E), comparing counts[e] * E with A exactly in integers.
 __global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts, float* __restrict__ bias,

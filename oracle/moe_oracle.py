@@ -252,7 +252,7 @@ def expected_touched_experts(n_experts, top_k, batch):
 
 def switch_aux_loss(probs, experts, n_experts):
     """Switch-Transformer balance statistic E * sum_e f_e * P_e, f_e = fraction of the N*k assignments
-    routed to e, P_e = mean router probability of e ([VL-post] "An auxiliary balance loss", reading
+    routed to e, P_e = mean router probability of e ([VL-post] "How the router and experts learn" (the auxiliary balance loss item), reading
     its N as the number of experts; [MoE-ch27] "Dispatch", closing paragraph). The caller applies
     the coefficient alpha."""
     probs = np.asarray(probs, np.float64)
@@ -263,14 +263,14 @@ def switch_aux_loss(probs, experts, n_experts):
 
 
 # --------------------------------------------------------------------------------------------
-# Routing variants: [VL-post] "Capacity limits" and "Balancing without a loss"; [MoE-ch27] "The
+# Routing variants: [VL-post] "How the router and experts learn" (the capacity-limit and loss-free balancing items); [MoE-ch27] "The
 # router", the note on other routers (a sigmoid score per expert with a learned bias).
 # --------------------------------------------------------------------------------------------
 
 def route_sigmoid_bias(x, w_router, k, bias=None, norm_topk_prob=True):
     """Sigmoid-score router. scores = sigmoid(logits) in float32; the k experts with the largest
     scores + bias are picked (descending, equal keys to the lower index); the bias only picks and
-    never enters the weights ([VL-post] "Balancing without a loss"), so the weights are the picked
+    never enters the weights ([VL-post] "How the router and experts learn", loss-free balancing item), so the weights are the picked
     scores, divided by their sum when norm_topk_prob (the same flag as the softmax router).
     Returns (logits f64, scores f32, keys f32, weights, experts)."""
     logits = router_logits(x, w_router)
@@ -287,7 +287,7 @@ def route_sigmoid_bias(x, w_router, k, bias=None, norm_topk_prob=True):
 
 
 def capacity_keep(experts, n_experts, capacity):
-    """Capacity limit ([VL-post] "Capacity limits"): every expert has `capacity` slots per batch;
+    """Capacity limit ([VL-post] "How the router and experts learn", capacity-limit item): every expert has `capacity` slots per batch;
     the assignments a = n*k + j claim them in assignment order and those that overflow are dropped
     (their token passes through the block unchanged: the dropped pair contributes nothing).
     Returns keep[N, k] (bool). A plain loop over the assignments."""
@@ -304,7 +304,7 @@ def capacity_keep(experts, n_experts, capacity):
 
 def forward_capacity(x, weights, experts, gate_up, down, keep):
     """y[n] = sum_j keep[n,j] * w[n,j] * expert_{e[n,j]}(x[n]) for a given routing and keep mask
-    ([MoE-ch27] "The router" equation with [VL-post] "Capacity limits"), expert by expert."""
+    ([MoE-ch27] "The router" equation with [VL-post] "How the router and experts learn" (capacity-limit item)), expert by expert."""
     x = np.asarray(x, np.float64)
     w = np.asarray(weights, np.float64)
     experts = np.asarray(experts)
@@ -317,7 +317,7 @@ def forward_capacity(x, weights, experts, gate_up, down, keep):
 
 
 def bias_update(bias, counts, n_tokens, top_k, gamma):
-    """One step of the selection-bias nudge ([VL-post] "Balancing without a loss": overloaded
+    """One step of the selection-bias nudge ([VL-post] "How the router and experts learn", loss-free balancing item: overloaded
     experts get their bias lowered slightly, idle ones raised): b_e - gamma * sign(c_e - N k / E),
     in float32; an expert exactly at the mean load keeps its bias."""
     counts = np.asarray(counts, np.float64)

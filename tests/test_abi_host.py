@@ -50,6 +50,9 @@ def test_workspace_bytes_host_only(lib):
     A = 16384 * 8
     assert n >= A * 2048 * 4 + A * 768 * 2            # fp32 expert outputs + bf16 h
     assert n < A * 2048 * 4 * 1.3
+    # fp16 expert outputs: rows of 2 D value bytes + D / 16 exponent bytes instead of 4 D
+    f = B.moe_workspace_bytes(c.copy(expert_out=B.MOE_EXPERT_OUT_F16S))
+    assert n - f == A * (2048 * 4 - (2 * 2048 + 2048 // 16))
     c5 = B.make_config(8192, 2048, 512, 10, 256, shared_inter=512)
     assert B.moe_workspace_bytes(c5) > B.moe_workspace_bytes(c5.copy(shared_inter=0))
 

@@ -1,5 +1,5 @@
 """Router load statistics and the balance loss (moe_router_stats) on the GPU, against the oracle's
-switch_aux_loss ("Qwen3-VL + MoE: train to deploy", section "An auxiliary balance loss") and its
+switch_aux_loss ("Qwen3-VL + MoE: train to deploy", section "How the router and experts learn", the item on an auxiliary balance loss) and its
 closed forms."""
 import numpy as np
 import pytest

@@ -1,5 +1,5 @@
 """Routing variants on the GPU against the oracle ("Qwen3-VL + MoE: train to deploy", sections
-"Capacity limits" and "Balancing without a loss"; "27. Mixture of experts", section "The router",
+"How the router and experts learn" (its capacity-limit and loss-free balancing items); "27. Mixture of experts", section "The router",
 the note on sigmoid routers): moe_route_sigmoid, moe_permute_capped (+ moe_combine skipping
 dropped pairs) and moe_router_bias_update."""
 import numpy as np

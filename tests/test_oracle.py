@@ -339,7 +339,7 @@ def test_k_gap():
     assert O.k_gap(p, 4)[0] == np.inf
 
 
-# ---- routing variants ([VL-post] "Capacity limits", "Balancing without a loss";
+# ---- routing variants ([VL-post] "How the router and experts learn" (capacity-limit and loss-free balancing items);
 #      [MoE-ch27] "The router", the note on sigmoid routers) ----
 
 def test_sigmoid_zero_bias_picks_what_softmax_picks():
