@@ -369,18 +369,24 @@ def fp8_e4m3_encode(v):
     return ((np.signbit(v).astype(np.int64) << 7) | (exp_field << 3) | mant).astype(np.uint8)
 
 
+INT4_GROUP = 32          # input columns per int4 group
+INT4_MULT_MAX = 32       # largest group multiplier: |code * mult| <= 7 * 32 = 224
+
+
 def quantize_weights(w, bits):
     """Quantise a [G, R, K] stack (R output rows, K inputs) to signed `bits`-bit codes (8 or 4), or
-    to OCP e4m3 bytes for bits == "f8" (see quantize_fp8).
+    to OCP e4m3 bytes for bits == "f8" (see quantize_fp8). Returns (codes int8 [G, R, K], scales
+    float32 [G, R], mults): mults is None except for int4 (see quantize_int4_groups).
 
-    For each row r:
+    int8, for each row r:
       m     = max |w[r, :]|                          (float32, exact for bf16 values)
-      scale = m / Q                                  (float32 division, Q = 2**(bits-1) - 1)
-      code  = clamp(rint(w / scale), -Q, Q)          (float32 quotient, ties to even; 0 if scale 0)
-    so code * scale reconstructs w to within scale / 2. Returns (codes int8 [G, R, K],
-    scales float32 [G, R])."""
+      scale = m / 127                                (float32 division)
+      code  = clamp(rint(w / scale), -127, 127)      (float32 quotient, ties to even; 0 if scale 0)
+    so code * scale reconstructs w to within scale / 2."""
     if bits == "f8":
-        return quantize_fp8(w)
+        return (*quantize_fp8(w), None)
+    if bits == 4:
+        return quantize_int4_groups(w)
     Q = np.float32(2 ** (bits - 1) - 1)
     w32 = np.asarray(w, np.float32)
     m = np.abs(w32).max(axis=-1)
@@ -389,7 +395,37 @@ def quantize_weights(w, bits):
     div = np.where(nz, scales, np.float32(1.0))[..., None]
     codes = np.clip(np.rint((w32 / div).astype(np.float32)), -Q, Q)
     codes = np.where(nz[..., None], codes, np.float32(0.0))
-    return codes.astype(np.int8), scales
+    return codes.astype(np.int8), scales, None
+
+
+def quantize_int4_groups(w):
+    """int4 with a scale per group of INT4_GROUP input columns, written as the row's float32 scale
+    times a small integer per group ([MoE-ch27] "Stretch exercises", item 3: experts in 4 bits; the
+    pages fix no quantiser). For each row r and group q (columns 32 q .. 32 q + 31), in float32:
+      s     = max |w[r, :]| / 224                     (224 = 7 * INT4_MULT_MAX)
+      mult  = min(ceil(max |w[r, group q]| / (7 * s)), 32)   (0 for an all-zero group)
+      step  = s * mult
+      code  = clamp(rint(w / step), -7, 7)            (ties to even; 0 where step is 0)
+    The weight is code * mult * s: code * mult is an integer of magnitude at most 224, exact in
+    bfloat16, so the codes times their group multiplier enter a bf16 product exactly and the row
+    scale s still factors out of the row's sum. A group's step is the smallest multiple of s that
+    covers its largest |w| in 7 steps. Returns (codes int8 [G, R, K], s float32 [G, R],
+    mult uint8 [G, R, K / 32]); K must be a multiple of 32."""
+    w32 = np.asarray(w, np.float32)
+    K = w32.shape[-1]
+    assert K % INT4_GROUP == 0, "int4 groups need K % 32 == 0"
+    s = (np.abs(w32).max(axis=-1) / np.float32(7 * INT4_MULT_MAX)).astype(np.float32)
+    grp = w32.reshape(*w32.shape[:-1], K // INT4_GROUP, INT4_GROUP)
+    gmax = np.abs(grp).max(axis=-1)
+    unit = (np.float32(7) * s).astype(np.float32)[..., None]          # 7 s, the span of one multiplier
+    safe = np.where(unit > 0, unit, np.float32(1.0))
+    mult = np.where(unit > 0, np.ceil((gmax / safe).astype(np.float32)), np.float32(0.0))
+    mult = np.minimum(mult, np.float32(INT4_MULT_MAX))
+    step = (s[..., None] * mult).astype(np.float32)[..., None]
+    div = np.where(step > 0, step, np.float32(1.0))
+    codes = np.clip(np.rint((grp / div).astype(np.float32)), -7, 7)
+    codes = np.where(step > 0, codes, np.float32(0.0)).reshape(w32.shape)
+    return codes.astype(np.int8), s, mult.astype(np.uint8)
 
 
 def quantize_fp8(w):
@@ -408,11 +444,14 @@ def quantize_fp8(w):
     return np.where(nz[..., None], codes, np.uint8(0)), scales
 
 
-def dequantize_weights(codes, scales):
+def dequantize_weights(codes, scales, mults=None):
     """The weights the quantised layer computes with: w'[g, r, c] = code[g, r, c] * scale[g, r], in
-    float64 (exact: a small integer, or an e4m3 value for uint8 FP8 codes, times a float32)."""
+    float64 (exact: a small integer, or an e4m3 value for uint8 FP8 codes, times a float32); with
+    int4 group multipliers, code * mult[g, r, c // 32] * scale[g, r]."""
     codes = np.asarray(codes)
     vals = fp8_e4m3_value(codes) if codes.dtype == np.uint8 else codes.astype(np.float64)
+    if mults is not None:
+        vals = vals * np.repeat(np.asarray(mults, np.float64), INT4_GROUP, axis=-1)
     return vals * np.asarray(scales, np.float64)[..., None]
 
 

@@ -57,8 +57,8 @@ class Dequant:
         return len(self.view)
 
     def __getitem__(self, g):
-        c, s = O.quantize_weights(np.asarray(self.view[g], np.float32)[None], self.bits)
-        return O.dequantize_weights(c, s)[0]
+        c, s, m = O.quantize_weights(np.asarray(self.view[g], np.float32)[None], self.bits)
+        return O.dequantize_weights(c, s, m)[0]
 
 
 def quant_stack(cfg, w_dev, G, R, K):

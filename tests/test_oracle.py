@@ -417,64 +417,110 @@ def test_bias_update_sign_rule():
 # Weight-only quantisation (quantize_weights / dequantize_weights)
 # ----------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("bits", [8, 4])
-def test_quantize_exact_on_its_grid(bits):
-    """Values that are integer multiples of a power of two, with the largest at Q units in every
-    row, have scale exactly that power and codes equal to the multiples: the reconstruction is exact."""
-    Q = 2 ** (bits - 1) - 1
+def test_quantize_exact_on_its_grid():
+    """int8: values that are integer multiples of a power of two, with the largest at 127 units in
+    every row, have scale exactly that power and codes equal to the multiples: exact reconstruction."""
     unit = 2.0 ** -9
-    rng = np.random.default_rng(bits)
-    mult = rng.integers(-Q, Q + 1, size=(3, 32, 256))
-    mult[..., 7] = Q * np.where(rng.random((3, 32)) < 0.5, 1, -1)   # every row reaches the full range
+    rng = np.random.default_rng(8)
+    mult = rng.integers(-127, 128, size=(3, 32, 256))
+    mult[..., 7] = 127 * np.where(rng.random((3, 32)) < 0.5, 1, -1)   # every row reaches the full range
     w = (mult * unit).astype(np.float32)
-    codes, scales = O.quantize_weights(w, bits)
-    assert scales.shape == (3, 32) and np.all(scales == np.float32(unit))
+    codes, scales, m = O.quantize_weights(w, 8)
+    assert m is None and scales.shape == (3, 32) and np.all(scales == np.float32(unit))
     assert np.array_equal(codes.astype(np.int64), mult)
     assert np.array_equal(O.dequantize_weights(codes, scales), w.astype(np.float64))
 
 
+def test_quantize_int4_exact_on_its_grid():
+    """int4 groups: w = code * mult * 2^-10 with codes in [-7, 7], a +-7 in every group, each group's
+    multiplier drawn from 1..32 and one group per row at 32: the quantiser returns exactly those
+    codes, multipliers and the row scale 2^-10, and the reconstruction is exact."""
+    unit = 2.0 ** -10
+    rng = np.random.default_rng(4)
+    G, R, K = 2, 16, 256
+    codes = rng.integers(-7, 8, size=(G, R, K))
+    codes[..., ::32] = 7 * np.where(rng.random((G, R, K // 32)) < 0.5, 1, -1)
+    mults = rng.integers(1, 33, size=(G, R, K // 32))
+    mults[..., 3] = 32
+    w = (codes * np.repeat(mults, 32, axis=-1) * unit).astype(np.float32)
+    c, s, m = O.quantize_weights(w, 4)
+    assert np.all(s == np.float32(unit)) and np.array_equal(m.astype(np.int64), mults)
+    assert np.array_equal(c.astype(np.int64), codes)
+    assert np.array_equal(O.dequantize_weights(c, s, m), w.astype(np.float64))
+
+
 def test_quantize_worked_int4_row():
-    """By hand: a row with max |w| = 1 has scale fl32(1/7); 0.3 * 7 = 2.1 -> 2, 0.6 * 7 = 4.2 -> 4,
-    -1 -> -7, -0.05 * 7 = -0.35 -> 0; the rest of the row is zero. A second row, scaled by 1/2 and
-    negated, gets the same codes negated (the scale follows the row, not the stack)."""
-    w = np.zeros((1, 2, 64), np.float32)
-    w[0, 0, :4] = [0.3, -1.0, 0.6, -0.05]
-    w[0, 1] = -0.5 * w[0, 0]
-    codes, scales = O.quantize_weights(w, 4)
-    assert scales[0, 0] == np.float32(1.0) / np.float32(7.0)
-    assert scales[0, 1] == np.float32(0.5) / np.float32(7.0)
-    assert codes[0, 0, :4].tolist() == [2, -7, 4, 0] and codes[0, 1, :4].tolist() == [-2, 7, -4, 0]
-    assert not codes[0, :, 4:].any()
+    """By hand, one row of two groups. Row max 1, so s = fl32(1/224). Group 0 holds the row max:
+    multiplier 1 / (7 s) = 32, step 32 s = fl32(1/7): 1 -> 7, -0.6 * 7 = -4.2 -> -4, 0.3 * 7 = 2.1 -> 2.
+    Group 1's max is 0.1: multiplier ceil(0.1 * 32) = ceil(3.2) = 4, step 4 / 224 = 1/56:
+    0.1 * 56 = 5.6 -> 6, -0.05 * 56 = -2.8 -> -3. A second row equal to row 0 with group 1 zeroed
+    gets multiplier 0 and zero codes there; an all-zero row has scale 0."""
+    w = np.zeros((1, 3, 64), np.float32)
+    w[0, 0, :3] = [1.0, -0.6, 0.3]
+    w[0, 0, 32:34] = [0.1, -0.05]
+    w[0, 1, :32] = w[0, 0, :32]
+    codes, s, m = O.quantize_weights(w, 4)
+    assert s[0, 0] == np.float32(1.0) / np.float32(224.0) and s[0, 1] == s[0, 0] and s[0, 2] == 0
+    assert m[0].tolist() == [[32, 4], [32, 0], [0, 0]]
+    assert codes[0, 0, :3].tolist() == [7, -4, 2] and codes[0, 0, 32:34].tolist() == [6, -3]
+    assert np.array_equal(codes[0, 1, :32], codes[0, 0, :32]) and not codes[0, 1, 32:].any()
+    assert not codes[0, 2].any()
+    nz = np.zeros(64, bool)
+    nz[[0, 1, 2, 32, 33]] = True
+    assert not codes[0, 0, ~nz].any()
 
 
-def test_quantize_ties_to_even_and_zero_rows():
-    """Quotients exactly halfway between two codes round to the even one; an all-zero row has
-    scale 0 and codes 0 (no division by zero)."""
-    unit = np.float32(2.0 ** -8)
-    w = np.zeros((1, 2, 128), np.float32)
-    w[0, 0, 0] = 127 * unit                       # scale = unit exactly
-    w[0, 0, 1:5] = np.array([2.5, 3.5, -2.5, -0.5], np.float32) * unit
-    codes, scales = O.quantize_weights(w, 8)
-    assert scales[0, 0] == unit and scales[0, 1] == 0
-    assert codes[0, 0, 1:5].tolist() == [2, 4, -2, 0]
-    assert not codes[0, 1].any()
+def test_quantize_int4_rows_with_the_max_in_every_group_are_per_row_absmax():
+    """When every group of a row holds the row's largest |w|, every multiplier is 32 and the step is
+    32 s = fl32(max / 7) exactly (dividing by 224 = 7 * 32 and multiplying by 32 only shifts the
+    exponent), so the codes are the plain per-row absmax int4 codes rint(w / fl32(max / 7))."""
+    rng = np.random.default_rng(44)
+    w = I.bf16_bits_to_f32(I.round_to_bf16_bits(rng.normal(0.0, 0.02, size=(1, 8, 256)).astype(np.float32)))
+    top = np.abs(w).max(axis=-1, keepdims=True)
+    w[..., ::32] = top * np.where(rng.random((1, 8, 8)) < 0.5, 1, -1)      # the max in every group
+    codes, s, m = O.quantize_weights(w, 4)
+    assert np.all(m == 32)
+    row_scale = (np.abs(w).max(axis=-1) / np.float32(7)).astype(np.float32)
+    assert np.array_equal((s * np.float32(32)).astype(np.float32), row_scale)
+    ref = np.clip(np.rint((w / row_scale[..., None]).astype(np.float32)), -7, 7)
+    assert np.array_equal(codes.astype(np.float32), ref)
+
+
+def test_quantize_int4_multiplier_is_the_smallest_that_covers_the_group():
+    """Brute force over all 33 multipliers: the chosen one is the smallest m with 7 m s >= the
+    group's largest |w| (up to float32 rounding of the quotient), and 0 only for all-zero groups."""
+    rng = np.random.default_rng(45)
+    w = rng.normal(0.0, 1.0, size=(1, 24, 128)).astype(np.float32)
+    w[..., :32] *= rng.random((1, 24, 1)).astype(np.float32) ** 3      # some groups much smaller
+    w[0, 5, 64:96] = 0.0
+    _, s, m = O.quantize_weights(w, 4)
+    gmax = np.abs(w.astype(np.float64)).reshape(1, 24, 4, 32).max(-1)
+    for r in range(24):
+        for q in range(4):
+            need = [mm for mm in range(33) if 7 * mm * float(s[0, r]) >= gmax[0, r, q] * (1 - 1e-6)]
+            assert m[0, r, q] == need[0], (r, q, m[0, r, q], need[:2])
+    assert m[0, 5, 2] == 0
 
 
 @pytest.mark.parametrize("bits", [8, 4])
 def test_quantize_error_bound_and_range(bits):
-    """Round to nearest: |code * scale - w| <= scale / 2, plus the float32 quotient's rounding
-    (at most Q * 2^-24 code units), codes within [-Q, Q], and each row's largest |w| maps to +-Q."""
+    """Round to nearest: |w' - w| <= step / 2, plus the float32 quotient's rounding (at most
+    Q * 2^-23 steps), with step the row scale (int8) or the group's s * mult (int4, never above the
+    row's 32 s); codes within [-Q, Q], and each row's largest |w| maps to +-Q."""
     Q = 2 ** (bits - 1) - 1
     rng = np.random.default_rng(40 + bits)
     w = I.bf16_bits_to_f32(I.round_to_bf16_bits(rng.normal(0.0, 0.02, size=(2, 48, 384)).astype(np.float32)))
     w[1] *= 3.0                                   # rows of different ranges
-    codes, scales = O.quantize_weights(w, bits)
-    err = np.abs(O.dequantize_weights(codes, scales) - w.astype(np.float64))
-    assert np.all(err <= scales.astype(np.float64)[..., None] * (0.5 + Q * 2.0 ** -23))
-    assert np.all(err.max(axis=-1) > 0.3 * scales)          # the bound is nearly reached in each row
+    codes, scales, m = O.quantize_weights(w, bits)
+    step = scales.astype(np.float64)[..., None] * (np.repeat(m.astype(np.float64), 32, -1) if m is not None else 1.0)
+    err = np.abs(O.dequantize_weights(codes, scales, m) - w.astype(np.float64))
+    assert np.all(err <= step * (0.5 + Q * 2.0 ** -23))
+    assert np.all(err.max(axis=-1) > 0.3 * step.max(axis=-1))          # the bound is nearly reached in each row
     assert codes.min() >= -Q and codes.max() <= Q
     at_max = np.take_along_axis(codes, np.abs(w).argmax(-1)[..., None], -1)[..., 0]
     assert np.all(np.abs(at_max) == Q)
+    if m is not None:
+        assert m.max() == 32 and np.all(step <= 32 * scales.astype(np.float64)[..., None])
 
 
 def test_quantized_layer_is_the_layer_on_dequantised_weights():
@@ -489,12 +535,21 @@ def test_quantized_layer_is_the_layer_on_dequantised_weights():
     gu, dn = gu.astype(np.float32), dn.astype(np.float32)
     x = rng.normal(size=(N, D))
     wr = rng.normal(0, 0.05, size=(G, D))
-    qg, sg = O.quantize_weights(gu, 8)
-    qd, sd = O.quantize_weights(dn, 8)
+    qg, sg, _ = O.quantize_weights(gu, 8)
+    qd, sd, _ = O.quantize_weights(dn, 8)
     gq, dq = O.dequantize_weights(qg, sg), O.dequantize_weights(qd, sd)
     assert np.array_equal(gq, gu.astype(np.float64)) and np.array_equal(dq, dn.astype(np.float64))
     y, _ = O.forward_grouped(x, wr, gq, dq, k)
     assert np.allclose(y, O.forward_loop(x, wr, gq, dq, k), rtol=0, atol=1e-12)
+    # int4 groups: weights on their grid (a +-7 code and the full multiplier in group 0 of each row)
+    c4 = rng.integers(-7, 8, size=(G, 2 * I_, D))
+    c4[..., 0] = 7
+    m4 = rng.integers(1, 33, size=(G, 2 * I_, D // 32))
+    m4[..., 0] = 32
+    c4[..., 32::32] = -7
+    gu4 = (c4 * np.repeat(m4, 32, -1) * 2.0 ** -14).astype(np.float32)
+    q4 = O.quantize_weights(gu4, 4)
+    assert np.array_equal(O.dequantize_weights(*q4), gu4.astype(np.float64))
 
 
 # ----------------------------------------------------------------------------------------------
@@ -612,12 +667,12 @@ def test_quantize_fp8_exact_on_its_grid_and_error_bound():
     vals[..., 5] = 448.0
     k = rng.integers(-12, -4, size=(2, 16, 1))
     w = (vals * 2.0 ** k).astype(np.float32)
-    codes, scales = O.quantize_weights(w, "f8")
+    codes, scales, _ = O.quantize_weights(w, "f8")
     assert np.array_equal(scales, (2.0 ** k[..., 0]).astype(np.float32))
     assert np.array_equal(O.dequantize_weights(codes, scales), w.astype(np.float64))
     w = I.bf16_bits_to_f32(I.round_to_bf16_bits(rng.normal(0.0, 0.02, size=(3, 32, 256)).astype(np.float32)))
     w[0, 0] = 0.0
-    codes, scales = O.quantize_weights(w, "f8")
+    codes, scales, _ = O.quantize_weights(w, "f8")
     assert scales[0, 0] == 0 and not codes[0, 0].any()
     deq = O.dequantize_weights(codes, scales)
     q = np.abs(w / np.where(scales > 0, scales, 1)[..., None])
