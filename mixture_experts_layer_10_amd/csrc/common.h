@@ -211,6 +211,33 @@ __device__ __forceinline__ u32x4 codes4_to_bf16(uint32_t c) {
   return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 
+// int4 words: eight codes k = 0..7 of one row at consecutive columns, code k as the nibble
+// code + 8 (0..15) in byte k % 4, low nibble for k < 4, high nibble for k >= 4.
+// With their group multiplier m (0..32): code * m exactly as bf16 (an integer of magnitude <= 224).
+__device__ __forceinline__ u32x4 codes4m_to_bf16(uint32_t c, uint32_t m) {
+  const float fm = static_cast<float>(m), off = -8.f * fm;
+  uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+  // opaque to the compiler, so that each code converts with one byte-to-float instruction instead
+  // of a 4-bit field extract and a conversion
+  asm("" : "+v"(lo), "+v"(hi));
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[k] = fmaf(static_cast<float>((lo >> (8 * k)) & 0xffu), fm, off);
+    f[k + 4] = fmaf(static_cast<float>((hi >> (8 * k)) & 0xffu), fm, off);
+  }
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+// The same word as the bf16 values 136 + code (128 + the stored nibble): each 16-bit half is the
+// byte 0x43 over a nibble, so one byte permute builds two of them. A product with these weights
+// exceeds the one with the codes by 136 times the sum of the other operand.
+__device__ __forceinline__ u32x4 codes4_biased_bf16(uint32_t c) {
+  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+  constexpr uint32_t kTop = 0x43434343u;
+  return u32x4{__builtin_amdgcn_perm(kTop, lo, 0x04010400u), __builtin_amdgcn_perm(kTop, lo, 0x04030402u),
+               __builtin_amdgcn_perm(kTop, hi, 0x04010400u), __builtin_amdgcn_perm(kTop, hi, 0x04030402u)};
+}
+
 // FP8 (OCP e4m3) codes -> bf16, exactly (3-bit mantissa, exponents 2^-9 .. 2^8 inside bf16's range):
 // code i in byte i, converted by the hardware e4m3 -> fp32 instruction two at a time.
 __device__ __forceinline__ u32x4 codesf8_to_bf16(u32x2 c) {

@@ -400,8 +400,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int A_INS = (A_GROUPS + NW - 1) / NW, B_INS = BNB / 16 / NW;
   constexpr int OUT_COLS = kSwiGLU ? BNB / 2 : BNB;
   constexpr int QS = kQ ? code_slot(kQ) : 16;              // bytes per lane slot of a weight block
-  constexpr int QB = 64 * QS;                              // bytes of one 16 x 32 weight block
-  constexpr int B_DMA = QS == 8 ? 2 * B_INS : B_INS;       // weight DMA instructions per wave per stage
+  // LDS bytes of one 16 x 32 weight block; int4: 256 bytes of codes, then its 16 rows' group
+  // multipliers (4 bytes per row, byte t for the slice of buffer t), repeated to fill 256 bytes
+  constexpr bool kQ4 = kQ == kQInt4;
+  constexpr int QB = kQ4 ? 512 : 64 * QS;
+  constexpr int B_DMA = (QS == 8 || kQ4) ? 2 * B_INS : B_INS;   // weight DMA instructions per wave per stage
   constexpr int PER_STAGE = A_INS + B_DMA;
   static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
   static_assert(!kWKN || (!kSwiGLU && !kPacked && kQ == 0 && BNB == 256), "[K][N] weights: bf16 down form, 256 columns");
@@ -419,10 +422,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * kSK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA2[BM * kSK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA3[BM * kSK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BNB * kSK * QS / 16];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BNB * kSK * QS / 16];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BNB * kSK * QS / 16];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB3[BNB * kSK * QS / 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BNB * QB / 32];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BNB * QB / 32];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BNB * QB / 32];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB3[BNB * QB / 32];
   __shared__ int s_pref[1025];
   __shared__ int s_off[1025];           // group row offsets (no global round trip per tile)
   __shared__ int s_tmp[16];
@@ -494,7 +497,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     // pipelined loop: the same sources as byte offsets from X (A) and from the group's weights bB (B)
     uint32_t oA[A_INS], oB[B_INS];
     const char* bB;
-    const char* srcQ[B_INS];          // quantised: this lane's 4 code bytes of k-block 0
+    const char* srcQ[B_INS];          // quantised: this lane's code bytes of k-block 0 (int4: its
+                                      // super-block slot)
+    const char* srcM[kQ4 ? B_INS : 1];  // int4: its row's multipliers in super-block 0
     float sc[TN];                     // quantised: scale of each of this lane's output columns
   };
   // tile r of this workgroup: (valid, group, m-tile, n-tile) from the tables in LDS
@@ -590,7 +595,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
         } else {
           rb = min(T.c0 / 16 + grp, NOUT / 16 - 1);
         }
-        if constexpr (kQ != 0)
+        if constexpr (kQ4) {
+          const char* sp = static_cast<const char*>(a.w) + quant_code_bytes(g, R, K, 4) +
+                           static_cast<int64_t>(rb) * (K / 128) * kQ4Super;
+          T.srcQ[j] = sp + lane * 16;
+          T.srcM[j] = sp + 1024 + 4 * (lane & 15);
+        } else if constexpr (kQ != 0)
           T.srcQ[j] = static_cast<const char*>(a.w) + quant_code_bytes(g, R, K, code_bits(kQ)) +
                       static_cast<int64_t>(rb) * (K / kSK) * QB + lane * 4;
         else if constexpr (pipe)
@@ -637,7 +647,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     for (int j = 0; j < A_INS; ++j) dma16(T.srcA[j] + kb, sa + ((wave * A_INS + j) % A_GROUPS) * 512);
 #pragma unroll
     for (int j = 0; j < B_INS; ++j) {
-      if constexpr (kQ != 0) {
+      if constexpr (kQ4) {
+        const int64_t so = static_cast<int64_t>(ks >> 2) * kQ4Super;
+        char* dst = reinterpret_cast<char*>(sb) + (wave * B_INS + j) * QB;
+        dma4(T.srcQ[j] + so + 4 * (ks & 3), dst);
+        dma4(T.srcM[j] + so, dst + 256);
+      } else if constexpr (kQ != 0) {
         const char* src = T.srcQ[j] + static_cast<int64_t>(ks) * QB;
         char* dst = reinterpret_cast<char*>(sb) + (wave * B_INS + j) * QB;
         dma4(src, dst);
@@ -657,6 +672,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     }
     if (n < A_INS) {
       dma16(T.srcA[n] + ks * kSK, sa + ((wave * A_INS + n) % A_GROUPS) * 512);
+    } else if constexpr (kQ4) {
+      const int b = n - A_INS, j = b / 2;
+      const int64_t so = static_cast<int64_t>(ks >> 2) * kQ4Super;
+      char* dst = reinterpret_cast<char*>(sb) + (wave * B_INS + j) * QB;
+      if (b % 2 == 0) dma4(T.srcQ[j] + so + 4 * (ks & 3), dst);
+      else dma4(T.srcM[j] + so, dst + 256);
     } else if constexpr (kQ != 0) {
       const int b = n - A_INS, j = QS == 8 ? b / 2 : b, half = QS == 8 ? b % 2 : 0;
       dma4(T.srcQ[j] + static_cast<int64_t>(ks) * QB + half * 256,
@@ -691,6 +712,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
     constexpr bool kDma = decltype(Dc)::value;
     // both k-steps' fragments are read first (the reads of the second overlap the first's steps)
     u32x4 fa[2][TM], fb[2][TN];
+    // int4: this lane's group multiplier in each block (one per slice: buffer t holds slices t mod 4)
+    uint32_t qm[kQ4 ? TN : 1];
+    if constexpr (kQ4) {
+      const int t = sb == sB0 ? 0 : sb == sB1 ? 1 : sb == sB2 ? 2 : 3;
+      const char* mb = reinterpret_cast<const char*>(sb) + (rb0 / 16 + ((lane >> 4) & 1)) * QB + 256 + 4 * (lane & 15) + t;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        constexpr int H = TN / 2;
+        const int rowoff = kSwiGLU ? (j < H ? j * 32 : BNB / 2 + (j - H) * 32) : j * 32;
+        qm[j] = *reinterpret_cast<const uint8_t*>(mb + rowoff / 16 * QB);
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -703,8 +736,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
           fb[kk][j] = codes8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
         else if constexpr (kQ == kQFp8)
           fb[kk][j] = codesf8_to_bf16(*reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
-        else if constexpr (kQ == kQInt4)
-          fb[kk][j] = codes4_to_bf16(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB));
+        else if constexpr (kQ4)
+          fb[kk][j] = codes4m_to_bf16(*reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sb) + koB[kk] + rowoff / 16 * QB), qm[j]);
         else if constexpr (kWKN)
           fb[kk][j] = lds_tr_frag<256>(sb, kk, rb0 + rowoff, lane);
         else
@@ -1099,7 +1132,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <int kQ> struct WRaw { typedef u32x4 T; };          // bf16: 8 values = 16 bytes per lane
 template <> struct WRaw<8> { typedef u32x2 T; };              // int8: 8 codes = 8 bytes
-template <> struct WRaw<4> { typedef uint32_t T; };           // int4: 8 codes = 4 bytes
+template <> struct WRaw<4> { typedef uint32_t T; };           // int4: 8 codes = 4 bytes (prefill LDS slots)
 template <> struct WRaw<kQFp8> { typedef u32x2 T; };          // fp8: 8 codes = 8 bytes
 
 template <int kQ>
@@ -1146,8 +1179,12 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   for (int c = 0; c < CB; ++c) col[c] = (cb0 + c) * 16 + (lane & 15);
   // wrow[j]: this lane's weight bytes of k-step 0 of block j; k-step ks is WSTEP bytes further.
   // packed: a column block's 16 rows are one row block; k-step ks of it is one block in lane order.
+  // int4: a lane's slot of a super-block holds U = 4 k-steps of codes (16 bytes), and its row's four
+  // group multipliers sit at moff from it (one 4-byte load per super-block)
+  constexpr bool kQ4 = kQ == kQInt4;
   const char* wrow[NB];
   constexpr int WSTEP = kQ ? 64 * code_slot(kQ) : (kPacked ? 1024 : 64);
+  const int moff = 1024 + 4 * (lane & 15) - lane * 16;
   const char* Wg = static_cast<const char*>(a.w) +
                    (kQ ? quant_code_bytes(g, R, K, code_bits(kQ)) : static_cast<int64_t>(g) * R * K * 2);
   float scl[NB];                             // quantised: the scale of each block's row for this lane
@@ -1159,7 +1196,9 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   for (int j = 0; j < NB; ++j) {
     const int cb = min(cb0 + j / NS, ncb - 1);
     const int up = (j % NS) * a.I;           // SwiGLU: the up rows follow the I gate rows
-    if constexpr (kPacked) {
+    if constexpr (kQ4) {
+      wrow[j] = Wg + static_cast<int64_t>(up / 16 + cb) * (K / 128) * kQ4Super + lane * 16;
+    } else if constexpr (kPacked) {
       constexpr int SLOT = kQ ? code_slot(kQ) : 16;   // bytes per lane slot
       wrow[j] = Wg + static_cast<int64_t>(up / 16 + cb) * (K / 32) * WSTEP + lane * SLOT;
     } else {
@@ -1185,27 +1224,65 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
       for (int j = 0; j < NB; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // register double buffer: the loads of the next U k-steps are issued before the matrix-core
     // steps of the current ones, so U k-steps of weight loads are always in flight
-    Raw fb[2][U][NB];
+    Raw fb[2][kQ4 ? 1 : U][NB];
+    u32x4 fq[2][kQ4 ? NB : 1];                   // int4: the super-block slots
+    uint32_t fm[2][kQ4 ? NB : 1];                // int4: their rows' group multipliers
     u32x4 fa[2][U][MB];
     auto load = [&](int buf, int k0) {
+      if constexpr (kQ4) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const char* sp = wrow[j] + static_cast<int64_t>(k0 / U) * kQ4Super;
+          fq[buf][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp));
+          fm[buf][j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sp + moff));
+        }
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        if constexpr (!kQ4) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          fb[buf][u][j] = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(wrow[j] + static_cast<int64_t>(k0 + u) * WSTEP));
+          for (int j = 0; j < NB; ++j)
+            fb[buf][u][j] = __builtin_nontemporal_load(reinterpret_cast<const Raw*>(wrow[j] + static_cast<int64_t>(k0 + u) * WSTEP));
+        }
 #pragma unroll
         for (int b = 0; b < MB; ++b) fa[buf][u][b] = *reinterpret_cast<const u32x4*>(xrow[b] + (k0 + u) * 32);
       }
     };
+    // int4: the words enter the matrix cores as the bf16 values 136 + code (two per byte permute);
+    // a k-step's product with them, less 136 times the step's activation sums (one product with
+    // ones, shared by the task's blocks), times the step's group multiplier, is added to the sums
     auto math = [&](int buf) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        if constexpr (kQ4) {
+          constexpr uint32_t kOne2 = 0x3F803F80u;               // two bf16 ones
+          f32x4 sum[MB];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const u32x4 w = to_bf16_frag<kQ>(fb[buf][u][j]);
+          for (int b = 0; b < MB; ++b)
+            sum[b] = mfma16(fa[buf][u][b], u32x4{kOne2, kOne2, kOne2, kOne2}, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int b = 0; b < MB; ++b) acc[b][j] = mfma16(fa[buf][u][b], w, acc[b][j]);
+          for (int j = 0; j < NB; ++j) {
+            const u32x4 w = codes4_biased_bf16(fq[buf][j][u]);
+            const float mj = static_cast<float>((fm[buf][j] >> (8 * u)) & 0xffu);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+              const f32x4 t = mfma16(fa[buf][u][b], w, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[b][j][e] = fmaf(mj, fmaf(-136.f, sum[b][e], t[e]), acc[b][j][e]);
+              // the sums are formed here, not sunk to the end of the batch (which would keep every
+              // step's products live at once)
+              asm volatile("" : "+v"(acc[b][j]));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const u32x4 w = to_bf16_frag<kQ>(fb[buf][u][j]);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[b][j] = mfma16(fa[buf][u][b], w, acc[b][j]);
+          }
         }
+      }
     };
     const int full = ksteps / U;                 // U-step batches
     int ks = full * U;
@@ -1220,13 +1297,15 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
       }
       if (q < full) math(0);                     // odd batch count: the last one sits in buffer 0
     }
-    for (; ks < ksteps; ++ks) {
+    if constexpr (!kQ4) {                        // int4 has none (K % 128 == 0)
+      for (; ks < ksteps; ++ks) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const u32x4 w = to_bf16_frag<kQ>(__builtin_nontemporal_load(reinterpret_cast<const Raw*>(wrow[j] + static_cast<int64_t>(ks) * WSTEP)));
+        for (int j = 0; j < NB; ++j) {
+          const u32x4 w = to_bf16_frag<kQ>(__builtin_nontemporal_load(reinterpret_cast<const Raw*>(wrow[j] + static_cast<int64_t>(ks) * WSTEP)));
 #pragma unroll
-        for (int b = 0; b < MB; ++b)
-          acc[b][j] = mfma16(*reinterpret_cast<const u32x4*>(xrow[b] + ks * 32), w, acc[b][j]);
+          for (int b = 0; b < MB; ++b)
+            acc[b][j] = mfma16(*reinterpret_cast<const u32x4*>(xrow[b] + ks * 32), w, acc[b][j]);
+        }
       }
     }
     if constexpr (kQ != 0) {
@@ -1433,7 +1512,7 @@ static void launch_stream(const GemmArgs& a, hipStream_t st) {
   constexpr int out_cols = kSwiGLU ? BNB / 2 : BNB;
   const int NOUT = kSwiGLU ? a.I : a.D;
   const int n_tiles = (NOUT + out_cols - 1) / out_cols;
-  constexpr int lds = 4 * (BM * 2 + BNB * (kQ ? code_bits(kQ) : 16) / 8) * kSK;
+  constexpr int lds = 4 * (BM * 2 + BNB * (kQ ? (kQ == kQInt4 ? 8 : code_bits(kQ)) : 16) / 8) * kSK;
   // Short-row tiles (few rows per group) are pure weight streams: one workgroup per tile lets the
   // dispatcher start a new tile wherever one finishes instead of running fixed rounds with a
   // half-empty last round. Tall tiles keep a persistent grid (one prologue per workgroup).

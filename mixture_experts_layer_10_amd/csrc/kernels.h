@@ -88,11 +88,21 @@ bool bwd_fusable(bool bf16, bool grouped, int64_t max_rows, int G, int D, int I)
 // matrix-core lane order (lane l: row rb*16 + l % 16, k = kb*32 + 8 (l / 16) .. + 7).
 void launch_pack(const uint16_t* src, uint16_t* dst, int64_t G, int R, int K, hipStream_t st);
 
-// Quantised stack of a [G, R, K] bf16 matrix (R % 16 == 0, K % 32 == 0) with b = 8 or 4 bits:
-// codes in the packed block order, block (g, rb, kb) of 64 b bytes at ((g * R/16 + rb) * K/32 + kb)
-// * 64 b, slot l (b bytes) = row rb*16 + l % 16, columns kb*32 + 8 (l / 16) .. + 7; then one fp32
-// scale per row, [G, R], from byte G R K b / 8 on.
-__host__ __device__ inline int64_t quant_code_bytes(int64_t G, int64_t R, int64_t K, int bits) { return G * R * K * bits / 8; }
+// Quantised stack of a [G, R, K] bf16 matrix (R % 16 == 0), codes first, then one fp32 scale per
+// row, [G, R], from byte quant_code_bytes(G, R, K, b) on.
+// int8 / FP8 (K % 32 == 0): codes in the packed block order, block (g, rb, kb) of 512 bytes at
+// ((g * R/16 + rb) * K/32 + kb) * 512, slot l (8 bytes) = row rb*16 + l % 16, columns kb*32 +
+// 8 (l / 16) .. + 7.
+// int4 (K % 128 == 0): super-blocks of 16 rows x 128 columns, (g, rb, kq) at ((g * R/16 + rb) *
+// K/128 + kq) * kQ4Super: 1024 bytes of codes, slot l (16 bytes) = row rb*16 + l % 16, its bytes
+// 4 t .. 4 t + 3 the eight codes of columns (4 kq + t) * 32 + 8 (l / 16) .. + 7 (code i as the
+// nibble code + 8 in byte i % 4, the high nibble for i >= 4);
+// then 64 bytes of group multipliers, byte 1024 + 4 r + t = row rb*16 + r, columns (4 kq + t) * 32
+// .. + 31. A weight is code * multiplier * row scale.
+constexpr int kQ4Super = 1088;
+__host__ __device__ inline int64_t quant_code_bytes(int64_t G, int64_t R, int64_t K, int bits) {
+  return bits == 4 ? G * (R / 16) * (K / 128) * kQ4Super : G * R * K * bits / 8;
+}
 // Code kinds (GemmArgs::qbits and kernel template arguments): bits per code, FP8 marked apart.
 constexpr int kQInt8 = 8, kQInt4 = 4, kQFp8 = 9;
 __host__ __device__ constexpr int code_bits(int kind) { return kind == kQFp8 ? 8 : kind; }    // 0 for bf16

@@ -607,6 +607,8 @@ static int quant_shape_checks(const moe_config* cfg, int64_t n_groups, int64_t r
     return fail(MOE_ERR_UNSUPPORTED, "quantisation needs rows %% 16 == 0 and cols %% 32 == 0 (got %lld x %lld)",
                 (long long)rows, (long long)cols);
   if (rows > (1 << 24) || cols > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "rows/cols above 2^24");
+  if (quant_kind(cfg) == kQInt4 && cols % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "int4 needs cols %% 128 == 0 (got %lld)", (long long)cols);
   return MOE_OK;
 }
 

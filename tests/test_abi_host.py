@@ -148,7 +148,12 @@ def test_quantized_bytes_and_layout_rules(lib, layout, bits):
     c = B.make_config(64, 256, 16, 2, 128, shared_inter=384, layout=layout)
     assert B.moe_workspace_bytes(c) > 0
     G, R, K = 16, 256, 2048
-    assert B.moe_quantized_bytes(c, G, R, K) == G * R * K * bits // 8 + G * R * 4
+    codes = G * (R // 16) * (K // 128) * 1088 if bits == 4 else G * R * K * bits // 8   # int4: 64 multiplier bytes per 1 KB
+    assert B.moe_quantized_bytes(c, G, R, K) == codes + G * R * 4
+    if bits == 4:                                            # int4 super-blocks are 128 columns wide
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_quantized_bytes(c, G, R, 96)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "128" in str(ei.value)
     # the quantised layouts follow the packed shape rules
     for bad in (B.make_config(64, 256, 16, 2, 128, dtype="f32", layout=layout),
                 B.make_config(64, 256, 16, 2, 96, layout=layout),

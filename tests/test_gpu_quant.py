@@ -25,19 +25,25 @@ BITS = [8, 4, "f8"]
 SEED = {8: 8, 4: 4, "f8": 9}
 
 
-def quant_reference_bytes(codes, scales, bits):
-    """Documented byte image of a quantised stack: codes in block order (block (g, rb, kb), slot
-    l = row l % 16, column chunk l / 16, 8 codes per slot; int4 two per byte, low nibble first),
-    then the fp32 scales as [G, R]."""
+def quant_reference_bytes(codes, scales, bits, mults=None):
+    """Documented byte image of a quantised stack, then the fp32 scales as [G, R].
+    int8 / FP8: codes in block order (block (g, rb, kb), slot l = row l % 16, column chunk l / 16,
+    8 codes per slot). int4: super-blocks (g, rb, kq) of 16 rows x 128 columns, 1024 code bytes with
+    slot l = row l % 16, chunk l / 16 of each of the four 32-column k-steps t (4 bytes per t: code i
+    as the nibble code + 8 in byte i % 4, high nibble for i >= 4), then the 16 rows' multipliers,
+    4 bytes per row (one per t)."""
     G, R, K = codes.shape
-    slots = codes.reshape(G, R // 16, 16, K // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1, 8)
-    if bits == "f8":
-        code_bytes = slots.astype(np.uint8).reshape(-1)
-    elif bits == 8:
-        code_bytes = slots.astype(np.int8).view(np.uint8).reshape(-1)
+    if bits != 4:
+        slots = codes.reshape(G, R // 16, 16, K // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1, 8)
+        code_bytes = slots.astype(np.uint8).reshape(-1) if bits == "f8" else slots.astype(np.int8).view(np.uint8).reshape(-1)
     else:
-        nib = (slots.astype(np.int16) & 0xF).astype(np.uint8)
-        code_bytes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).reshape(-1)
+        # (g, rb, r, kq, t, q8, i) -> (g, rb, kq, q8, r, t, i): slot l = q8 * 16 + r, bytes 4 t ..;
+        # code i of a word as the nibble code + 8 in byte i % 4, high nibble for i >= 4
+        c = codes.reshape(G, R // 16, 16, K // 128, 4, 4, 8).transpose(0, 1, 3, 5, 2, 4, 6)
+        nib = (c.astype(np.int16) + 8).astype(np.uint8)
+        cb = (nib[..., :4] | (nib[..., 4:] << 4)).reshape(G, R // 16, K // 128, 1024)
+        m = np.asarray(mults, np.uint8).reshape(G, R // 16, 16, K // 128, 4).transpose(0, 1, 3, 2, 4)
+        code_bytes = np.concatenate([cb, m.reshape(G, R // 16, K // 128, 64)], axis=-1).reshape(-1)
     sc = np.ascontiguousarray(np.asarray(scales, np.float32))
     return np.concatenate([code_bytes, sc.view(np.uint8).reshape(-1)])
 
@@ -68,8 +74,11 @@ def quant_stack(cfg, w_dev, G, R, K):
 
 
 @pytest.mark.parametrize("bits", BITS)
-@pytest.mark.parametrize("G,R,K", [(1, 16, 32), (3, 48, 96), (2, 1536, 2048), (5, 2048, 768)])
+@pytest.mark.parametrize("G,R,K", [(1, 16, 32), (3, 48, 96), (1, 16, 128), (3, 48, 384), (2, 1536, 2048),
+                                   (5, 2048, 768)])
 def test_quantize_weights_bit_exact(bits, G, R, K):
+    if bits == 4 and K % 128:
+        pytest.skip("int4 super-blocks need K % 128 == 0 (refused at the boundary, tests/test_abi_host.py)")
     say(f"[quantize] {bits} {G}x{R}x{K}")
     rng = np.random.default_rng(G * 100 + R + K + SEED[bits])
     w = rng.normal(0.0, 0.02, size=(G, R, K)).astype(np.float32)
@@ -80,11 +89,11 @@ def test_quantize_weights_bit_exact(bits, G, R, K):
     cfg = B.make_config(1, 128, 16, 1, 128, layout=LAYOUT[bits])
     got = quant_stack(cfg, src, G, R, K)
     torch.cuda.synchronize()
-    codes, scales = O.quantize_weights(I.bf16_bits_to_f32(bits16), bits)
-    ref = quant_reference_bytes(codes, scales, bits)
+    codes, scales, mults = O.quantize_weights(I.bf16_bits_to_f32(bits16), bits)
+    ref = quant_reference_bytes(codes, scales, bits, mults)
     gb = got.cpu().numpy()
     assert gb.size == ref.size
-    n_codes = G * R * K * (4 if bits == 4 else 8) // 8
+    n_codes = G * (R // 16) * (K // 128) * 1088 if bits == 4 else G * R * K
     bad = np.nonzero(gb[:n_codes] != ref[:n_codes])[0]
     assert bad.size == 0, f"{bad.size} code bytes differ, first at {bad[:5]}"
     assert np.array_equal(gb[n_codes:], ref[n_codes:])
