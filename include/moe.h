@@ -45,8 +45,8 @@
  * (with the same n_groups, rows and cols the expert entry points see), w_router is packed as for
  * MOE_LAYOUT_PACKED and w_shared_gate keeps its layout. Same shape rules as MOE_LAYOUT_PACKED. The
  * layer then computes with the weights code * scale (for FP8, the e4m3 value of the code times the
- * scale): the codes enter the matrix cores exactly (as bf16) and each output column's fp32 sum is
- * multiplied by its row's scale.
+ * scale; for int4, code * group multiplier * row scale): the codes enter the matrix cores exactly
+ * (as bf16) and each output column's fp32 sum is multiplied by its row's scale.
  *
  * Expert outputs (moe_config.expert_out): the per-assignment outputs out[p, :] that the down
  * projection writes and moe_combine weights and sums ("27. Mixture of experts", section "Dispatch",
@@ -207,24 +207,36 @@ int moe_expert_ffn(const moe_config* cfg, int64_t n_groups, int64_t inter, int64
 int moe_pack_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src,
                      void* dst, void* stream);
 
-/* Weight-only quantisation of a row-major bf16 stack src [G, R, K] (R % 16 == 0, K % 32 == 0)
- * into dst, once at model load. b = 8 (cfg.weight_layout MOE_LAYOUT_Q8 or MOE_LAYOUT_F8) or 4
- * (MOE_LAYOUT_Q4); cfg gives dtype (must be bf16) and weight_layout, its other fields are not used.
- * Rule, per output row r (symmetric absmax, one scale per row; the pages give the bit widths, not
- * the quantiser):
- *   m = max |w| over the row, scale = m / Q in fp32 (IEEE division), Q = 127 (b = 8) or 7 (b = 4)
- *   code = clamp(rint(w / scale), -Q, Q), the fp32 quotient rounded to nearest, ties to even;
- *   an all-zero row has scale 0 and codes 0.
- * FP8 (MOE_LAYOUT_F8): scale = m / 448 and code = the OCP e4m3 byte (1 sign, 4 exponent bits with
- *   bias 7, 3 mantissa bits, subnormals below 2^-6) nearest to clamp(w / scale, -448, 448), ties to
- *   the even mantissa, the sign of zero kept; an all-zero row has scale 0 and codes 0.
- * dst layout (moe_quantized_bytes() bytes, 16-byte aligned, not overlapping src):
- *   codes: G R K b / 8 bytes in the block order of moe_pack_weights: block (g, rb, kb) of rows
- *     rb*16 .. +15 and columns kb*32 .. +31 takes 64 b bytes at ((g * R/16 + rb) * K/32 + kb) * 64 b;
- *     its slot l (b bytes, l = 0..63) holds the codes of row rb*16 + l % 16, columns
- *     kb*32 + 8 (l / 16) + i, i = 0..7: b = 8 byte i (two's complement, or the e4m3 byte for
- *     FP8), b = 4 bits 4i..4i+3 (two's complement; byte i / 2, low nibble first);
- *   scales: fp32 [G, R] from byte G R K b / 8 on. */
+/* Weight-only quantisation of a row-major bf16 stack src [G, R, K] into dst, once at model load:
+ * int8 or FP8 (cfg.weight_layout MOE_LAYOUT_Q8 / MOE_LAYOUT_F8; R % 16 == 0, K % 32 == 0) or int4
+ * (MOE_LAYOUT_Q4; R % 16 == 0, K % 128 == 0); cfg gives dtype (must be bf16) and weight_layout, its
+ * other fields are not used. The pages give bit widths, not a quantiser. Rules, per output row r
+ * (every division an IEEE fp32 division, every rounding to nearest with ties to even):
+ *   int8: m = max |w| over the row, scale = m / 127, code = clamp(rint(w / scale), -127, 127).
+ *   FP8: scale = m / 448, code = the OCP e4m3 byte (1 sign, 4 exponent bits with bias 7, 3
+ *     mantissa bits, subnormals below 2^-6) nearest to clamp(w / scale, -448, 448), the sign of zero
+ *     kept.
+ *   int4 (a scale per 32 columns, as the row scale times an integer): s = m / 224 (the row scale);
+ *     for each group q of columns 32 q .. 32 q + 31, mult = min(ceil(max |w over q| / (7 s)), 32)
+ *     with 7 s an fp32 product, step = s * mult (fp32), code = clamp(rint(w / step), -7, 7); the
+ *     weight is code * mult * s, and code * mult (|.| <= 224) is exact in bf16.
+ *   An all-zero row has scale 0 and codes 0 (int4: multipliers 0); an all-zero int4 group has
+ *   multiplier 0 and codes 0.
+ * dst layout (moe_quantized_bytes() bytes, 16-byte aligned, not overlapping src): codes, then the
+ * scales fp32 [G, R] (int4: the row scales s).
+ *   int8 / FP8 codes, G R K bytes in the block order of moe_pack_weights: block (g, rb, kb) of rows
+ *     rb*16 .. +15 and columns kb*32 .. +31 takes 512 bytes at ((g * R/16 + rb) * K/32 + kb) * 512;
+ *     its slot l (8 bytes, l = 0..63) holds the codes of row rb*16 + l % 16, columns
+ *     kb*32 + 8 (l / 16) + i, i = 0..7, in byte i (two's complement, or the e4m3 byte).
+ *   int4 codes, in super-blocks of 16 rows x 128 columns: super-block (g, rb, kq) of rows rb*16 ..
+ *     +15 and columns kq*128 .. +127 takes 1088 bytes at ((g * R/16 + rb) * K/128 + kq) * 1088.
+ *     Its first 1024 bytes are 64 slots of 16 bytes; slot l holds row rb*16 + l % 16, and its bytes
+ *     4 t .. 4 t + 3 (t = 0..3) the codes of columns (4 kq + t) * 32 + 8 (l / 16) + i, i = 0..7, code
+ *     i as the 4-bit value code + 8 in byte i % 4, the low nibble for i < 4 and the high nibble for
+ *     i >= 4. The last 64 bytes are the multipliers: byte 1024 + 4 r + t for row rb*16 + r and
+ *     columns (4 kq + t) * 32 .. + 31.
+ * moe_quantized_bytes: G R K + 4 G R bytes for int8 / FP8, 1088 G (R / 16) (K / 128) + 4 G R for
+ * int4. */
 int moe_quantized_bytes(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, size_t* bytes);
 int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, int64_t cols, const void* src,
                          void* dst, void* stream);
