@@ -137,10 +137,12 @@ EXPERT_OUT = {"f32": 0, "f16s": 1}
 
 
 def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, data=None, extras=True, expert_out="f16s"):
-    """Times `steps` whole-path steps. With inner_events the gate_up launch of every timed step is
-    bracketed by events on its stream (its duration comes from the timed region itself); without,
-    the timed steps carry no events (a recorded event idles the GPU for a few microseconds, which
-    matters at decode sizes) and the gate_up duration comes from a second run of `steps` steps.
+    """Times `steps` whole-path steps. With inner_events every timed step is the decomposed chain of
+    ABI calls with its gate_up launch bracketed by events on its stream (its duration comes from the
+    timed region itself; at this size moe_forward launches exactly these kernels); without, the timed
+    steps are moe_forward calls carrying no events (a recorded event idles the GPU for a few
+    microseconds, which matters at decode sizes) and the gate_up duration comes from a second run of
+    `steps` decomposed steps.
     layout: 1 packed bf16 experts (rows if the shape cannot be packed), 2 / 3 / 4 int8 / int4 / fp8
     experts. expert_out: "f16s" keeps the per-assignment expert outputs as fp16 values with a
     power-of-two exponent per 16 columns where the layer allows it (bf16 rows or packed weights,
@@ -170,13 +172,15 @@ def run_workload(name, steps, warmup, out_dtype, inner_events=True, layout=1, da
         f"{LAYOUT_NAMES[cfg.weight_layout]}, expert outputs {'f16s' if cfg.expert_out else 'f32'})")
     chain = Chain(cfg, dev)
     y_ref = B.forward(cfg, dev)
+    bits = lambda t: t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+    chain.decomposed()
+    torch.cuda.synchronize()
+    assert torch.equal(bits(chain.y), bits(y_ref)), "the decomposed chain and moe_forward disagree"
+    counts = chain.counts.cpu().numpy()
     for _ in range(warmup):
         chain.step()
     torch.cuda.synchronize()
-    assert torch.equal(chain.y.view(torch.int16 if chain.y.dtype == torch.bfloat16 else torch.int32),
-                       y_ref.view(torch.int16 if y_ref.dtype == torch.bfloat16 else torch.int32)), \
-        "chain and moe_forward disagree"
-    counts = chain.counts.cpu().numpy()
+    assert torch.equal(bits(chain.y), bits(y_ref)), "moe_forward is not deterministic"
     touched = int((counts > 0).sum())
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     all0, all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -475,7 +479,11 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    main_run = run_workload(args.workload, args.steps, args.warmup, args.out_dtype, expert_out=args.expert_out)
+    # gate_up events inside the timed steps where the decomposed chain launches what moe_forward
+    # launches (batches above 64 tokens); smaller batches time moe_forward itself
+    from mixture_experts_layer_10_amd import inputs as I
+    main_run = run_workload(args.workload, args.steps, args.warmup, args.out_dtype, expert_out=args.expert_out,
+                            inner_events=I.WORKLOADS[args.workload].n_tokens > 64)
     shape, alg = main_run["shape"], main_run["alg"]
     gemm_s = main_run["gate_up_ms"] / 1e3
     # the roofline that binds: arithmetic intensity of the gate_up launch against the ridge point

@@ -1,7 +1,8 @@
-"""The block as the chain of C-ABI calls moe_forward makes internally (route -> permute ->
-gate_up -> down -> [shared gate_up -> down] -> combine), with every buffer allocated once.
-Used by the benchmark to time the expert GEMMs on their own with events on the launch stream;
-the chain produces the same bits as moe_forward."""
+"""The block with every buffer allocated once, run either as one moe_forward call (step() without
+events) or as the chain of C-ABI calls moe_forward is made of (route -> permute -> gate_up -> down
+-> [shared gate_up -> down] -> combine; decomposed()), so that the benchmark can put events around
+the gate_up launch. Both produce the same bits; moe_forward may merge the routing and grouping of
+small batches into fewer launches."""
 from __future__ import annotations
 
 import torch
@@ -29,6 +30,15 @@ class Chain:
         self.A = A
 
     def step(self, gate_up_events=None):
+        """One pass of the block: moe_forward, or the decomposed chain when gate_up events are given."""
+        if gate_up_events is not None:
+            return self.decomposed(gate_up_events)
+        c, d = self.cfg, self.dev
+        B.moe_forward(c, d["x"], d["w_router"], d["gate_up"], d["down"], d.get("shared_gate_up"), d.get("shared_down"),
+                      d.get("w_shared_gate") if self.gated else None, self.y, self.weights, self.experts, self.ws)
+        return self.y
+
+    def decomposed(self, gate_up_events=None):
         c, d = self.cfg, self.dev
         B.moe_route(c, d["x"], d["w_router"], d.get("w_shared_gate") if self.gated else None, None,
                     self.weights, self.experts, self.shared_scale, self.ws)

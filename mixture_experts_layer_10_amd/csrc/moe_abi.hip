@@ -173,9 +173,9 @@ static size_t permute_ws_bytes(const moe_config* c) {
     if (_s != MOE_OK) return _s; \
   } while (0)
 
-static int route_impl(const moe_config* c, const void* x, const void* w_router, const void* w_shared_gate,
-                      float* logits, float* weights, int32_t* experts, float* shared_scale, float* partial,
-                      hipStream_t st, bool sigmoid = false, const float* bias = nullptr) {
+static RouteArgs route_args(const moe_config* c, const void* x, const void* w_router, const void* w_shared_gate,
+                            float* logits, float* weights, int32_t* experts, float* shared_scale, float* partial,
+                            bool sigmoid = false, const float* bias = nullptr) {
   RouteArgs a{};
   a.sigmoid = sigmoid;
   a.bias = bias;
@@ -194,13 +194,18 @@ static int route_impl(const moe_config* c, const void* x, const void* w_router, 
   a.norm = c->norm_topk_prob;
   a.bf16 = c->dtype == MOE_BF16;
   a.packed = c->weight_layout != MOE_LAYOUT_ROWS;     // quantised layouts keep a packed bf16 router
-  launch_route(a, st);
+  return a;
+}
+
+static int route_impl(const moe_config* c, const void* x, const void* w_router, const void* w_shared_gate,
+                      float* logits, float* weights, int32_t* experts, float* shared_scale, float* partial,
+                      hipStream_t st, bool sigmoid = false, const float* bias = nullptr) {
+  launch_route(route_args(c, x, w_router, w_shared_gate, logits, weights, experts, shared_scale, partial, sigmoid, bias), st);
   return check_launch("moe_route");
 }
 
-static int permute_impl(const moe_config* c, const int32_t* experts, const void* x, int32_t* counts,
-                        int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, int32_t* block_counts,
-                        hipStream_t st, int64_t capacity = INT64_MAX) {
+static PermuteArgs permute_args(const moe_config* c, const int32_t* experts, int32_t* counts, int32_t* offsets,
+                                int32_t* token_of, int32_t* slot_pos, int32_t* block_counts, int64_t capacity = INT64_MAX) {
   PermuteArgs a{};
   a.capacity = capacity;
   a.experts = experts;
@@ -212,6 +217,13 @@ static int permute_impl(const moe_config* c, const int32_t* experts, const void*
   a.A = c->n_tokens * c->top_k;
   a.E = static_cast<int>(c->n_experts);
   a.k = static_cast<int>(c->top_k);
+  return a;
+}
+
+static int permute_impl(const moe_config* c, const int32_t* experts, const void* x, int32_t* counts,
+                        int32_t* offsets, int32_t* token_of, int32_t* slot_pos, void* x_perm, int32_t* block_counts,
+                        hipStream_t st, int64_t capacity = INT64_MAX) {
+  const PermuteArgs a = permute_args(c, experts, counts, offsets, token_of, slot_pos, block_counts, capacity);
   launch_permute(a, st);
   if (x_perm)
     launch_gather_rows(x, token_of, offsets + a.E, x_perm, a.A, c->hidden * static_cast<int64_t>(elem_bytes(c->dtype)), st);
