@@ -42,10 +42,11 @@ def log(msg):
 
 def algorithmic(shape, touched, wbits=None):
     """FLOPs and bytes the method itself must do (not the dense all-expert work it avoids).
-    wbits: bits per expert weight when the experts are quantised (one fp32 scale per weight row)."""
+    wbits: bits per expert weight when the experts are quantised (one fp32 scale per weight row;
+    int4 also one multiplier byte per 32 weights)."""
     N, D, E, k, I, Is = shape.n_tokens, shape.hidden, shape.n_experts, shape.top_k, shape.inter, shape.shared_inter
     b = 2 if shape.dtype == "bf16" else 4
-    wb = b if wbits is None else wbits / 8              # bytes per expert weight
+    wb = b if wbits is None else wbits / 8 + (1 / 32 if wbits == 4 else 0)   # bytes per expert weight
     rows = lambda n_out_rows: 0 if wbits is None else n_out_rows * 4      # scale bytes
     flops = 2 * N * D * E + 6 * D * I * N * k + (6 * D * Is * N + 2 * N * D if Is else 0)
     bytes_ = (touched * (3 * D * I * wb + rows(2 * I + D)) + E * D * b
