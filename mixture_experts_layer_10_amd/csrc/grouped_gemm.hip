@@ -433,6 +433,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
   __shared__ int s_cnt[2 * NW * 8];
   // pipelined loop with gathered rows: the next tile's BM row indices, staged by DMA a tile ahead
   __shared__ __attribute__((aligned(16))) int s_rows[BM];
+  // epilogue staging, 2 KB per wave: the fp16-form outputs of down (16 rows x 128 bytes at a time,
+  // stored 8 rows x 128 contiguous bytes per instruction) and gate_up's h (32 rows x 64 bytes,
+  // stored 16 rows x 64 contiguous bytes per instruction)
+  __shared__ __attribute__((aligned(16))) char s_stage[kSwap && !kBwd ? NW * 2048 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -941,7 +945,107 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] *= cur.sc[j];
     }
-    if constexpr (kSwap) {
+    bool staged = false;
+    if constexpr (kSwap && !kSwiGLU && !kBwd && TN == 2) {
+      if (a.out_f16s && NOUT % 64 == 0) {
+        // fp16 form, a wave's 64 columns whole (in or out): per 32-row block, each lane forms its
+        // four 16-byte runs (see below), the rows of each half-block go through the wave's 2 KB of
+        // LDS, and every lane then stores 16 bytes of one row: 8 rows x 128 contiguous bytes per
+        // instruction. The row's four exponent bytes are contiguous and go as one 4-byte store.
+        staged = true;
+        char* st = s_stage + wave * 2048;
+        const int hf = lane >> 5, r32 = lane & 31;
+        const int wcol = c0 + wn * TN * 32;
+        const int64_t RB = f16s_row_bytes(NOUT);
+        char* O = static_cast<char*>(a.out);
+        if (wcol < NOUT) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int rb = m0 + (wm * TM + i) * 32;            // first row of the block
+            u32x4 run[TN][2];
+            uint32_t exw = 0;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int g = 0; g < 2; ++g) {
+                const f32x16& c = acc[i][j];
+                float m = 0.f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(c[8 * g + t]));
+                m = fmaxf(m, __shfl_xor(m, 32, kWave));
+                const int ex = f16s_exp(m);
+                exw |= static_cast<uint32_t>(ex & 0xff) << (8 * (2 * j + g));
+                // lane l < 32 holds columns 0-3 and 8-11 of the group, l + 32 columns 4-7 and
+                // 12-15: one 8-byte exchange gives each a contiguous half (0-7 or 8-15)
+                const int q0 = 2 * g;
+                const u32x2 lo = u32x2{pack_f16x2_scaled(c[4 * q0], c[4 * q0 + 1], ex), pack_f16x2_scaled(c[4 * q0 + 2], c[4 * q0 + 3], ex)};
+                const u32x2 hi = u32x2{pack_f16x2_scaled(c[4 * q0 + 4], c[4 * q0 + 5], ex), pack_f16x2_scaled(c[4 * q0 + 6], c[4 * q0 + 7], ex)};
+                const u32x2 send = hf ? lo : hi;
+                const u32x2 got = u32x2{static_cast<uint32_t>(__shfl_xor(static_cast<int>(send[0]), 32, kWave)),
+                                        static_cast<uint32_t>(__shfl_xor(static_cast<int>(send[1]), 32, kWave))};
+                run[j][g] = hf ? u32x4{got[0], got[1], hi[0], hi[1]} : u32x4{lo[0], lo[1], got[0], got[1]};
+              }
+            if (hf == 0 && rb + r32 < rows)
+              *reinterpret_cast<uint32_t*>(O + (row0 + rb + r32) * RB + 2 * NOUT + wcol / 16) = exw;
+#pragma unroll
+            for (int ph = 0; ph < 2; ++ph) {
+              if ((r32 >> 4) == ph) {                           // rows 16 ph .. 16 ph + 15 of the block
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                  for (int g = 0; g < 2; ++g)
+                    *reinterpret_cast<u32x4*>(st + (r32 & 15) * 128 + 64 * j + 32 * g + 16 * hf) = run[j][g];
+              }
+#pragma unroll
+              for (int it = 0; it < 2; ++it) {
+                const int off = it * 1024 + lane * 16;
+                const int r = rb + 16 * ph + (off >> 7);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(st + off);
+                if (r < rows) *reinterpret_cast<u32x4*>(O + (row0 + r) * RB + 2 * wcol + (off & 127)) = v;
+              }
+            }
+          }
+        }
+      }
+    }
+    if constexpr (kSwap && kSwiGLU && !kBwd && TN == 2) {
+      if (NOUT % 32 == 0) {
+        // h, a wave's 32 columns whole (in or out): per 32-row block each lane forms four 8-byte
+        // runs (columns 8 q + 4 (lane / 32) .. + 3), the block's 32 rows x 64 bytes go through the
+        // wave's 2 KB of LDS, and each lane then stores 16 bytes of one row, 16 rows x 64 contiguous
+        // bytes per instruction
+        staged = true;
+        char* st = s_stage + wave * 2048;
+        const int hf = lane >> 5, r32 = lane & 31;
+        const int wcol = c0 + wn * 32;
+        uint16_t* Hh = static_cast<uint16_t*>(a.out);
+        if (wcol < NOUT) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int rb = m0 + (wm * TM + i) * 32;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint16_t v[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) v[t] = f32_to_bf16(silu(acc[i][0][4 * q + t]) * acc[i][1][4 * q + t]);
+              *reinterpret_cast<u32x2*>(st + r32 * 64 + 16 * q + 8 * hf) =
+                  u32x2{v[0] | (static_cast<uint32_t>(v[1]) << 16), v[2] | (static_cast<uint32_t>(v[3]) << 16)};
+            }
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+              const int off = it * 1024 + lane * 16;
+              const int r = rb + (off >> 6);
+              const u32x4 v = *reinterpret_cast<const u32x4*>(st + off);
+              if (r < rows)
+                *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(Hh + (row0 + r) * NOUT + wcol) + (off & 63)) = v;
+            }
+          }
+        }
+      }
+    }
+    if (staged) {
+      // stored above
+    } else if constexpr (kSwap) {
       // block (i, j): token m0 + (wm TM + i) 32 + lane % 32; element e is output column
       // 8 (e / 4) + 4 (lane / 32) + e % 4 of the block
       const bool vec = NOUT % 4 == 0;
@@ -1043,12 +1147,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
               const int ex = f16s_exp(m);
               const int gcol = c0 + (wn * TN + j) * 32 + 16 * g;   // NOUT % 16 == 0: in or out whole
               if (gcol < NOUT) {
-#pragma unroll
-                for (int qq = 0; qq < 2; ++qq) {
-                  const int q = 2 * g + qq, col = gcol + 8 * qq + 4 * (lane >> 5);
-                  *reinterpret_cast<u32x2*>(Ob + 2 * col) =
-                      u32x2{pack_f16x2_scaled(c[4 * q], c[4 * q + 1], ex), pack_f16x2_scaled(c[4 * q + 2], c[4 * q + 3], ex)};
-                }
+                // lane l < 32 holds columns 0-3 and 8-11 of the group, l + 32 columns 4-7 and 12-15:
+                // one exchange of 8 bytes gives each a contiguous half (0-7, or 8-15) to store as 16 bytes
+                const int q0 = 2 * g;
+                const u32x2 lo = u32x2{pack_f16x2_scaled(c[4 * q0], c[4 * q0 + 1], ex), pack_f16x2_scaled(c[4 * q0 + 2], c[4 * q0 + 3], ex)};
+                const u32x2 hi = u32x2{pack_f16x2_scaled(c[4 * q0 + 4], c[4 * q0 + 5], ex), pack_f16x2_scaled(c[4 * q0 + 6], c[4 * q0 + 7], ex)};
+                const bool upper = lane >= 32;
+                const u32x2 send = upper ? lo : hi;
+                const u32x2 got = u32x2{static_cast<uint32_t>(__shfl_xor(static_cast<int>(send[0]), 32, kWave)),
+                                        static_cast<uint32_t>(__shfl_xor(static_cast<int>(send[1]), 32, kWave))};
+                const u32x4 v = upper ? u32x4{got[0], got[1], hi[0], hi[1]} : u32x4{lo[0], lo[1], got[0], got[1]};
+                *reinterpret_cast<u32x4*>(Ob + 2 * (gcol + 8 * (upper ? 1 : 0))) = v;
                 if (lane < 32) Ob[2 * NOUT + gcol / 16] = static_cast<char>(ex);
               }
             }
