@@ -75,18 +75,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // exponent per 16 columns): one thread per 16-column group of the token, 32 bytes of values and its
 // exponent byte per slot row, eight rows' loads in flight. Each value is restored exactly
 // (fp16 * 2^exp) and then summed as in combine_kernel: fp32, slot order, then the shared term.
-template <bool kOutBf16>
+template <bool kOutBf16, int TPB>
 __global__ __launch_bounds__(256) void combine_f16s_kernel(CombineArgs a) {
-  __shared__ float s_w[512];
-  __shared__ int s_p[512];
-  const int64_t n = blockIdx.x;
-  const int G = a.D / 16, k = a.k, tid = threadIdx.x;
-  for (int j = tid; j < k; j += blockDim.x) {
-    const int p = a.slot_pos[n * k + j];
-    s_w[j] = p >= 0 ? a.weights[n * k + j] : 0.f;
-    s_p[j] = p;
+  __shared__ float s_w_all[TPB][512];
+  __shared__ int s_p_all[TPB][512];
+  // TPB tokens per workgroup, blockDim.x / TPB threads each
+  const int per = blockDim.x / TPB, sub = threadIdx.x / per;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * TPB + sub;
+  const int G = a.D / 16, k = a.k, tid = threadIdx.x - sub * per;
+  float* s_w = s_w_all[sub];
+  int* s_p = s_p_all[sub];
+  if (n < a.N) {
+    for (int j = tid; j < k; j += per) {
+      const int p = a.slot_pos[n * k + j];
+      s_w[j] = p >= 0 ? a.weights[n * k + j] : 0.f;
+      s_p[j] = p;
+    }
   }
   __syncthreads();
+  if (n >= a.N) return;
   const int64_t RB = f16s_row_bytes(a.D);
   const char* base = reinterpret_cast<const char*>(a.out_perm);
   const float s = a.shared_out ? (a.shared_scale ? a.shared_scale[n] : 1.0f) : 0.0f;
@@ -99,7 +106,7 @@ __global__ __launch_bounds__(256) void combine_f16s_kernel(CombineArgs a) {
         acc[8 * h + 2 * i + 1] = fmaf(w, f16_unscale(static_cast<uint16_t>(v[h][i] >> 16), ex), acc[8 * h + 2 * i + 1]);
       }
   };
-  for (int g = tid; g < G; g += blockDim.x) {
+  for (int g = tid; g < G; g += per) {
     float acc[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) acc[t] = 0.f;
@@ -153,11 +160,21 @@ __global__ __launch_bounds__(256) void combine_f16s_kernel(CombineArgs a) {
 void launch_combine(const CombineArgs& a, hipStream_t st) {
   const unsigned grid = static_cast<unsigned>(a.N);
   if (a.in_f16s) {
-    const unsigned block = static_cast<unsigned>(std::min(256, (a.D / 16 + 63) / 64 * 64));
-    if (a.out_bf16)
-      combine_f16s_kernel<true><<<grid, block, 0, st>>>(a);
-    else
-      combine_f16s_kernel<false><<<grid, block, 0, st>>>(a);
+    // a thread per 16-column group (up to 256 per token); two tokens per workgroup when a token
+    // needs at most 128 threads
+    const int per = std::min(256, (a.D / 16 + 63) / 64 * 64);
+    if (per <= 128) {
+      const unsigned grid2 = static_cast<unsigned>((a.N + 1) / 2);
+      if (a.out_bf16)
+        combine_f16s_kernel<true, 2><<<grid2, 2 * per, 0, st>>>(a);
+      else
+        combine_f16s_kernel<false, 2><<<grid2, 2 * per, 0, st>>>(a);
+    } else {
+      if (a.out_bf16)
+        combine_f16s_kernel<true, 1><<<grid, per, 0, st>>>(a);
+      else
+        combine_f16s_kernel<false, 1><<<grid, per, 0, st>>>(a);
+    }
     return;
   }
   if (a.out_bf16)
