@@ -503,7 +503,9 @@ def main():
     cfg = main_run["cfg"]
     packed = "true" if cfg.weight_layout else "false"
     streaming = shape.n_tokens * shape.top_k <= 64 * shape.n_experts
-    kname = (f"gemm_wstream_kernel<1,true,{packed},0>" if streaming
+    mean_rows = shape.n_tokens * shape.top_k // shape.n_experts          # 16-row slabs per pass: 1, 2 or 4
+    slabs = 1 if mean_rows <= 8 else 2 if mean_rows <= 20 else 4
+    kname = (f"gemm_wstream_kernel<{slabs},true,{packed},0>" if streaming
              else f"gemm_stream_kernel<2,4,4,2,true,{packed},0,false,false,true>")
     roof["kernel"] = kname + (" (grouped gate_up + SwiGLU, weight streaming)" if streaming else " (grouped gate_up + SwiGLU)")
     if args.workload == "prefill":

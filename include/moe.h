@@ -27,23 +27,24 @@
  *   down        [E, D, I]
  *   shared_gate_up [2I_s, D], shared_down [D, I_s], w_shared_gate [D]
  * dtype (moe_config.dtype) applies to x and every weight; routing outputs are always fp32
- * weights and int32 expert ids; intermediate expert outputs are fp32.
+ * weights and int32 expert ids; the per-assignment expert outputs are fp32 or an fp16 form (see
+ * "Expert outputs").
  *
- * Packed weights (moe_config.weight_layout = MOE_LAYOUT_PACKED): w_router (as a [1, E, D] stack),
- * gate_up, down, shared_gate_up and shared_down instead hold the output of moe_pack_weights, a
- * one-time rearrangement (at model load) of each [G, R, K] matrix into 16 x 32 blocks of 1 KB
- * stored in the order the matrix cores read them, so that every weight load is one contiguous
- * kilobyte. The values are the same; results are bitwise identical to the row layout. bf16 only,
- * with hidden, inter and shared_inter multiples of 128 and n_experts a multiple of 16.
- * w_shared_gate is a vector and keeps its layout.
+ * Packed weights (moe_config.weight_layout = MOE_LAYOUT_PACKED): gate_up, down, shared_gate_up,
+ * shared_down and, when n_experts is a multiple of 16, w_router (as a [1, E, D] stack) instead hold
+ * the output of moe_pack_weights, a one-time rearrangement (at model load) of each [G, R, K] matrix
+ * into 16 x 32 blocks of 1 KB stored in the order the matrix cores read them, so that every weight
+ * load is one contiguous kilobyte. With another n_experts, w_router keeps the row layout. The values
+ * are the same; results are bitwise identical to the row layout. bf16 only, with hidden, inter and
+ * shared_inter multiples of 128. w_shared_gate is a vector and keeps its layout.
  *
  * Quantised experts (moe_config.weight_layout = MOE_LAYOUT_Q8, MOE_LAYOUT_Q4 or MOE_LAYOUT_F8;
  * weight-only quantisation of the experts with the router kept in bf16: "Qwen3-VL-MoE" Keras port,
  * section "Lower memory"; "27. Mixture of experts", section "Dispatch" and stretch exercise 3;
  * "Qwen3-VL + MoE: train to deploy", the FP8 copy of the 30B model): gate_up,
  * down, shared_gate_up and shared_down each hold a quantised stack made by moe_quantize_weights
- * (with the same n_groups, rows and cols the expert entry points see), w_router is packed as for
- * MOE_LAYOUT_PACKED and w_shared_gate keeps its layout. Same shape rules as MOE_LAYOUT_PACKED. The
+ * (with the same n_groups, rows and cols the expert entry points see), w_router is packed (or not)
+ * as for MOE_LAYOUT_PACKED and w_shared_gate keeps its layout. Same shape rules as MOE_LAYOUT_PACKED. The
  * layer then computes with the weights code * scale (for FP8, the e4m3 value of the code times the
  * scale; for int4, code * group multiplier * row scale): the codes enter the matrix cores exactly
  * (as bf16) and each output column's fp32 sum is multiplied by its row's scale.

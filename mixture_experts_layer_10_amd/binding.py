@@ -74,9 +74,13 @@ def f16s_supported(cfg: MoeConfig) -> bool:
 
 
 def packable(cfg: MoeConfig) -> bool:
-    """Whether the packed weight layout applies (bf16, widths multiples of 128, E multiple of 16)."""
-    return (cfg.dtype == MOE_BF16 and cfg.hidden % 128 == 0 and cfg.inter % 128 == 0
-            and cfg.shared_inter % 128 == 0 and cfg.n_experts % 16 == 0)
+    """Whether the packed weight layout applies (bf16, widths multiples of 128)."""
+    return cfg.dtype == MOE_BF16 and cfg.hidden % 128 == 0 and cfg.inter % 128 == 0 and cfg.shared_inter % 128 == 0
+
+
+def router_packed(cfg: MoeConfig) -> bool:
+    """Whether a packed or quantised layout packs the router too (n_experts a multiple of 16)."""
+    return cfg.weight_layout != MOE_LAYOUT_ROWS and cfg.n_experts % 16 == 0
 
 
 _lib = None
@@ -318,12 +322,15 @@ def torch_dtype(code):
 
 
 def pack_device_weights(cfg: MoeConfig, dev: dict):
-    """A copy of ``dev`` whose weight matrices (router, gate_up, down and the shared pair) are in the
-    packed layout, made by moe_pack_weights (a one-time step, like loading the model)."""
+    """A copy of ``dev`` whose weight matrices (gate_up, down, the shared pair and, when E % 16 == 0,
+    the router) are in the packed layout, made by moe_pack_weights (a one-time step, like loading
+    the model)."""
     import torch
     D, E, I, Is = cfg.hidden, cfg.n_experts, cfg.inter, cfg.shared_inter
     out = dict(dev)
-    shapes = {"w_router": (1, E, D), "gate_up": (E, 2 * I, D), "down": (E, D, I)}
+    shapes = {"gate_up": (E, 2 * I, D), "down": (E, D, I)}
+    if router_packed(cfg):
+        shapes["w_router"] = (1, E, D)
     if Is:
         shapes.update(shared_gate_up=(1, 2 * Is, D), shared_down=(1, D, Is))
     for name, (g, r, c) in shapes.items():
@@ -336,14 +343,15 @@ def pack_device_weights(cfg: MoeConfig, dev: dict):
 
 def quantize_device_weights(cfg: MoeConfig, dev: dict):
     """A copy of ``dev`` (row layout) for a quantised ``cfg``: the router packed (bf16) by
-    moe_pack_weights, gate_up, down and the shared pair quantised by moe_quantize_weights into uint8
+    moe_pack_weights when E % 16 == 0, gate_up, down and the shared pair quantised by moe_quantize_weights into uint8
     buffers of moe_quantized_bytes() bytes (a one-time step, like loading the model)."""
     import torch
     D, E, I, Is = cfg.hidden, cfg.n_experts, cfg.inter, cfg.shared_inter
     out = dict(dev)
-    dst = torch.empty_like(dev["w_router"])
-    moe_pack_weights(cfg, 1, E, D, dev["w_router"], dst)
-    out["w_router"] = dst
+    if router_packed(cfg):
+        dst = torch.empty_like(dev["w_router"])
+        moe_pack_weights(cfg, 1, E, D, dev["w_router"], dst)
+        out["w_router"] = dst
     shapes = {"gate_up": (E, 2 * I, D), "down": (E, D, I)}
     if Is:
         shapes.update(shared_gate_up=(1, 2 * Is, D), shared_down=(1, D, Is))

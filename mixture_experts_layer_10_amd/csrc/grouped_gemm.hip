@@ -1267,7 +1267,7 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   constexpr int NS = kSwiGLU ? 2 : 1;        // weight blocks per column block (gate, up)
   constexpr int NB = CB * NS;                // weight blocks of 16 rows per task; block j: column
                                              // block j / NS, part j % NS
-  constexpr int U = 4;                       // k-steps per load batch (two batches in flight)
+  constexpr int U = (MB == 4 && !kQ) ? 2 : 4;   // k-steps per load batch (two batches in flight)
   const int lane = threadIdx.x & 63;
   const int K = kSwiGLU ? a.D : a.I;
   const int NOUT = kSwiGLU ? a.I : a.D;

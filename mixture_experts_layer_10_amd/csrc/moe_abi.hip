@@ -65,6 +65,8 @@ static int quant_kind(const moe_config* c) {
   }
 }
 static int quant_bits(const moe_config* c) { return code_bits(quant_kind(c)); }
+// The router's weights are packed (as a [1, E, D] stack) with the experts' when E % 16 == 0.
+static bool router_packed(const moe_config* c) { return c->weight_layout != MOE_LAYOUT_ROWS && c->n_experts % 16 == 0; }
 
 // Weight loads are 16 bytes wide (bf16 rows, packed blocks, quantised codes and scales).
 static int check_weight_align(const void* p, const char* name) {
@@ -98,8 +100,6 @@ static int validate_config(const moe_config* c) {
     if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights need dtype bf16");
     if (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128)
       return fail(MOE_ERR_UNSUPPORTED, "packed weights need hidden, inter and shared_inter multiples of 128");
-    if (c->n_experts % 16)
-      return fail(MOE_ERR_UNSUPPORTED, "packed weights need n_experts = %lld to be a multiple of 16", (long long)c->n_experts);
   }
   if (c->expert_out != MOE_EXPERT_OUT_F32 && c->expert_out != MOE_EXPERT_OUT_F16S)
     return fail(MOE_ERR_INVALID_ARG, "expert_out = %d (must be 0 or 1)", c->expert_out);
@@ -193,7 +193,8 @@ static RouteArgs route_args(const moe_config* c, const void* x, const void* w_ro
   a.k = static_cast<int>(c->top_k);
   a.norm = c->norm_topk_prob;
   a.bf16 = c->dtype == MOE_BF16;
-  a.packed = c->weight_layout != MOE_LAYOUT_ROWS;     // quantised layouts keep a packed bf16 router
+  // packed and quantised layouts keep a packed bf16 router when E is a multiple of 16, else rows
+  a.packed = router_packed(c);
   return a;
 }
 

@@ -79,6 +79,7 @@ PACKED_SHAPES = {
     "small": I.custom_shape("small_packed", 5, 256, 32, 2, 128, seed=31),
     "xs_e208": I.custom_shape("xs_e208", 8200, 512, 208, 6, 128, seed=32),     # x-stationary, E > 128
     "xs_e48": I.custom_shape("xs_e48", 8193, 1024, 48, 4, 256, seed=33),       # x-stationary 16x16, ragged
+    "e12": I.custom_shape("e12_packed", 300, 256, 12, 3, 128, shared_inter=256, seed=35),   # router in rows
 }
 
 
@@ -122,8 +123,9 @@ def test_packed_router_equals_rows(name, with_ws):
     compare_routing(to_np(w1).astype(np.float64), to_np(e1), w_ref, e_ref, probs, s.top_k)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "fanout", "small", "xs_e208"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "fanout", "small", "xs_e208", "keras", "e12"])
 def test_packed_forward_equals_rows(name):
+    # keras (E = 60) and e12: packed experts with the router in rows (E not a multiple of 16)
     say(f"[packed forward] {name}")
     d, dev = packed_data(name)
     s = d.shape
