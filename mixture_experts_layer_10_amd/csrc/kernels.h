@@ -24,6 +24,9 @@ struct RouteArgs {
 };
 constexpr int kMaxRouteSlices = 16;
 int route_slices_for(int64_t N, int D, int E, bool bf16);   // slices used when scratch is given
+// fp32 scratch the router uses when given a workspace: the split contraction's partial logits, or
+// the logits of the dense-product router for long batches with E > 128 (0: none)
+int64_t route_scratch_floats(int64_t N, int D, int E, bool bf16);
 int route_slices(const RouteArgs& a);
 void launch_route(const RouteArgs& a, hipStream_t st);
 

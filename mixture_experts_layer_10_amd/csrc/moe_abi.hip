@@ -119,9 +119,8 @@ static int validate_config(const moe_config* c) {
 
 // Scratch of a split router contraction: slices x N x E fp32 (0 when it runs in one pass).
 static size_t route_partial_bytes(const moe_config* c) {
-  const int slices = route_slices_for(c->n_tokens, static_cast<int>(c->hidden), static_cast<int>(c->n_experts),
-                                      c->dtype == MOE_BF16);
-  return slices > 1 ? static_cast<size_t>(slices) * static_cast<size_t>(c->n_tokens) * static_cast<size_t>(c->n_experts) * 4 : 0;
+  return static_cast<size_t>(route_scratch_floats(c->n_tokens, static_cast<int>(c->hidden), static_cast<int>(c->n_experts),
+                                                  c->dtype == MOE_BF16)) * 4;
 }
 
 struct Layout {

@@ -860,10 +860,39 @@ int route_slices_for(int64_t N, int D, int E, bool bf16) {
 
 int route_slices(const RouteArgs& a) { return a.partial ? route_slices_for(a.N, a.D, a.E, a.bf16) : 1; }
 
+// Long batches with many experts (the x-stationary range, E > 128): the logits are one dense
+// product x W_r^T on the matrix cores (the grouped GEMM's down form with one group: K = D, output
+// width E, fp32), written to the scratch and read back by the selection (route_finish_kernel with
+// one slice). Each x-stationary workgroup would read all of W_r from L2 (N / 32 times 2 E D bytes);
+// 256 x 256 tiles read it N / 256 times and keep the matrix cores fed.
+static bool route_gemm_ok(int64_t N, int D, int E, bool bf16) { return route_xs_ok(N, D, bf16) && E > 128; }
+
+int64_t route_scratch_floats(int64_t N, int D, int E, bool bf16) {
+  if (route_gemm_ok(N, D, E, bf16)) return N * E;
+  const int slices = route_slices_for(N, D, E, bf16);
+  return slices > 1 ? slices * N * E : 0;
+}
+
 template <int EP, bool kPW>
 static void launch_route_bf16(const RouteArgs& a, hipStream_t st) {
   const unsigned grid = static_cast<unsigned>((a.N + kRtTok - 1) / kRtTok);
   const int slices = route_slices(a);
+  if (a.partial && route_gemm_ok(a.N, a.D, a.E, a.bf16)) {
+    GemmArgs g{};
+    g.x = a.x;
+    g.w = a.w_router;
+    g.out = a.partial;
+    g.max_rows = a.N;
+    g.G = 1;
+    g.D = a.E;                              // output width
+    g.I = a.D;                              // contraction
+    g.bf16 = true;
+    g.packed = kPW;
+    launch_down(g, st);
+    constexpr int TOK = EP <= 2 ? 16 : 4;
+    route_finish_kernel<EP, TOK, 1><<<static_cast<unsigned>((a.N + TOK - 1) / TOK), kRouteThreads, 0, st>>>(a, 1);
+    return;
+  }
   if (route_xs_ok(a.N, a.D, a.bf16)) {
     if (EP == 1 && a.k <= 8)
       route_xs16_kernel<8, kPW><<<grid, kXsThreads, 0, st>>>(a);
