@@ -1257,13 +1257,17 @@ __device__ __forceinline__ u32x4 to_bf16_frag(typename WRaw<kQ>::T v) {
 // as many matrix-core steps (one block for MB = 4, whose accumulators would not fit the registers
 // otherwise). Measured on the 64-token decode layer: two blocks beat one (int8 and int4) and four
 // (int4, whose registers then allow one wave per SIMD only).
-template <int kQ, int MB> constexpr int wstream_cols() { return kQ && MB < 4 ? 2 : 1; }
+// bf16 down with four slabs: two blocks, so that each activation fragment (h rows, re-read by every
+// task of the expert) feeds twice the steps.
+template <int kQ, int MB, bool kSwiGLU> constexpr int wstream_cols() {
+  return (kQ && MB < 4) || (!kQ && MB == 4 && !kSwiGLU) ? 2 : 1;
+}
 
 template <int MB, bool kSwiGLU, bool kPacked, int kQ>
 __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
   typedef typename WRaw<kQ>::T Raw;
-  constexpr int CB = wstream_cols<kQ, MB>(); // column blocks per task
+  constexpr int CB = wstream_cols<kQ, MB, kSwiGLU>(); // column blocks per task
   constexpr int NS = kSwiGLU ? 2 : 1;        // weight blocks per column block (gate, up)
   constexpr int NB = CB * NS;                // weight blocks of 16 rows per task; block j: column
                                              // block j / NS, part j % NS
@@ -1477,11 +1481,11 @@ static void launch_wstream(const GemmArgs& a, hipStream_t st) {
   auto grid = [&](int cb) { return static_cast<unsigned>((a.G * ((ncb + cb - 1) / cb) + 3) / 4); };
   const int64_t mean_rows = a.offsets ? a.max_rows / std::max(a.G, 1) : a.max_rows;
   if (mean_rows <= 8)
-    gemm_wstream_kernel<1, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 1>()), 256, 0, st>>>(a);
+    gemm_wstream_kernel<1, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 1, kSwiGLU>()), 256, 0, st>>>(a);
   else if (mean_rows <= 20)
-    gemm_wstream_kernel<2, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 2>()), 256, 0, st>>>(a);
+    gemm_wstream_kernel<2, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 2, kSwiGLU>()), 256, 0, st>>>(a);
   else
-    gemm_wstream_kernel<4, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 4>()), 256, 0, st>>>(a);
+    gemm_wstream_kernel<4, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 4, kSwiGLU>()), 256, 0, st>>>(a);
 }
 
 // ---------------------------------------------------------------------------------------------
