@@ -37,6 +37,10 @@ static int check_launch(const char* what) {
   return MOE_OK;
 }
 
+static int hip_ok(hipError_t e, const char* what) {
+  return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
 int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -453,6 +457,35 @@ static int noalloc_scratch(void** out) {
   }
   *out = g_scratch_ptr[dev];
   return MOE_OK;
+}
+
+// A second stream per device for the shared expert, which reads x and its own weights only: it
+// runs beside the router, the permutation and the routed products (whose launches leave CUs free:
+// the dense-product router fills 64 of them for 8,192 tokens and 512 experts) and is joined before
+// the combine. Created on a device's first such call, default priority, never destroyed. The
+// mutex keeps each call's fork, side launches and join together, so calls from several host
+// threads on one device queue their shared-expert work one after another on the side stream.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;
+};
+static std::mutex g_side_mu[kMaxDevices];
+static SideStream g_side[kMaxDevices];
+
+// The device's side stream, or nullptr where none can be made (then the caller stays on its stream).
+static SideStream* side_stream_locked(int dev) {
+  SideStream& s = g_side[dev];
+  if (!s.tried) {
+    s.tried = true;
+    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      s.stream = nullptr;
+    }
+  }
+  return s.stream ? &s : nullptr;
 }
 
 }  // namespace moe
@@ -883,9 +916,11 @@ static int forward_checks(const moe_config* cfg, const void* x, const void* w_ro
 }
 
 // The block on a checked, large-enough, 256-byte aligned workspace.
+// fork: the shared expert may run on the device's side stream (not for moe_forward_noalloc, which
+// creates nothing).
 static int forward_impl(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up, const void* down,
                         const void* shared_gate_up, const void* shared_down, const void* w_shared_gate, void* y,
-                        float* weights_out, int32_t* experts_out, void* ws, void* stream) {
+                        float* weights_out, int32_t* experts_out, void* ws, void* stream, bool fork) {
   const Layout L = layout_of(cfg);
   char* base = static_cast<char*>(ws);
   float* weights = weights_out ? weights_out : reinterpret_cast<float*>(base + L.weights);
@@ -900,6 +935,31 @@ static int forward_impl(const moe_config* cfg, const void* x, const void* w_rout
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t A = cfg->n_tokens * cfg->top_k;
 
+  // the shared expert first: on the side stream where there is one (fork), else ahead on st
+  float* sh_out = nullptr;
+  SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  if (cfg->shared_inter > 0) {
+    void* sh_h = base + L.sh_h;
+    sh_out = reinterpret_cast<float*>(base + L.sh_out);
+    hipStream_t ss = st;
+    int dev = -1;
+    if (fork && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+      side_lock = std::unique_lock<std::mutex>(g_side_mu[dev]);
+      side = side_stream_locked(dev);
+      if (side) {
+        MOE_TRY(hip_ok(hipEventRecord(side->fork, st), "moe_forward (fork of the shared expert)"));
+        MOE_TRY(hip_ok(hipStreamWaitEvent(side->stream, side->fork, 0), "moe_forward (fork of the shared expert)"));
+        ss = side->stream;
+      }
+    }
+    launch_gate_up(gemm_args(cfg, 1, cfg->shared_inter, cfg->n_tokens, x, nullptr, nullptr, shared_gate_up, sh_h), ss);
+    MOE_TRY(check_launch("moe_forward (shared gate_up)"));
+    launch_down(gemm_args(cfg, 1, cfg->shared_inter, cfg->n_tokens, sh_h, nullptr, nullptr, shared_down, sh_out), ss);
+    MOE_TRY(check_launch("moe_forward (shared down)"));
+    if (side) MOE_TRY(hip_ok(hipEventRecord(side->join, ss), "moe_forward (join of the shared expert)"));
+  }
+
   float* partial = L.route_partial == L.block_counts ? nullptr : reinterpret_cast<float*>(base + L.route_partial);
   MOE_TRY(route_impl(cfg, x, w_router, shared_scale ? w_shared_gate : nullptr, nullptr, weights, experts, shared_scale,
                      route_partial_bytes(cfg) ? partial : nullptr, st));
@@ -909,15 +969,7 @@ static int forward_impl(const moe_config* cfg, const void* x, const void* w_rout
   MOE_TRY(check_launch("moe_forward (gate_up)"));
   launch_down(gemm_args(cfg, cfg->n_experts, cfg->inter, A, h, nullptr, offsets, down, out), st);
   MOE_TRY(check_launch("moe_forward (down)"));
-  float* sh_out = nullptr;
-  if (cfg->shared_inter > 0) {
-    void* sh_h = base + L.sh_h;
-    sh_out = reinterpret_cast<float*>(base + L.sh_out);
-    launch_gate_up(gemm_args(cfg, 1, cfg->shared_inter, cfg->n_tokens, x, nullptr, nullptr, shared_gate_up, sh_h), st);
-    MOE_TRY(check_launch("moe_forward (shared gate_up)"));
-    launch_down(gemm_args(cfg, 1, cfg->shared_inter, cfg->n_tokens, sh_h, nullptr, nullptr, shared_down, sh_out), st);
-    MOE_TRY(check_launch("moe_forward (shared down)"));
-  }
+  if (side) MOE_TRY(hip_ok(hipStreamWaitEvent(st, side->join, 0), "moe_forward (join of the shared expert)"));
   MOE_TRY(combine_impl(cfg, out, weights, slot_pos, sh_out, shared_scale, y, st));
   return ok();
 }
@@ -932,7 +984,7 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
   if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes at %p, need %zu", ws_bytes, ws, need);
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MOE_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
   return forward_impl(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_shared_gate, y, weights_out,
-                      experts_out, ws, stream);
+                      experts_out, ws, stream, true);
 }
 
 int moe_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router, const void* gate_up,
@@ -948,7 +1000,7 @@ int moe_forward_noalloc(const moe_config* cfg, const void* x, const void* w_rout
   void* ws = nullptr;
   MOE_TRY(noalloc_scratch(&ws));
   return forward_impl(cfg, x, w_router, gate_up, down, shared_gate_up, shared_down, w_shared_gate, y, weights_out,
-                      experts_out, ws, stream);
+                      experts_out, ws, stream, false);
 }
 
 }  // extern "C"
