@@ -390,6 +390,16 @@ __device__ __forceinline__ void dispatch_live(int live, F&& f) {
   }
 }
 
+// Byte offsets in a wave's 2 KB epilogue staging. A row's 16-byte chunks are rotated by an XOR with
+// bits of the row, so that the 16 lanes writing one chunk of 16 consecutive rows hit 16 distinct
+// 16-byte bank slots of a 256-byte window (unrotated, rows 128 or 64 bytes apart fall on 2 or 4
+// slots: an 8- or 4-way bank conflict on every staging write); a row's chunks stay within it, so
+// reads of whole consecutive rows stay conflict-free.
+// fp16 form: 16 rows x 128 bytes, chunk c (0-7) of row r.
+__device__ __forceinline__ int stage_f16s_at(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// h: 32 rows x 64 bytes, chunk c (0-3) of row r.
+__device__ __forceinline__ int stage_h_at(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
 template <int WM, int TM, int WN, int TN, bool kSwiGLU, bool kPacked, int kQ = 0, bool kWKN = false, bool kBwd = false,
           bool kPipe = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
@@ -994,13 +1004,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                   for (int g = 0; g < 2; ++g)
-                    *reinterpret_cast<u32x4*>(st + (r32 & 15) * 128 + 64 * j + 32 * g + 16 * hf) = run[j][g];
+                    *reinterpret_cast<u32x4*>(st + stage_f16s_at(r32 & 15, 4 * j + 2 * g + hf)) = run[j][g];
               }
 #pragma unroll
               for (int it = 0; it < 2; ++it) {
                 const int off = it * 1024 + lane * 16;
                 const int r = rb + 16 * ph + (off >> 7);
-                const u32x4 v = *reinterpret_cast<const u32x4*>(st + off);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(st + stage_f16s_at(off >> 7, (off >> 4) & 7));
                 if (r < rows) *reinterpret_cast<u32x4*>(O + (row0 + r) * RB + 2 * wcol + (off & 127)) = v;
               }
             }
@@ -1028,14 +1038,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_stream_kernel(GemmArgs a) {
               uint16_t v[4];
 #pragma unroll
               for (int t = 0; t < 4; ++t) v[t] = f32_to_bf16(silu(acc[i][0][4 * q + t]) * acc[i][1][4 * q + t]);
-              *reinterpret_cast<u32x2*>(st + r32 * 64 + 16 * q + 8 * hf) =
+              *reinterpret_cast<u32x2*>(st + stage_h_at(r32, q) + 8 * hf) =
                   u32x2{v[0] | (static_cast<uint32_t>(v[1]) << 16), v[2] | (static_cast<uint32_t>(v[3]) << 16)};
             }
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
               const int off = it * 1024 + lane * 16;
               const int r = rb + (off >> 6);
-              const u32x4 v = *reinterpret_cast<const u32x4*>(st + off);
+              const u32x4 v = *reinterpret_cast<const u32x4*>(st + stage_h_at(off >> 6, (off >> 4) & 3));
               if (r < rows)
                 *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(Hh + (row0 + r) * NOUT + wcol) + (off & 63)) = v;
             }
