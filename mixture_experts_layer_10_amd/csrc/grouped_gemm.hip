@@ -1275,7 +1275,7 @@ template <int kQ, int MB, bool kSwiGLU> constexpr int wstream_cols() {
 }
 
 template <int MB, bool kSwiGLU, bool kPacked, int kQ>
-__global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
+__device__ __forceinline__ void wstream_body(const GemmArgs& a) {
   static_assert(kQ == 0 || kPacked, "quantised weights use the packed block order");
   typedef typename WRaw<kQ>::T Raw;
   constexpr int CB = wstream_cols<kQ, MB, kSwiGLU>(); // column blocks per task
@@ -1485,6 +1485,19 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
   }
 }
 
+template <int MB, bool kSwiGLU, bool kPacked, int kQ>
+__global__ __launch_bounds__(256) void gemm_wstream_kernel(GemmArgs a) {
+  wstream_body<MB, kSwiGLU, kPacked, kQ>(a);
+}
+
+// The four-slab bf16 gate_up form at two waves per SIMD: left to itself the compiler gives it 284
+// registers (one wave per SIMD); it fits 256 without spills, and a second wave keeps more weight
+// loads in flight.
+template <bool kPacked>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_wstream2_kernel(GemmArgs a) {
+  wstream_body<4, true, kPacked, 0>(a);
+}
+
 template <bool kSwiGLU, bool kPacked, int kQ = 0>
 static void launch_wstream(const GemmArgs& a, hipStream_t st) {
   const int NOUT = kSwiGLU ? a.I : a.D;
@@ -1495,6 +1508,8 @@ static void launch_wstream(const GemmArgs& a, hipStream_t st) {
     gemm_wstream_kernel<1, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 1, kSwiGLU>()), 256, 0, st>>>(a);
   else if (mean_rows <= 20)
     gemm_wstream_kernel<2, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 2, kSwiGLU>()), 256, 0, st>>>(a);
+  else if constexpr (kSwiGLU && kQ == 0)
+    gemm_wstream2_kernel<kPacked><<<grid(wstream_cols<kQ, 4, kSwiGLU>()), 256, 0, st>>>(a);
   else
     gemm_wstream_kernel<4, kSwiGLU, kPacked, kQ><<<grid(wstream_cols<kQ, 4, kSwiGLU>()), 256, 0, st>>>(a);
 }
