@@ -1,7 +1,6 @@
 // The grouping of a small batch (at most kPermSmallMax assignments) by one workgroup of 512
 // threads: histogram, scan and stable scatter ("27. Mixture of experts", section "Dispatch", grouped
-// dispatch steps 1-2), with ranks from ordered ballots and per-wave counts (deterministic). Shared by
-// the permutation's own kernel and the router kernel that also groups decode-size batches.
+// dispatch steps 1-2), with ranks from ordered ballots and per-wave counts (deterministic).
 #pragma once
 
 #include "common.h"
@@ -19,14 +18,22 @@ __device__ __forceinline__ void perm_block512(const PermuteArgs& a, int nbits) {
   __shared__ int s_wave[8];
   const int E = a.E, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t A = a.A;
+  // the batch's expert ids, all loads issued at once (A <= kPermSmallMax: 16 per thread), used by
+  // the count and by the scatter
+  constexpr int RND = kPermSmallMax / 512;
+  int ev[RND];
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int64_t i = static_cast<int64_t>(r) * 512 + tid;
+    ev[r] = i < A ? a.experts[i] : -1;
+  }
   if (tid < E) s_pos[tid] = 0;
   for (int w = 0; w < 8; ++w)
     if (tid < E) s_wcnt[w][tid] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < A; i += 512) {
-    const int e = a.experts[i];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&s_pos[e], 1);
-  }
+#pragma unroll
+  for (int r = 0; r < RND; ++r)
+    if (static_cast<unsigned>(ev[r]) < static_cast<unsigned>(E)) atomicAdd(&s_pos[ev[r]], 1);
   __syncthreads();
   const int total = tid < E ? static_cast<int>(min<int64_t>(s_pos[tid], a.capacity)) : 0;   // kept rows
   int inc = total;
@@ -49,9 +56,12 @@ __device__ __forceinline__ void perm_block512(const PermuteArgs& a, int nbits) {
   if (tid == E - 1) a.offsets[E] = excl + total;
   __syncthreads();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = 0; base < A; base += 512) {
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int64_t base = static_cast<int64_t>(r) * 512;
+    if (base >= A) break;                     // uniform
     const int64_t i = base + tid;
-    const int e_in = i < A ? a.experts[i] : 0;
+    const int e_in = i < A ? ev[r] : 0;
     const bool in_range = static_cast<unsigned>(e_in) < static_cast<unsigned>(E);
     const bool valid = i < A && in_range;
     const int e = valid ? e_in : 0;

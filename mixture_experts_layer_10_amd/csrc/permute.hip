@@ -19,6 +19,8 @@
 namespace moe {
 
 constexpr int kPermThreads = 256;
+constexpr int kPermRounds = kPermChunk / kPermThreads;   // assignments per thread and chunk
+static_assert(kPermRounds * kPermThreads == kPermChunk, "a chunk is whole rounds");
 
 int64_t permute_chunks(int64_t A) { return (A + kPermChunk - 1) / kPermChunk; }
 
@@ -30,10 +32,16 @@ __global__ __launch_bounds__(kPermThreads) void perm_count_kernel(PermuteArgs a)
   __syncthreads();
   const int64_t lo = static_cast<int64_t>(blockIdx.x) * kPermChunk;
   const int64_t hi = min<int64_t>(lo + kPermChunk, a.A);
-  for (int64_t i = lo + threadIdx.x; i < hi; i += kPermThreads) {
-    const int e = a.experts[i];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&s_cnt[e], 1);
+  // every load of the chunk issued before the first count (one memory latency, not one per round)
+  int ev[kPermRounds];
+#pragma unroll
+  for (int r = 0; r < kPermRounds; ++r) {
+    const int64_t i = lo + r * kPermThreads + threadIdx.x;
+    ev[r] = i < hi ? a.experts[i] : -1;
   }
+#pragma unroll
+  for (int r = 0; r < kPermRounds; ++r)
+    if (static_cast<unsigned>(ev[r]) < static_cast<unsigned>(E)) atomicAdd(&s_cnt[ev[r]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPermThreads) a.block_counts[blockIdx.x * static_cast<int64_t>(E) + e] = s_cnt[e];
 }
@@ -124,9 +132,19 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(PermuteArgs 
   const int64_t lo = static_cast<int64_t>(blockIdx.x) * kPermChunk;
   const int64_t hi = min<int64_t>(lo + kPermChunk, a.A);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = lo; base < hi; base += kPermThreads) {
+  // the chunk's expert ids, all loads issued before the first round
+  int ev[kPermRounds];
+#pragma unroll
+  for (int r = 0; r < kPermRounds; ++r) {
+    const int64_t i = lo + r * kPermThreads + tid;
+    ev[r] = i < hi ? a.experts[i] : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < kPermRounds; ++r) {
+    const int64_t base = lo + r * kPermThreads;
+    if (base >= hi) break;                    // uniform: the chunk's last round is done
     const int64_t i = base + tid;
-    const int e_in = i < hi ? a.experts[i] : 0;
+    const int e_in = ev[r];
     const bool in_range = static_cast<unsigned>(e_in) < static_cast<unsigned>(E);
     const bool valid = i < hi && in_range;
     const int e = valid ? e_in : 0;
