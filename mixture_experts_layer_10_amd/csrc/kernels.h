@@ -31,7 +31,7 @@ int route_slices(const RouteArgs& a);
 void launch_route(const RouteArgs& a, hipStream_t st);
 
 // Permutation: assignments are processed in chunks of kPermChunk by one workgroup each.
-constexpr int kPermChunk = 2048;
+constexpr int kPermChunk = 1024;
 struct PermuteArgs {
   const int32_t* experts;   // [A]
   int32_t* block_counts;    // [n_chunks * E] workspace

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_count_kernel(PermuteArgs a)
 // Pass 2 (one workgroup of 512 threads, one expert per thread): counts, offsets, and each chunk's
 // starting row for each expert (written back over block_counts). With at most kScanRegs chunks a
 // thread holds its expert's whole column in registers: one round of loads, one round of stores.
-constexpr int kScanRegs = 64;
+constexpr int kScanRegs = 128;
 
 template <bool kInRegs>
 __global__ __launch_bounds__(512) void perm_scan_kernel(PermuteArgs a, int n_chunks) {
