@@ -165,16 +165,6 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 #endif
 }
 
-// dma16 with the non-temporal hint: for data read once (it enters L2 with the lowest priority, so a
-// stream of it does not evict lines that other workgroups still reuse).
-__device__ __forceinline__ void dma16_nt(const void* src, const void* lds_dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const void*)lds_dst));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(base) : "memory");
-#endif
-}
-
 // dma16 from a uniform base (SGPRs) plus this lane's 32-bit byte offset: one VGPR per source
 // instead of a 64-bit address.
 __device__ __forceinline__ void dma16_sv(const void* base, uint32_t voff, const void* lds_dst) {

@@ -604,7 +604,7 @@ __global__ __launch_bounds__(kXsThreads) void route_xs_kernel(RouteArgs a) {
   for (int i = wave; i < kRtTok * IPR; i += kXsThreads / 64) {
     const int r = i / IPR, q = i - r * IPR;
     const int64_t n = min<int64_t>(n0 + r, a.N - 1);
-    dma16_nt(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
+    dma16(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
   }
   // weight rows of this wave's blocks; lane: row lane % 32, k-group lane / 32; k from kh * D / 2
   const int ks0 = kh * (D / 32);                            // first 16-wide k-step of this half
@@ -709,7 +709,7 @@ __global__ __launch_bounds__(kXsThreads) void route_xs16_kernel(RouteArgs a) {
   for (int i = wave; i < kRtTok * IPR; i += kXsThreads / 64) {
     const int r = i / IPR, q = i - r * IPR;
     const int64_t n = min<int64_t>(n0 + r, a.N - 1);
-    dma16_nt(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
+    dma16(x + n * D + (64 * q + (lane ^ (r & 15))) * 8, sX + r * D + q * 512);
   }
   const bool active = wave * 16 < E;                        // uniform
   // packed weights: block (wave, s) is this wave's 16 rows at k-step s, 1 KB in lane order
