@@ -137,8 +137,10 @@ def run_permute(cfg, experts_np, x=None):
     return counts, offsets, token_of, slot_pos, x_perm
 
 
+# one-workgroup grouping (A <= 8192), chunked grouping with a ragged last chunk, and more chunks than
+# the scan holds in registers (17,000 x 8 = 136,000 assignments: 133 chunks of 1,024)
 @pytest.mark.parametrize("N,k,E,seed", [(1, 1, 1, 0), (37, 3, 7, 1), (5000, 8, 128, 2), (2049, 10, 512, 3),
-                                        (4096, 2, 8, 4), (300, 6, 300, 5), (64, 8, 128, 6)])
+                                        (4096, 2, 8, 4), (300, 6, 300, 5), (64, 8, 128, 6), (17000, 8, 128, 9)])
 def test_permute_bit_exact(N, k, E, seed):
     say(f"[permute] N={N} k={k} E={E}")
     cfg = B.make_config(N, 64, E, k, 64)
