@@ -259,7 +259,8 @@ int moe_quantize_weights(const moe_config* cfg, int64_t n_groups, int64_t rows, 
  * moe_forward call). bf16 layers: matrix-core inputs are bf16 (h, w dy, da, db and dlogits rounded
  * once), accumulation fp32. fp32 layers: every intermediate stays fp32 (FMA weight-gradient kernel).
  * The sums over an expert's rows run in row order, deterministic.
- *   cfg: dtype bf16 or fp32, weight_layout MOE_LAYOUT_ROWS (else MOE_ERR_UNSUPPORTED)
+ *   cfg: dtype bf16 or fp32, weight_layout MOE_LAYOUT_ROWS (else MOE_ERR_UNSUPPORTED); expert_out
+ *     does not matter here (the backward's intermediates are its own, fp32 rows)
  *   x [N, D], w_router [E, D], gate_up [E, 2I, D], down [E, D, I], dy [N, D]   (cfg.dtype, row-major)
  *   shared_gate_up [2I_s, D], shared_down [D, I_s], w_shared_gate [D] (cfg.dtype): as moe_forward
  *     (required iff shared_inter > 0; w_shared_gate may be NULL: ungated)

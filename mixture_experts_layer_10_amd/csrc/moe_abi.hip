@@ -789,6 +789,7 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
   }
   moe_config c32 = *cfg;
   c32.out_dtype = MOE_F32;
+  c32.expert_out = MOE_EXPERT_OUT_F32;          // dx rows are fp32 whatever form the forward keeps
   MOE_TRY(combine_impl(&c32, F(L.dx_rows), F(L.ones), I32(L.slot_pos), F(L.dxr), nullptr, dx, st));
   // weight gradients over each expert's rows (bf16 with D, I multiples of 8: read in place;
   // otherwise through padded transposes), then over the tokens for W_r

@@ -118,3 +118,20 @@ def test_backward_deterministic():
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), k
+
+
+@pytest.mark.parametrize("name", ["small", "shared_gated"])
+def test_backward_ignores_expert_output_form(name):
+    """The backward keeps its own fp32 intermediates: a config whose forward keeps expert outputs in
+    the fp16 form gives bitwise the gradients of the fp32 form (the combine of the dx rows reads
+    fp32 rows either way)."""
+    say(f"[backward] {name}, fp16-form config")
+    d = I.make_inputs(SHAPES[name])
+    dev = B.to_device(d.store)
+    cfg = B.config_for(d.shape)
+    dy = bf16_dev(np.random.default_rng(4).standard_normal((d.shape.n_tokens, d.shape.hidden)))
+    a = B.backward(cfg, dev, dy)
+    b = B.backward(cfg.copy(expert_out=B.MOE_EXPERT_OUT_F16S), dev, dy)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), k
